@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for the Hadamard-rotated INT8 linear layer.
+
+This module holds only input generation (random draws and their rounding to
+bfloat16).  None of the layer's arithmetic is here, so the GPU path, the CPU
+oracle, the tests and the benchmark can all read the same bytes from it.
+
+Workload model.  The pages measure real diffusion transformers, which are not
+available here; these inputs stand in for them:
+  * activations are N(0, 1) with a few "outlier" input channels scaled by 20,
+    following the observation that activations concentrate their energy in a
+    few input channels (SD.Next dev-branch commit log, the LoRA svd-calibration
+    commit) and the extreme-activation stress rows of the benchmark commits;
+  * weights are N(0, 0.02); LoRA factors N(0, 0.01); the upstream gradient of
+    the PEFT step is N(0, 1e-3);
+  * the 3072 x 3072 shape is the flux.1 attention linear named in the same
+    commit log's benchmark shape list.
+N(0, s) means standard deviation s.  "1 % of channels" means round(0.01 * K)
+channels picked by a seeded permutation, scaled before the bf16 rounding.
+Every config draws from one ``numpy.random.default_rng(seed)`` in a fixed order.
+
+bf16 tensors are returned as ``numpy.uint16`` arrays of raw bfloat16 bits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """binary32 -> bfloat16 bits, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = 0x7FFF + ((u >> 16) & 1)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bits -> binary32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def gaussian(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+
+
+def outlier_activations(rng: np.random.Generator, m: int, k: int, channels=None,
+                        frac: float = 0.01, factor: float = 20.0) -> np.ndarray:
+    """x ~ N(0, 1) [m, k] (binary32) with some input channels scaled by ``factor``.
+    ``channels`` fixes them; otherwise round(frac * k) channels come from a seeded
+    permutation drawn right after x."""
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    if channels is None:
+        count = int(round(frac * k))
+        channels = np.sort(rng.permutation(k)[:count])
+    x[:, np.asarray(channels, dtype=np.int64)] *= np.float32(factor)
+    return x
+
+
+@dataclass(frozen=True)
+class LinearConfig:
+    """One workload: activation rows m, in-features k, out-features n."""
+    name: str
+    m: int
+    k: int
+    n: int
+    groups: tuple = (256,)
+    lora_rank: int = 0
+    lora_alpha: float = 0.0
+    backward: bool = False
+    outlier_channels: tuple | None = None
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def lora_scale(self) -> float:
+        return self.lora_alpha / self.lora_rank if self.lora_rank else 0.0
+
+
+# The five workloads of the layer.  "mlp" is two layers: up (k=3840 -> n=10240)
+# and down (k=10240 -> n=3840) on a synthetic hidden activation h.
+CONFIGS = {
+    "tiny": LinearConfig("tiny", 64, 512, 512, outlier_channels=(7, 300),
+                         note="x [64,512] N(0,1), channels 7 and 300 x20; W [512,512] N(0,0.02)"),
+    "attn": LinearConfig("attn", 4096, 3072, 3072,
+                         note="attention projection: x [4096,3072], W [3072,3072]"),
+    "mlp_up": LinearConfig("mlp_up", 4096, 3840, 10240, note="MLP up: x [4096,3840], W [10240,3840]"),
+    "mlp_down": LinearConfig("mlp_down", 4096, 10240, 3840, note="MLP down: h [4096,10240], W [3840,10240]"),
+    "quarot": LinearConfig("quarot", 8192, 3072, 3072, groups=(64, 128), lora_rank=32, lora_alpha=32.0,
+                           note="QuaRot-style blocks + LoRA r=32: x [8192,3072], W [3072,3072]"),
+    "peft": LinearConfig("peft", 16384, 3072, 3072, lora_rank=64, lora_alpha=32.0, backward=True,
+                         note="PEFT step: x, dY [16384,3072], W [3072,3072], LoRA r=64"),
+}
+
+
+def make_linear(m: int, k: int, n: int, seed: int = 0, outlier_channels=None, lora_rank: int = 0,
+                backward: bool = False, dy_std: float = 1e-3) -> dict:
+    """Inputs for one linear layer, drawn in the order x, W, [A, B], [dY]."""
+    rng = np.random.default_rng(seed)
+    out = {"x": to_bf16_bits(outlier_activations(rng, m, k, outlier_channels)),
+           "w": to_bf16_bits(gaussian(rng, (n, k), 0.02))}
+    if lora_rank:
+        out["lora_a"] = to_bf16_bits(gaussian(rng, (k, lora_rank), 0.01))
+        out["lora_b"] = to_bf16_bits(gaussian(rng, (lora_rank, n), 0.01))
+    if backward:
+        out["dy"] = to_bf16_bits(gaussian(rng, (m, n), dy_std))
+    return out
+
+
+def make_config(name: str, seed: int = 0) -> dict:
+    """Inputs of a named workload.  For the MLP pair both layers come from one
+    stream: x, W_up, h, W_down."""
+    if name in ("mlp", "mlp_up", "mlp_down"):
+        rng = np.random.default_rng(seed)
+        up, down = CONFIGS["mlp_up"], CONFIGS["mlp_down"]
+        x = to_bf16_bits(outlier_activations(rng, up.m, up.k))
+        w_up = to_bf16_bits(gaussian(rng, (up.n, up.k), 0.02))
+        h = to_bf16_bits(outlier_activations(rng, down.m, down.k))
+        w_down = to_bf16_bits(gaussian(rng, (down.n, down.k), 0.02))
+        if name == "mlp_up":
+            return {"x": x, "w": w_up}
+        if name == "mlp_down":
+            return {"x": h, "w": w_down}
+        return {"x": x, "w_up": w_up, "h": h, "w_down": w_down}
+    c = CONFIGS[name]
+    return make_linear(c.m, c.k, c.n, seed, c.outlier_channels, c.lora_rank, c.backward)

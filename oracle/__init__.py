@@ -1,0 +1,226 @@
+"""CPU oracle for the Hadamard-rotated INT8 quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the GPU library and its
+Python binding never do.  It shares no code with the GPU path.
+
+The arithmetic lives in ``sdnq_oracle.c`` (plain C, one binary32 operation per
+step, see the header there for the passages each step follows).  This module only
+builds that file with gcc and marshals numpy arrays in and out of it.
+
+Bit patterns: bf16 tensors travel as ``numpy.uint16`` arrays holding the raw
+bfloat16 bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sdnq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsdnq_oracle.so")
+# A different build of the oracle (used by the mutation test, which compiles
+# deliberately broken copies and checks that the pins reject them).
+_LIB_OVERRIDE = os.environ.get("SDNQ_ORACLE_LIB")
+
+# gcc flags: no contraction into FMA, no fast-math, generic x86-64 code so the
+# library also runs on a host with a different CPU model.
+_CFLAGS = ["-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+_lib = None
+
+OK, ERR_ARG, ERR_OVERFLOW = 0, 1, 2
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle shared library (in place by default) and return its path."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", *_CFLAGS, src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    lib.oracle_num_threads.restype = i32
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_fwht_unnormalized.argtypes = [p, i64, i32]
+    lib.oracle_norm_const.argtypes = [i32]
+    lib.oracle_norm_const.restype = ctypes.c_float
+    lib.oracle_bf16_from_f64.argtypes = [p, i64, p]
+    lib.oracle_f32_from_bf16.argtypes = [p, i64, p]
+    lib.oracle_rotate.argtypes = [p, i64, i64, i32, p, p]
+    lib.oracle_rotate_quantize.argtypes = [p, i64, i64, i32, p, p, p]
+    lib.oracle_gemm_i8.argtypes = [p, p, i64, i64, i64, i32, p]
+    lib.oracle_qlinear_forward.argtypes = [p, i64, i64, p, p, i64, i32, p, p, i32, ctypes.c_double,
+                                           p, p, p, p, p]
+    lib.oracle_qlinear_backward_input.argtypes = [p, i64, i64, p, p, i64, i32, p, p, p, i32,
+                                                  ctypes.c_double, p, p, p, p, p, p, p]
+    for name in ("oracle_fwht_unnormalized", "oracle_rotate", "oracle_rotate_quantize",
+                 "oracle_gemm_i8", "oracle_qlinear_forward", "oracle_qlinear_backward_input"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc == ERR_OVERFLOW:
+        raise OverflowError(f"{what}: an integer accumulator left the int32 range")
+    if rc != OK:
+        raise ValueError(f"{what}: invalid arguments (code {rc})")
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def fwht_unnormalized(v: np.ndarray, g: int) -> np.ndarray:
+    """Unnormalized butterfly H_g applied to every consecutive block of g values
+    along the last axis (binary32, in the oracle's fixed stage order)."""
+    a = _c(v, np.float32).copy()
+    if a.shape[-1] % g:
+        raise ValueError("last axis must be a multiple of g")
+    _check(_load().oracle_fwht_unnormalized(_ptr(a), a.size // g, g), "fwht")
+    return a
+
+
+def norm_const(g: int) -> np.float32:
+    return np.float32(_load().oracle_norm_const(g))
+
+
+def bf16_from_f64(v) -> np.ndarray:
+    a = _c(v, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    _load().oracle_bf16_from_f64(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def f32_from_bf16(h) -> np.ndarray:
+    a = _c(h, np.uint16)
+    out = np.empty(a.shape, np.float32)
+    _load().oracle_f32_from_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def rotate(x_bf16: np.ndarray, g: int, col_scale: np.ndarray | None = None) -> np.ndarray:
+    """Normalized block rotation of each row (binary32 result), no quantization."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    cs = None if col_scale is None else _c(col_scale, np.float32)
+    y = np.empty((rows, cols), np.float32)
+    _check(_load().oracle_rotate(_ptr(x), rows, cols, g, _ptr(cs), _ptr(y)), "rotate")
+    return y
+
+
+def rotate_quantize(x_bf16: np.ndarray, g: int, col_scale: np.ndarray | None = None):
+    """Rotate then quantize each row: returns (codes int8 [rows, cols], scales f32 [rows])."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    cs = None if col_scale is None else _c(col_scale, np.float32)
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows,), np.float32)
+    _check(_load().oracle_rotate_quantize(_ptr(x), rows, cols, g, _ptr(cs), _ptr(q), _ptr(s)),
+           "rotate_quantize")
+    return q, s
+
+
+def gemm_i8(a: np.ndarray, b: np.ndarray, b_layout: int = 0) -> np.ndarray:
+    """Exact integer matmul.  b_layout 0: b is [n, k] (C = A B^T); 1: b is [k, n] (C = A B)."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    m, k = a.shape
+    n = b.shape[0] if b_layout == 0 else b.shape[1]
+    kb = b.shape[1] if b_layout == 0 else b.shape[0]
+    if kb != k:
+        raise ValueError("contraction lengths differ")
+    c = np.empty((m, n), np.int32)
+    _check(_load().oracle_gemm_i8(_ptr(a), _ptr(b), m, n, k, b_layout, _ptr(c)), "gemm_i8")
+    return c
+
+
+def qlinear_forward(x: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
+                    lora_a: np.ndarray | None = None, lora_b: np.ndarray | None = None,
+                    lora_scale: float = 0.0, intermediates: bool = True) -> dict:
+    """Forward of the layer for every row of x.  Returns y (bf16 bits) and, with
+    ``intermediates``, qx, sx, acc (int32) and base (fp32 dequantized product)."""
+    x = _c(x, np.uint16)
+    qw = _c(qw, np.int8)
+    sw = _c(sw, np.float32)
+    m, k = x.shape
+    n = qw.shape[0]
+    if qw.shape[1] != k or sw.shape != (n,):
+        raise ValueError("shape mismatch")
+    la = None if lora_a is None else _c(lora_a, np.uint16)
+    lb = None if lora_b is None else _c(lora_b, np.uint16)
+    rank = 0 if la is None else la.shape[1]
+    out = {"y": np.empty((m, n), np.uint16)}
+    if intermediates:
+        out.update(qx=np.empty((m, k), np.int8), sx=np.empty((m,), np.float32),
+                   acc=np.empty((m, n), np.int32), base=np.empty((m, n), np.float32))
+    rc = _load().oracle_qlinear_forward(
+        _ptr(x), m, k, _ptr(qw), _ptr(sw), n, g, _ptr(la), _ptr(lb), rank, float(lora_scale),
+        _ptr(out["y"]), _ptr(out.get("qx")), _ptr(out.get("sx")), _ptr(out.get("acc")),
+        _ptr(out.get("base")))
+    _check(rc, "qlinear_forward")
+    return out
+
+
+def qlinear_backward_input(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
+                           x: np.ndarray | None = None, lora_a: np.ndarray | None = None,
+                           lora_b: np.ndarray | None = None, lora_scale: float = 0.0,
+                           want_grads: bool = True, intermediates: bool = True) -> dict:
+    """Input gradient through the int8 weight (+ LoRA input gradient and, when x is
+    given and ``want_grads``, the LoRA weight gradients)."""
+    dy = _c(dy, np.uint16)
+    qw = _c(qw, np.int8)
+    sw = _c(sw, np.float32)
+    m, n = dy.shape
+    k = qw.shape[1]
+    if qw.shape[0] != n or sw.shape != (n,):
+        raise ValueError("shape mismatch")
+    la = None if lora_a is None else _c(lora_a, np.uint16)
+    lb = None if lora_b is None else _c(lora_b, np.uint16)
+    rank = 0 if la is None else la.shape[1]
+    xx = None if x is None else _c(x, np.uint16)
+    out = {"dx": np.empty((m, k), np.uint16)}
+    if la is not None and want_grads and xx is not None:
+        out["grad_a"] = np.empty((k, rank), np.uint16)
+        out["grad_b"] = np.empty((rank, n), np.uint16)
+    if intermediates:
+        out.update(qdy=np.empty((m, n), np.int8), sdy=np.empty((m,), np.float32),
+                   acc=np.empty((m, k), np.int32), dxbase=np.empty((m, k), np.float32))
+    rc = _load().oracle_qlinear_backward_input(
+        _ptr(dy), m, n, _ptr(qw), _ptr(sw), k, g, _ptr(xx), _ptr(la), _ptr(lb), rank,
+        float(lora_scale), _ptr(out["dx"]), _ptr(out.get("grad_a")), _ptr(out.get("grad_b")),
+        _ptr(out.get("qdy")), _ptr(out.get("sdy")), _ptr(out.get("acc")), _ptr(out.get("dxbase")))
+    _check(rc, "qlinear_backward_input")
+    return out

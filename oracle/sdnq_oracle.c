@@ -1,0 +1,497 @@
+/*
+ * CPU oracle for the Hadamard-rotated INT8 quantized linear layer
+ * (the SDNQ Hadamard path that ConvRot uses).
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg are the only users.  The GPU library never links,
+ * loads or calls this file, and this file includes nothing from the GPU library.
+ *
+ * Plain, slow and written to be read against the sources:
+ *  - "ConvRot / Hadamard SDNQ" (SimpleTuner docs), section "What The Options Do":
+ *    the rotation is block-wise along in-features with block size
+ *    hadamard_group_size (256 for ConvRot, smaller for the QuaRot-style path);
+ *    sdnq_group_size -1 means one static scale per full weight row.
+ *  - "SDNQ: SD.Next Quantization Engine", feature list and the SDNQConfig example:
+ *    Hadamard rotation applies to quantized weights and to the quantized matmul;
+ *    INT8 quantized matmul; group_size -1 is row-wise; dequantize_fp32 keeps
+ *    the scales and the dequantization in FP32; the training example says the
+ *    quantized matmul is used in the backward pass too.
+ *  - HSWQ README (Hybrid-Sensitivity-Weighted-Quantization), "Rigorous grid /
+ *    pack simulation": ConvRot INT8 is "Hadamard rotate, then channelwise
+ *    absmax" on a symmetric INT8 grid.
+ *  - "ConvRot / Hadamard SDNQ", "PEFT Behavior": the adapter stays in bf16 on top
+ *    of the frozen int8 base.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - H_g is the Sylvester (natural order) Hadamard matrix, i.e. the output order
+ *    of the in-place butterfly below; stages run h = 1, 2, 4, ..., g/2, each pair
+ *    (i, i+h) becomes (a+b, a-b) in fp32, with no fused multiply-add.
+ *  - normalization: every rotated value is multiplied by fl32(1/sqrt(g)).
+ *  - absmax over the whole row; s = fl32(a/127); codes = clamp(rne(fl32(y*r)),
+ *    -127, 127) with r = fl32(127/a) (0 when a == 0); rne = round half to even.
+ *  - activations: one scale per token (row of x) over all in-features.
+ *  - backward: dY is multiplied column-wise by the weight row scales before its
+ *    own per-token quantization (no rotation on that axis); the int32 product
+ *    with the int8 weight is scaled by the dY token scale and rotated back with
+ *    the same normalized block transform (it is symmetric and orthogonal).
+ *  - the LoRA side path sees the unrotated x; A is [K,r], B is [r,N]; its terms are
+ *    computed in fp64 from the bf16 values with no intermediate rounding.
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -fPIC -shared.
+ * x86-64 floats use SSE: every float operation below is one IEEE binary32
+ * operation rounded to nearest even.  OpenMP only splits independent rows or
+ * output elements; it never changes an order of summation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_OVERFLOW 2
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+/* bfloat16 bit pattern -> binary32: the bf16 bits are the high half. */
+static float bf16_decode(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary64 -> bfloat16 (8 significant bits, exponent range of binary32),
+ * round to nearest, ties to even, in a single rounding. */
+static uint16_t bf16_encode_f64(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7FC0u;
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    int e;
+    frexp(a, &e);              /* a = m * 2^e with m in [0.5, 1) */
+    int ulp_exp = e - 8;       /* spacing of 8-significant-bit numbers near a */
+    if (ulp_exp < -133)        /* bf16 subnormal spacing: 2^(-126-7) */
+        ulp_exp = -133;
+    double q = ldexp(a, -ulp_exp);          /* exact scaling by a power of two */
+    double rq = nearbyint(q);               /* default mode: ties to even */
+    double r = ldexp(rq, ulp_exp);
+    if (r >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);  /* rounds past the largest finite value */
+    float f = (float)r;                     /* exact: at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* --------------------------------------------------- Walsh-Hadamard core -- */
+
+static int is_pow2_upto256(int g)
+{
+    return g >= 1 && g <= 256 && (g & (g - 1)) == 0;
+}
+
+/* In-place unnormalized fast Walsh-Hadamard transform of one block of g floats:
+ * u = H_g v with H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]].
+ * Stages h = 1, 2, ..., g/2; each pair (i, i+h) with bit h of i clear becomes
+ * (a + b, a - b), each one binary32 operation. */
+static void fwht_block(float *v, int g)
+{
+    for (int h = 1; h < g; h <<= 1) {
+        for (int i = 0; i < g; i++) {
+            if ((i & h) == 0) {
+                float a = v[i];
+                float b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+}
+
+/* c_g = fl32(1/sqrt(g)); 1 for g == 1 (no rotation). */
+static float norm_const(int g)
+{
+    if (g == 1)
+        return 1.0f;
+    return (float)(1.0 / sqrt((double)g));
+}
+
+/* One row: decode bf16, optional column pre-scale, block rotation along the row,
+ * normalization.  y receives the rotated binary32 values. */
+static void rotate_row(const uint16_t *xr, int64_t cols, int g, const float *col_scale, float *y)
+{
+    for (int64_t i = 0; i < cols; i++) {
+        y[i] = bf16_decode(xr[i]);
+        if (col_scale)
+            y[i] = y[i] * col_scale[i];
+    }
+    if (g > 1) {
+        float c = norm_const(g);
+        for (int64_t b = 0; b < cols; b += g)
+            fwht_block(y + b, g);
+        for (int64_t i = 0; i < cols; i++)
+            y[i] = y[i] * c;
+    }
+}
+
+/* Symmetric absmax quantization of one rotated row to int8 codes in [-127, 127]. */
+static void quantize_row(const float *y, int64_t cols, int8_t *q, float *s)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < cols; i++)
+        a = fmaxf(a, fabsf(y[i]));
+    float r = (a > 0.0f) ? 127.0f / a : 0.0f;
+    *s = a / 127.0f;
+    for (int64_t i = 0; i < cols; i++) {
+        float t = nearbyintf(y[i] * r);
+        if (t > 127.0f)
+            t = 127.0f;
+        if (t < -127.0f)
+            t = -127.0f;
+        q[i] = (int8_t)t;
+    }
+}
+
+/* ----------------------------------------------------------- exports -- */
+
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}
+
+void oracle_set_num_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
+/* Unnormalized butterfly on `nblocks` consecutive blocks of g floats, in place. */
+int oracle_fwht_unnormalized(float *v, int64_t nblocks, int g)
+{
+    if (!v || nblocks < 0 || !is_pow2_upto256(g))
+        return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < nblocks; b++)
+        fwht_block(v + b * g, g);
+    return ORACLE_OK;
+}
+
+float oracle_norm_const(int g)
+{
+    return norm_const(g);
+}
+
+void oracle_bf16_from_f64(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = bf16_encode_f64(v[i]);
+}
+
+void oracle_f32_from_bf16(const uint16_t *h, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = bf16_decode(h[i]);
+}
+
+/* Rotation only (no quantization): y[rows, cols] binary32. */
+int oracle_rotate(const uint16_t *x, int64_t rows, int64_t cols, int g, const float *col_scale, float *y)
+{
+    if (!x || !y || rows < 0 || cols < 0 || !is_pow2_upto256(g) || cols % g != 0)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < rows; m++)
+        rotate_row(x + m * cols, cols, g, col_scale, y + m * cols);
+    return ORACLE_OK;
+}
+
+/* Rotate, then quantize each row: q[rows, cols] int8 and s[rows] binary32.
+ * Weights (offline) and activations (per token) go through the same steps. */
+int oracle_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
+                           const float *col_scale, int8_t *q, float *s)
+{
+    if (!x || !q || !s || rows < 0 || cols < 0 || !is_pow2_upto256(g) || cols % g != 0)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel
+    {
+        float *y = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+        if (!y) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ARG;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < rows; m++) {
+                rotate_row(x + m * cols, cols, g, col_scale, y);
+                quantize_row(y, cols, q + m * cols, s + m);
+            }
+            free(y);
+        }
+    }
+    return err;
+}
+
+/* Integer matmul with exact int64 accumulation, stored as int32.
+ *   b_layout 0: a[m,k], b[n,k]  ->  c[i,j] = sum_t a[i,t] * b[j,t]
+ *   b_layout 1: a[m,k], b[k,n]  ->  c[i,j] = sum_t a[i,t] * b[t,j]
+ * Returns ORACLE_ERR_OVERFLOW if any sum leaves the int32 range. */
+int oracle_gemm_i8(const int8_t *a, const int8_t *b, int64_t m, int64_t n, int64_t k,
+                   int b_layout, int32_t *c)
+{
+    if (!a || !b || !c || m < 0 || n < 0 || k < 0 || (b_layout != 0 && b_layout != 1))
+        return ORACLE_ERR_ARG;
+    int overflow = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; i++) {
+        for (int64_t j = 0; j < n; j++) {
+            int64_t acc = 0;
+            for (int64_t t = 0; t < k; t++) {
+                int64_t bv = b_layout == 0 ? b[j * k + t] : b[t * n + j];
+                acc += (int64_t)a[i * k + t] * bv;
+            }
+            if (acc > INT32_MAX || acc < INT32_MIN) {
+#pragma omp atomic write
+                overflow = 1;
+            }
+            c[i * n + j] = (int32_t)acc;
+        }
+    }
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
+/* Forward of the quantized linear layer for the rows of x:
+ *   q_x, s_x   = rotate + per-token quantize (x row, block g)
+ *   acc[m,n]   = sum_k q_x[m,k] * qw[n,k]                (exact, int32 range checked)
+ *   base[m,n]  = fl32(fl32(acc) * fl32(s_x[m] * s_w[n]))  (fp32 dequantization)
+ *   lora[m,n]  = ((x A) B)[m,n] * lora_scale              (fp64, unrotated x)
+ *   y[m,n]     = bf16_rne(base + lora)
+ * lora_a / lora_b may be NULL (rank ignored).  Every *_out pointer may be NULL. */
+int oracle_qlinear_forward(const uint16_t *x, int64_t m, int64_t k,
+                           const int8_t *qw, const float *sw, int64_t n, int g,
+                           const uint16_t *lora_a, const uint16_t *lora_b, int rank, double lora_scale,
+                           uint16_t *y, int8_t *qx_out, float *sx_out, int32_t *acc_out, float *base_out)
+{
+    if (!x || !qw || !sw || !y || m < 0 || k <= 0 || n < 0 || !is_pow2_upto256(g) || k % g != 0)
+        return ORACLE_ERR_ARG;
+    int use_lora = lora_a && lora_b && rank > 0;
+    int overflow = 0, alloc_fail = 0;
+#pragma omp parallel
+    {
+        float *yr = (float *)malloc(sizeof(float) * (size_t)k);
+        int8_t *qr = (int8_t *)malloc((size_t)k);
+        double *t = (double *)malloc(sizeof(double) * (size_t)(rank > 0 ? rank : 1));
+        if (!yr || !qr || !t) {
+#pragma omp atomic write
+            alloc_fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < m; i++) {
+                const uint16_t *xr = x + i * k;
+                float sx;
+                rotate_row(xr, k, g, NULL, yr);
+                quantize_row(yr, k, qr, &sx);
+                if (qx_out)
+                    memcpy(qx_out + i * k, qr, (size_t)k);
+                if (sx_out)
+                    sx_out[i] = sx;
+                if (use_lora) {
+                    for (int j = 0; j < rank; j++)
+                        t[j] = 0.0;
+                    for (int64_t kk = 0; kk < k; kk++) {
+                        double xv = (double)bf16_decode(xr[kk]);
+                        for (int j = 0; j < rank; j++)
+                            t[j] += xv * (double)bf16_decode(lora_a[kk * rank + j]);
+                    }
+                }
+                for (int64_t j = 0; j < n; j++) {
+                    const int8_t *wr = qw + j * k;
+                    int64_t acc = 0;
+                    for (int64_t kk = 0; kk < k; kk++)
+                        acc += (int64_t)qr[kk] * (int64_t)wr[kk];
+                    if (acc > INT32_MAX || acc < INT32_MIN) {
+#pragma omp atomic write
+                        overflow = 1;
+                    }
+                    float base = (float)(int32_t)acc * (sx * sw[j]);
+                    if (acc_out)
+                        acc_out[i * n + j] = (int32_t)acc;
+                    if (base_out)
+                        base_out[i * n + j] = base;
+                    double out = (double)base;
+                    if (use_lora) {
+                        double l = 0.0;
+                        for (int r = 0; r < rank; r++)
+                            l += t[r] * (double)bf16_decode(lora_b[(int64_t)r * n + j]);
+                        out += l * lora_scale;
+                    }
+                    y[i * n + j] = bf16_encode_f64(out);
+                }
+            }
+        }
+        free(yr);
+        free(qr);
+        free(t);
+    }
+    if (alloc_fail)
+        return ORACLE_ERR_ARG;
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
+/* Gradient with respect to the layer input, through the same int8 weight:
+ *   dY'[m,j]    = fl32(dY[m,j] * s_w[j])                     (fold the weight row scales)
+ *   q_dy, s_dy  = per-token absmax quantization of dY' (no rotation: g = 1)
+ *   acc[m,kk]   = sum_j q_dy[m,j] * qw[j,kk]                  (exact, int32 range checked)
+ *   z[m,kk]     = fl32(fl32(acc) * s_dy[m])
+ *   dxbase      = the forward's normalized block rotation applied to each row of z
+ *   g_r         = dY B^T * lora_scale                         (fp64)
+ *   dx          = bf16_rne(dxbase + g_r A^T)
+ *   grad_a      = bf16_rne(x^T g_r)          [k, rank]
+ *   grad_b      = bf16_rne((x A)^T dY * lora_scale)  [rank, n]
+ * x is read only when grad_a or grad_b is requested.  Every *_out may be NULL. */
+int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
+                                  const int8_t *qw, const float *sw, int64_t k, int g,
+                                  const uint16_t *x, const uint16_t *lora_a, const uint16_t *lora_b,
+                                  int rank, double lora_scale,
+                                  uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                  int8_t *qdy_out, float *sdy_out, int32_t *acc_out, float *dxbase_out)
+{
+    if (!dy || !qw || !sw || !dx || m < 0 || n <= 0 || k <= 0 || !is_pow2_upto256(g) || k % g != 0)
+        return ORACLE_ERR_ARG;
+    int use_lora = lora_a && lora_b && rank > 0;
+    int want_grads = use_lora && (grad_a || grad_b);
+    if (want_grads && !x)
+        return ORACLE_ERR_ARG;
+    int overflow = 0, alloc_fail = 0;
+
+    double *gr = NULL, *tx = NULL;
+    if (use_lora) {
+        gr = (double *)calloc((size_t)(m > 0 ? m : 1) * (size_t)rank, sizeof(double));
+        if (!gr)
+            return ORACLE_ERR_ARG;
+        /* g_r[m, r] = sum_j dY[m, j] * B[r, j] * lora_scale */
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < m; i++) {
+            for (int r = 0; r < rank; r++) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < n; j++)
+                    acc += (double)bf16_decode(dy[i * n + j]) * (double)bf16_decode(lora_b[(int64_t)r * n + j]);
+                gr[i * rank + r] = acc * lora_scale;
+            }
+        }
+    }
+
+#pragma omp parallel
+    {
+        float *yr = (float *)malloc(sizeof(float) * (size_t)n);
+        int8_t *qr = (int8_t *)malloc((size_t)n);
+        float *z = (float *)malloc(sizeof(float) * (size_t)k);
+        int64_t *acc = (int64_t *)malloc(sizeof(int64_t) * (size_t)k);
+        if (!yr || !qr || !z || !acc) {
+#pragma omp atomic write
+            alloc_fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < m; i++) {
+                float sdy;
+                rotate_row(dy + i * n, n, 1, sw, yr);
+                quantize_row(yr, n, qr, &sdy);
+                if (qdy_out)
+                    memcpy(qdy_out + i * n, qr, (size_t)n);
+                if (sdy_out)
+                    sdy_out[i] = sdy;
+                for (int64_t kk = 0; kk < k; kk++)
+                    acc[kk] = 0;
+                for (int64_t j = 0; j < n; j++) {
+                    int64_t qv = qr[j];
+                    const int8_t *wr = qw + j * k;
+                    for (int64_t kk = 0; kk < k; kk++)
+                        acc[kk] += qv * (int64_t)wr[kk];
+                }
+                for (int64_t kk = 0; kk < k; kk++) {
+                    if (acc[kk] > INT32_MAX || acc[kk] < INT32_MIN) {
+#pragma omp atomic write
+                        overflow = 1;
+                    }
+                    if (acc_out)
+                        acc_out[i * k + kk] = (int32_t)acc[kk];
+                    z[kk] = (float)(int32_t)acc[kk] * sdy;
+                }
+                if (g > 1) {
+                    float c = norm_const(g);
+                    for (int64_t b = 0; b < k; b += g)
+                        fwht_block(z + b, g);
+                    for (int64_t kk = 0; kk < k; kk++)
+                        z[kk] = z[kk] * c;
+                }
+                for (int64_t kk = 0; kk < k; kk++) {
+                    if (dxbase_out)
+                        dxbase_out[i * k + kk] = z[kk];
+                    double out = (double)z[kk];
+                    if (use_lora) {
+                        double l = 0.0;
+                        for (int r = 0; r < rank; r++)
+                            l += gr[i * rank + r] * (double)bf16_decode(lora_a[kk * rank + r]);
+                        out += l;
+                    }
+                    dx[i * k + kk] = bf16_encode_f64(out);
+                }
+            }
+        }
+        free(yr);
+        free(qr);
+        free(z);
+        free(acc);
+    }
+
+    if (want_grads && !alloc_fail) {
+        if (grad_a) {
+            /* grad_a[kk, r] = sum_i x[i, kk] * g_r[i, r] */
+#pragma omp parallel for schedule(static)
+            for (int64_t kk = 0; kk < k; kk++) {
+                for (int r = 0; r < rank; r++) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < m; i++)
+                        acc += (double)bf16_decode(x[i * k + kk]) * gr[i * rank + r];
+                    grad_a[kk * rank + r] = bf16_encode_f64(acc);
+                }
+            }
+        }
+        if (grad_b) {
+            tx = (double *)calloc((size_t)(m > 0 ? m : 1) * (size_t)rank, sizeof(double));
+            if (!tx) {
+                alloc_fail = 1;
+            } else {
+                /* t[i, r] = sum_kk x[i, kk] * A[kk, r] */
+#pragma omp parallel for schedule(static)
+                for (int64_t i = 0; i < m; i++) {
+                    for (int64_t kk = 0; kk < k; kk++) {
+                        double xv = (double)bf16_decode(x[i * k + kk]);
+                        for (int r = 0; r < rank; r++)
+                            tx[i * rank + r] += xv * (double)bf16_decode(lora_a[kk * rank + r]);
+                    }
+                }
+                /* grad_b[r, j] = lora_scale * sum_i t[i, r] * dY[i, j] */
+#pragma omp parallel for schedule(static)
+                for (int64_t j = 0; j < n; j++) {
+                    for (int r = 0; r < rank; r++) {
+                        double acc = 0.0;
+                        for (int64_t i = 0; i < m; i++)
+                            acc += tx[i * rank + r] * (double)bf16_decode(dy[i * n + j]);
+                        grad_b[(int64_t)r * n + j] = bf16_encode_f64(acc * lora_scale);
+                    }
+                }
+            }
+        }
+    }
+    free(gr);
+    free(tx);
+    if (alloc_fail)
+        return ORACLE_ERR_ARG;
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}

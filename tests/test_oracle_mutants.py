@@ -1,0 +1,60 @@
+"""Mutation check of the oracle pins (CPU only).
+
+Each case plants one plausible mistake in a scratch copy of the oracle source,
+compiles it, and runs the pin suite against that build: the suite must fail.
+The clamp bound is left out on purpose: |fl32(y * r)| <= 127 (1 + 2^-23) for
+every element, so clamping at -128 instead of -127 changes no output.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "sub_swapped": ("v[i + h] = a - b;", "v[i + h] = b - a;"),
+    "stage_order_descending": ("for (int h = 1; h < g; h <<= 1) {", "for (int h = g / 2; h >= 1; h >>= 1) {"),
+    "divide_by_scale": ("float t = nearbyintf(y[i] * r);", "float t = nearbyintf(y[i] / *s);"),
+    "round_half_away": ("float t = nearbyintf(y[i] * r);", "float t = roundf(y[i] * r);"),
+    "no_normalization": ("y[i] = y[i] * c;", "y[i] = y[i];"),
+    "no_column_scale": ("y[i] = y[i] * col_scale[i];", "y[i] = y[i];"),
+    "backward_weight_transposed": ("acc[kk] += qv * (int64_t)wr[kk];", "acc[kk] += qv * (int64_t)qw[kk * n + j];"),
+    "backward_no_inverse_rotation": ("for (int64_t b = 0; b < k; b += g)\n                        fwht_block(z + b, g);",
+                                     "for (int64_t b = 0; b < 0; b += g)\n                        fwht_block(z + b, g);"),
+    "scale_over_128": ("*s = a / 127.0f;", "*s = a / 128.0f;"),
+    "lora_b_transposed": ("l += t[r] * (double)bf16_decode(lora_b[(int64_t)r * n + j]);",
+                          "l += t[r] * (double)bf16_decode(lora_b[(int64_t)j * rank + r]);"),
+    "grad_b_unscaled": ("grad_b[(int64_t)r * n + j] = bf16_encode_f64(acc * lora_scale);",
+                        "grad_b[(int64_t)r * n + j] = bf16_encode_f64(acc);"),
+    "bf16_truncation": ("double rq = nearbyint(q);", "double rq = floor(q);"),
+    "weight_scale_index": ("float base = (float)(int32_t)acc * (sx * sw[j]);",
+                           "float base = (float)(int32_t)acc * (sx * sw[i % n]);"),
+}
+
+
+def _run(name, tmp):
+    old, new = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(old) >= 1, name
+    path = os.path.join(tmp, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new, 1))
+    lib = oracle.build(force=True, src=path, out=os.path.join(tmp, f"lib{name}.so"))
+    env = dict(os.environ, SDNQ_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+@pytest.mark.slow
+def test_every_planted_mistake_is_caught(tmp_path):
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = dict(ex.map(lambda n: _run(n, str(tmp_path)), sorted(MUTANTS)))
+    survivors = [n for n, rc in results.items() if rc == 0]
+    assert not survivors, f"pins did not catch: {survivors}"

@@ -1,0 +1,445 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself (closed forms, hand-derived fixtures, textbook/library routines,
+brute force, exact rational arithmetic, error bounds, autograd), chosen so that
+a plausible slip (a dropped term, a wrong sign or index, a transposed operand, a
+different Hadamard ordering or rounding mode) fails at least one of them.
+
+Sources of the definitions being pinned: "ConvRot / Hadamard SDNQ" (SimpleTuner
+docs, "What The Options Do"), "SDNQ: SD.Next Quantization Engine" (feature list,
+SDNQConfig example, quantized-training example) and the HSWQ README ("Rigorous
+grid / pack simulation").
+"""
+import json
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from hadamard_rotated_int8_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def nearest_f32(fr: Fraction) -> np.float32:
+    """Binary32 nearest to a rational (ties to even), by exact comparison."""
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+
+    def key(c):
+        return (abs(Fraction(float(c)) - fr), int(np.float32(c).view(np.uint32)) & 1)
+    return min(cands, key=key)
+
+
+def f32_bits(v) -> int:
+    return int(np.float32(v).view(np.uint32))
+
+
+def bf(a):
+    return synth.to_bf16_bits(np.asarray(a, np.float32))
+
+
+# ------------------------------------------------------------- P1 / P3 --
+
+@pytest.mark.parametrize("g", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_butterfly_on_identity_is_sylvester_hadamard(g):
+    """P1: the butterfly applied to the identity reproduces scipy's Sylvester
+    Hadamard matrix exactly; it is symmetric and H H^T = g I (integer exact)."""
+    h = oracle.fwht_unnormalized(np.eye(g, dtype=np.float32), g)
+    ref = scipy.linalg.hadamard(g)
+    # row i of the result is H e_i = column i of H
+    assert np.array_equal(h.T, ref.astype(np.float32))
+    assert np.array_equal(h, h.T)
+    assert np.array_equal(h.astype(np.int64) @ h.astype(np.int64).T, g * np.eye(g, dtype=np.int64))
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_sylvester_entry_closed_form(g):
+    """H[i, j] = (-1)^popcount(i & j) for the natural-order Sylvester matrix."""
+    h = oracle.fwht_unnormalized(np.eye(g, dtype=np.float32), g)
+    i, j = np.meshgrid(np.arange(g), np.arange(g), indexing="ij")
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(h, np.where(pc % 2 == 0, 1.0, -1.0).astype(np.float32))
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_butterfly_involution_on_integers(g):
+    """H (H v) = g v exactly for small integer v (every partial sum is exact)."""
+    rng = np.random.default_rng(1)
+    v = rng.integers(-100, 101, size=(5, g)).astype(np.float32)
+    hv = oracle.fwht_unnormalized(oracle.fwht_unnormalized(v, g), g)
+    assert np.array_equal(hv, g * v)
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_butterfly_matches_dense_fp64_within_rounding(g):
+    """P3: on random binary32 input the butterfly agrees with the fp64 dense
+    product within the log2(g)-level rounding bound."""
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal((7, 4 * g)).astype(np.float32)
+    u = oracle.fwht_unnormalized(v, g).astype(np.float64)
+    hd = scipy.linalg.hadamard(g).astype(np.float64)
+    ref = (v.astype(np.float64).reshape(7, 4, g) @ hd.T).reshape(7, 4 * g)
+    bound = np.log2(g) * 2.0 ** -24 * 1.01 * (np.abs(v.astype(np.float64)).reshape(7, 4, g).sum(-1))
+    err = np.abs(u - ref).reshape(7, 4, g).max(-1)
+    assert np.all(err <= bound)
+
+
+# ------------------------------------------------------------------ P2 --
+
+@pytest.mark.parametrize("g", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_norm_const_is_nearest_binary32_to_inverse_sqrt(g):
+    """c_g = fl32(1/sqrt(g)), checked with 60-digit decimal arithmetic."""
+    getcontext().prec = 60
+    exact = Decimal(1) / Decimal(g).sqrt()
+    c = oracle.norm_const(g)
+    lo = np.nextafter(c, np.float32(0))
+    hi = np.nextafter(c, np.float32(1))
+    d = abs(Decimal(float(c)) - exact)
+    assert d <= abs(Decimal(float(lo)) - exact) and d <= abs(Decimal(float(hi)) - exact)
+
+
+def test_norm_const_bit_patterns():
+    assert f32_bits(oracle.norm_const(64)) == 0x3E000000
+    assert f32_bits(oracle.norm_const(128)) == 0x3DB504F3
+    assert f32_bits(oracle.norm_const(256)) == 0x3D800000
+    assert oracle.norm_const(1) == 1.0
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_normalized_transform_is_orthonormal(g):
+    """P2: (c H)(c H)^T = I to a few binary32 ulps (exact for g = 64, 256)."""
+    h = oracle.fwht_unnormalized(np.eye(g, dtype=np.float32), g).astype(np.float64)
+    c = float(oracle.norm_const(g))
+    dev = np.abs((c * h) @ (c * h).T - np.eye(g)).max()
+    if g in (64, 256):
+        assert dev == 0.0
+    else:
+        assert dev < 4 * 2.0 ** -24
+
+
+# ------------------------------------------------------------------ P4 --
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_rotation_invariance_of_the_product(g):
+    """P4: x W^T = (x R)(W R)^T with R the normalized block rotation, on the
+    oracle's unquantized binary32 rotation (within binary32 rounding)."""
+    rng = np.random.default_rng(3)
+    x = bf(rng.standard_normal((16, 512)))
+    w = bf(rng.standard_normal((24, 512)) * 0.02)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    ref = xf @ wf.T
+    rot = oracle.rotate(x, g).astype(np.float64) @ oracle.rotate(w, g).astype(np.float64).T
+    assert np.linalg.norm(rot - ref) / np.linalg.norm(ref) < 2e-6
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_rotation_equals_block_diagonal_dense_product(g):
+    """The rotation acts on contiguous g-blocks along the row, in block order."""
+    rng = np.random.default_rng(4)
+    x = bf(rng.standard_normal((5, 3 * g)))
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    r = np.kron(np.eye(3), scipy.linalg.hadamard(g) / np.sqrt(g))
+    ref = xf @ r.T
+    got = oracle.rotate(x, g).astype(np.float64)
+    assert np.abs(got - ref).max() < 1e-5 * np.abs(xf).max() * np.sqrt(g)
+
+
+def test_rotation_g1_is_identity_and_column_scale_multiplies():
+    rng = np.random.default_rng(5)
+    x = bf(rng.standard_normal((3, 64)))
+    cs = rng.uniform(0.5, 2.0, 64).astype(np.float32)
+    xf = synth.bf16_bits_to_f32(x)
+    assert np.array_equal(oracle.rotate(x, 1), xf)
+    assert np.array_equal(oracle.rotate(x, 1, cs), xf * cs)
+
+
+# ------------------------------------------------------------------ P5 --
+
+def _cases():
+    with open(GOLDEN) as f:
+        return {c["name"]: c for c in json.load(f)["cases"]}
+
+
+@pytest.mark.parametrize("name", ["g4_ramp", "g1_rne_ties", "g1_multiply_by_reciprocal", "g4_stage_order"])
+def test_hand_worked_rows(name):
+    c = _cases()[name]
+    x = bf(np.array([c["x"]], np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(x)[0], np.array(c["x"], np.float32))
+    y = oracle.rotate(x, c["g"])
+    assert np.array_equal(y[0], np.array(c["rotated"], np.float32))
+    q, s = oracle.rotate_quantize(x, c["g"])
+    assert q[0].tolist() == c["codes"]
+    expect = nearest_f32(Fraction(*c["scale_rational"]))
+    assert f32_bits(expect) == int(c["scale_bits"], 16)
+    assert f32_bits(s[0]) == int(c["scale_bits"], 16)
+
+
+def test_hand_worked_stage_order_in_a_256_block():
+    """The butterfly's stage order is visible in binary32: ascending stages give
+    2^-24 where descending ones give the exact 2^-23 (derivation in the fixture)."""
+    c = _cases()["g256_stage_order"]
+    x = np.zeros((1, c["cols"]), np.float32)
+    x[0, :4] = c["x_head"]
+    xb = bf(x)
+    assert np.array_equal(synth.bf16_bits_to_f32(xb), x)
+    y = oracle.rotate(xb, c["g"])
+    assert np.array_equal(y[0], np.tile(np.array(c["rotated_period"], np.float32), c["cols"] // 4))
+    q, s = oracle.rotate_quantize(xb, c["g"])
+    assert np.array_equal(q[0], np.tile(np.array(c["codes_period"], np.int8), c["cols"] // 4))
+    assert f32_bits(nearest_f32(Fraction(*c["scale_rational"]))) == int(c["scale_bits"], 16)
+    assert f32_bits(s[0]) == int(c["scale_bits"], 16)
+
+
+def test_hand_worked_constant_block():
+    c = _cases()["g256_constant_block"]
+    x = bf(np.full((1, c["cols"]), c["x_constant"], np.float32))
+    y = oracle.rotate(x, c["g"])
+    assert y[0, 0] == c["rotated_first"] and np.all(y[0, 1:] == 0)
+    q, s = oracle.rotate_quantize(x, c["g"])
+    assert q[0, 0] == c["codes_first"] and np.all(q[0, 1:] == 0)
+    assert f32_bits(nearest_f32(Fraction(*c["scale_rational"]))) == int(c["scale_bits"], 16)
+    assert f32_bits(s[0]) == int(c["scale_bits"], 16)
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_one_hot_codes_follow_the_hadamard_sign_pattern(g):
+    """P5: x = e_j gives codes +-127 in j's block with sign (-1)^popcount(i & j_local),
+    zeros elsewhere; s = fl32(c_g / 127)."""
+    cols, hot = 512, 300
+    x = np.zeros((1, cols), np.float32)
+    x[0, hot] = 1.0
+    q, s = oracle.rotate_quantize(bf(x), g)
+    b0 = (hot // g) * g
+    jl = hot - b0
+    sign = np.array([1 if bin(i & jl).count("1") % 2 == 0 else -1 for i in range(g)])
+    expect = np.zeros(cols, np.int64)
+    expect[b0:b0 + g] = 127 * sign
+    assert np.array_equal(q[0].astype(np.int64), expect)
+    c = oracle.norm_const(g)
+    assert s[0] == np.float32(c) / np.float32(127)
+    if g == 256:
+        case = _cases()["g256_one_hot"]
+        assert f32_bits(s[0]) == int(case["scale_bits"], 16)
+
+
+def test_zero_row_gives_zero_scale_and_codes():
+    q, s = oracle.rotate_quantize(np.zeros((2, 256), np.uint16), 256)
+    assert np.all(q == 0) and np.all(s == 0)
+
+
+def test_g1_is_textbook_per_row_absmax_on_integer_grid_rows():
+    """g = 1 on rows whose absmax is 127: r = 1, codes are the round-half-even
+    of the values (numpy's rint is round-half-even)."""
+    rng = np.random.default_rng(6)
+    v = (rng.integers(-254, 255, size=(4, 64)) / 2.0).astype(np.float32)
+    v[:, 0] = 127.0
+    q, s = oracle.rotate_quantize(bf(v), 1)
+    assert np.all(s == 1.0)
+    assert np.array_equal(q.astype(np.int64), np.rint(v).astype(np.int64))
+
+
+# ------------------------------------------------------------------ P6 --
+
+@pytest.mark.parametrize("b_layout", [0, 1])
+def test_gemm_brute_force_python_loops(b_layout):
+    rng = np.random.default_rng(7)
+    m, n, k = 3, 5, 70
+    a = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    b = rng.integers(-128, 128, size=(n, k) if b_layout == 0 else (k, n)).astype(np.int8)
+    c = oracle.gemm_i8(a, b, b_layout)
+    for i in range(m):
+        for j in range(n):
+            s = 0
+            for t in range(k):
+                bv = int(b[j, t]) if b_layout == 0 else int(b[t, j])
+                s += int(a[i, t]) * bv
+            assert c[i, j] == s
+
+
+def test_gemm_int32_range_check():
+    k_ok, k_bad = 133144, 133145
+    a = np.full((1, k_ok), 127, np.int8)
+    assert oracle.gemm_i8(a, a, 0)[0, 0] == 127 * 127 * k_ok
+    a = np.full((1, k_bad), 127, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i8(a, a, 0)
+
+
+def test_tiny_config_accumulators_equal_int64_matmul():
+    d = synth.make_config("tiny")
+    qw, sw = oracle.rotate_quantize(d["w"], 256)
+    out = oracle.qlinear_forward(d["x"], qw, sw, 256)
+    ref = out["qx"].astype(np.int64) @ qw.astype(np.int64).T
+    assert np.array_equal(out["acc"].astype(np.int64), ref)
+    q, s = oracle.rotate_quantize(d["x"], 256)
+    assert np.array_equal(q, out["qx"]) and np.array_equal(s, out["sx"])
+
+
+# ------------------------------------------------------------------ P7 --
+
+@pytest.mark.parametrize("g", [1, 64, 128, 256])
+def test_quantization_error_bound_and_full_scale_code(g):
+    d = synth.make_config("tiny")
+    y = oracle.rotate(d["x"], g).astype(np.float64)
+    q, s = oracle.rotate_quantize(d["x"], g)
+    s64 = s.astype(np.float64)[:, None]
+    err = np.abs(y - q.astype(np.float64) * s64)
+    assert np.all(err <= 0.5 * s64 * (1 + 1e-6) + 1e-6 * np.abs(y))
+    assert np.all(np.abs(q.astype(np.int64)).max(axis=1) == 127)
+    assert q.min() >= -127
+
+
+# ------------------------------------------------------------------ P8 --
+
+def test_rotation_reduces_quantization_error_on_outlier_inputs():
+    """The method's premise ("ConvRot can reduce quantization damage"): on
+    outlier-channel activations the rotated int8 product is closer to the fp64
+    product than the unrotated one."""
+    d = synth.make_config("tiny")
+    xf = synth.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(d["w"]).astype(np.float64)
+    ref = xf @ wf.T
+    errs = {}
+    for g in (1, 64, 128, 256):
+        qw, sw = oracle.rotate_quantize(d["w"], g)
+        base = oracle.qlinear_forward(d["x"], qw, sw, g)["base"].astype(np.float64)
+        errs[g] = np.linalg.norm(base - ref) / np.linalg.norm(ref)
+    assert errs[256] < 0.5 * errs[1]
+    assert errs[64] < 0.5 * errs[1] and errs[128] < 0.5 * errs[1]
+    assert errs[256] < 2e-2
+
+
+# ------------------------------------------------------ forward output --
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_forward_dequant_matches_fp64_scaled_codes(g):
+    """O9: base = acc * s_x * s_w within binary32 rounding (catches a transposed
+    or mis-indexed scale), and y = bf16(base) exactly without LoRA."""
+    rng = np.random.default_rng(8)
+    m, k, n = 9, 512, 40
+    x = bf(rng.standard_normal((m, k)))
+    w = bf(rng.standard_normal((n, k)) * 0.02)
+    qw, sw = oracle.rotate_quantize(w, g)
+    out = oracle.qlinear_forward(x, qw, sw, g)
+    ref = (out["qx"].astype(np.float64) * out["sx"][:, None]) @ (qw.astype(np.float64) * sw[:, None]).T
+    assert np.all(np.abs(out["base"] - ref) <= 3e-7 * np.abs(ref) + 1e-30)
+    assert np.array_equal(out["y"], torch.from_numpy(out["base"]).to(torch.bfloat16).view(torch.int16)
+                          .numpy().view(np.uint16))
+
+
+def test_forward_lora_term_against_torch_fp64():
+    rng = np.random.default_rng(9)
+    m, k, n, r = 6, 256, 48, 8
+    x = bf(rng.standard_normal((m, k)))
+    w = bf(rng.standard_normal((n, k)) * 0.02)
+    la = bf(rng.standard_normal((k, r)) * 0.3)
+    lb = bf(rng.standard_normal((r, n)) * 0.3)
+    qw, sw = oracle.rotate_quantize(w, 256)
+    scale = 0.75
+    out = oracle.qlinear_forward(x, qw, sw, 256, la, lb, scale)
+    t = lambda a: torch.from_numpy(synth.bf16_bits_to_f32(a).astype(np.float64))
+    lora = (t(x) @ t(la) @ t(lb) * scale).numpy()
+    expect = oracle.bf16_from_f64(out["base"].astype(np.float64) + lora)
+    assert np.array_equal(out["y"], expect)
+    # the LoRA term is not negligible in this case
+    assert np.abs(lora).mean() > 0.5 * np.abs(out["base"]).mean()
+
+
+# ------------------------------------------------------------- backward --
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_backward_base_matches_fp64_dense(g):
+    """B1-B5 on a non-square weight: z = (q_dy s_dy) qw, then the normalized block
+    rotation (fp64 dense with scipy's Hadamard) equals the oracle's dxbase within
+    binary32 rounding; the fold multiplies dY by s_w column-wise."""
+    rng = np.random.default_rng(10)
+    m, n, k = 7, 384, 512
+    dy = bf(rng.standard_normal((m, n)) * 1e-3)
+    w = bf(rng.standard_normal((n, k)) * 0.02)
+    qw, sw = oracle.rotate_quantize(w, g)
+    out = oracle.qlinear_backward_input(dy, qw, sw, g)
+    q2, s2 = oracle.rotate_quantize(dy, 1, col_scale=sw)
+    assert np.array_equal(q2, out["qdy"]) and np.array_equal(s2, out["sdy"])
+    acc = out["qdy"].astype(np.int64) @ qw.astype(np.int64)
+    assert np.array_equal(acc, out["acc"].astype(np.int64))
+    z = acc.astype(np.float64) * out["sdy"].astype(np.float64)[:, None]
+    r = np.kron(np.eye(k // g), scipy.linalg.hadamard(g) / np.sqrt(g))
+    ref = z @ r.T
+    assert np.abs(out["dxbase"] - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_backward_approximates_unquantized_input_gradient():
+    """P9: dX ~ dY W (original, unrotated bf16 weight) up to quantization error."""
+    d = synth.make_linear(32, 768, 512, seed=11, backward=True)
+    qw, sw = oracle.rotate_quantize(d["w"], 256)
+    out = oracle.qlinear_backward_input(d["dy"], qw, sw, 256)
+    ref = synth.bf16_bits_to_f32(d["dy"]).astype(np.float64) @ synth.bf16_bits_to_f32(d["w"]).astype(np.float64)
+    dx = synth.bf16_bits_to_f32(out["dx"]).astype(np.float64)
+    assert np.linalg.norm(dx - ref) / np.linalg.norm(ref) < 2e-2
+
+
+def test_lora_gradients_against_torch_autograd():
+    """dA, dB and the LoRA part of dX equal torch autograd (fp64) of
+    sum(dY * ((x A) B * scale)) up to the final bf16 rounding."""
+    d = synth.make_linear(24, 256, 128, seed=12, lora_rank=16, backward=True)
+    scale = 2.0
+    qw, sw = oracle.rotate_quantize(d["w"], 64)
+    out = oracle.qlinear_backward_input(d["dy"], qw, sw, 64, d["x"], d["lora_a"], d["lora_b"], scale)
+    t = lambda a, grad=False: torch.tensor(synth.bf16_bits_to_f32(a).astype(np.float64), requires_grad=grad)
+    x, A, B, dY = t(d["x"], True), t(d["lora_a"], True), t(d["lora_b"], True), t(d["dy"])
+    ((x @ A @ B * scale) * dY).sum().backward()
+    for name, ref in (("grad_a", A.grad), ("grad_b", B.grad)):
+        assert np.array_equal(out[name], oracle.bf16_from_f64(ref.numpy())), name
+    dx_expect = oracle.bf16_from_f64(out["dxbase"].astype(np.float64) + x.grad.numpy())
+    assert np.array_equal(out["dx"], dx_expect)
+
+
+# ------------------------------------------------------------- bf16 rounding --
+
+def test_bf16_encoder_matches_torch_on_binary32_values():
+    rng = np.random.default_rng(13)
+    v = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 20000),
+                        # exact ties: 8 significant bits plus a half ulp
+                        (1.0 + (2 * rng.integers(0, 128, 2000) + 1) * 2.0 ** -8).astype(np.float32)])
+    v = v.astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_from_f64(v.astype(np.float64)), ref)
+
+
+def test_bf16_encoder_single_rounding_and_specials():
+    cases = [
+        (1.0 + 2.0 ** -8, 0x3F80),                  # tie -> even
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),              # tie -> even (up)
+        (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),     # just above the tie (binary32 first would give 0x3F80)
+        (-(1.0 + 2.0 ** -8 + 2.0 ** -40), 0xBF81),
+        (0.0, 0x0000), (-0.0, 0x8000),
+        (2.0 ** -133, 0x0001),                      # smallest subnormal
+        (2.0 ** -134, 0x0000),                      # tie with zero -> even
+        (3 * 2.0 ** -134, 0x0002),                  # tie -> even
+        ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),     # largest finite
+        ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),     # tie at the top rounds to infinity
+        (float("inf"), 0x7F80), (float("-inf"), 0xFF80),
+    ]
+    got = oracle.bf16_from_f64(np.array([v for v, _ in cases], np.float64))
+    assert got.tolist() == [b for _, b in cases]
+
+
+def test_synth_bf16_rounding_agrees_with_torch():
+    """The input generator's rounding is torch's binary32 -> bf16 (ties to even)."""
+    rng = np.random.default_rng(14)
+    v = (rng.standard_normal(50000) * 30).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.to_bf16_bits(v), ref)
+
+
+def test_argument_errors():
+    with pytest.raises(ValueError):
+        oracle.rotate_quantize(np.zeros((2, 100), np.uint16), 64)    # cols % g != 0
+    with pytest.raises(ValueError):
+        oracle.rotate_quantize(np.zeros((2, 96), np.uint16), 96)     # g not a power of two
