@@ -1,0 +1,186 @@
+"""Throughput of the Hadamard-rotated INT8 linear layer on one MI355X.
+
+Workload (one step): the MLP pair of a transformer block at 4096 tokens,
+  up:   x [4096, 3840] bf16 -> rotate (g = 256) + per-token int8 -> GEMM with
+        W_up [10240, 3840] int8 -> y_up [4096, 10240] bf16
+  down: h [4096, 10240] bf16 -> rotate (g = 256) + per-token int8 -> GEMM with
+        W_down [3840, 10240] int8 -> y_down [4096, 3840] bf16
+Inputs are seeded synthetic (outlier-channel activations, N(0, 0.02) weights),
+resident in HBM before the timed region; the weights are rotated and quantized
+once, outside it (offline preparation).
+
+value = int8 ops of both GEMMs (2 M N K each) / wall time per step, in TOPS,
+with the activation rotate+quantize kernels inside the step.  Per-kernel times
+come from HIP events recorded on the launch stream around each kernel.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+M, K_UP, N_UP = 4096, 3840, 10240
+K_DOWN, N_DOWN = 10240, 3840
+G = 256
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def to_dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(inp, target_s: float) -> dict:
+    """The oracle (plain C, OpenMP over rows) on a bounded sample of the same
+    workload: the first R token rows of both layers, weights prepared outside."""
+    import oracle
+    qwu, swu = oracle.rotate_quantize(inp["w_up"], G)
+    qwd, swd = oracle.rotate_quantize(inp["w_down"], G)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.qlinear_forward(inp["x"][:rows], qwu, swu, G, intermediates=False)
+        oracle.qlinear_forward(inp["h"][:rows], qwd, swd, G, intermediates=False)
+        return time.perf_counter() - t0
+
+    rows = 8
+    t = run(rows)
+    rows = int(min(M, max(8, rows * target_s / max(t, 1e-3))))
+    t = run(rows)
+    ops = 2.0 * rows * (N_UP * K_UP + N_DOWN * K_DOWN)
+    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} of {M} token rows through both layers (rotate+quantize, exact int GEMM, "
+                      f"fp32 dequant, bf16 out); weights prepared outside; {t:.1f} s",
+            "seconds": round(t, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hadamard_rotated_int8_amd as h
+    from hadamard_rotated_int8_amd import synth
+
+    L = h.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    inp = synth.make_config("mlp", seed=0)
+    x, hh = to_dev_bf16(torch, inp["x"]), to_dev_bf16(torch, inp["h"])
+    w_up, w_down = to_dev_bf16(torch, inp["w_up"]), to_dev_bf16(torch, inp["w_down"])
+    qw_up, sw_up = h.sdnq_rotate_quantize_weight(w_up, G)
+    qw_down, sw_down = h.sdnq_rotate_quantize_weight(w_down, G)
+    del w_up, w_down
+    qx = torch.empty((M, K_UP), dtype=torch.int8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    qh = torch.empty((M, K_DOWN), dtype=torch.int8, device=dev)
+    shh = torch.empty((M,), dtype=torch.float32, device=dev)
+    y_up = torch.empty((M, N_UP), dtype=torch.bfloat16, device=dev)
+    y_down = torch.empty((M, N_DOWN), dtype=torch.bfloat16, device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {h.status_string(rc)}")
+
+    kernels = ["rotq_up", "gemm_up", "rotq_down", "gemm_down"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        check(L.sdnq_rotate_quantize_act(P(x), M, K_UP, G, None, P(qx), P(sx), sp), "rotq up")
+        if ev: ev[1].record(stream)
+        check(L.sdnq_qlinear_forward_quantized(P(qx), P(sx), M, K_UP, P(qw_up), P(sw_up), N_UP, None, None, 0,
+                                               0.0, P(y_up), None, 0, sp), "gemm up")
+        if ev: ev[2].record(stream)
+        check(L.sdnq_rotate_quantize_act(P(hh), M, K_DOWN, G, None, P(qh), P(shh), sp), "rotq down")
+        if ev: ev[3].record(stream)
+        check(L.sdnq_qlinear_forward_quantized(P(qh), P(shh), M, K_DOWN, P(qw_down), P(sw_down), N_DOWN, None, None,
+                                               0, 0.0, P(y_down), None, 0, sp), "gemm down")
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+    avg_ms = per.mean(axis=0)
+    ms_per_step = wall * 1e3 / args.steps
+    ops_up = 2.0 * M * N_UP * K_UP
+    ops_down = 2.0 * M * N_DOWN * K_DOWN
+    tops = (ops_up + ops_down) / (ms_per_step * 1e-3) / 1e12
+
+    gemm_s = (avg_ms[1] + avg_ms[3]) * 1e-3
+    gemm_tops = (ops_up + ops_down) / gemm_s / 1e12
+    rot_bytes = (M * K_UP * 3 + M * 4) + (M * K_DOWN * 3 + M * 4)  # bf16 in, int8 out, fp32 scale
+    rot_s = (avg_ms[0] + avg_ms[2]) * 1e-3
+    rot_gbs = rot_bytes / rot_s / 1e9
+
+    out = {
+        "metric": "INT8 TOPS of fused Hadamard-quantized linear, % of MI355X INT8 MFMA peak",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "pct_of_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "MLP up+down of one block: x[4096,3840] -> W_up[10240,3840], "
+                               "h[4096,10240] -> W_down[3840,10240], Hadamard block 256, per-token int8 "
+                               "activations, row-wise int8 weights, bf16 out",
+                   "tokens": M, "hadamard_group": G},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "gemm_i8_kernel (forward epilogue)",
+                     "per_launch_ops": [ops_up, ops_down]},
+        "rotate_quantize_roofline": {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(rot_gbs / HBM_PEAK_GBS, 4),
+                                     "per_launch_bytes": [M * K_UP * 3 + M * 4, M * K_DOWN * 3 + M * 4]},
+        "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,22 @@
-"""Hadamard-rotated INT8 quantized linear layer for AMD Instinct MI355X (gfx950)."""
+"""Hadamard-rotated INT8 quantized linear layer for AMD Instinct MI355X (gfx950).
+
+The public API is the C ABI of ``libsdnq_hip.so`` (``include/sdnq_hip.h``); the
+functions below are its ctypes binding, with the same names.
+"""
+from ._binding import (  # noqa: F401
+    SDNQ_ERR_INVALID_ARG,
+    SDNQ_ERR_LAUNCH,
+    SDNQ_ERR_UNSUPPORTED,
+    SDNQ_ERR_WORKSPACE,
+    SDNQ_OK,
+    SdnqError,
+    lib,
+    sdnq_gemm_i8_i32,
+    sdnq_qlinear_backward_input,
+    sdnq_qlinear_forward,
+    sdnq_qlinear_forward_quantized,
+    sdnq_rotate_quantize_act,
+    sdnq_rotate_quantize_weight,
+    sdnq_workspace_bytes,
+    status_string,
+)

@@ -1,0 +1,209 @@
+"""ctypes binding of libsdnq_hip.so (the C ABI declared in include/sdnq_hip.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch tensors supply device memory and the current HIP stream; the
+functions check dtype, device, shape and contiguity, allocate outputs (and the
+workspace when none is given) with torch, and call the entry point of the same
+name.  A missing or unloadable library raises at the first call; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsdnq_hip.so")
+
+SDNQ_OK, SDNQ_ERR_INVALID_ARG, SDNQ_ERR_UNSUPPORTED, SDNQ_ERR_WORKSPACE, SDNQ_ERR_LAUNCH = range(5)
+
+_lib = None
+
+
+class SdnqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python hadamard_rotated_int8_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    sigs = {
+        "sdnq_rotate_quantize_weight": [p, i64, i64, i32, p, p, p],
+        "sdnq_rotate_quantize_act": [p, i64, i64, i32, p, p, p, p],
+        "sdnq_qlinear_forward": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p, sz, p],
+        "sdnq_qlinear_forward_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
+        "sdnq_qlinear_backward_input": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
+        "sdnq_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p, sz, p],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.sdnq_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.sdnq_workspace_bytes.restype = sz
+    L.sdnq_status_string.argtypes = [ctypes.c_int]
+    L.sdnq_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().sdnq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SDNQ_OK:
+        raise SdnqError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, ndim, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def _workspace(nbytes: int, dev, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace
+
+
+def sdnq_workspace_bytes(m: int, n: int, k: int, rank: int = 0, is_backward: bool = False) -> int:
+    return int(lib().sdnq_workspace_bytes(m, n, k, rank, int(bool(is_backward))))
+
+
+def sdnq_rotate_quantize_weight(w: torch.Tensor, g: int):
+    """W [n, k] bf16 -> (qw [n, k] int8, w_scale [n] fp32)."""
+    _need(w, torch.bfloat16, 2, "w")
+    n, k = w.shape
+    qw = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    sw = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check(lib().sdnq_rotate_quantize_weight(_ptr(w), n, k, g, _ptr(qw), _ptr(sw), _stream(w.device)),
+           "sdnq_rotate_quantize_weight")
+    return qw, sw
+
+
+def sdnq_rotate_quantize_act(x: torch.Tensor, g: int, col_scale: torch.Tensor | None = None):
+    """x [m, k] bf16 -> (qx [m, k] int8, x_scale [m] fp32)."""
+    _need(x, torch.bfloat16, 2, "x")
+    if col_scale is not None:
+        _need(col_scale, torch.float32, 1, "col_scale")
+    m, k = x.shape
+    qx = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    sx = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(lib().sdnq_rotate_quantize_act(_ptr(x), m, k, g, _ptr(col_scale), _ptr(qx), _ptr(sx),
+                                          _stream(x.device)), "sdnq_rotate_quantize_act")
+    return qx, sx
+
+
+def sdnq_qlinear_forward(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale=0.0, out=None,
+                         workspace=None):
+    """y [m, n] bf16 = dequant(rotq(x) . qw^T) + lora_scale * (x lora_a) lora_b."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(qw, torch.int8, 2, "qw")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    m, k = x.shape
+    n = qw.shape[0]
+    rank = 0
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, torch.bfloat16, 2, "lora_a")
+        _need(lora_b, torch.bfloat16, 2, "lora_b")
+        rank = lora_a.shape[1]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    nb = sdnq_workspace_bytes(m, n, k, rank, False)
+    ws = _workspace(nb, x.device, workspace)
+    _check(lib().sdnq_qlinear_forward(_ptr(x), m, k, _ptr(qw), _ptr(w_scale), n, g, _ptr(lora_a), _ptr(lora_b),
+                                      rank, float(lora_scale), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
+           "sdnq_qlinear_forward")
+    return y
+
+
+def sdnq_qlinear_forward_quantized(qx, x_scale, qw, w_scale, t=None, lora_b=None, lora_scale=0.0, out=None,
+                                   workspace=None):
+    """y [m, n] bf16 from pre-quantized activations (qx, x_scale)."""
+    _need(qx, torch.int8, 2, "qx")
+    _need(x_scale, torch.float32, 1, "x_scale")
+    _need(qw, torch.int8, 2, "qw")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    m, k = qx.shape
+    n = qw.shape[0]
+    rank = 0
+    if t is not None or lora_b is not None:
+        _need(t, torch.bfloat16, 2, "t")
+        _need(lora_b, torch.bfloat16, 2, "lora_b")
+        rank = t.shape[1]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=qx.device)
+    nb = sdnq_workspace_bytes(m, n, k, rank, False)
+    ws = _workspace(nb, qx.device, workspace) if rank else workspace
+    _check(lib().sdnq_qlinear_forward_quantized(_ptr(qx), _ptr(x_scale), m, k, _ptr(qw), _ptr(w_scale), n,
+                                                _ptr(t), _ptr(lora_b), rank, float(lora_scale), _ptr(y),
+                                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(qx.device)),
+           "sdnq_qlinear_forward_quantized")
+    return y
+
+
+def sdnq_qlinear_backward_input(dy, qw, w_scale, g, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
+                                want_lora_grads=True, workspace=None):
+    """Returns (dx [m, k] bf16, grad_a [k, r] or None, grad_b [r, n] or None)."""
+    _need(dy, torch.bfloat16, 2, "dy")
+    _need(qw, torch.int8, 2, "qw")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    m, n = dy.shape
+    k = qw.shape[1]
+    rank = 0
+    ga = gb = None
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, torch.bfloat16, 2, "lora_a")
+        _need(lora_b, torch.bfloat16, 2, "lora_b")
+        rank = lora_a.shape[1]
+        if want_lora_grads and x is not None:
+            _need(x, torch.bfloat16, 2, "x")
+            ga = torch.empty((k, rank), dtype=torch.bfloat16, device=dy.device)
+            gb = torch.empty((rank, n), dtype=torch.bfloat16, device=dy.device)
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dy.device)
+    nb = sdnq_workspace_bytes(m, n, k, rank, True)
+    ws = _workspace(nb, dy.device, workspace)
+    _check(lib().sdnq_qlinear_backward_input(_ptr(dy), m, n, _ptr(qw), _ptr(w_scale), k, g, _ptr(x), _ptr(lora_a),
+                                             _ptr(lora_b), rank, float(lora_scale), _ptr(dx), _ptr(ga), _ptr(gb),
+                                             _ptr(ws), ws.numel(), _stream(dy.device)),
+           "sdnq_qlinear_backward_input")
+    return dx, ga, gb
+
+
+def sdnq_gemm_i8_i32(a, b, b_layout: int = 0, workspace=None):
+    """Exact int32 product: b_layout 0: a [m,k] . b[n,k]^T;  1: a [m,k] . b [k,n]."""
+    _need(a, torch.int8, 2, "a")
+    _need(b, torch.int8, 2, "b")
+    m, k = a.shape
+    n = b.shape[0] if b_layout == 0 else b.shape[1]
+    c = torch.empty((m, n), dtype=torch.int32, device=a.device)
+    ws = _workspace(k * n, a.device, workspace) if b_layout == 1 else workspace
+    _check(lib().sdnq_gemm_i8_i32(_ptr(a), _ptr(b), m, n, k, b_layout, _ptr(c), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(a.device)), "sdnq_gemm_i8_i32")
+    return c

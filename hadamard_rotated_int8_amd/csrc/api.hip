@@ -1,0 +1,296 @@
+// C ABI of libsdnq_hip: argument validation, workspace carving and the launch
+// sequence of each entry point.  Every check runs before the first launch, so a
+// call that fails writes nothing.  See sdnq_hip.h for the contract.
+#include <string.h>
+
+#include "sdnq_internal.hpp"
+
+using namespace sdnq;
+
+namespace {
+
+constexpr int64_t kMaxFeature = 65536;  // a whole row stays on chip in the rotate+quantize kernel
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_group(int32_t g) { return g == 1 || g == 64 || g == 128 || g == 256; }
+
+bool valid_rank(int32_t rank) { return rank >= 16 && rank <= 128 && rank % 16 == 0; }
+
+sdnq_status_t check_feature(int64_t d) {
+  if (d <= 0) return SDNQ_ERR_INVALID_ARG;
+  if (d % 16 != 0 || d > kMaxFeature) return SDNQ_ERR_UNSUPPORTED;
+  return SDNQ_OK;
+}
+
+// Workspace layouts (each region starts on a 256-byte boundary).
+struct FwdLayout {
+  size_t qx, sx, t, at, bt, total;
+};
+FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
+  FwdLayout L{};
+  size_t off = 0;
+  L.qx = off; off += align_up((size_t)m * (size_t)k);
+  L.sx = off; off += align_up((size_t)m * 4);
+  if (rank > 0) {
+    L.t = off; off += align_up((size_t)m * (size_t)rank * 2);
+    L.at = off; off += align_up((size_t)rank * (size_t)k * 2);
+    L.bt = off; off += align_up((size_t)n * (size_t)rank * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+struct BwdLayout {
+  size_t qdy, sdy, wt, gr, tx, at, part, total;
+};
+BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
+  BwdLayout L{};
+  size_t off = 0;
+  L.qdy = off; off += align_up((size_t)m * (size_t)n);
+  L.sdy = off; off += align_up((size_t)m * 4);
+  L.wt = off; off += align_up((size_t)k * (size_t)n);
+  if (rank > 0) {
+    L.gr = off; off += align_up((size_t)m * (size_t)rank * 2);
+    L.tx = off; off += align_up((size_t)m * (size_t)rank * 2);
+    L.at = off; off += align_up((size_t)rank * (size_t)k * 2);
+    const size_t cells = (size_t)rank * (size_t)(k > n ? k : n);
+    L.part = off; off += align_up((size_t)lora_grad_splits(m) * cells * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+char *ws_at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+sdnq_status_t launched(hipError_t e) { return e == hipSuccess ? SDNQ_OK : SDNQ_ERR_LAUNCH; }
+
+#define SDNQ_TRY(expr)                          \
+  do {                                          \
+    sdnq_status_t s_ = (expr);                  \
+    if (s_ != SDNQ_OK) return s_;               \
+  } while (0)
+
+#define SDNQ_LAUNCH(expr)                       \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return SDNQ_ERR_LAUNCH; \
+  } while (0)
+
+// LoRA arguments: either no adapter (both factors NULL, any rank ignored) or both
+// factors with a supported rank.
+sdnq_status_t check_lora(const void *a, const void *b, int32_t rank, int32_t *eff_rank) {
+  if (!a && !b) {
+    *eff_rank = 0;
+    return SDNQ_OK;
+  }
+  if (!a || !b) return SDNQ_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b)) return SDNQ_ERR_INVALID_ARG;
+  if (!valid_rank(rank)) return SDNQ_ERR_UNSUPPORTED;
+  *eff_rank = rank;
+  return SDNQ_OK;
+}
+
+sdnq_status_t check_rotq(const void *x, int64_t m, int64_t k, int32_t g, const void *col_scale, const void *q,
+                         const void *s) {
+  if (m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!x || !q || !s)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(k));
+  if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return SDNQ_ERR_INVALID_ARG;
+  if (col_scale && !aligned16(col_scale)) return SDNQ_ERR_INVALID_ARG;
+  return SDNQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sdnq_status_string(sdnq_status_t status) {
+  switch (status) {
+    case SDNQ_OK: return "success";
+    case SDNQ_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or misaligned pointer)";
+    case SDNQ_ERR_UNSUPPORTED: return "unsupported configuration (block size, dimension multiple, size limit or rank)";
+    case SDNQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDNQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t sdnq_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t rank, int32_t is_backward) {
+  if (m < 0 || n <= 0 || k <= 0 || rank < 0) return 0;
+  if (rank > 0 && !valid_rank(rank)) return 0;
+  return is_backward ? bwd_layout(m, n, k, rank).total : fwd_layout(m, n, k, rank).total;
+}
+
+sdnq_status_t sdnq_rotate_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int32_t g, int8_t *qw,
+                                          float *w_scale, void *stream) {
+  SDNQ_TRY(check_rotq(w, n, k, g, nullptr, qw, w_scale));
+  if (n == 0) return SDNQ_OK;
+  (void)hipGetLastError();
+  return launched(launch_rotate_quantize(w, n, k, g, nullptr, qw, w_scale, (hipStream_t)stream));
+}
+
+sdnq_status_t sdnq_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int32_t g, const float *col_scale,
+                                       int8_t *qx, float *x_scale, void *stream) {
+  SDNQ_TRY(check_rotq(x, m, k, g, col_scale, qx, x_scale));
+  if (m == 0) return SDNQ_OK;
+  (void)hipGetLastError();
+  return launched(launch_rotate_quantize(x, m, k, g, col_scale, qx, x_scale, (hipStream_t)stream));
+}
+
+sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_scale, int64_t m, int64_t k,
+                                             const int8_t *qw, const float *w_scale, int64_t n, const uint16_t *t,
+                                             const uint16_t *lora_b, int32_t rank, float lora_scale, uint16_t *y,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!qx || !x_scale || !y)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(k));
+  SDNQ_TRY(check_feature(n));
+  if (!aligned16(qx) || !aligned16(x_scale) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y))
+    return SDNQ_ERR_INVALID_ARG;
+  int32_t r = 0;
+  SDNQ_TRY(check_lora(t, lora_b, rank, &r));
+  const FwdLayout L = fwd_layout(m, n, k, r);
+  if (r > 0 && (!workspace || workspace_bytes < L.total || !aligned16(workspace))) return SDNQ_ERR_WORKSPACE;
+  if (m == 0) return SDNQ_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  GemmArgs ga{};
+  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k;
+  ga.row_scale = x_scale; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
+  if (r > 0) {
+    uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
+    SDNQ_LAUNCH(launch_transpose_u16(lora_b, r, n, bt, s));
+    ga.lora_t = t; ga.lora_r = bt; ga.rank = r; ga.lora_scale = lora_scale;
+  }
+  return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
+}
+
+sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
+                                   int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b,
+                                   int32_t rank, float lora_scale, uint16_t *y, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!x || !y)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(k));
+  SDNQ_TRY(check_feature(n));
+  if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y)) return SDNQ_ERR_INVALID_ARG;
+  int32_t r = 0;
+  SDNQ_TRY(check_lora(lora_a, lora_b, rank, &r));
+  const FwdLayout L = fwd_layout(m, n, k, r);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SDNQ_ERR_WORKSPACE;
+  if (m == 0) return SDNQ_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  int8_t *qx = reinterpret_cast<int8_t *>(ws_at(workspace, L.qx));
+  float *sx = reinterpret_cast<float *>(ws_at(workspace, L.sx));
+  SDNQ_LAUNCH(launch_rotate_quantize(x, m, k, g, nullptr, qx, sx, s));
+
+  GemmArgs ga{};
+  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k;
+  ga.row_scale = sx; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
+  if (r > 0) {
+    uint16_t *t = reinterpret_cast<uint16_t *>(ws_at(workspace, L.t));
+    uint16_t *at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
+    uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
+    SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));   // A [k, r] -> A^T [r, k]
+    SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, 1.0f, t, s));  // t = x A
+    SDNQ_LAUNCH(launch_transpose_u16(lora_b, r, n, bt, s));   // B [r, n] -> B^T [n, r]
+    ga.lora_t = t; ga.lora_r = bt; ga.rank = r; ga.lora_scale = lora_scale;
+  }
+  return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
+}
+
+sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw,
+                                          const float *w_scale, int64_t k, int32_t g, const uint16_t *x,
+                                          const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                          float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+  if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!dy || !dx)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(k));
+  SDNQ_TRY(check_feature(n));
+  if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
+  if (!aligned16(dy) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(dx)) return SDNQ_ERR_INVALID_ARG;
+  int32_t r = 0;
+  SDNQ_TRY(check_lora(lora_a, lora_b, rank, &r));
+  const bool want_ga = grad_a != nullptr, want_gb = grad_b != nullptr;
+  if ((want_ga || want_gb) && (r == 0 || (m > 0 && !x))) return SDNQ_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (grad_a && !aligned16(grad_a)) || (grad_b && !aligned16(grad_b)))
+    return SDNQ_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(m, n, k, r);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SDNQ_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (m == 0) {
+    // Empty batch: the LoRA gradients are empty sums.
+    (void)hipGetLastError();
+    if (want_ga) SDNQ_LAUNCH(launch_fill_zero_u16(grad_a, k * r, s));
+    if (want_gb) SDNQ_LAUNCH(launch_fill_zero_u16(grad_b, (int64_t)r * n, s));
+    return SDNQ_OK;
+  }
+  (void)hipGetLastError();
+  int8_t *qdy = reinterpret_cast<int8_t *>(ws_at(workspace, L.qdy));
+  float *sdy = reinterpret_cast<float *>(ws_at(workspace, L.sdy));
+  int8_t *wt = reinterpret_cast<int8_t *>(ws_at(workspace, L.wt));
+  // dY' = dY * w_scale (column fold), per-token quantization, no rotation along n.
+  SDNQ_LAUNCH(launch_rotate_quantize(dy, m, n, 1, w_scale, qdy, sdy, s));
+  SDNQ_LAUNCH(launch_transpose_i8(qw, n, k, wt, s));  // qw [n, k] -> [k, n]
+
+  GemmArgs ga{};
+  ga.a = qdy; ga.b = wt; ga.m = m; ga.n = k; ga.k = n;
+  ga.row_scale = sdy; ga.out_bf16 = dx; ga.g = g;
+  uint16_t *gr = nullptr, *tx = nullptr, *at = nullptr;
+  if (r > 0) {
+    gr = reinterpret_cast<uint16_t *>(ws_at(workspace, L.gr));
+    SDNQ_LAUNCH(launch_lora_down(dy, m, n, lora_b, r, lora_scale, gr, s));  // g_r = scale * dY B^T
+    ga.lora_t = gr; ga.lora_r = lora_a; ga.rank = r; ga.lora_scale = 1.0f;  // + g_r A^T
+  }
+  SDNQ_LAUNCH(launch_gemm_i8(Epilogue::kBackward, ga, s));
+
+  if (r > 0) {
+    float *part = reinterpret_cast<float *>(ws_at(workspace, L.part));
+    if (want_ga) SDNQ_LAUNCH(launch_lora_grad(x, k, gr, r, m, 1.0f, part, grad_a, s));  // x^T g_r
+    if (want_gb) {
+      tx = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tx));
+      at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
+      SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));
+      SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, 1.0f, tx, s));                  // t = x A
+      SDNQ_LAUNCH(launch_lora_grad(tx, r, dy, n, m, lora_scale, part, grad_b, s));  // scale * t^T dY
+    }
+  }
+  return SDNQ_OK;
+}
+
+sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int64_t n, int64_t k, int32_t b_layout,
+                               int32_t *c, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!b || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!a || !c)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(k));
+  SDNQ_TRY(check_feature(n));
+  if (b_layout != 0 && b_layout != 1) return SDNQ_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return SDNQ_ERR_INVALID_ARG;
+  if (b_layout == 1 && (!workspace || workspace_bytes < (size_t)k * (size_t)n || !aligned16(workspace)))
+    return SDNQ_ERR_WORKSPACE;
+  if (m == 0) return SDNQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const int8_t *bb = b;
+  if (b_layout == 1) {
+    int8_t *bt = static_cast<int8_t *>(workspace);
+    SDNQ_LAUNCH(launch_transpose_i8(b, k, n, bt, s));  // b [k, n] -> [n, k]
+    bb = bt;
+  }
+  GemmArgs ga{};
+  ga.a = a; ga.b = bb; ga.m = m; ga.n = n; ga.k = k; ga.c_i32 = c; ga.g = 1;
+  return launched(launch_gemm_i8(Epilogue::kInt32, ga, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+// G1: block Walsh-Hadamard rotation fused with per-row absmax int8 quantization.
+//
+// What it computes (one row of a bf16 [rows, cols] matrix at a time):
+//   y = fl32(1/sqrt(g)) * H_g v on every contiguous block of g values of the row
+//       ("ConvRot / Hadamard SDNQ", "What The Options Do": rotation block =
+//       hadamard_group_size along in-features), with v = x (or x * col_scale);
+//   a = max |y| over the whole row; s = fl32(a / 127); r = fl32(127 / a);
+//   q = round_half_even(fl32(y * r)) in [-127, 127]  (a row with a < 2^-100 is
+//       first scaled by 2^100, exactly, so that 127 / a stays finite)
+//       (HSWQ README, "Rigorous grid / pack simulation": rotate, then absmax on
+//       a symmetric INT8 grid).
+// The butterfly runs the stages h = 1, 2, ..., g/2 in that order, every pair
+// (i, i+h) becoming (a+b, a-b) in binary32, so the codes and scales are
+// bit-identical to a scalar evaluation of the same steps.
+//
+// Layout.  A row is cut into superblocks of 256 values; a quad of 4 adjacent lanes
+// owns one superblock.  Lane l4 of the quad holds the 64 values
+//     e = 32*i + 8*l4 + j      (i = 0..7, j = 0..7)
+// loaded as eight 16-byte loads (each quad reads 64 contiguous bytes per load).
+// So value-index bits 0-2 (j) and 5-7 (i) live in registers and bits 3-4 in the
+// lane-within-quad: stages h = 1, 2, 4, 32, 64, 128 are register butterflies and
+// h = 8, 16 are quad_perm DPP exchanges.  The whole row stays in registers until
+// its absmax is known (one workgroup holds `rows_per_wg` complete rows).
+//
+// Cross-lane stages keep a per-lane sign: the upper lane of a pair computes
+// fma(partner, -1, self) = self - partner = -(a - b), which rounds exactly like
+// a - b up to the sign; the sign of every lane is (-1)^popcount(l4) after both
+// stages and is folded into the normalization multiply.
+#include "sdnq_internal.hpp"
+
+namespace sdnq {
+namespace {
+
+constexpr int kMaxRowsPerWg = 32;
+constexpr int kMaxThreads = 1024;
+// 1.5 * 2^23: adding it to |t| < 2^22 rounds t to an integer (ties to even) and
+// leaves that integer, two's complement, in the low mantissa bits.
+constexpr float kRoundMagic = 12582912.0f;
+
+// fl32(1/sqrt(128)) = 2^-3.5 rounded to nearest binary32.
+constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;
+static_assert(__builtin_bit_cast(uint32_t, kInvSqrt128) == 0x3DB504F3u, "1/sqrt(128) constant");
+
+template <int G>
+__device__ __forceinline__ float norm_const() {
+  if constexpr (G == 64) return 0.125f;
+  else if constexpr (G == 128) return kInvSqrt128;
+  else if constexpr (G == 256) return 0.0625f;
+  else return 1.0f;
+}
+
+// Byte 0 of the magic-rounded value = the int8 code.
+__device__ __forceinline__ uint32_t code_bits(float t) { return __float_as_uint(t + kRoundMagic); }
+
+__device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+  // v_perm_b32: selector byte values 0-3 pick the second operand's bytes, 4-7 the first's.
+  uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);  // [c0.b0, c1.b0, 0, 0]
+  uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);  // [c2.b0, c3.b0, 0, 0]
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);         // [lo.b0, lo.b1, hi.b0, hi.b1]
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <int G, bool COLSCALE>
+__global__ __launch_bounds__(kMaxThreads) void rotq_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
+    int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg) {
+  __shared__ uint32_t row_max[kMaxRowsPerWg];
+
+  const int tid = threadIdx.x;
+  const int r_local = tid / t_row;
+  const int qt = tid - r_local * t_row;
+  const int sb = qt >> 2;     // superblock of this quad
+  const int l4 = qt & 3;      // lane within the quad
+  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + r_local;
+  const bool row_ok = row < rows;
+  if (tid < rows_per_wg) row_max[tid] = 0u;
+
+  // ---- load: 8 x 16 bytes, e0(i) = sb*256 + 32*i + 8*l4
+  const int64_t base = sb * 256 + 8 * l4;
+  v4u raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t e0 = base + 32 * i;
+    if (row_ok && e0 < cols)
+      raw[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(x + row * cols + e0));
+    else
+      raw[i] = v4u{0u, 0u, 0u, 0u};
+  }
+
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v[i][2 * w] = bf16_lo(raw[i][w]);
+      v[i][2 * w + 1] = bf16_hi(raw[i][w]);
+    }
+  }
+
+  if constexpr (COLSCALE) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t e0 = base + 32 * i;
+      if (e0 < cols) {
+        const float4 c0 = *reinterpret_cast<const float4 *>(col_scale + e0);
+        const float4 c1 = *reinterpret_cast<const float4 *>(col_scale + e0 + 4);
+        v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
+        v[i][2] = v[i][2] * c0.z; v[i][3] = v[i][3] * c0.w;
+        v[i][4] = v[i][4] * c1.x; v[i][5] = v[i][5] * c1.y;
+        v[i][6] = v[i][6] * c1.z; v[i][7] = v[i][7] * c1.w;
+      }
+    }
+  }
+
+  float sign = 1.0f;  // per-lane sign of the stored values after the DPP stages
+  if constexpr (G > 1) {
+    // h = 1, 2, 4: value bits 0-2 (register index j)
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if ((j & h) == 0) {
+            const float a = v[i][j], b = v[i][j + h];
+            v[i][j] = a + b;
+            v[i][j + h] = a - b;
+          }
+        }
+      }
+    }
+    // h = 8: lane xor 1 within the quad; h = 16: lane xor 2
+    {
+      const float m1 = (l4 & 1) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = __builtin_fmaf(dpp<0xB1>(v[i][j]), m1, v[i][j]);
+      const float m2 = (l4 & 2) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = __builtin_fmaf(dpp<0x4E>(v[i][j]), m2, v[i][j]);
+      sign = m1 * m2;
+    }
+    // h = 32, 64, 128: value bits 5-7 (register index i), up to g/2
+#pragma unroll
+    for (int hi = 1; hi < 8; hi <<= 1) {
+      if (32 * hi < G) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if ((i & hi) == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float a = v[i][j], b = v[i + hi][j];
+              v[i][j] = a + b;
+              v[i + hi][j] = a - b;
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // g = 128: the normalization constant is inexact, so apply it to every value now.
+  if constexpr (G == 128) {
+    const float sc = sign * norm_const<G>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * sc;
+  }
+
+  float loc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) loc = fmaxf(loc, fabsf(v[i][j]));
+
+  __syncthreads();
+  if (row_ok) atomicMax(&row_max[r_local], __float_as_uint(loc));
+  __syncthreads();
+  float a = __uint_as_float(row_max[r_local]);
+
+  // g = 64, 256: norm_const is a power of two, so a = fl32(max|u| * c) = max|fl32(u * c)|.
+  if constexpr (G == 64 || G == 256) a = a * norm_const<G>();
+  const float s = a / 127.0f;
+  // Rows with a < 2^-100 are scaled by 2^100 (exact) before r = 127/a is formed,
+  // which would otherwise overflow binary32.
+  const bool tiny = a < 0x1p-100f;
+  const float up = tiny ? 0x1p100f : 1.0f;
+  const float as = a * up;
+  const float r = (as > 0.0f) ? 127.0f / as : 0.0f;
+  if (row_ok && qt == 0) scale[row] = s;
+
+  // Multiplier turning the stored value into fl32(y * r).
+  //  - g = 64/256, a >= 2^-100: y = u*c exactly for every value that can get a
+  //    nonzero code, and (c * r) is exact, so fl32(u * (c*r)) = fl32(fl32(u*c) * r);
+  //    values with u*c below the normal range give |y*r| < 2^-19 on both routes.
+  //  - g = 1/128: the stored value already is y.
+  //  - tiny rows: normalize exactly as written, scale by 2^100, then multiply by r.
+  float mult = r;
+  if (!tiny) {
+    if constexpr (G == 64 || G == 256) mult = r * norm_const<G>() * sign;
+  } else {
+    float sc = 1.0f;
+    if constexpr (G == 64 || G == 256) sc = sign * norm_const<G>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = (v[i][j] * sc) * up;
+  }
+
+  if (row_ok) {
+    int8_t *qr = q + row * cols;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t e0 = base + 32 * i;
+      if (e0 < cols) {
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float t = v[i][j] * mult;
+          c[j] = code_bits(t);
+        }
+        uint2 packed;
+        packed.x = pack4(c[0], c[1], c[2], c[3]);
+        packed.y = pack4(c[4], c[5], c[6], c[7]);
+        *reinterpret_cast<uint2 *>(qr + e0) = packed;
+      }
+    }
+  }
+}
+
+// Rows per workgroup: the count with the fewest idle lanes in the last wavefront,
+// then the one closest to 256 threads.
+int pick_rows_per_wg(int t_row) {
+  int best_r = 1;
+  double best_waste = 2.0;
+  int best_dist = 1 << 30;
+  for (int r = 1; r <= kMaxRowsPerWg && r * t_row <= kMaxThreads; ++r) {
+    const int threads = r * t_row;
+    const int padded = (threads + 63) / 64 * 64;
+    const double waste = double(padded - threads) / padded;
+    const int dist = threads > 256 ? threads - 256 : 256 - threads;
+    if (waste < best_waste - 1e-9 || (waste < best_waste + 1e-9 && dist < best_dist)) {
+      best_r = r;
+      best_waste = waste;
+      best_dist = dist;
+    }
+  }
+  return best_r;
+}
+
+template <int G, bool CS>
+hipError_t launch_typed(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale,
+                        int8_t *q, float *scale, hipStream_t stream) {
+  const int t_row = 4 * (int)((cols + 255) / 256);
+  const int rpw = pick_rows_per_wg(t_row);
+  const int64_t blocks = (rows + rpw - 1) / rpw;
+  hipLaunchKernelGGL((rotq_kernel<G, CS>), dim3((unsigned)blocks), dim3(rpw * t_row), 0, stream, x,
+                     rows, cols, col_scale, q, scale, t_row, rpw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
+                                  const float *col_scale, int8_t *q, float *scale,
+                                  hipStream_t stream) {
+  const bool cs = col_scale != nullptr;
+  switch (g) {
+    case 1: return cs ? launch_typed<1, true>(x, rows, cols, col_scale, q, scale, stream)
+                      : launch_typed<1, false>(x, rows, cols, col_scale, q, scale, stream);
+    case 64: return cs ? launch_typed<64, true>(x, rows, cols, col_scale, q, scale, stream)
+                       : launch_typed<64, false>(x, rows, cols, col_scale, q, scale, stream);
+    case 128: return cs ? launch_typed<128, true>(x, rows, cols, col_scale, q, scale, stream)
+                        : launch_typed<128, false>(x, rows, cols, col_scale, q, scale, stream);
+    case 256: return cs ? launch_typed<256, true>(x, rows, cols, col_scale, q, scale, stream)
+                        : launch_typed<256, false>(x, rows, cols, col_scale, q, scale, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdnq

@@ -1,0 +1,81 @@
+// Internal declarations shared by the HIP translation units of libsdnq_hip.
+// Kernels are written for gfx950 (CDNA4): 64-lane wavefronts, MFMA, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sdnq_hip.h"
+
+namespace sdnq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// bf16 bits -> fp32 (exact): the bf16 pattern is the high half of the fp32 one.
+__device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ------------------------------------------------------------------ launches --
+// Each returns hipSuccess or the launch error; arguments are validated by the caller.
+
+// G1: rotate (block g) + per-row absmax int8 quantization of a bf16 [rows, cols] matrix.
+hipError_t launch_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
+                                  const float *col_scale, int8_t *q, float *scale,
+                                  hipStream_t stream);
+
+// G2 epilogue selector.
+enum class Epilogue { kInt32, kForward, kBackward };
+
+struct GemmArgs {
+  const int8_t *a;        // [m, k]  column operand (tokens)
+  const int8_t *b;        // [n, k]  row operand (weight rows, or transposed weight)
+  int64_t m, n, k;
+  // kInt32
+  int32_t *c_i32;         // [m, n]
+  // kForward / kBackward
+  const float *row_scale; // [m]  token scale
+  const float *col_scale; // [n]  weight row scale (forward only, else nullptr)
+  const uint16_t *lora_t; // [m, rank] bf16 left factor (nullable)
+  const uint16_t *lora_r; // [n, rank] bf16 right factor, one row per output column (nullable)
+  int rank;
+  float lora_scale;
+  int g;                  // backward: inverse rotation block along n (1, 64, 128, 256)
+  uint16_t *out_bf16;     // [m, n]
+};
+
+hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream);
+
+// int8 [rows, cols] -> [cols, rows]
+hipError_t launch_transpose_i8(const int8_t *in, int64_t rows, int64_t cols, int8_t *out,
+                               hipStream_t stream);
+// 16-bit [rows, cols] -> [cols, rows]
+hipError_t launch_transpose_u16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out,
+                                hipStream_t stream);
+
+// out[0 .. count) = 0 (16-bit elements)
+hipError_t launch_fill_zero_u16(uint16_t *out, int64_t count, hipStream_t stream);
+
+// out[m, r] = bf16(scale * sum_c x[m, c] * rmat[r, c]); x [m, cols], rmat [rank, cols] bf16.
+hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat,
+                            int rank, float scale, uint16_t *out, hipStream_t stream);
+
+// Token reduction: part[s, a, b] = sum over the tokens of split s of p[t, a] * q[t, b]
+// (p [m, pa], q [m, qb] bf16), then out[a, b] = bf16(scale * sum_s part[s, a, b]).
+int lora_grad_splits(int64_t m);
+hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
+                            float scale, float *partials, uint16_t *out, hipStream_t stream);
+
+}  // namespace sdnq

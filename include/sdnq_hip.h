@@ -1,0 +1,151 @@
+/*
+ * sdnq_hip.h -- C ABI of the Hadamard-rotated INT8 quantized linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the SDNQ Hadamard path used by ConvRot:
+ *  - "ConvRot / Hadamard SDNQ" (SimpleTuner docs), "What The Options Do": the
+ *    weight is rotated block-wise along in-features with block size
+ *    hadamard_group_size (256 for ConvRot, smaller blocks for the QuaRot-style
+ *    path) and quantized to int8 with static full-row scales (group_size -1);
+ *    the int8 quantized matmul stays active; "PEFT Behavior": LoRA adapters stay
+ *    trainable in bf16 on the frozen int8 base.
+ *  - "SDNQ: SD.Next Quantization Engine", feature list: Hadamard rotation on the
+ *    quantized weights and on the quantized matmul, INT8 quantized matmul;
+ *    SDNQConfig example: dequantize_fp32 keeps scales and dequantization in FP32;
+ *    quantized-training example: the quantized matmul runs in the backward pass.
+ *  - HSWQ README, "Rigorous grid / pack simulation": ConvRot INT8 is "Hadamard
+ *    rotate, then channelwise absmax" on a symmetric INT8 grid.
+ *
+ * Definitions used throughout (the pages give the method in words only; these
+ * are the readings this library implements):
+ *  - H_g: the g x g Sylvester Hadamard matrix in natural order; the rotation of a
+ *    row multiplies each contiguous block of g values by H_g and by fl32(1/sqrt(g)),
+ *    evaluated as an in-place fp32 butterfly with stages h = 1, 2, ..., g/2, each
+ *    pair (i, i+h) becoming (a+b, a-b).  g = 1 means no rotation.
+ *  - row quantization: a = max |y| over the whole row, scale s = fl32(a/127),
+ *    r = fl32(127/a) (0 if a == 0), code = round-half-even(fl32(y*r)) clamped to
+ *    [-127, 127].  A row with a < 2^-100 is first multiplied by 2^100 (exact), so
+ *    that r stays finite; s is always fl32(a/127) of the row as given.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are row-major and contiguous.  bf16 tensors are passed as
+ *    uint16_t bit patterns.  Every pointer is a DEVICE pointer.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on `stream` and returns; it never allocates, frees or
+ *    synchronizes and keeps no state between calls, so calls on different
+ *    streams with disjoint buffers may run concurrently.
+ *  - The caller owns every buffer, including the workspace.
+ *  - Argument checks run before anything is enqueued: a call that returns an
+ *    error has written nothing.  Errors raised by a kernel that already started
+ *    (a memory fault on a bad pointer) surface at the caller's next
+ *    synchronization, as with any HIP kernel.
+ *  - Shape limits: m >= 0; n, k >= 1; every feature dimension (k, n) must be a
+ *    multiple of 16 and at most 65536 (a whole row is held on chip while its
+ *    absmax is found; this also keeps 127*127*K far below 2^31, the int32
+ *    accumulator bound); k % g == 0.
+ *  - m == 0 is an empty batch: pointers to buffers with m rows may be NULL, nothing
+ *    is read, and the only work enqueued is zeroing grad_a / grad_b when the
+ *    backward pass requests them (empty sums).
+ *  - Alignment: every pointer must be 16-byte aligned.
+ *  - Non-finite inputs (NaN, Inf) give unspecified outputs; they are not checked.
+ */
+#ifndef SDNQ_HIP_H
+#define SDNQ_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDNQ_OK = 0,
+    SDNQ_ERR_INVALID_ARG = 1,  /* null required pointer, negative or zero size, misaligned pointer */
+    SDNQ_ERR_UNSUPPORTED = 2,  /* g not in {1,64,128,256}, k % g != 0, a feature dimension not a
+                                  multiple of 16 or above 65536, rank not in {16,32,...,128} */
+    SDNQ_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than sdnq_workspace_bytes() */
+    SDNQ_ERR_LAUNCH = 4        /* a kernel launch was rejected by the HIP runtime */
+} sdnq_status_t;
+
+/* Offline weight preparation: rotate each row of w[n,k] (bf16) along k with block
+ * g, then quantize each row with its own absmax scale.
+ *   out: qw[n,k] int8 codes, w_scale[n] fp32 (the full-row static scale). */
+sdnq_status_t sdnq_rotate_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int32_t g,
+                                          int8_t *qw, float *w_scale, void *stream);
+
+/* Run-time activation quantization: for each token (row) of x[m,k] (bf16),
+ * optionally multiply column j by col_scale[j] (fp32, nullable; used by the
+ * backward pass to fold the weight row scales into dY, with g = 1), rotate with
+ * block g, then quantize the row with its own absmax scale (per-token).
+ *   out: qx[m,k] int8, x_scale[m] fp32. */
+sdnq_status_t sdnq_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int32_t g,
+                                       const float *col_scale, int8_t *qx, float *x_scale,
+                                       void *stream);
+
+/* Forward of the quantized linear layer:
+ *   y[m,n] = bf16( fp32(rotq(x) . qw^T) * x_scale[m] * w_scale[n]
+ *                  + lora_scale * ((x lora_a) lora_b)[m,n] )
+ * x[m,k] bf16; qw[n,k] int8 and w_scale[n] fp32 from sdnq_rotate_quantize_weight
+ * with the same g; lora_a[k,rank] and lora_b[rank,n] bf16 (both NULL and rank 0
+ * for no adapter; the adapter sees the unrotated x); y[m,n] bf16.
+ * The int8 x codes and the int32 accumulators never leave the GPU's workspace and
+ * registers; the LoRA factor x.lora_a is rounded to bf16 in the workspace.
+ * workspace: at least sdnq_workspace_bytes(m, n, k, rank, 0) bytes. */
+sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k,
+                                   const int8_t *qw, const float *w_scale, int64_t n, int32_t g,
+                                   const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                   float lora_scale, uint16_t *y,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward from activations that are already rotated and quantized (qx, x_scale
+ * from sdnq_rotate_quantize_act with the weight's g): the int8 GEMM with its fused
+ * dequantization epilogue.  t[m,rank] (bf16, = x lora_a) and lora_b[rank,n] are
+ * nullable; when given, lora_scale * (t lora_b) is added.
+ * workspace: at least sdnq_workspace_bytes(m, n, k, rank, 0) bytes. */
+sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_scale, int64_t m,
+                                             int64_t k, const int8_t *qw, const float *w_scale,
+                                             int64_t n, const uint16_t *t, const uint16_t *lora_b,
+                                             int32_t rank, float lora_scale, uint16_t *y,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream);
+
+/* Input gradient of the layer, through the same int8 weight (PEFT backward):
+ *   dY'      = dy[m,n] * w_scale[n]            (column-wise fold of the row scales)
+ *   q, s     = per-token int8 quantization of dY' (no rotation along n)
+ *   dx[m,k]  = bf16( R_g( fp32(q . qw) * s[m] ) + lora_scale * (dy lora_b^T) lora_a^T )
+ * where R_g is the normalized block rotation along k (symmetric and orthogonal,
+ * hence its own inverse).  When grad_a / grad_b are non-NULL (LoRA present):
+ *   grad_a[k,rank] = bf16( x^T (lora_scale * dy lora_b^T) )
+ *   grad_b[rank,n] = bf16( lora_scale * (x lora_a)^T dy )
+ * x[m,k] bf16 is read only for grad_a / grad_b.  The LoRA factors are rounded to
+ * bf16 in the workspace.  workspace: at least sdnq_workspace_bytes(m, n, k, rank, 1). */
+sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
+                                          const int8_t *qw, const float *w_scale, int64_t k,
+                                          int32_t g, const uint16_t *x, const uint16_t *lora_a,
+                                          const uint16_t *lora_b, int32_t rank, float lora_scale,
+                                          uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace size in bytes for sdnq_qlinear_forward(_quantized) (is_backward = 0) or
+ * sdnq_qlinear_backward_input (is_backward = 1) at these sizes; 0 on invalid sizes. */
+size_t sdnq_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t rank, int32_t is_backward);
+
+/* Static, NUL-terminated description of a status code. */
+const char *sdnq_status_string(sdnq_status_t status);
+
+/* Diagnostics: the int8 GEMM of the layer with an int32 store instead of the
+ * dequantization epilogue (the accumulators the forward uses, exact).
+ *   b_layout 0: a[m,k], b[n,k] -> c[m,n] = a . b^T   (forward orientation)
+ *   b_layout 1: a[m,k], b[k,n] -> c[m,n] = a . b     (backward orientation; b is
+ *               transposed through the workspace first)
+ * workspace: b_layout 1 needs k*n bytes, b_layout 0 none (may be NULL). */
+sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int64_t n, int64_t k,
+                               int32_t b_layout, int32_t *c, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDNQ_HIP_H */

@@ -197,9 +197,11 @@ def qlinear_forward(x: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
 def qlinear_backward_input(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
                            x: np.ndarray | None = None, lora_a: np.ndarray | None = None,
                            lora_b: np.ndarray | None = None, lora_scale: float = 0.0,
-                           want_grads: bool = True, intermediates: bool = True) -> dict:
+                           want_grads: bool = True, intermediates: bool = True,
+                           want_dx: bool = True) -> dict:
     """Input gradient through the int8 weight (+ LoRA input gradient and, when x is
-    given and ``want_grads``, the LoRA weight gradients)."""
+    given and ``want_grads``, the LoRA weight gradients).  ``want_dx=False`` computes
+    the LoRA weight gradients only."""
     dy = _c(dy, np.uint16)
     qw = _c(qw, np.int8)
     sw = _c(sw, np.float32)
@@ -211,7 +213,9 @@ def qlinear_backward_input(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: in
     lb = None if lora_b is None else _c(lora_b, np.uint16)
     rank = 0 if la is None else la.shape[1]
     xx = None if x is None else _c(x, np.uint16)
-    out = {"dx": np.empty((m, k), np.uint16)}
+    out = {"dx": np.empty((m, k), np.uint16) if want_dx else None}
+    if not want_dx:
+        intermediates = False
     if la is not None and want_grads and xx is not None:
         out["grad_a"] = np.empty((k, rank), np.uint16)
         out["grad_b"] = np.empty((rank, n), np.uint16)

@@ -29,6 +29,8 @@
  *  - normalization: every rotated value is multiplied by fl32(1/sqrt(g)).
  *  - absmax over the whole row; s = fl32(a/127); codes = clamp(rne(fl32(y*r)),
  *    -127, 127) with r = fl32(127/a) (0 when a == 0); rne = round half to even.
+ *    For a < 2^-100, 127/a can overflow binary32, so such a row is scaled by
+ *    2^100 (exactly) before r and the codes are formed.
  *  - activations: one scale per token (row of x) over all in-features.
  *  - backward: dY is multiplied column-wise by the weight row scales before its
  *    own per-token quantization (no rotation on that axis); the int32 product
@@ -142,16 +144,21 @@ static void rotate_row(const uint16_t *xr, int64_t cols, int g, const float *col
     }
 }
 
-/* Symmetric absmax quantization of one rotated row to int8 codes in [-127, 127]. */
+/* Symmetric absmax quantization of one rotated row to int8 codes in [-127, 127].
+ * A row whose absmax is below 2^-100 is first multiplied by 2^100 (exact for every
+ * binary32 value), so that r = 127/a stays finite; s is always fl32(a/127) of the
+ * row as given.  Rows at or above 2^-100 are used as they are (the factor is 1). */
 static void quantize_row(const float *y, int64_t cols, int8_t *q, float *s)
 {
     float a = 0.0f;
     for (int64_t i = 0; i < cols; i++)
         a = fmaxf(a, fabsf(y[i]));
-    float r = (a > 0.0f) ? 127.0f / a : 0.0f;
     *s = a / 127.0f;
+    float up = (a < 0x1p-100f) ? 0x1p100f : 1.0f;
+    float as = a * up;
+    float r = (as > 0.0f) ? 127.0f / as : 0.0f;
     for (int64_t i = 0; i < cols; i++) {
-        float t = nearbyintf(y[i] * r);
+        float t = nearbyintf((y[i] * up) * r);
         if (t > 127.0f)
             t = 127.0f;
         if (t < -127.0f)
@@ -353,7 +360,8 @@ int oracle_qlinear_forward(const uint16_t *x, int64_t m, int64_t k,
  *   dx          = bf16_rne(dxbase + g_r A^T)
  *   grad_a      = bf16_rne(x^T g_r)          [k, rank]
  *   grad_b      = bf16_rne((x A)^T dY * lora_scale)  [rank, n]
- * x is read only when grad_a or grad_b is requested.  Every *_out may be NULL. */
+ * x is read only when grad_a or grad_b is requested.  dx may be NULL to compute the
+ * LoRA gradients only.  Every *_out may be NULL. */
 int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
                                   const int8_t *qw, const float *sw, int64_t k, int g,
                                   const uint16_t *x, const uint16_t *lora_a, const uint16_t *lora_b,
@@ -361,10 +369,12 @@ int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
                                   uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                                   int8_t *qdy_out, float *sdy_out, int32_t *acc_out, float *dxbase_out)
 {
-    if (!dy || !qw || !sw || !dx || m < 0 || n <= 0 || k <= 0 || !is_pow2_upto256(g) || k % g != 0)
+    if (!dy || !qw || !sw || m < 0 || n <= 0 || k <= 0 || !is_pow2_upto256(g) || k % g != 0)
         return ORACLE_ERR_ARG;
     int use_lora = lora_a && lora_b && rank > 0;
     int want_grads = use_lora && (grad_a || grad_b);
+    if (!dx && !want_grads)
+        return ORACLE_ERR_ARG;
     if (want_grads && !x)
         return ORACLE_ERR_ARG;
     int overflow = 0, alloc_fail = 0;
@@ -386,8 +396,8 @@ int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
         }
     }
 
-#pragma omp parallel
-    {
+#pragma omp parallel if (dx)
+    if (dx) {
         float *yr = (float *)malloc(sizeof(float) * (size_t)n);
         int8_t *qr = (int8_t *)malloc((size_t)n);
         float *z = (float *)malloc(sizeof(float) * (size_t)k);
@@ -451,14 +461,26 @@ int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
 
     if (want_grads && !alloc_fail) {
         if (grad_a) {
-            /* grad_a[kk, r] = sum_i x[i, kk] * g_r[i, r] */
-#pragma omp parallel for schedule(static)
-            for (int64_t kk = 0; kk < k; kk++) {
-                for (int r = 0; r < rank; r++) {
-                    double acc = 0.0;
+            /* grad_a[kk, r] = sum_i x[i, kk] * g_r[i, r], summed over ascending i */
+#pragma omp parallel
+            {
+                int nt = omp_get_num_threads(), id = omp_get_thread_num();
+                int64_t k_lo = k * id / nt, k_hi = k * (id + 1) / nt;
+                double *acc = (double *)calloc((size_t)((k_hi - k_lo) * rank + 1), sizeof(double));
+                if (!acc) {
+#pragma omp atomic write
+                    alloc_fail = 1;
+                } else {
                     for (int64_t i = 0; i < m; i++)
-                        acc += (double)bf16_decode(x[i * k + kk]) * gr[i * rank + r];
-                    grad_a[kk * rank + r] = bf16_encode_f64(acc);
+                        for (int64_t kk = k_lo; kk < k_hi; kk++) {
+                            double xv = (double)bf16_decode(x[i * k + kk]);
+                            for (int r = 0; r < rank; r++)
+                                acc[(kk - k_lo) * rank + r] += xv * gr[i * rank + r];
+                        }
+                    for (int64_t kk = k_lo; kk < k_hi; kk++)
+                        for (int r = 0; r < rank; r++)
+                            grad_a[kk * rank + r] = bf16_encode_f64(acc[(kk - k_lo) * rank + r]);
+                    free(acc);
                 }
             }
         }
@@ -476,14 +498,27 @@ int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
                             tx[i * rank + r] += xv * (double)bf16_decode(lora_a[kk * rank + r]);
                     }
                 }
-                /* grad_b[r, j] = lora_scale * sum_i t[i, r] * dY[i, j] */
-#pragma omp parallel for schedule(static)
-                for (int64_t j = 0; j < n; j++) {
-                    for (int r = 0; r < rank; r++) {
-                        double acc = 0.0;
+                /* grad_b[r, j] = lora_scale * sum_i t[i, r] * dY[i, j], summed over ascending i */
+#pragma omp parallel
+                {
+                    int nt = omp_get_num_threads(), id = omp_get_thread_num();
+                    int64_t j_lo = n * id / nt, j_hi = n * (id + 1) / nt;
+                    double *acc = (double *)calloc((size_t)((j_hi - j_lo) * rank + 1), sizeof(double));
+                    if (!acc) {
+#pragma omp atomic write
+                        alloc_fail = 1;
+                    } else {
                         for (int64_t i = 0; i < m; i++)
-                            acc += tx[i * rank + r] * (double)bf16_decode(dy[i * n + j]);
-                        grad_b[(int64_t)r * n + j] = bf16_encode_f64(acc * lora_scale);
+                            for (int r = 0; r < rank; r++) {
+                                double tv = tx[i * rank + r];
+                                for (int64_t j = j_lo; j < j_hi; j++)
+                                    acc[(int64_t)r * (j_hi - j_lo) + (j - j_lo)] += tv * (double)bf16_decode(dy[i * n + j]);
+                            }
+                        for (int r = 0; r < rank; r++)
+                            for (int64_t j = j_lo; j < j_hi; j++)
+                                grad_b[(int64_t)r * n + j] =
+                                    bf16_encode_f64(acc[(int64_t)r * (j_hi - j_lo) + (j - j_lo)] * lora_scale);
+                        free(acc);
                     }
                 }
             }

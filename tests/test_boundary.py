@@ -1,0 +1,175 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load and export every function `include/sdnq_hip.h` declares,
+and every argument check must return its status before anything is enqueued.
+The error-path calls pass fake device addresses that are never dereferenced
+when validation rejects the call; they are skipped when a GPU is present, where
+the GPU test file repeats them with real buffers.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import hadamard_rotated_int8_amd as h
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdnq_hip.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdnq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sdnq_rotate_quantize_weight", "sdnq_rotate_quantize_act", "sdnq_qlinear_forward",
+              "sdnq_qlinear_backward_input", "sdnq_qlinear_forward_quantized", "sdnq_workspace_bytes",
+              "sdnq_status_string", "sdnq_gemm_i8_i32"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = h.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", h._binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sdnq_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    for s in range(5):
+        assert len(h.status_string(s)) > 5
+    assert "unknown" in h.status_string(99)
+
+
+def test_workspace_bytes():
+    f = h.sdnq_workspace_bytes
+    assert f(4096, 3072, 3072) >= 4096 * 3072 + 4096 * 4
+    assert f(4096, 3072, 3072, 32) > f(4096, 3072, 3072, 0)
+    assert f(16384, 3072, 3072, 64, True) >= 16384 * 3072 + 3072 * 3072
+    assert f(0, 16, 16) == 0 or f(0, 16, 16) >= 0
+    assert f(-1, 16, 16) == 0
+    assert f(16, 0, 16) == 0
+    assert f(16, 16, 16, 17) == 0   # unsupported rank
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer validation runs only without a GPU")
+
+A = 0x10000   # fake 16-byte-aligned device addresses (never dereferenced on these paths)
+B = 0x20000
+C = 0x30000
+D = 0x40000
+W = 0x50000
+WS = 1 << 40
+
+
+def rqa(x=A, m=4, k=256, g=256, cs=None, q=B, s=C):
+    return h.lib().sdnq_rotate_quantize_act(x, m, k, g, cs, q, s, None)
+
+
+def fwd(x=A, m=4, k=256, qw=B, sw=C, n=256, g=256, la=None, lb=None, r=0, y=D, ws=W, wsb=WS):
+    return h.lib().sdnq_qlinear_forward(x, m, k, qw, sw, n, g, la, lb, r, 1.0, y, ws, wsb, None)
+
+
+def bwd(dy=A, m=4, n=256, qw=B, sw=C, k=256, g=256, x=None, la=None, lb=None, r=0, dx=D, ga=None, gb=None,
+        ws=W, wsb=WS):
+    return h.lib().sdnq_qlinear_backward_input(dy, m, n, qw, sw, k, g, x, la, lb, r, 1.0, dx, ga, gb, ws, wsb, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), INVALID), (dict(q=None), INVALID), (dict(s=None), INVALID),
+    (dict(m=-1), INVALID), (dict(k=0), INVALID), (dict(k=-16), INVALID),
+    (dict(g=32), UNSUPPORTED), (dict(g=512), UNSUPPORTED), (dict(g=0), UNSUPPORTED),
+    (dict(k=320, g=256), UNSUPPORTED), (dict(k=200, g=1), UNSUPPORTED),
+    (dict(k=65536 + 256, g=256), UNSUPPORTED),
+    (dict(x=A + 8), INVALID), (dict(q=B + 4), INVALID), (dict(s=C + 2), INVALID),
+    (dict(g=1, cs=D + 4), INVALID),
+    (dict(m=0), OK),
+    (dict(m=0, x=None, q=None, s=None), OK),   # an empty batch may pass NULL row buffers
+    (dict(m=0, g=32), UNSUPPORTED),            # ... but is still validated
+])
+def test_rotate_quantize_act_validation(kw, expect):
+    assert rqa(**kw) == expect
+
+
+@no_gpu
+def test_rotate_quantize_weight_validation():
+    L = h.lib()
+    assert L.sdnq_rotate_quantize_weight(None, 4, 256, 256, B, C, None) == INVALID
+    assert L.sdnq_rotate_quantize_weight(A, 4, 256, 100, B, C, None) == UNSUPPORTED
+    assert L.sdnq_rotate_quantize_weight(A, 0, 256, 256, B, C, None) == OK
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), INVALID), (dict(qw=None), INVALID), (dict(sw=None), INVALID), (dict(y=None), INVALID),
+    (dict(m=-3), INVALID), (dict(n=0), INVALID), (dict(k=0), INVALID),
+    (dict(n=200), UNSUPPORTED), (dict(k=300, g=1), UNSUPPORTED), (dict(g=7), UNSUPPORTED),
+    (dict(k=192, g=128), UNSUPPORTED),
+    (dict(la=0x60000, lb=None, r=32), INVALID), (dict(la=None, lb=0x60000, r=32), INVALID),
+    (dict(la=0x60000, lb=0x70000, r=24), UNSUPPORTED), (dict(la=0x60000, lb=0x70000, r=0), UNSUPPORTED),
+    (dict(la=0x60000, lb=0x70000, r=256), UNSUPPORTED), (dict(la=0x60008, lb=0x70000, r=32), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(ws=W + 8), WORKSPACE),
+    (dict(y=D + 2), INVALID),
+    (dict(m=0), OK),
+    (dict(m=0, x=None, y=None), OK),
+    (dict(m=0, qw=None), INVALID),
+])
+def test_forward_validation(kw, expect):
+    assert fwd(**kw) == expect
+
+
+@no_gpu
+def test_forward_workspace_limit_is_exact():
+    need = h.sdnq_workspace_bytes(4, 256, 256, 0, False)
+    assert fwd(m=4, wsb=need - 1) == WORKSPACE
+    need = h.sdnq_workspace_bytes(4, 256, 256, 32, False)
+    assert fwd(m=4, la=0x60000, lb=0x70000, r=32, wsb=need - 1) == WORKSPACE
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dy=None), INVALID), (dict(qw=None), INVALID), (dict(dx=None), INVALID),
+    (dict(m=-1), INVALID), (dict(n=0), INVALID),
+    (dict(g=100), UNSUPPORTED), (dict(n=100), UNSUPPORTED),
+    (dict(ga=0x80000), INVALID),                                    # grads without an adapter
+    (dict(la=0x60000, lb=0x70000, r=32, ga=0x80000), INVALID),      # grads without x
+    (dict(la=0x60000, lb=0x70000, r=32, x=0x90000, gb=0x80004), INVALID),
+    (dict(ws=None), WORKSPACE),
+    (dict(m=0), OK),
+])
+def test_backward_validation(kw, expect):
+    assert bwd(**kw) == expect
+
+
+@no_gpu
+def test_gemm_validation():
+    L = h.lib()
+    assert L.sdnq_gemm_i8_i32(None, B, 4, 32, 32, 0, C, None, 0, None) == INVALID
+    assert L.sdnq_gemm_i8_i32(A, B, 4, 32, 32, 2, C, None, 0, None) == INVALID
+    assert L.sdnq_gemm_i8_i32(A, B, 4, 30, 32, 0, C, None, 0, None) == UNSUPPORTED
+    assert L.sdnq_gemm_i8_i32(A, B, 4, 32, 32, 1, C, None, 0, None) == WORKSPACE
+    assert L.sdnq_gemm_i8_i32(A, B, 0, 32, 32, 0, C, None, 0, None) == OK
+
+
+def test_binding_rejects_wrong_types_before_calling():
+    with pytest.raises((TypeError, ValueError)):
+        h.sdnq_rotate_quantize_act(torch.zeros(4, 256, dtype=torch.float32), 256)
+    with pytest.raises((TypeError, ValueError)):
+        h.sdnq_rotate_quantize_act(torch.zeros(4, 256, dtype=torch.bfloat16), 256)  # CPU tensor

@@ -19,8 +19,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MUTANTS = {
     "sub_swapped": ("v[i + h] = a - b;", "v[i + h] = b - a;"),
     "stage_order_descending": ("for (int h = 1; h < g; h <<= 1) {", "for (int h = g / 2; h >= 1; h >>= 1) {"),
-    "divide_by_scale": ("float t = nearbyintf(y[i] * r);", "float t = nearbyintf(y[i] / *s);"),
-    "round_half_away": ("float t = nearbyintf(y[i] * r);", "float t = roundf(y[i] * r);"),
+    "divide_by_scale": ("float t = nearbyintf((y[i] * up) * r);", "float t = nearbyintf(y[i] / *s);"),
+    "round_half_away": ("float t = nearbyintf((y[i] * up) * r);", "float t = roundf((y[i] * up) * r);"),
+    "no_tiny_row_rescale": ("float up = (a < 0x1p-100f) ? 0x1p100f : 1.0f;", "float up = 1.0f;"),
     "no_normalization": ("y[i] = y[i] * c;", "y[i] = y[i];"),
     "no_column_scale": ("y[i] = y[i] * col_scale[i];", "y[i] = y[i];"),
     "backward_weight_transposed": ("acc[kk] += qv * (int64_t)wr[kk];", "acc[kk] += qv * (int64_t)qw[kk * n + j];"),
@@ -29,8 +30,10 @@ MUTANTS = {
     "scale_over_128": ("*s = a / 127.0f;", "*s = a / 128.0f;"),
     "lora_b_transposed": ("l += t[r] * (double)bf16_decode(lora_b[(int64_t)r * n + j]);",
                           "l += t[r] * (double)bf16_decode(lora_b[(int64_t)j * rank + r]);"),
-    "grad_b_unscaled": ("grad_b[(int64_t)r * n + j] = bf16_encode_f64(acc * lora_scale);",
-                        "grad_b[(int64_t)r * n + j] = bf16_encode_f64(acc);"),
+    "grad_b_unscaled": ("bf16_encode_f64(acc[(int64_t)r * (j_hi - j_lo) + (j - j_lo)] * lora_scale);",
+                        "bf16_encode_f64(acc[(int64_t)r * (j_hi - j_lo) + (j - j_lo)]);"),
+    "grad_a_wrong_factor": ("acc[(kk - k_lo) * rank + r] += xv * gr[i * rank + r];",
+                            "acc[(kk - k_lo) * rank + r] += xv * gr[i * rank + (rank - 1 - r)];"),
     "bf16_truncation": ("double rq = nearbyint(q);", "double rq = floor(q);"),
     "weight_scale_index": ("float base = (float)(int32_t)acc * (sx * sw[j]);",
                            "float base = (float)(int32_t)acc * (sx * sw[i % n]);"),

@@ -166,7 +166,8 @@ def _cases():
         return {c["name"]: c for c in json.load(f)["cases"]}
 
 
-@pytest.mark.parametrize("name", ["g4_ramp", "g1_rne_ties", "g1_multiply_by_reciprocal", "g4_stage_order"])
+@pytest.mark.parametrize("name", ["g4_ramp", "g1_rne_ties", "g1_multiply_by_reciprocal", "g4_stage_order",
+                                  "g1_tiny_row"])
 def test_hand_worked_rows(name):
     c = _cases()[name]
     x = bf(np.array([c["x"]], np.float32))
@@ -398,6 +399,16 @@ def test_lora_gradients_against_torch_autograd():
         assert np.array_equal(out[name], oracle.bf16_from_f64(ref.numpy())), name
     dx_expect = oracle.bf16_from_f64(out["dxbase"].astype(np.float64) + x.grad.numpy())
     assert np.array_equal(out["dx"], dx_expect)
+
+
+def test_lora_gradients_only_call_matches_the_full_call():
+    d = synth.make_linear(40, 256, 192, seed=15, lora_rank=32, backward=True)
+    qw, sw = oracle.rotate_quantize(d["w"], 128)
+    full = oracle.qlinear_backward_input(d["dy"], qw, sw, 128, d["x"], d["lora_a"], d["lora_b"], 0.5)
+    only = oracle.qlinear_backward_input(d["dy"], qw, sw, 128, d["x"], d["lora_a"], d["lora_b"], 0.5,
+                                         want_dx=False)
+    assert only["dx"] is None
+    assert np.array_equal(full["grad_a"], only["grad_a"]) and np.array_equal(full["grad_b"], only["grad_b"])
 
 
 # ------------------------------------------------------------- bf16 rounding --
