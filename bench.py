@@ -13,7 +13,7 @@ value = int8 ops of both GEMMs (2 M N K each) / wall time per step, in TOPS,
 with the activation rotate+quantize kernels inside the step.  Per-kernel times
 come from HIP events recorded on the launch stream around each kernel.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -124,6 +126,13 @@ def main():
         check(L.sdnq_qlinear_forward_quantized(P(qh), P(shh), M, K_DOWN, P(qw_down), P(sw_down), N_DOWN, None, None,
                                                0, 0.0, P(y_down), None, 0, sp), "gemm down")
         if ev: ev[4].record(stream)
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -165,8 +165,8 @@ sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_sc
   ga.row_scale = x_scale; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
   if (r > 0) {
     uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
-    SDNQ_LAUNCH(launch_transpose_u16(lora_b, r, n, bt, s));
-    ga.lora_t = t; ga.lora_r = bt; ga.rank = r; ga.lora_scale = lora_scale;
+    SDNQ_LAUNCH(launch_transpose_scale_bf16(lora_b, r, n, lora_scale, bt, s));  // bf16(scale B)^T
+    ga.lora_t = t; ga.lora_r = bt; ga.rank = r;
   }
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
@@ -200,10 +200,10 @@ sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, cons
     uint16_t *t = reinterpret_cast<uint16_t *>(ws_at(workspace, L.t));
     uint16_t *at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
     uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
-    SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));   // A [k, r] -> A^T [r, k]
-    SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, 1.0f, t, s));  // t = x A
-    SDNQ_LAUNCH(launch_transpose_u16(lora_b, r, n, bt, s));   // B [r, n] -> B^T [n, r]
-    ga.lora_t = t; ga.lora_r = bt; ga.rank = r; ga.lora_scale = lora_scale;
+    SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));          // A [k, r] -> A^T [r, k]
+    SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, lora_scale, t, s));  // t = bf16(scale * x A)
+    SDNQ_LAUNCH(launch_transpose_u16(lora_b, r, n, bt, s));          // B [r, n] -> B^T [n, r]
+    ga.lora_t = t; ga.lora_r = bt; ga.rank = r;
   }
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
@@ -251,7 +251,7 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
   if (r > 0) {
     gr = reinterpret_cast<uint16_t *>(ws_at(workspace, L.gr));
     SDNQ_LAUNCH(launch_lora_down(dy, m, n, lora_b, r, lora_scale, gr, s));  // g_r = scale * dY B^T
-    ga.lora_t = gr; ga.lora_r = lora_a; ga.rank = r; ga.lora_scale = 1.0f;  // + g_r A^T
+    ga.lora_t = gr; ga.lora_r = lora_a; ga.rank = r;  // + g_r A^T
   }
   SDNQ_LAUNCH(launch_gemm_i8(Epilogue::kBackward, ga, s));
 

@@ -4,25 +4,27 @@
 //
 // Forward ("SDNQ: SD.Next Quantization Engine": INT8 quantized matmul with a
 // fused scale epilogue, FP32 dequantization as with dequantize_fp32):
-//   y[m, n] = bf16( fp32(acc) * (row_scale[m] * col_scale[n])
-//                   + lora_scale * sum_j T[m, j] * R[n, j] )
+//   y[m, n] = bf16( fp32(acc) * (row_scale[m] * col_scale[n]) + sum_j T[m, j] * R[n, j] )
+// (the LoRA scale is folded into T or R by the caller)
 // Backward input (the quantized matmul of the training path): B is the
 // transposed int8 weight, and
 //   dx[m, :] = bf16( rot_g( fp32(acc[m, :]) * row_scale[m] ) + sum_j T[m, j] * R[:, j] )
 // where rot_g is the normalized block Walsh-Hadamard rotation along the output
 // columns (the same transform as the forward's, which is its own inverse).
 //
-// Tiling.  A workgroup of 4 wavefronts computes a 256 x 256 output tile; K is
-// consumed 128 bytes at a time through a two-stage LDS ring (2 x 64 KB).  Each
-// wavefront owns a (256/WAVES_M) x (256/WAVES_N) sub-tile made of 32 x 32 MFMA
-// tiles (v_mfma_i32_32x32x32_i8, int32 accumulators in registers).  The MFMA
+// Tiling.  A workgroup of 8 wavefronts (two per SIMD, so one hides the other's
+// waits) computes a 256 x 256 output tile; K is consumed 64 bytes at a time
+// through a 4-stage LDS ring (4 x 32 KB) filled by buffer loads that write LDS
+// directly, three k-tiles ahead.  Each wavefront owns a (256/WAVES_M) x
+// (256/WAVES_N) sub-tile of eight 32 x 32 MFMA tiles (v_mfma_i32_32x32x32_i8,
+// 128 int32 accumulators).  The MFMA
 // "row" operand is the B side (weight rows, output column n) and the "column"
 // operand the A side (tokens m), so each lane ends up holding, for one token,
 // runs of 4 consecutive output columns: bf16 stores of 8 bytes.
 //
-// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-// c ^ ((r >> 1) & 7), which makes both the 16-byte fragment reads (16 rows, one
-// chunk) and the stores (2 rows, 8 chunks) conflict-free.
+// LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 2) & 3), which makes the 16-byte fragment reads (16 rows, one chunk)
+// conflict-free (the bank-conflict counter reads zero).
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the block index is
 // remapped so that each XCD walks a contiguous run of tiles, ordered in groups
@@ -32,11 +34,15 @@
 namespace sdnq {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4;
+constexpr int kStageBytes = (BM + BN) * BK;  // 32 KB: A tile then B tile, rows of 64 bytes
+constexpr int kThreads = 512;  // 8 wavefronts: two per SIMD
 constexpr int kGroupM = 4;
+constexpr unsigned kOutOfRange = 0x80000000u;  // any offset past num_records reads as zero
 
 constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128))
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int G>
 __device__ __forceinline__ float norm_const() {
@@ -45,8 +51,6 @@ __device__ __forceinline__ float norm_const() {
   else if constexpr (G == 256) return 0.0625f;
   else return 1.0f;
 }
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + 16 * (chunk ^ ((row >> 1) & 7)); }
 
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn) {
   const int nblk = gridDim.x, bid = blockIdx.x;
@@ -62,12 +66,12 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
   tn = in / gm;
 }
 
-// One LoRA 32 x 32 output tile: out[i = n][j = m] = sum_r R[n, r] * T[m, r]
-// (bf16 MFMA, fp32 accumulate).  Rows beyond the matrix are clamped (their
-// results are never stored).
+// LoRA term of one 32 x 32 output tile, accumulated onto the dequantized base
+// values: out[i = n][j = m] = base + sum_r R[n, r] * T[m, r] (bf16 MFMA, fp32
+// accumulate; lora_scale is already folded into T or R).  Rows beyond the matrix
+// are clamped (their results are never stored).
 __device__ __forceinline__ v16f lora_tile(const uint16_t *__restrict__ T, const uint16_t *__restrict__ R,
-                                          int64_t m, int64_t n, int rank, int lane) {
-  v16f acc = {};
+                                          int64_t m, int64_t n, int rank, int lane, v16f acc) {
   const int koff = 8 * (lane >> 5);
   const uint16_t *tr = T + m * rank + koff;
   const uint16_t *rr = R + n * rank + koff;
@@ -79,58 +83,84 @@ __device__ __forceinline__ v16f lora_tile(const uint16_t *__restrict__ T, const 
   return acc;
 }
 
-template <Epilogue EPI, int WAVES_M, int G>
+// s_waitcnt vmcnt(n) then s_barrier, as one compiler barrier.  The direct-to-LDS
+// loads are invisible to the compiler's wait tracking, so their completion is
+// awaited here explicitly before any wavefront reads what the others loaded.
+__device__ __forceinline__ void wait_loads_and_barrier(int outstanding) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (outstanding >= 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (outstanding >= 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <Epilogue EPI, int WAVES_M, int G, bool LORA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int tiles_m, int tiles_n) {
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WAVES_N = 8 / WAVES_M;
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int SM = TM / 32, SN = TN / 32;
-  static_assert(SM * SN == 16, "16 MFMA tiles per wavefront");
+  static_assert(SM * SN == 8, "8 MFMA tiles (128 int32 accumulators) per wavefront");
 
-  __shared__ __attribute__((aligned(16))) int8_t smem[2][2][BM * BK];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * kStageBytes];
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int64_t M = args.m, N = args.n, K = args.k;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets LDS bases live in SGPRs
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
-  // Global -> LDS assignment: 8 chunks of 16 B per operand per thread;
-  // chunk id = it * 256 + tid -> tile row it * 32 + (tid >> 3), 16-byte column tid & 7.
-  const int lrow = tid >> 3, lc = tid & 7;
-  // Row offsets relative to the tile's first row (tail rows clamped to the last one;
-  // their results are never stored).
-  const int8_t *a_tile = args.a + m0 * K + 16 * lc;
-  const int8_t *b_tile = args.b + n0 * K + 16 * lc;
-  int a_off[8], b_off[8];
+  // ---- direct global -> LDS loads (buffer_load_dwordx4 ... lds)
+  // A stage holds the A tile (256 rows x 64 B) then the B tile.  Load j (0..1)
+  // of a wavefront fills the 16-row group g = 8*j + wave: lane i lands at byte
+  // 16*i of that 1 KB group, i.e. row 16*g + i/4, stored chunk i%4.  Rows are
+  // XOR-swizzled (stored chunk = logical chunk ^ ((row >> 2) & 3)), so lane i
+  // fetches logical chunk c = (i & 3) ^ ((i >> 4) & 3).  Rows past the matrix
+  // end lie past the buffer's num_records and read as zero, and so do chunks
+  // past K (their offset is pushed out of range).
+  const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+  const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(args.a + m0 * K), 0, (int)(rows_a * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(args.b + n0 * K), 0, (int)(rows_b * K), 0x00020000);
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  unsigned voff[2];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    int64_t ra = m0 + it * 32 + lrow;
-    int64_t rb = n0 + it * 32 + lrow;
-    ra = ra < M ? ra : M - 1;
-    rb = rb < N ? rb : N - 1;
-    a_off[it] = (int)((ra - m0) * K);
-    b_off[it] = (int)((rb - n0) * K);
-  }
+  for (int j = 0; j < 2; ++j) voff[j] = (unsigned)((16 * (8 * j + wave) + (lane >> 2)) * K + 16 * lc);
 
-  v4i ra[8], rb[8];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
-    const bool ok = k0 + 16 * lc < K;
+  const int nk = (int)((K + BK - 1) / BK);
+  auto issue_loads = [&](int kt) {
+    const int st = kt & (STAGES - 1);
+    const unsigned k0 = (unsigned)kt * BK;
+    // Only a k-tile that runs past K needs the per-lane range check.
+    const unsigned oob = ((int64_t)k0 + BK <= K) ? 0u : (((int64_t)k0 + 16 * lc < K) ? 0u : kOutOfRange);
+    int8_t *base = smem + st * kStageBytes;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      ra[it] = ok ? *reinterpret_cast<const v4i *>(a_tile + a_off[it] + k0) : v4i{0, 0, 0, 0};
-      rb[it] = ok ? *reinterpret_cast<const v4i *>(b_tile + b_off[it] + k0) : v4i{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) {
+      const int g = 8 * j + wave;
+      const unsigned off = (voff[j] + k0) | oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void *)(base + g * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_void *)(base + BM * BK + g * 1024), 16, off, 0, 0, 0);
     }
   };
-  auto sstore = [&](int stage) {
+
+  // ---- fragment reads: lane l reads row (tile row base + l % 32), logical chunk
+  // 2*kk + l / 32, stored at chunk ^ ((l >> 2) & 3).
+  const int frow = (lane & 31) * BK;
+  const int fcol0 = 16 * ((0 + (lane >> 5)) ^ ((lane >> 2) & 3));
+  const int fcol1 = 16 * ((2 + (lane >> 5)) ^ ((lane >> 2) & 3));
+  struct Frags {
+    v4i a[SM], b[SN];
+  };
+  auto read_frags = [&](int kt, int kk, Frags &f) {
+    const int8_t *base = smem + (kt & (STAGES - 1)) * kStageBytes + frow + (kk ? fcol1 : fcol0);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int off = swz(it * 32 + lrow, lc);
-      *reinterpret_cast<v4i *>(&smem[stage][0][off]) = ra[it];
-      *reinterpret_cast<v4i *>(&smem[stage][1][off]) = rb[it];
-    }
+    for (int i = 0; i < SM; ++i) f.a[i] = *reinterpret_cast<const v4i *>(base + (wm * TM + i * 32) * BK);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) f.b[j] = *reinterpret_cast<const v4i *>(base + BM * BK + (wn * TN + j * 32) * BK);
   };
 
   v16i acc[SM][SN];
@@ -139,35 +169,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 #pragma unroll
     for (int j = 0; j < SN; ++j) acc[i][j] = v16i{};
 
-  const int nk = (int)((K + BK - 1) / BK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    const int8_t *As = smem[kt & 1][0];
-    const int8_t *Bs = smem[kt & 1][1];
+  auto mfma_all = [&](const Frags &f) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int ch = 2 * kk + (lane >> 5);
-      v4i fa[SM], fb[SN];
-#pragma unroll
-      for (int i = 0; i < SM; ++i)
-        fa[i] = *reinterpret_cast<const v4i *>(As + swz(wm * TM + i * 32 + (lane & 31), ch));
+    for (int i = 0; i < SM; ++i)
 #pragma unroll
       for (int j = 0; j < SN; ++j)
-        fb[j] = *reinterpret_cast<const v4i *>(Bs + swz(wn * TN + j * 32 + (lane & 31), ch));
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- pipeline: tiles kt+1..kt+3 are in flight while tile kt is consumed.
+  // Iteration kt: read (kt, kk=1) | MFMA (kt, kk=0) | wait for tile kt+1, barrier |
+  // load tile kt+3 into the stage tile kt-1 used | read (kt+1, kk=0) | MFMA (kt, kk=1).
+  // Tiles past the last one are issued too: every lane's offset is then out of
+  // range, so they only write zeros into a free stage.  This keeps the loop body
+  // branch-free and the number of loads in flight constant (4 per tile).
+  for (int t = 0; t < STAGES - 1; ++t) issue_loads(t);
+  wait_loads_and_barrier(8);
+  Frags f0, f1;
+  read_frags(0, 0, f0);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    read_frags(kt, 1, f1);
+    mfma_all(f0);
 #pragma unroll
-      for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    for (int u = 0; u < SM + SN; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     }
-    if (more) sstore((kt + 1) & 1);
-    __syncthreads();
+    wait_loads_and_barrier(4);
+    issue_loads(kt + 3);
+    read_frags(kt + 1, 0, f0);
+    mfma_all(f1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    }
   }
+  // The zero-fill loads of the last iterations may still be landing in LDS.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ------------------------------------------------------------ epilogues --
   // Accumulator layout (32 x 32 tile, lane l, register r):
@@ -191,7 +232,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       }
     }
   } else if constexpr (EPI == Epilogue::kForward) {
-    const bool lora = args.rank > 0;
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
@@ -199,41 +239,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       const float sx = args.row_scale[mc];
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
-        v16f l = {};
-        if (lora) {
-          int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
-          nr = nr < N ? nr : N - 1;
-          l = lora_tile(args.lora_t, args.lora_r, mc, nr, args.rank, lane);
-        }
-        if (m >= M) continue;
+        const int64_t nb = n0 + wn * TN + j * 32 + 4 * half;
+        v16f o;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t n = n0 + wn * TN + j * 32 + 8 * q4 + 4 * half;
-          if (n < N) {
-            const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
-            float o[4];
-            o[0] = (float)acc[i][j][4 * q4 + 0] * (sx * sw.x);
-            o[1] = (float)acc[i][j][4 * q4 + 1] * (sx * sw.y);
-            o[2] = (float)acc[i][j][4 * q4 + 2] * (sx * sw.z);
-            o[3] = (float)acc[i][j][4 * q4 + 3] * (sx * sw.w);
-            if (lora) {
+          int64_t n = nb + 8 * q4;
+          n = n < N ? n : N - 4;
+          const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
+          o[4 * q4 + 0] = (float)acc[i][j][4 * q4 + 0] * (sx * sw.x);
+          o[4 * q4 + 1] = (float)acc[i][j][4 * q4 + 1] * (sx * sw.y);
+          o[4 * q4 + 2] = (float)acc[i][j][4 * q4 + 2] * (sx * sw.z);
+          o[4 * q4 + 3] = (float)acc[i][j][4 * q4 + 3] * (sx * sw.w);
+        }
+        if constexpr (LORA) {
+          int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
+          nr = nr < N ? nr : N - 1;
+          o = lora_tile(args.lora_t, args.lora_r, mc, nr, args.rank, lane, o);
+        }
+        if (m < M) {
 #pragma unroll
-              for (int t = 0; t < 4; ++t) o[t] = __builtin_fmaf(args.lora_scale, l[4 * q4 + t], o[t]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int64_t n = nb + 8 * q4;
+            if (n < N) {
+              uint2 packed;
+              packed.x = pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]);
+              packed.y = pack_bf16x2(o[4 * q4 + 2], o[4 * q4 + 3]);
+              *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
             }
-            uint2 packed;
-            packed.x = pack_bf16x2(o[0], o[1]);
-            packed.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
           }
         }
+        __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile at a time: bounds register pressure
       }
     }
   } else {
-    // Backward: WAVES_M = 4, so one wavefront holds all 256 output columns of
-    // its 64 tokens: column c = 32*j + 8*(r/4) + 4*half + (r%4) of the tile,
+    // Backward: WAVES_M = 8, so one wavefront holds all 256 output columns of
+    // its 32 tokens: column c = 32*j + 8*(r/4) + 4*half + (r%4) of the tile,
     // i.e. bits 0-1 = r%4, bit 2 = lane half, bits 3-4 = r/4, bits 5-7 = j.
-    static_assert(WAVES_M == 4 && SN == 8, "backward epilogue needs full-width wavefront tiles");
-    const bool lora = args.rank > 0;
+    static_assert(WAVES_M == 8 && SN == 8, "backward epilogue needs full-width wavefront tiles");
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
@@ -322,55 +364,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
-        v16f l = {};
-        if (lora) {
+        v16f o;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = z[j][r];
+        if constexpr (LORA) {
           int64_t nr = n0 + j * 32 + (lane & 31);
           nr = nr < N ? nr : N - 1;
-          l = lora_tile(args.lora_t, args.lora_r, mc, nr, args.rank, lane);
+          o = lora_tile(args.lora_t, args.lora_r, mc, nr, args.rank, lane, o);
         }
-        if (m >= M) continue;
+        if (m < M) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t n = n0 + j * 32 + 8 * q4 + 4 * half;
-          if (n < N) {
-            float o[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              o[t] = z[j][4 * q4 + t];
-              if (lora) o[t] = __builtin_fmaf(args.lora_scale, l[4 * q4 + t], o[t]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int64_t n = n0 + j * 32 + 8 * q4 + 4 * half;
+            if (n < N) {
+              uint2 packed;
+              packed.x = pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]);
+              packed.y = pack_bf16x2(o[4 * q4 + 2], o[4 * q4 + 3]);
+              *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
             }
-            uint2 packed;
-            packed.x = pack_bf16x2(o[0], o[1]);
-            packed.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 }
 
-template <Epilogue EPI, int WAVES_M, int G>
+template <Epilogue EPI, int WAVES_M, int G, bool LORA>
 hipError_t launch_typed(const GemmArgs &args, hipStream_t stream) {
   const int tiles_m = (int)((args.m + BM - 1) / BM);
   const int tiles_n = (int)((args.n + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<EPI, WAVES_M, G>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_i8_kernel<EPI, WAVES_M, G, LORA>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
                      args, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_backward(const GemmArgs &args, hipStream_t stream) {
+  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 8, G, true>(args, stream)
+                       : launch_typed<Epilogue::kBackward, 8, G, false>(args, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream) {
   switch (epi) {
-    case Epilogue::kInt32: return launch_typed<Epilogue::kInt32, 2, 1>(args, stream);
-    case Epilogue::kForward: return launch_typed<Epilogue::kForward, 2, 1>(args, stream);
+    case Epilogue::kInt32: return launch_typed<Epilogue::kInt32, 2, 1, false>(args, stream);
+    case Epilogue::kForward:
+      return args.rank > 0 ? launch_typed<Epilogue::kForward, 2, 1, true>(args, stream)
+                           : launch_typed<Epilogue::kForward, 2, 1, false>(args, stream);
     case Epilogue::kBackward:
       switch (args.g) {
-        case 1: return launch_typed<Epilogue::kBackward, 4, 1>(args, stream);
-        case 64: return launch_typed<Epilogue::kBackward, 4, 64>(args, stream);
-        case 128: return launch_typed<Epilogue::kBackward, 4, 128>(args, stream);
-        case 256: return launch_typed<Epilogue::kBackward, 4, 256>(args, stream);
+        case 1: return launch_backward<1>(args, stream);
+        case 64: return launch_backward<64>(args, stream);
+        case 128: return launch_backward<128>(args, stream);
+        case 256: return launch_backward<256>(args, stream);
         default: return hipErrorInvalidValue;
       }
   }

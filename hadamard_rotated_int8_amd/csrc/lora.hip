@@ -211,7 +211,33 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in
   }
 }
 
+__global__ __launch_bounds__(256) void transpose_scale_bf16_kernel(const uint16_t *__restrict__ in, int64_t rows,
+                                                                   int64_t cols, float scale,
+                                                                   uint16_t *__restrict__ out) {
+  __shared__ uint16_t tile[32][33];
+  const int64_t r0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 32;
+  for (int idx = threadIdx.x; idx < 32 * 32; idx += 256) {
+    const int r = idx / 32, c = idx % 32;
+    if (r0 + r < rows && c0 + c < cols) {
+      const float v = __uint_as_float((uint32_t)in[(r0 + r) * cols + c0 + c] << 16) * scale;
+      tile[r][c] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 32 * 32; idx += 256) {
+    const int c = idx / 32, r = idx % 32;
+    if (r0 + r < rows && c0 + c < cols) out[(c0 + c) * rows + r0 + r] = tile[r][c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t cols, float scale, uint16_t *out,
+                                       hipStream_t stream) {
+  const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
+  hipLaunchKernelGGL(transpose_scale_bf16_kernel, grid, dim3(256), 0, stream, in, rows, cols, scale, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
                             float scale, uint16_t *out, hipStream_t stream) {

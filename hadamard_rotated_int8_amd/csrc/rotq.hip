@@ -59,9 +59,32 @@ __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2,
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);         // [lo.b0, lo.b1, hi.b0, hi.b1]
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+// One cross-lane butterfly stage on 8 registers: v = fma(v[partner lane], m, v)
+// as a single v_fmac_f32 with a quad_perm DPP source.  The product by m = +-1 is
+// exact and the fma rounds once, so each result equals fl(a + b) or -fl(a - b).
+// The leading s_nop gives the two wait states a DPP read needs after a VALU write
+// of its source; inside the block no instruction reads a register written by the
+// two before it.
+#define SDNQ_FMAC_DPP8(PERM)                                                                    \
+  "s_nop 1\n\t"                                                                                \
+  "v_fmac_f32_dpp %0, %0, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %1, %1, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %2, %2, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %3, %3, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %4, %4, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %5, %5, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %6, %6, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %7, %7, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf"
+
+__device__ __forceinline__ void dpp_stage_xor1(float (&r)[8], float m) {
+  asm volatile(SDNQ_FMAC_DPP8("[1,0,3,2]")
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "v"(m));
+}
+__device__ __forceinline__ void dpp_stage_xor2(float (&r)[8], float m) {
+  asm volatile(SDNQ_FMAC_DPP8("[2,3,0,1]")
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "v"(m));
 }
 
 template <int G, bool COLSCALE>
@@ -137,14 +160,10 @@ __global__ __launch_bounds__(kMaxThreads) void rotq_kernel(
     {
       const float m1 = (l4 & 1) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[i][j] = __builtin_fmaf(dpp<0xB1>(v[i][j]), m1, v[i][j]);
+      for (int i = 0; i < 8; ++i) dpp_stage_xor1(v[i], m1);
       const float m2 = (l4 & 2) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[i][j] = __builtin_fmaf(dpp<0x4E>(v[i][j]), m2, v[i][j]);
+      for (int i = 0; i < 8; ++i) dpp_stage_xor2(v[i], m2);
       sign = m1 * m2;
     }
     // h = 32, 64, 128: value bits 5-7 (register index i), up to g/2

@@ -49,9 +49,9 @@ struct GemmArgs {
   const float *row_scale; // [m]  token scale
   const float *col_scale; // [n]  weight row scale (forward only, else nullptr)
   const uint16_t *lora_t; // [m, rank] bf16 left factor (nullable)
-  const uint16_t *lora_r; // [n, rank] bf16 right factor, one row per output column (nullable)
+  const uint16_t *lora_r; // [n, rank] bf16 right factor, one row per output column (nullable);
+                          // the LoRA scale is already folded into one of the two factors
   int rank;
-  float lora_scale;
   int g;                  // backward: inverse rotation block along n (1, 64, 128, 256)
   uint16_t *out_bf16;     // [m, n]
 };
@@ -64,6 +64,9 @@ hipError_t launch_transpose_i8(const int8_t *in, int64_t rows, int64_t cols, int
 // 16-bit [rows, cols] -> [cols, rows]
 hipError_t launch_transpose_u16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out,
                                 hipStream_t stream);
+// bf16 [rows, cols] -> bf16(scale * in)^T [cols, rows]
+hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t cols, float scale,
+                                       uint16_t *out, hipStream_t stream);
 
 // out[0 .. count) = 0 (16-bit elements)
 hipError_t launch_fill_zero_u16(uint16_t *out, int64_t count, hipStream_t stream);

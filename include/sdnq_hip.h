@@ -90,7 +90,7 @@ sdnq_status_t sdnq_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, 
  * with the same g; lora_a[k,rank] and lora_b[rank,n] bf16 (both NULL and rank 0
  * for no adapter; the adapter sees the unrotated x); y[m,n] bf16.
  * The int8 x codes and the int32 accumulators never leave the GPU's workspace and
- * registers; the LoRA factor x.lora_a is rounded to bf16 in the workspace.
+ * registers; the LoRA factor lora_scale * (x lora_a) is rounded to bf16 in the workspace.
  * workspace: at least sdnq_workspace_bytes(m, n, k, rank, 0) bytes. */
 sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k,
                                    const int8_t *qw, const float *w_scale, int64_t n, int32_t g,
@@ -101,7 +101,8 @@ sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k,
 /* Forward from activations that are already rotated and quantized (qx, x_scale
  * from sdnq_rotate_quantize_act with the weight's g): the int8 GEMM with its fused
  * dequantization epilogue.  t[m,rank] (bf16, = x lora_a) and lora_b[rank,n] are
- * nullable; when given, lora_scale * (t lora_b) is added.
+ * nullable; when given, t . bf16(lora_scale * lora_b) is added (exactly
+ * lora_scale * (t lora_b) when lora_scale is a power of two).
  * workspace: at least sdnq_workspace_bytes(m, n, k, rank, 0) bytes. */
 sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_scale, int64_t m,
                                              int64_t k, const int8_t *qw, const float *w_scale,
