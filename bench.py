@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings of the other workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 256 MiB device-to-device copy first (scales the HBM byte counters)")
     return ap.parse_args()
@@ -74,6 +75,68 @@ def cpu_baseline(inp, target_s: float) -> dict:
             "sample": f"first {rows} of {M} token rows through both layers (rotate+quantize, exact int GEMM, "
                       f"fp32 dequant, bf16 out); weights prepared outside; {t:.1f} s",
             "seconds": round(t, 2)}
+
+
+def measure_rows(torch, h, synth, reps: int = 10) -> dict:
+    """Whole-call timings (HIP events on the launch stream) of the other steps of
+    the layer, each on its own workload: weight preparation, the attention
+    projection forward, the QuaRot-style forward with LoRA (g = 64 and 128) and
+    the PEFT backward (input gradient + LoRA gradients)."""
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    rows = {}
+    a = synth.make_config("attn")
+    x, w = to_dev_bf16(torch, a["x"]), to_dev_bf16(torch, a["w"])
+    us = timed(lambda: h.sdnq_rotate_quantize_weight(w, 256))
+    nb = 3072 * 3072 * 3 + 3072 * 4
+    rows["a0_weight_prep_3072x3072_g256"] = {"us": round(us, 2), "GB/s": round(nb / us / 1e3, 1)}
+    qw, sw = h.sdnq_rotate_quantize_weight(w, 256)
+    ws = torch.empty(h.sdnq_workspace_bytes(4096, 3072, 3072, 0, False), dtype=torch.uint8, device=dev)
+    y = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda: h.sdnq_qlinear_forward(x, qw, sw, 256, out=y, workspace=ws))
+    ops = 2.0 * 4096 * 3072 * 3072
+    rows["attn_forward_4096x3072x3072_g256"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+                                                "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2)}
+    del x, w, ws, y
+    q = synth.make_config("quarot")
+    c = synth.CONFIGS["quarot"]
+    x, w = to_dev_bf16(torch, q["x"]), to_dev_bf16(torch, q["w"])
+    la, lb = to_dev_bf16(torch, q["lora_a"]), to_dev_bf16(torch, q["lora_b"])
+    ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, c.lora_rank, False), dtype=torch.uint8, device=dev)
+    y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
+    ops = 2.0 * c.m * c.n * c.k
+    for g in (64, 128):
+        qw, sw = h.sdnq_rotate_quantize_weight(w, g)
+        us = timed(lambda: h.sdnq_qlinear_forward(x, qw, sw, g, la, lb, c.lora_scale, out=y, workspace=ws))
+        rows[f"quarot_lora_forward_8192x3072x3072_g{g}_r32"] = {
+            "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+            "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2)}
+    del x, w, la, lb, ws, y
+    p = synth.make_config("peft")
+    c = synth.CONFIGS["peft"]
+    x, w, dy = to_dev_bf16(torch, p["x"]), to_dev_bf16(torch, p["w"]), to_dev_bf16(torch, p["dy"])
+    la, lb = to_dev_bf16(torch, p["lora_a"]), to_dev_bf16(torch, p["lora_b"])
+    qw, sw = h.sdnq_rotate_quantize_weight(w, 256)
+    ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, c.lora_rank, True), dtype=torch.uint8, device=dev)
+    us = timed(lambda: h.sdnq_qlinear_backward_input(dy, qw, sw, 256, x, la, lb, c.lora_scale, workspace=ws))
+    ops = 2.0 * c.m * c.n * c.k
+    rows["peft_backward_16384x3072x3072_g256_r64"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+                                                      "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
+                                                      "note": "dX through the int8 weight + LoRA dX, dA, dB"}
+    return rows
 
 
 def main():
@@ -186,6 +249,8 @@ def main():
                                      "per_launch_bytes": [M * K_UP * 3 + M * 4, M * K_DOWN * 3 + M * 4]},
         "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
     }
+    if not args.no_rows:
+        out["rows"] = measure_rows(torch, h, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

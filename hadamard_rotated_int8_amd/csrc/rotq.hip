@@ -20,7 +20,8 @@
 // So value-index bits 0-2 (j) and 5-7 (i) live in registers and bits 3-4 in the
 // lane-within-quad: stages h = 1, 2, 4, 32, 64, 128 are register butterflies and
 // h = 8, 16 are quad_perm DPP exchanges.  The whole row stays in registers until
-// its absmax is known (one workgroup holds `rows_per_wg` complete rows).
+// its absmax is known (one workgroup holds `rows_per_wg` complete rows at a
+// time and walks over row groups persistently, prefetching the next group).
 //
 // Cross-lane stages keep a per-lane sign: the upper lane of a pair computes
 // fma(partner, -1, self) = self - partner = -(a - b), which rounds exactly like
@@ -87,169 +88,202 @@ __device__ __forceinline__ void dpp_stage_xor2(float (&r)[8], float m) {
                : "v"(m));
 }
 
-template <int G, bool COLSCALE>
-__global__ __launch_bounds__(kMaxThreads) void rotq_kernel(
+template <int G, bool COLSCALE, int MAXT>
+__global__ __launch_bounds__(MAXT) void rotq_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
-    int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg) {
-  __shared__ uint32_t row_max[kMaxRowsPerWg];
+    int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg, int64_t groups) {
+  // Persistent: workgroup b handles row groups b, b + gridDim.x, ... and loads the
+  // next group's values while it transforms the current one.  Row maxima go
+  // through three rotating LDS slots: slot (it+1)%3 is cleared at the start of
+  // iteration it, before that iteration's barrier, so one barrier per group
+  // separates every clear from the atomics that follow it and from the reads
+  // that precede it.
+  __shared__ uint32_t row_max[3][kMaxRowsPerWg];
 
   const int tid = threadIdx.x;
   const int r_local = tid / t_row;
   const int qt = tid - r_local * t_row;
   const int sb = qt >> 2;     // superblock of this quad
   const int l4 = qt & 3;      // lane within the quad
-  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + r_local;
-  const bool row_ok = row < rows;
-  if (tid < rows_per_wg) row_max[tid] = 0u;
-
-  // ---- load: 8 x 16 bytes, e0(i) = sb*256 + 32*i + 8*l4
   const int64_t base = sb * 256 + 8 * l4;
-  v4u raw[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t e0 = base + 32 * i;
-    if (row_ok && e0 < cols)
-      raw[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(x + row * cols + e0));
-    else
-      raw[i] = v4u{0u, 0u, 0u, 0u};
+  if (tid < rows_per_wg) {
+    row_max[0][tid] = 0u;
+    row_max[1][tid] = 0u;
   }
+  __syncthreads();
 
-  float v[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      v[i][2 * w] = bf16_lo(raw[i][w]);
-      v[i][2 * w + 1] = bf16_hi(raw[i][w]);
-    }
-  }
-
-  if constexpr (COLSCALE) {
+  // ---- load: 8 x 16 bytes, e0(i) = sb*256 + 32*i + 8*l4.  Buffer loads over the
+  // group's rows: lanes past the last row or column read zeros, without a branch.
+  auto group_rows = [&](int64_t grp) -> int64_t {
+    const int64_t first = grp * rows_per_wg;
+    const int64_t left = rows - first;
+    return grp < groups ? (left < rows_per_wg ? left : rows_per_wg) : 0;
+  };
+  auto load = [&](int64_t grp, v4u (&raw)[8]) {
+    const int64_t nrows = group_rows(grp);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + (grp < groups ? grp : 0) * rows_per_wg * cols), 0, (int)(nrows * cols * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t e0 = base + 32 * i;
-      if (e0 < cols) {
-        const float4 c0 = *reinterpret_cast<const float4 *>(col_scale + e0);
-        const float4 c1 = *reinterpret_cast<const float4 *>(col_scale + e0 + 4);
-        v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
-        v[i][2] = v[i][2] * c0.z; v[i][3] = v[i][3] * c0.w;
-        v[i][4] = v[i][4] * c1.x; v[i][5] = v[i][5] * c1.y;
-        v[i][6] = v[i][6] * c1.z; v[i][7] = v[i][7] * c1.w;
+      const unsigned off = (e0 < cols) ? (unsigned)((r_local * cols + e0) * 2) : 0x80000000u;
+      raw[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  };
+
+  v4u raw[8];
+  int64_t grp = blockIdx.x;
+  load(grp, raw);
+  for (int it = 0; grp < groups; ++it, grp += gridDim.x) {
+    const int64_t row = grp * rows_per_wg + r_local;
+    const bool row_ok = row < rows;
+    if (tid < rows_per_wg) row_max[(it + 1) % 3][tid] = 0u;
+
+    float v[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        v[i][2 * w] = bf16_lo(raw[i][w]);
+        v[i][2 * w + 1] = bf16_hi(raw[i][w]);
       }
     }
-  }
+    // The raw registers are free again: fetch the next group into them, so its
+    // loads stay in flight through the whole transform of this group.
+    __builtin_amdgcn_sched_barrier(0);
+    load(grp + gridDim.x, raw);
+    __builtin_amdgcn_sched_barrier(0);
 
-  float sign = 1.0f;  // per-lane sign of the stored values after the DPP stages
-  if constexpr (G > 1) {
-    // h = 1, 2, 4: value bits 0-2 (register index j)
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    if constexpr (COLSCALE) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if ((j & h) == 0) {
-            const float a = v[i][j], b = v[i][j + h];
-            v[i][j] = a + b;
-            v[i][j + h] = a - b;
-          }
+        const int64_t e0 = base + 32 * i;
+        if (e0 < cols) {
+          const float4 c0 = *reinterpret_cast<const float4 *>(col_scale + e0);
+          const float4 c1 = *reinterpret_cast<const float4 *>(col_scale + e0 + 4);
+          v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
+          v[i][2] = v[i][2] * c0.z; v[i][3] = v[i][3] * c0.w;
+          v[i][4] = v[i][4] * c1.x; v[i][5] = v[i][5] * c1.y;
+          v[i][6] = v[i][6] * c1.z; v[i][7] = v[i][7] * c1.w;
         }
       }
     }
-    // h = 8: lane xor 1 within the quad; h = 16: lane xor 2
-    {
-      const float m1 = (l4 & 1) ? -1.0f : 1.0f;
+
+    float sign = 1.0f;  // per-lane sign of the stored values after the DPP stages
+    if constexpr (G > 1) {
+      // h = 1, 2, 4: value bits 0-2 (register index j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dpp_stage_xor1(v[i], m1);
-      const float m2 = (l4 & 2) ? -1.0f : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dpp_stage_xor2(v[i], m2);
-      sign = m1 * m2;
-    }
-    // h = 32, 64, 128: value bits 5-7 (register index i), up to g/2
-#pragma unroll
-    for (int hi = 1; hi < 8; hi <<= 1) {
-      if (32 * hi < G) {
+      for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          if ((i & hi) == 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float a = v[i][j], b = v[i + hi][j];
+          for (int j = 0; j < 8; ++j) {
+            if ((j & h) == 0) {
+              const float a = v[i][j], b = v[i][j + h];
               v[i][j] = a + b;
-              v[i + hi][j] = a - b;
+              v[i][j + h] = a - b;
+            }
+          }
+        }
+      }
+      // h = 8: lane xor 1 within the quad; h = 16: lane xor 2
+      {
+        const float m1 = (l4 & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dpp_stage_xor1(v[i], m1);
+        const float m2 = (l4 & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dpp_stage_xor2(v[i], m2);
+        sign = m1 * m2;
+      }
+      // h = 32, 64, 128: value bits 5-7 (register index i), up to g/2
+#pragma unroll
+      for (int hi = 1; hi < 8; hi <<= 1) {
+        if (32 * hi < G) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if ((i & hi) == 0) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const float a = v[i][j], b = v[i + hi][j];
+                v[i][j] = a + b;
+                v[i + hi][j] = a - b;
+              }
             }
           }
         }
       }
     }
-  }
 
-  // g = 128: the normalization constant is inexact, so apply it to every value now.
-  if constexpr (G == 128) {
-    const float sc = sign * norm_const<G>();
+    // g = 128: the normalization constant is inexact, so apply it to every value now.
+    if constexpr (G == 128) {
+      const float sc = sign * norm_const<G>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * sc;
+    }
+
+    float loc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * sc;
-  }
+      for (int j = 0; j < 8; ++j) loc = fmaxf(loc, fabsf(v[i][j]));
 
-  float loc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) loc = fmaxf(loc, fabsf(v[i][j]));
+    uint32_t *slot = row_max[it % 3];
+    if (row_ok) atomicMax(&slot[r_local], __float_as_uint(loc));
+    // LDS-only barrier: the prefetch of the next group stays in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float a = __uint_as_float(slot[r_local]);
 
-  __syncthreads();
-  if (row_ok) atomicMax(&row_max[r_local], __float_as_uint(loc));
-  __syncthreads();
-  float a = __uint_as_float(row_max[r_local]);
+    // g = 64, 256: norm_const is a power of two, so a = fl32(max|u| * c) = max|fl32(u * c)|.
+    if constexpr (G == 64 || G == 256) a = a * norm_const<G>();
+    const float s = a / 127.0f;
+    // Rows with a < 2^-100 are scaled by 2^100 (exact) before r = 127/a is formed,
+    // which would otherwise overflow binary32.
+    const bool tiny = a < 0x1p-100f;
+    const float up = tiny ? 0x1p100f : 1.0f;
+    const float as = a * up;
+    const float r = (as > 0.0f) ? 127.0f / as : 0.0f;
+    if (row_ok && qt == 0) scale[row] = s;
 
-  // g = 64, 256: norm_const is a power of two, so a = fl32(max|u| * c) = max|fl32(u * c)|.
-  if constexpr (G == 64 || G == 256) a = a * norm_const<G>();
-  const float s = a / 127.0f;
-  // Rows with a < 2^-100 are scaled by 2^100 (exact) before r = 127/a is formed,
-  // which would otherwise overflow binary32.
-  const bool tiny = a < 0x1p-100f;
-  const float up = tiny ? 0x1p100f : 1.0f;
-  const float as = a * up;
-  const float r = (as > 0.0f) ? 127.0f / as : 0.0f;
-  if (row_ok && qt == 0) scale[row] = s;
+    // Multiplier turning the stored value into fl32(y * r).
+    //  - g = 64/256, a >= 2^-100: y = u*c exactly for every value that can get a
+    //    nonzero code, and (c * r) is exact, so fl32(u * (c*r)) = fl32(fl32(u*c) * r);
+    //    values with u*c below the normal range give |y*r| < 2^-19 on both routes.
+    //  - g = 1/128: the stored value already is y.
+    //  - tiny rows: normalize exactly as written, scale by 2^100, then multiply by r.
+    float mult = r;
+    if (!tiny) {
+      if constexpr (G == 64 || G == 256) mult = r * norm_const<G>() * sign;
+    } else {
+      float sc = 1.0f;
+      if constexpr (G == 64 || G == 256) sc = sign * norm_const<G>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = (v[i][j] * sc) * up;
+    }
 
-  // Multiplier turning the stored value into fl32(y * r).
-  //  - g = 64/256, a >= 2^-100: y = u*c exactly for every value that can get a
-  //    nonzero code, and (c * r) is exact, so fl32(u * (c*r)) = fl32(fl32(u*c) * r);
-  //    values with u*c below the normal range give |y*r| < 2^-19 on both routes.
-  //  - g = 1/128: the stored value already is y.
-  //  - tiny rows: normalize exactly as written, scale by 2^100, then multiply by r.
-  float mult = r;
-  if (!tiny) {
-    if constexpr (G == 64 || G == 256) mult = r * norm_const<G>() * sign;
-  } else {
-    float sc = 1.0f;
-    if constexpr (G == 64 || G == 256) sc = sign * norm_const<G>();
+    {
+      // Buffer stores over the group's rows: lanes past the last row or column
+      // fall outside the buffer and are dropped.
+      const int64_t nrows = group_rows(grp);
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(q + grp * rows_per_wg * cols), 0, (int)(nrows * cols), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = (v[i][j] * sc) * up;
-  }
-
-  if (row_ok) {
-    int8_t *qr = q + row * cols;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t e0 = base + 32 * i;
-      if (e0 < cols) {
+      for (int i = 0; i < 8; ++i) {
+        const int64_t e0 = base + 32 * i;
         uint32_t c[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float t = v[i][j] * mult;
           c[j] = code_bits(t);
         }
-        uint2 packed;
-        packed.x = pack4(c[0], c[1], c[2], c[3]);
-        packed.y = pack4(c[4], c[5], c[6], c[7]);
-        *reinterpret_cast<uint2 *>(qr + e0) = packed;
+        const unsigned off = (e0 < cols) ? (unsigned)(r_local * cols + e0) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(v2u, (v2u){pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])}), rq, off,
+            0, 0);
       }
     }
   }
@@ -257,11 +291,11 @@ __global__ __launch_bounds__(kMaxThreads) void rotq_kernel(
 
 // Rows per workgroup: the count with the fewest idle lanes in the last wavefront,
 // then the one closest to 256 threads.
-int pick_rows_per_wg(int t_row) {
+int pick_rows_per_wg(int t_row, int max_threads) {
   int best_r = 1;
   double best_waste = 2.0;
   int best_dist = 1 << 30;
-  for (int r = 1; r <= kMaxRowsPerWg && r * t_row <= kMaxThreads; ++r) {
+  for (int r = 1; r <= kMaxRowsPerWg && r * t_row <= max_threads; ++r) {
     const int threads = r * t_row;
     const int padded = (threads + 63) / 64 * 64;
     const double waste = double(padded - threads) / padded;
@@ -275,15 +309,59 @@ int pick_rows_per_wg(int t_row) {
   return best_r;
 }
 
+// Resident workgroups per CU for a kernel at a block size (cached; the launch
+// configuration only depends on the kernel and the block size).
+template <int G, bool CS, int MAXT>
+int blocks_per_cu(int threads) {
+  static int cached_threads[kMaxThreads / 4 + 1];
+  static int cached_blocks[kMaxThreads / 4 + 1];
+  const int slot = threads / 4;
+  if (cached_threads[slot] == threads) return cached_blocks[slot];
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT>, threads, 0) != hipSuccess ||
+      n < 1)
+    n = 1;
+  cached_blocks[slot] = n;
+  cached_threads[slot] = threads;
+  return n;
+}
+
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int G, bool CS, int MAXT>
+hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
+                        float *scale, int t_row, int rpw, hipStream_t stream) {
+  const int threads = rpw * t_row;
+  const int64_t groups = (rows + rpw - 1) / rpw;
+  int64_t blocks = (int64_t)cu_count() * blocks_per_cu<G, CS, MAXT>(threads);
+  if (blocks > groups) blocks = groups;
+  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT>), dim3((unsigned)blocks), dim3(threads), 0, stream, x, rows, cols,
+                     col_scale, q, scale, t_row, rpw, groups);
+  return hipGetLastError();
+}
+
+// Rows of up to 32768 values run in workgroups of at most 512 threads (up to 256
+// VGPRs per lane, room for the prefetch buffer); longer rows need up to 1024.
 template <int G, bool CS>
 hipError_t launch_typed(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale,
                         int8_t *q, float *scale, hipStream_t stream) {
   const int t_row = 4 * (int)((cols + 255) / 256);
-  const int rpw = pick_rows_per_wg(t_row);
-  const int64_t blocks = (rows + rpw - 1) / rpw;
-  hipLaunchKernelGGL((rotq_kernel<G, CS>), dim3((unsigned)blocks), dim3(rpw * t_row), 0, stream, x,
-                     rows, cols, col_scale, q, scale, t_row, rpw);
-  return hipGetLastError();
+  if (t_row <= 512) {
+    const int rpw = pick_rows_per_wg(t_row, 512);
+    return launch_sized<G, CS, 512>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);
+  }
+  const int rpw = pick_rows_per_wg(t_row, kMaxThreads);
+  return launch_sized<G, CS, kMaxThreads>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);
 }
 
 }  // namespace

@@ -82,9 +82,17 @@ def assert_rq_exact(x_bits, g, col_scale=None):
     (128, 37, 384), (128, 19, 1152), (128, 64, 3072),
     (64, 33, 320), (64, 5, 64), (64, 70, 3072), (64, 9, 192),
     (1, 11, 16), (1, 21, 48), (1, 40, 272), (1, 64, 3072),
+    (256, 3, 40960), (64, 2, 65536),        # rows longer than 32768 values: 1024-thread workgroups
 ])
 def test_rotate_quantize_bit_exact(g, m, k):
     x = synth.make_linear(m, k, 16, seed=100 + g + m)["x"]
+    assert_rq_exact(x, g)
+
+
+@pytest.mark.parametrize("g,m,k", [(64, 20000, 3072), (256, 9000, 10240), (1, 30000, 512)])
+def test_rotate_quantize_many_rows_bit_exact(g, m, k):
+    """Enough rows that every persistent workgroup walks several row groups."""
+    x = synth.make_linear(m, k, 16, seed=7 + g)["x"]
     assert_rq_exact(x, g)
 
 
