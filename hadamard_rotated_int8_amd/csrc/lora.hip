@@ -14,21 +14,23 @@ namespace sdnq {
 namespace {
 
 // ----------------------------------------------------------- lora_down --
-// A workgroup of 4 wavefronts handles 32 tokens; each wavefront takes a quarter
-// of the contraction and keeps 32 x rank fp32 partial sums, which are added in
-// wavefront order through LDS.  MFMA 16x16x32: row operand = R rows (rank index),
-// column operand = x rows (token), so lane l owns token l % 16 and the four
-// consecutive rank indices 4 * (l / 16) + 0..3 of each 16 x 16 tile.
-constexpr int kDownTokens = 32;
+// A workgroup of 4 wavefronts handles 16*TT tokens; each wavefront takes a
+// quarter of the contraction and keeps 16*TT x rank fp32 partial sums, which are
+// added in wavefront order through LDS.  MFMA 16x16x32: row operand = R rows
+// (rank index), column operand = x rows (token), so lane l owns token l % 16 and
+// the four consecutive rank indices 4 * (l / 16) + 0..3 of each 16 x 16 tile.
+// The contraction is walked in batches of 4 steps of 32 whose loads are all
+// issued before the batch's MFMAs, so several steps of loads stay in flight.
 constexpr int kMaxRank = 128;
+constexpr int kDownBatch = 4;
 
-template <int RT>  // RT = rank / 16
+template <int RT, int TT>  // RT = rank / 16, TT = tokens / 16
 __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restrict__ x, int64_t m, int64_t cols,
                                                         const uint16_t *__restrict__ rmat, float scale,
                                                         uint16_t *__restrict__ out) {
-  __shared__ v4f red[4][2][RT][64];
+  __shared__ v4f red[4][TT][RT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kDownTokens;
+  const int64_t t0 = (int64_t)blockIdx.x * (16 * TT);
   const int rank = RT * 16;
 
   // contraction range of this wavefront, in steps of 32
@@ -39,9 +41,9 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restri
   c_end = c_end < cols ? c_end : cols;
 
   const int koff = 8 * (lane >> 4);
-  const uint16_t *xr[2];
+  const uint16_t *xr[TT];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < TT; ++s) {
     int64_t t = t0 + s * 16 + (lane & 15);
     t = t < m ? t : m - 1;
     xr[s] = x + t * cols + koff;
@@ -50,46 +52,51 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restri
 #pragma unroll
   for (int u = 0; u < RT; ++u) rr[u] = rmat + (int64_t)(u * 16 + (lane & 15)) * cols + koff;
 
-  v4f acc[2][RT];
+  v4f acc[TT][RT];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < TT; ++s)
 #pragma unroll
     for (int u = 0; u < RT; ++u) acc[s][u] = v4f{};
 
-  for (int64_t c0 = c_begin; c0 < c_end; c0 += 32) {
-    const bool ok = c0 + koff < cols;
-    v8bf bx[2], br[RT];
+  for (int64_t cb = c_begin; cb < c_end; cb += 32 * kDownBatch) {
+    v8bf bx[kDownBatch][TT], br[kDownBatch][RT];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) bx[s] = ok ? *reinterpret_cast<const v8bf *>(xr[s] + c0) : v8bf{};
+    for (int b = 0; b < kDownBatch; ++b) {
+      const int64_t c0 = cb + 32 * b;
+      const bool ok = c0 < c_end && c0 + koff < cols;
 #pragma unroll
-    for (int u = 0; u < RT; ++u) br[u] = ok ? *reinterpret_cast<const v8bf *>(rr[u] + c0) : v8bf{};
+      for (int s = 0; s < TT; ++s) bx[b][s] = ok ? *reinterpret_cast<const v8bf *>(xr[s] + c0) : v8bf{};
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int u = 0; u < RT; ++u) br[b][u] = ok ? *reinterpret_cast<const v8bf *>(rr[u] + c0) : v8bf{};
+    }
 #pragma unroll
-      for (int u = 0; u < RT; ++u) acc[s][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br[u], bx[s], acc[s][u], 0, 0, 0);
+    for (int b = 0; b < kDownBatch; ++b)
+#pragma unroll
+      for (int s = 0; s < TT; ++s)
+#pragma unroll
+        for (int u = 0; u < RT; ++u)
+          acc[s][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br[b][u], bx[b][s], acc[s][u], 0, 0, 0);
   }
 
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < TT; ++s)
 #pragma unroll
     for (int u = 0; u < RT; ++u) red[wave][s][u][lane] = acc[s][u];
   __syncthreads();
-  if (wave == 0) {
+  // wavefront w writes token subtiles s = w, w + 4, ... (sums in wavefront order)
+  for (int s = wave; s < TT; s += 4) {
+    const int64_t t = t0 + s * 16 + (lane & 15);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t t = t0 + s * 16 + (lane & 15);
+    for (int u = 0; u < RT; ++u) {
+      v4f sum = red[0][s][u][lane];
 #pragma unroll
-      for (int u = 0; u < RT; ++u) {
-        v4f sum = red[0][s][u][lane];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) sum = sum + red[w][s][u][lane];
-        if (t < m) {
-          const int r0 = u * 16 + 4 * (lane >> 4);
-          uint2 packed;
-          packed.x = pack_bf16x2(scale * sum[0], scale * sum[1]);
-          packed.y = pack_bf16x2(scale * sum[2], scale * sum[3]);
-          *reinterpret_cast<uint2 *>(out + t * rank + r0) = packed;
-        }
+      for (int w = 1; w < 4; ++w) sum = sum + red[w][s][u][lane];
+      if (t < m) {
+        const int r0 = u * 16 + 4 * (lane >> 4);
+        uint2 packed;
+        packed.x = pack_bf16x2(scale * sum[0], scale * sum[1]);
+        packed.y = pack_bf16x2(scale * sum[2], scale * sum[3]);
+        *reinterpret_cast<uint2 *>(out + t * rank + r0) = packed;
       }
     }
   }
@@ -211,6 +218,50 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in
   }
 }
 
+// int8 transpose of a rows x cols matrix whose sides are multiples of 16, in
+// 128 x 128 tiles: 16-byte row chunks in, LDS with a 4-byte row pad, 16-byte
+// column chunks (gathered byte by byte from LDS) out.
+constexpr int kT8 = 128;
+constexpr int kT8Pitch = kT8 + 4;
+
+__global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t *__restrict__ in, int64_t rows,
+                                                           int64_t cols, int8_t *__restrict__ out) {
+  __shared__ __align__(16) uint8_t tile[kT8 * kT8Pitch];
+  const int64_t r0 = (int64_t)blockIdx.y * kT8, c0 = (int64_t)blockIdx.x * kT8;
+  const int tid = threadIdx.x;
+  v4u v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // item = (row, chunk of 16 columns)
+    const int item = tid + 256 * i, r = item >> 3, ch = item & 7;
+    const bool ok = r0 + r < rows && c0 + 16 * ch < cols;
+    v[i] = ok ? *reinterpret_cast<const v4u *>(in + (r0 + r) * cols + c0 + 16 * ch) : v4u{};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int item = tid + 256 * i, r = item >> 3, ch = item & 7;
+    uint32_t *d = reinterpret_cast<uint32_t *>(tile + r * kT8Pitch + 16 * ch);
+    d[0] = v[i][0];
+    d[1] = v[i][1];
+    d[2] = v[i][2];
+    d[3] = v[i][3];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // item = (output row = input column c, chunk of 16 input rows)
+    const int item = tid + 256 * i, c = item >> 3, ch = item & 7;
+    if (c0 + c < cols && r0 + 16 * ch < rows) {
+      v4u o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint8_t *src = tile + (16 * ch + 4 * w) * kT8Pitch + c;
+        o[w] = (uint32_t)src[0] | ((uint32_t)src[kT8Pitch] << 8) | ((uint32_t)src[2 * kT8Pitch] << 16) |
+               ((uint32_t)src[3 * kT8Pitch] << 24);
+      }
+      *reinterpret_cast<v4u *>(out + (c0 + c) * rows + r0 + 16 * ch) = o;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void transpose_scale_bf16_kernel(const uint16_t *__restrict__ in, int64_t rows,
                                                                    int64_t cols, float scale,
                                                                    uint16_t *__restrict__ out) {
@@ -239,19 +290,28 @@ hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
-                            float scale, uint16_t *out, hipStream_t stream) {
-  const dim3 grid((unsigned)((m + kDownTokens - 1) / kDownTokens));
+template <int TT>
+hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
+                              float scale, uint16_t *out, hipStream_t stream) {
+  const dim3 grid((unsigned)((m + 16 * TT - 1) / (16 * TT)));
   switch (rank / 16) {
-#define SDNQ_DOWN(RT)                                                                                  \
-  case RT:                                                                                             \
-    hipLaunchKernelGGL(lora_down_kernel<RT>, grid, dim3(256), 0, stream, x, m, cols, rmat, scale, out); \
+#define SDNQ_DOWN(RT)                                                                                         \
+  case RT:                                                                                                    \
+    hipLaunchKernelGGL((lora_down_kernel<RT, TT>), grid, dim3(256), 0, stream, x, m, cols, rmat, scale, out); \
     break;
     SDNQ_DOWN(1) SDNQ_DOWN(2) SDNQ_DOWN(3) SDNQ_DOWN(4) SDNQ_DOWN(5) SDNQ_DOWN(6) SDNQ_DOWN(7) SDNQ_DOWN(8)
 #undef SDNQ_DOWN
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// 64 tokens per workgroup when there are enough tokens to fill the chip that way
+// (the rank x cols factor is then re-read from L2 half as often), else 32.
+hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
+                            float scale, uint16_t *out, hipStream_t stream) {
+  if (m >= 16384) return launch_lora_down_t<4>(x, m, cols, rmat, rank, scale, out, stream);
+  return launch_lora_down_t<2>(x, m, cols, rmat, rank, scale, out, stream);
 }
 
 int lora_grad_splits(int64_t m) {
@@ -284,8 +344,9 @@ hipError_t launch_fill_zero_u16(uint16_t *out, int64_t count, hipStream_t stream
 }
 
 hipError_t launch_transpose_i8(const int8_t *in, int64_t rows, int64_t cols, int8_t *out, hipStream_t stream) {
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-  hipLaunchKernelGGL((transpose_kernel<int8_t, 64>), grid, dim3(256), 0, stream, in, rows, cols, out);
+  if (rows % 16 || cols % 16) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((cols + kT8 - 1) / kT8), (unsigned)((rows + kT8 - 1) / kT8));
+  hipLaunchKernelGGL(transpose_i8_kernel, grid, dim3(256), 0, stream, in, rows, cols, out);
   return hipGetLastError();
 }
 

@@ -211,6 +211,15 @@ def test_forward_with_lora(g, rank, scale):
     assert err < REL_L2
 
 
+@pytest.mark.parametrize("rank", [48, 128])
+def test_forward_with_lora_many_tokens(rank):
+    """16400 tokens: the LoRA down-projection's wide-workgroup variant with a ragged last workgroup."""
+    y, ref = forward_case(16400, 320, 256, 64, rank=rank, seed=5 + rank, scale=0.75)
+    err = rel_l2(y, ref["y"])
+    say(f"    rel-L2 {err:.3e}  max-token {max_token_rel(y, ref['y']):.3e}")
+    assert err < REL_L2
+
+
 def test_forward_quantized_entry_matches_forward():
     inp = synth.make_linear(200, 512, 384, seed=3, lora_rank=32)
     say("  forward_quantized vs forward")
@@ -264,3 +273,10 @@ def test_backward_with_lora_grads(g, rank):
 def test_backward_ragged_tokens_and_tiles():
     inp, (dx, ga, gb), ref, _ = backward_case(33, 272, 512, 256, rank=32, seed=9)
     assert max(rel_l2(dx, ref["dx"]), rel_l2(ga, ref["grad_a"]), rel_l2(gb, ref["grad_b"])) < REL_L2
+
+
+def test_backward_many_tokens_with_lora():
+    inp, (dx, ga, gb), ref, _ = backward_case(16400, 272, 256, 128, rank=48, seed=11, scale=0.5)
+    errs = (rel_l2(dx, ref["dx"]), rel_l2(ga, ref["grad_a"]), rel_l2(gb, ref["grad_b"]))
+    say(f"    dx {errs[0]:.3e}  grad_a {errs[1]:.3e}  grad_b {errs[2]:.3e}")
+    assert max(errs) < REL_L2
