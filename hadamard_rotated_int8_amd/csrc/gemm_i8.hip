@@ -34,8 +34,7 @@
 namespace sdnq {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4;
-constexpr int kStageBytes = (BM + BN) * BK;  // 32 KB: A tile then B tile, rows of 64 bytes
+constexpr int BM = 256, BK = 64, STAGES = 4;
 constexpr int kThreads = 512;  // 8 wavefronts: two per SIMD
 constexpr int kGroupM = 4;
 constexpr unsigned kOutOfRange = 0x80000000u;  // any offset past num_records reads as zero
@@ -83,25 +82,44 @@ __device__ __forceinline__ v16f lora_tile(const uint16_t *__restrict__ T, const 
   return acc;
 }
 
-// s_waitcnt vmcnt(n) then s_barrier, as one compiler barrier.  The direct-to-LDS
+// s_waitcnt vmcnt(N) then s_barrier, as one compiler barrier.  The direct-to-LDS
 // loads are invisible to the compiler's wait tracking, so their completion is
 // awaited here explicitly before any wavefront reads what the others loaded.
-__device__ __forceinline__ void wait_loads_and_barrier(int outstanding) {
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
   __builtin_amdgcn_sched_barrier(0);
-  if (outstanding >= 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else if (outstanding >= 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <Epilogue EPI, int WAVES_M, int G, bool LORA>
+// Tile geometry for an output tile of BM x BN_.  A stage holds the A tile then
+// the B tile, rows of BK bytes, loaded in groups of 16 rows (1 KB, one
+// direct-to-LDS load per wavefront).  The groups are dealt to the 8 wavefronts
+// round-robin; when they do not divide evenly the spare slots load nothing (an
+// out-of-range offset) into a 1 KB dummy area, so every wavefront issues the same
+// number of loads and one vmcnt value fits all.
+template <int BN_>
+struct TileCfg {
+  static constexpr int kStageBytes = (BM + BN_) * BK;
+  static constexpr int kGroups = (BM + BN_) / 16;
+  static constexpr int kLoadsPerWave = (kGroups + 7) / 8;
+  static constexpr bool kDummy = kGroups % 8 != 0;
+  static constexpr int kLdsBytes = STAGES * kStageBytes + (kDummy ? 1024 : 0);
+  static_assert(BN_ % 32 == 0 && BM / 16 == 16, "A groups fill load slots 0 and 1");
+};
+
+template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  using Cfg = TileCfg<BN>;
+  constexpr int kStageBytes = Cfg::kStageBytes;
+  constexpr int LPW = Cfg::kLoadsPerWave;
   constexpr int WAVES_N = 8 / WAVES_M;
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int SM = TM / 32, SN = TN / 32;
-  static_assert(SM * SN == 8, "8 MFMA tiles (128 int32 accumulators) per wavefront");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && SM * SN <= 10, "at most 160 int32 accumulators per wavefront");
 
-  __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[Cfg::kLdsBytes];
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -113,13 +131,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
   // ---- direct global -> LDS loads (buffer_load_dwordx4 ... lds)
-  // A stage holds the A tile (256 rows x 64 B) then the B tile.  Load j (0..1)
-  // of a wavefront fills the 16-row group g = 8*j + wave: lane i lands at byte
-  // 16*i of that 1 KB group, i.e. row 16*g + i/4, stored chunk i%4.  Rows are
-  // XOR-swizzled (stored chunk = logical chunk ^ ((row >> 2) & 3)), so lane i
-  // fetches logical chunk c = (i & 3) ^ ((i >> 4) & 3).  Rows past the matrix
-  // end lie past the buffer's num_records and read as zero, and so do chunks
-  // past K (their offset is pushed out of range).
+  // A stage holds the A tile (256 rows x 64 B) then the B tile (BN rows).  Load
+  // slot j of a wavefront fills the 16-row group 8*j + wave of the stage (slots
+  // 0, 1: A groups; slots 2..: B groups): lane i lands at byte 16*i of that 1 KB
+  // group, i.e. row 16*g + i/4, stored chunk i%4.  Rows are XOR-swizzled (stored
+  // chunk = logical chunk ^ ((row >> 2) & 3)), so lane i fetches logical chunk
+  // c = (i & 3) ^ ((i >> 4) & 3).  Rows past the matrix end lie past the
+  // buffer's num_records and read as zero, and so do chunks past K (their offset
+  // is pushed out of range).
   const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
   const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
   const __amdgpu_buffer_rsrc_t rsrc_a =
@@ -127,9 +146,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   const __amdgpu_buffer_rsrc_t rsrc_b =
       __builtin_amdgcn_make_buffer_rsrc((void *)(args.b + n0 * K), 0, (int)(rows_b * K), 0x00020000);
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);
-  unsigned voff[2];
+  // per slot: row group within its operand, or -1 for a spare slot
+  int grp[LPW];
+  unsigned voff[LPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) voff[j] = (unsigned)((16 * (8 * j + wave) + (lane >> 2)) * K + 16 * lc);
+  for (int j = 0; j < LPW; ++j) {
+    const int g = 8 * j + wave;
+    grp[j] = j < 2 ? g : (g - BM / 16 < BN / 16 ? g - BM / 16 : -1);
+    voff[j] = (unsigned)((16 * (grp[j] < 0 ? 0 : grp[j]) + (lane >> 2)) * K + 16 * lc);
+  }
+  int8_t *const dummy = smem + STAGES * kStageBytes;
 
   const int nk = (int)((K + BK - 1) / BK);
   auto issue_loads = [&](int kt) {
@@ -139,11 +165,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     const unsigned oob = ((int64_t)k0 + BK <= K) ? 0u : (((int64_t)k0 + 16 * lc < K) ? 0u : kOutOfRange);
     int8_t *base = smem + st * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int g = 8 * j + wave;
-      const unsigned off = (voff[j] + k0) | oob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void *)(base + g * 1024), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_void *)(base + BM * BK + g * 1024), 16, off, 0, 0, 0);
+    for (int j = 0; j < LPW; ++j) {
+      // wavefront-uniform selects, no branch: a spare slot loads nothing into the dummy area
+      const bool spare = Cfg::kDummy && j >= 2 && grp[j] < 0;
+      int8_t *dst = spare ? dummy : base + (j < 2 ? 0 : BM * BK) + grp[j] * 1024;
+      const unsigned off = spare ? kOutOfRange : ((voff[j] + k0) | oob);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 2 ? rsrc_a : rsrc_b, (lds_void *)dst, 16, off, 0, 0, 0);
     }
   };
 
@@ -184,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   // range, so they only write zeros into a free stage.  This keeps the loop body
   // branch-free and the number of loads in flight constant (4 per tile).
   for (int t = 0; t < STAGES - 1; ++t) issue_loads(t);
-  wait_loads_and_barrier(8);
+  wait_loads_and_barrier<2 * LPW>();
   Frags f0, f1;
   read_frags(0, 0, f0);
 
@@ -192,19 +219,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     read_frags(kt, 1, f1);
     mfma_all(f0);
 #pragma unroll
-    for (int u = 0; u < SM + SN; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    for (int u = 0; u < SM * SN; ++u) {
+      if (u < SM + SN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
     }
-    wait_loads_and_barrier(4);
+    wait_loads_and_barrier<LPW>();
     issue_loads(kt + 3);
     read_frags(kt + 1, 0, f0);
     mfma_all(f1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS load
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    for (int u = 0; u < SM * SN; ++u) {
+      if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // 1 global->LDS load
+      if (u < SM + SN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
     }
   }
   // The zero-fill loads of the last iterations may still be landing in LDS.
@@ -390,29 +417,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   }
 }
 
-template <Epilogue EPI, int WAVES_M, int G, bool LORA>
+template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA>
 hipError_t launch_typed(const GemmArgs &args, hipStream_t stream) {
   const int tiles_m = (int)((args.m + BM - 1) / BM);
   const int tiles_n = (int)((args.n + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<EPI, WAVES_M, G, LORA>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
-                     args, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_i8_kernel<EPI, BN, WAVES_M, G, LORA>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
+                     stream, args, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_backward(const GemmArgs &args, hipStream_t stream) {
-  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 8, G, true>(args, stream)
-                       : launch_typed<Epilogue::kBackward, 8, G, false>(args, stream);
+  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 256, 8, G, true>(args, stream)
+                       : launch_typed<Epilogue::kBackward, 256, 8, G, false>(args, stream);
+}
+
+int gemm_cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Output tile width along N for the forward and int32 epilogues.  One workgroup
+// fills a compute unit, so a launch runs in ceil(tiles / CUs) rounds, each as
+// long as one tile (proportional to its width).  The width with the fewest
+// column-rounds wins (ties go to 256): e.g. 4096 x 10240 takes 2 rounds of
+// 256 x 320 tiles instead of 2.5 (so 3) of 256 x 256, and 4096 x 3072 one round
+// of 256 x 192 instead of 0.75 of 256 x 256.
+int gemm_tile_n(int64_t m, int64_t n) {
+  const int64_t cus = gemm_cu_count();
+  const int64_t tiles_m = (m + BM - 1) / BM;
+  auto cost = [&](int bn) { return (tiles_m * ((n + bn - 1) / bn) + cus - 1) / cus * bn; };
+  int best = 256;
+  for (int bn : {320, 192})
+    if (cost(bn) < cost(best)) best = bn;
+  return best;
+}
+
+template <Epilogue EPI, bool LORA>
+hipError_t launch_forward_like(const GemmArgs &args, hipStream_t stream) {
+  switch (gemm_tile_n(args.m, args.n)) {
+    case 320: return launch_typed<EPI, 320, 4, 1, LORA>(args, stream);
+    case 192: return launch_typed<EPI, 192, 4, 1, LORA>(args, stream);
+    default: return launch_typed<EPI, 256, 2, 1, LORA>(args, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream) {
   switch (epi) {
-    case Epilogue::kInt32: return launch_typed<Epilogue::kInt32, 2, 1, false>(args, stream);
+    case Epilogue::kInt32: return launch_forward_like<Epilogue::kInt32, false>(args, stream);
     case Epilogue::kForward:
-      return args.rank > 0 ? launch_typed<Epilogue::kForward, 2, 1, true>(args, stream)
-                           : launch_typed<Epilogue::kForward, 2, 1, false>(args, stream);
+      return args.rank > 0 ? launch_forward_like<Epilogue::kForward, true>(args, stream)
+                           : launch_forward_like<Epilogue::kForward, false>(args, stream);
     case Epilogue::kBackward:
       switch (args.g) {
         case 1: return launch_backward<1>(args, stream);

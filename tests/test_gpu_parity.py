@@ -169,6 +169,34 @@ def test_gemm_int32_bit_exact(m, n, k, b_layout):
     assert np.array_equal(c.cpu().numpy(), ref)
 
 
+# Shapes that select each output tile width on a 256-CU device (the launch picks
+# the width with the fewest column-rounds): small grids take 192 columns,
+# 4000 x 3840 takes 256 (240 tiles) and 4000 x 5104 takes 320 (256 tiles), all
+# with ragged row, column and K tails.
+TILE_WIDTH_SHAPES = [(4000, 3840, 80), (4000, 5104, 80), (260, 400, 48)]
+
+
+@pytest.mark.parametrize("b_layout", [0, 1])
+@pytest.mark.parametrize("m,n,k", TILE_WIDTH_SHAPES)
+def test_gemm_int32_every_tile_width(m, n, k, b_layout):
+    rng = np.random.default_rng(m + n + k + b_layout)
+    a = rng.integers(-128, 128, (m, k)).astype(np.int8)
+    b = rng.integers(-128, 128, (n, k) if b_layout == 0 else (k, n)).astype(np.int8)
+    say(f"  gemm_i8_i32 m={m} n={n} k={k} layout={b_layout}")
+    c = h.sdnq_gemm_i8_i32(d(a), d(b), b_layout)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i8(a, b, b_layout)
+    assert np.array_equal(c.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("m,n", [(4000, 3840), (4000, 5104)])
+def test_forward_every_tile_width(m, n):
+    y, ref = forward_case(m, 256, n, 256, seed=m + n)
+    assert np.array_equal(y, ref["y"]), f"rel-L2 {rel_l2(y, ref['y']):.3e}"
+    y, ref = forward_case(m, 256, n, 128, rank=32, seed=m + n + 1, scale=0.5)
+    assert rel_l2(y, ref["y"]) < REL_L2
+
+
 def test_gemm_int32_extreme_values():
     k = 4096
     a = np.full((32, k), -128, np.int8)
