@@ -65,21 +65,38 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
   tn = in / gm;
 }
 
-// LoRA term of one 32 x 32 output tile, accumulated onto the dequantized base
-// values: out[i = n][j = m] = base + sum_r R[n, r] * T[m, r] (bf16 MFMA, fp32
-// accumulate; lora_scale is already folded into T or R).  Rows beyond the matrix
-// are clamped (their results are never stored).
-__device__ __forceinline__ v16f lora_tile(const uint16_t *__restrict__ T, const uint16_t *__restrict__ R,
-                                          int64_t m, int64_t n, int rank, int lane, v16f acc) {
+// LoRA term of all of a wavefront's 32 x 32 output tiles at once:
+// o[i][j] += sum_r R[nrow[j], r] * T[mrow[i], r], one 16-wide rank step at a
+// time (bf16 MFMA 32x32x16, fp32 accumulate), with the next step's fragments
+// loaded while this step's MFMAs run, so the loads of all tiles overlap instead
+// of paying one memory round trip per tile.  Lane l holds row l % 32 of its
+// tile and rank entries 8 * (l / 32) .. + 7 of each step.
+template <int SM, int SN>
+__device__ __forceinline__ void lora_all(const uint16_t *__restrict__ T, const uint16_t *__restrict__ R,
+                                         const int64_t (&mrow)[SM], const int64_t (&nrow)[SN], int rank, int lane,
+                                         v16f (&o)[SM][SN]) {
   const int koff = 8 * (lane >> 5);
-  const uint16_t *tr = T + m * rank + koff;
-  const uint16_t *rr = R + n * rank + koff;
+  v8bf ta[SM], rb[SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i) ta[i] = *reinterpret_cast<const v8bf *>(T + mrow[i] * rank + koff);
+#pragma unroll
+  for (int j = 0; j < SN; ++j) rb[j] = *reinterpret_cast<const v8bf *>(R + nrow[j] * rank + koff);
   for (int k0 = 0; k0 < rank; k0 += 16) {
-    const v8bf a = *reinterpret_cast<const v8bf *>(rr + k0);
-    const v8bf b = *reinterpret_cast<const v8bf *>(tr + k0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    const int kn = k0 + 16 < rank ? k0 + 16 : k0;  // the last step reloads its own fragments
+    v8bf tn[SM], rn[SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) tn[i] = *reinterpret_cast<const v8bf *>(T + mrow[i] * rank + kn + koff);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) rn[j] = *reinterpret_cast<const v8bf *>(R + nrow[j] * rank + kn + koff);
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) o[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[j], ta[i], o[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) ta[i] = tn[i];
+#pragma unroll
+    for (int j = 0; j < SN; ++j) rb[j] = rn[j];
   }
-  return acc;
 }
 
 // s_waitcnt vmcnt(N) then s_barrier, as one compiler barrier.  The direct-to-LDS
@@ -258,6 +275,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         }
       }
     }
+  } else if constexpr (EPI == Epilogue::kForward && LORA) {
+    // dequantize every tile, add the LoRA term of all tiles together, then store
+    v16f o[SM][SN];
+    int64_t mrow[SM], nrow[SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
+      mrow[i] = m < M ? m : M - 1;
+      const float sx = args.row_scale[mrow[i]];
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        const int64_t nb = n0 + wn * TN + j * 32 + 4 * half;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int64_t n = nb + 8 * q4;
+          n = n < N ? n : N - 4;
+          const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
+          o[i][j][4 * q4 + 0] = (float)acc[i][j][4 * q4 + 0] * (sx * sw.x);
+          o[i][j][4 * q4 + 1] = (float)acc[i][j][4 * q4 + 1] * (sx * sw.y);
+          o[i][j][4 * q4 + 2] = (float)acc[i][j][4 * q4 + 2] * (sx * sw.z);
+          o[i][j][4 * q4 + 3] = (float)acc[i][j][4 * q4 + 3] * (sx * sw.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
+      nrow[j] = nr < N ? nr : N - 1;
+    }
+    lora_all<SM, SN>(args.lora_t, args.lora_r, mrow, nrow, args.rank, lane, o);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int64_t n = n0 + wn * TN + j * 32 + 4 * half + 8 * q4;
+          if (n < N) {
+            uint2 packed;
+            packed.x = pack_bf16x2(o[i][j][4 * q4 + 0], o[i][j][4 * q4 + 1]);
+            packed.y = pack_bf16x2(o[i][j][4 * q4 + 2], o[i][j][4 * q4 + 3]);
+            *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
+          }
+        }
+      }
+    }
   } else if constexpr (EPI == Epilogue::kForward) {
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
@@ -277,11 +342,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
           o[4 * q4 + 1] = (float)acc[i][j][4 * q4 + 1] * (sx * sw.y);
           o[4 * q4 + 2] = (float)acc[i][j][4 * q4 + 2] * (sx * sw.z);
           o[4 * q4 + 3] = (float)acc[i][j][4 * q4 + 3] * (sx * sw.w);
-        }
-        if constexpr (LORA) {
-          int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
-          nr = nr < N ? nr : N - 1;
-          o = lora_tile(args.lora_t, args.lora_r, mc, nr, args.rank, lane, o);
         }
         if (m < M) {
 #pragma unroll
@@ -389,16 +449,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
           for (int r = 0; r < 16; ++r) z[j][r] = z[j][r] * c;
       }
 
+      v16f ot[1][SN];
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ot[0][j][r] = z[j][r];
+      if constexpr (LORA) {
+        const int64_t mrow[1] = {mc};
+        int64_t nrow[SN];
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+          const int64_t nr = n0 + j * 32 + (lane & 31);
+          nrow[j] = nr < N ? nr : N - 1;
+        }
+        lora_all<1, SN>(args.lora_t, args.lora_r, mrow, nrow, args.rank, lane, ot);
+      }
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
-        v16f o;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] = z[j][r];
-        if constexpr (LORA) {
-          int64_t nr = n0 + j * 32 + (lane & 31);
-          nr = nr < N ? nr : N - 1;
-          o = lora_tile(args.lora_t, args.lora_r, mc, nr, args.rank, lane, o);
-        }
+        const v16f &o = ot[0][j];
         if (m < M) {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {

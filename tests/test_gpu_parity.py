@@ -298,6 +298,15 @@ def test_backward_with_lora_grads(g, rank):
     assert max(errs) < REL_L2
 
 
+@pytest.mark.parametrize("g,k", [(128, 384), (64, 320), (256, 512)])
+def test_backward_partial_column_tile(g, k):
+    """The last 256-column tile of dX is partly past K; the rotation blocks stay whole."""
+    inp, (dx, ga, gb), ref, _ = backward_case(260, 208, k, g, rank=16, seed=k + g, scale=0.25)
+    errs = (rel_l2(dx, ref["dx"]), rel_l2(ga, ref["grad_a"]), rel_l2(gb, ref["grad_b"]))
+    say(f"    dx {errs[0]:.3e}  grad_a {errs[1]:.3e}  grad_b {errs[2]:.3e}")
+    assert max(errs) < REL_L2
+
+
 def test_backward_ragged_tokens_and_tiles():
     inp, (dx, ga, gb), ref, _ = backward_case(33, 272, 512, 256, rank=32, seed=9)
     assert max(rel_l2(dx, ref["dx"]), rel_l2(ga, ref["grad_a"]), rel_l2(gb, ref["grad_b"])) < REL_L2
