@@ -10,8 +10,10 @@ resident in HBM before the timed region; the weights are rotated and quantized
 once, outside it (offline preparation).
 
 value = int8 ops of both GEMMs (2 M N K each) / wall time per step, in TOPS,
-with the activation rotate+quantize kernels inside the step.  Per-kernel times
-come from HIP events recorded on the launch stream around each kernel.
+with the activation rotate+quantize kernels inside the step (the timed region
+holds nothing else).  Per-kernel launch durations come afterwards from HIP
+events on the launch stream around K back-to-back launches of each kernel; the
+GEMM's feed the roofline object.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
 """
@@ -39,14 +41,37 @@ G = 256
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings of the other workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 256 MiB device-to-device copy first (scales the HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_mlp_4096tok_hbm_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc", "gemm_i8.hip")
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch (up, down) from the committed rocprofv3 counter
+    summary, or None when the GEMM source has changed since it was taken.  The
+    file holds `key: value` lines: source_sha256, up_bytes, down_bytes."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return [int(kv["up_bytes"]), int(kv["down_bytes"])]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def to_dev_bf16(torch, bits):
@@ -66,14 +91,18 @@ def cpu_baseline(inp, target_s: float) -> dict:
         oracle.qlinear_forward(inp["h"][:rows], qwd, swd, G, intermediates=False)
         return time.perf_counter() - t0
 
-    rows = 8
-    t = run(rows)
-    rows = int(min(M, max(8, rows * target_s / max(t, 1e-3))))
-    t = run(rows)
-    ops = 2.0 * rows * (N_UP * K_UP + N_DOWN * K_DOWN)
+    # size the sample from a small probe, then repeat it until about target_s has passed
+    probe = run(64)
+    rows = int(min(M, max(64, 64 * target_s / max(probe, 1e-3))))
+    t, reps = 0.0, 0
+    while reps == 0 or t < 0.6 * target_s:
+        t += run(rows)
+        reps += 1
+    rows_total = rows * reps
+    ops = 2.0 * rows_total * (N_UP * K_UP + N_DOWN * K_DOWN)
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {rows} of {M} token rows through both layers (rotate+quantize, exact int GEMM, "
-                      f"fp32 dequant, bf16 out); weights prepared outside; {t:.1f} s",
+            "sample": f"first {rows} of {M} token rows through both layers, {reps} time(s) (rotate+quantize, "
+                      f"exact int GEMM, fp32 dequant, bf16 out); weights prepared outside; {t:.1f} s",
             "seconds": round(t, 2)}
 
 
@@ -142,7 +171,7 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
@@ -177,18 +206,18 @@ def main():
 
     kernels = ["rotq_up", "gemm_up", "rotq_down", "gemm_down"]
 
-    def step(ev=None):
-        if ev: ev[0].record(stream)
-        check(L.sdnq_rotate_quantize_act(P(x), M, K_UP, G, None, P(qx), P(sx), sp), "rotq up")
-        if ev: ev[1].record(stream)
-        check(L.sdnq_qlinear_forward_quantized(P(qx), P(sx), M, K_UP, P(qw_up), P(sw_up), N_UP, None, None, 0,
-                                               0.0, P(y_up), None, 0, sp), "gemm up")
-        if ev: ev[2].record(stream)
-        check(L.sdnq_rotate_quantize_act(P(hh), M, K_DOWN, G, None, P(qh), P(shh), sp), "rotq down")
-        if ev: ev[3].record(stream)
-        check(L.sdnq_qlinear_forward_quantized(P(qh), P(shh), M, K_DOWN, P(qw_down), P(sw_down), N_DOWN, None, None,
-                                               0, 0.0, P(y_down), None, 0, sp), "gemm down")
-        if ev: ev[4].record(stream)
+    calls = [
+        lambda: check(L.sdnq_rotate_quantize_act(P(x), M, K_UP, G, None, P(qx), P(sx), sp), "rotq up"),
+        lambda: check(L.sdnq_qlinear_forward_quantized(P(qx), P(sx), M, K_UP, P(qw_up), P(sw_up), N_UP, None, None,
+                                                       0, 0.0, P(y_up), None, 0, sp), "gemm up"),
+        lambda: check(L.sdnq_rotate_quantize_act(P(hh), M, K_DOWN, G, None, P(qh), P(shh), sp), "rotq down"),
+        lambda: check(L.sdnq_qlinear_forward_quantized(P(qh), P(shh), M, K_DOWN, P(qw_down), P(sw_down), N_DOWN,
+                                                       None, None, 0, 0.0, P(y_down), None, 0, sp), "gemm down"),
+    ]
+
+    def step():
+        for c in calls:
+            c()
 
     if args.copy_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -201,16 +230,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: K whole steps, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)] for i in range(args.steps)])
-    avg_ms = per.mean(axis=0)
+    # per-kernel times inside steps: K more steps with HIP events on the launch
+    # stream between the kernels (the events add a small gap to each kernel)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    in_step_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                           for i in range(args.steps)]).mean(axis=0)
+
+    # per-kernel launch duration: HIP events on the launch stream around K
+    # back-to-back launches of each kernel (same inputs as in the step)
+    avg_ms = []
+    for c in calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c()
+        e0.record(stream)
+        for _ in range(args.steps):
+            c()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg_ms.append(e0.elapsed_time(e1) / args.steps)
+    avg_ms = np.array(avg_ms)
     ms_per_step = wall * 1e3 / args.steps
     ops_up = 2.0 * M * N_UP * K_UP
     ops_down = 2.0 * M * N_DOWN * K_DOWN
@@ -219,9 +271,10 @@ def main():
     gemm_s = (avg_ms[1] + avg_ms[3]) * 1e-3
     gemm_tops = (ops_up + ops_down) / gemm_s / 1e12
     rot_bytes = (M * K_UP * 3 + M * 4) + (M * K_DOWN * 3 + M * 4)  # bf16 in, int8 out, fp32 scale
-    rot_s = (avg_ms[0] + avg_ms[2]) * 1e-3
+    rot_s = (in_step_ms[0] + in_step_ms[2]) * 1e-3  # in-step: the activations come from HBM, not a warm cache
     rot_gbs = rot_bytes / rot_s / 1e9
 
+    traffic = measured_traffic()
     out = {
         "metric": "INT8 TOPS of fused Hadamard-quantized linear, % of MI355X INT8 MFMA peak",
         "value": round(tops, 2),
@@ -241,13 +294,18 @@ def main():
                                "activations, row-wise int8 weights, bf16 out",
                    "tokens": M, "hadamard_group": G},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": None if traffic is None else int(sum(traffic) / 2),
+                     "traffic_per_launch": traffic,
                      "kernel": "gemm_i8_kernel (forward epilogue)",
+                     "timing": "HIP events around K back-to-back launches of each GEMM",
                      "per_launch_ops": [ops_up, ops_down]},
         "rotate_quantize_roofline": {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": HBM_PEAK_GBS,
                                      "unit": "GB/s", "frac": round(rot_gbs / HBM_PEAK_GBS, 4),
-                                     "per_launch_bytes": [M * K_UP * 3 + M * 4, M * K_DOWN * 3 + M * 4]},
+                                     "per_launch_bytes": [M * K_UP * 3 + M * 4, M * K_DOWN * 3 + M * 4],
+                                     "timing": "HIP events between the kernels of whole steps"},
         "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
+        "kernel_in_step_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, in_step_ms)},
     }
     if not args.no_rows:
         out["rows"] = measure_rows(torch, h, synth)
