@@ -103,87 +103,126 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restri
 }
 
 // ----------------------------------------------------------- lora_grad --
-// Workgroup tile: 64 (a) x 64 (b) outputs, 4 wavefronts of 32 x 32 (2 x 2 MFMA
-// 16x16 tiles); tokens are consumed 32 at a time through LDS.  The contraction
-// runs over tokens, which are the slow index of both P and Q, so the MFMA
-// operands (8 consecutive tokens of one column per lane) are gathered from the
-// row-major LDS tiles with 16-bit reads.
+// Workgroup tile: 64 (a) x 64 (b) outputs, 4 wavefronts of 32 x 32 (one
+// v_mfma_f32_32x32x16_bf16 accumulator each), over one split of at most 1024
+// tokens, 64 tokens per step.  The contraction runs over tokens, the slow index
+// of both P and Q, so the tiles are staged row-major in LDS (direct-to-LDS
+// buffer loads, 3-stage ring) and the MFMA operands are read with
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the
+// address of 4 consecutive bf16 of token row (j / 4), column quad (j % 4), and
+// lane l receives column (l % 16) of those 4 token rows.  So lane l gets 4
+// consecutive tokens of one column, which is the operand layout (two reads give
+// the 8 tokens of a 16-token MFMA step).
+// LDS rows are 128 bytes (64 bf16); 16-byte chunk c of row t is stored at chunk
+// c ^ (t & 7) so the transposing reads spread over the banks.
 constexpr int kGradTile = 64;
-constexpr int kGradTokens = 32;
-constexpr int kGradPad = 68;  // LDS row stride in bf16: 136 B keeps 8-byte stores aligned and puts rows 8 apart 16 banks apart
+constexpr int kGradTokens = 64;
+constexpr int kGradStages = 3;
+constexpr int kGradStageBytes = 2 * kGradTokens * kGradTile * 2;  // P tile then Q tile
 constexpr int kMaxSplits = 16;
 constexpr int64_t kTokensPerSplit = 1024;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __global__ __launch_bounds__(256) void lora_grad_partial_kernel(const uint16_t *__restrict__ p, int64_t pa,
                                                                 const uint16_t *__restrict__ q, int64_t qb,
                                                                 int64_t m, int64_t tokens_per_split,
                                                                 float *__restrict__ partials) {
-  __shared__ uint16_t ps[kGradTokens][kGradPad];
-  __shared__ uint16_t qs[kGradTokens][kGradPad];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGradStages * kGradStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t a0 = (int64_t)blockIdx.x * kGradTile;
   const int64_t b0 = (int64_t)blockIdx.y * kGradTile;
   const int split = blockIdx.z;
   const int64_t tb = split * tokens_per_split;
   int64_t te = tb + tokens_per_split;
   te = te < m ? te : m;
+  te = te > tb ? te : tb;  // an empty split reads nothing (num_records 0) and writes zeros
+  const int nsteps = (int)((te - tb + kGradTokens - 1) / kGradTokens);
 
-  // loader: each thread moves 8 bf16 of one token row of each tile
-  const int lt = tid >> 3;        // token within the step, 0..31
-  const int lcol = 8 * (tid & 7); // column within the tile, 0..56
-
-  const int wa = wave & 1, wb = wave >> 1;
-  v4f acc[2][2];
+  // Loads: per step 16 KB = 16 blocks of 1 KB (8 token rows x 128 B); wavefront w
+  // issues blocks w, w + 4, w + 8, w + 12 (the first two of P, the last two of Q).
+  // Lane i of a block lands in LDS slot i: row 8 * blk + i / 8, stored chunk i % 8,
+  // which holds logical chunk (i % 8) ^ (row & 7).  Rows past the split and
+  // columns past the matrix read as zero.
+  const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p + tb * pa), 0, (int)((te - tb) * pa * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(q + tb * qb), 0, (int)((te - tb) * qb * 2), 0x00020000);
+  unsigned off[4];
+  bool ok[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v4f{};
-
-  for (int64_t t0 = tb; t0 < te; t0 += kGradTokens) {
-    const int64_t t = t0 + lt;
-    uint4 pv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
-    if (t < te) {
-      if (a0 + lcol < pa) pv = *reinterpret_cast<const uint4 *>(p + t * pa + a0 + lcol);
-      if (b0 + lcol < qb) qv = *reinterpret_cast<const uint4 *>(q + t * qb + b0 + lcol);
-    }
-    __syncthreads();
-    *reinterpret_cast<uint2 *>(&ps[lt][lcol]) = make_uint2(pv.x, pv.y);
-    *reinterpret_cast<uint2 *>(&ps[lt][lcol + 4]) = make_uint2(pv.z, pv.w);
-    *reinterpret_cast<uint2 *>(&qs[lt][lcol]) = make_uint2(qv.x, qv.y);
-    *reinterpret_cast<uint2 *>(&qs[lt][lcol + 4]) = make_uint2(qv.z, qv.w);
-    __syncthreads();
-    // operands: lane l -> column (l % 16) of its 16-wide tile, tokens 8*(l/16) + 0..7
-    const int tk = 8 * (lane >> 4);
-    v8bf fa[2], fb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ca = wa * 32 + i * 16 + (lane & 15);
-      const int cb = wb * 32 + i * 16 + (lane & 15);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        fa[i][e] = __builtin_bit_cast(__bf16, ps[tk + e][ca]);
-        fb[i][e] = __builtin_bit_cast(__bf16, qs[tk + e][cb]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  for (int u = 0; u < 4; ++u) {
+    const int blk = 4 * (u & 1) + wave;  // block within its operand, 0..7
+    const int row = 8 * blk + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const int64_t col = (u < 2 ? a0 : b0) + 8 * chunk;
+    const int64_t width = u < 2 ? pa : qb;
+    ok[u] = col < width;
+    off[u] = (unsigned)((row * width + col) * 2);
   }
-
-  // acc[i][j] element e: a = a0 + wa*32 + i*16 + 4*(lane/16) + e, b = b0 + wb*32 + j*16 + lane%16
-  float *dst = partials + (int64_t)split * pa * qb;
+  auto issue = [&](int step) {
+    uint8_t *base = smem + (step % kGradStages) * kGradStageBytes;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t b = b0 + wb * 32 + j * 16 + (lane & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t a = a0 + wa * 32 + i * 16 + 4 * (lane >> 4) + e;
-        if (a < pa && b < qb) dst[a * qb + b] = acc[i][j][e];
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int64_t width = u < 2 ? pa : qb;
+      const unsigned step_off = (unsigned)((int64_t)step * kGradTokens * width * 2);
+      const unsigned o = ok[u] ? off[u] + step_off : 0x80000000u;
+      uint8_t *dst = base + (u < 2 ? 0 : kGradStageBytes / 2) + (4 * (u & 1) + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(u < 2 ? rs_p : rs_q, (lds_void *)dst, 16, o, 0, 0, 0);
     }
+  };
+
+  // Transposing operand reads: wavefront (wa, wb) multiplies columns wa*32.. of P
+  // by columns wb*32.. of Q.  Lane l, group G = l / 16, j = l % 16: token row
+  // 8 * (G / 2) + 4 * h + j / 4 of the 16-token step, column quad j % 4 of
+  // the 16 columns 16 * (G % 2) of its 32.
+  const int wa = wave & 1, wb = wave >> 1;
+  const int G = lane >> 4, jl = lane & 15;
+  const int trow = 8 * (G >> 1) + (jl >> 2);
+  int cbyte[2];
+#pragma unroll
+  for (int o2 = 0; o2 < 2; ++o2) {
+    const int col = (o2 == 0 ? wa : wb) * 32 + 16 * (G & 1) + 4 * (jl & 3);
+    cbyte[o2] = col * 2;  // byte offset in the (unswizzled) 128-byte row
+  }
+  auto tr_read = [&](const uint8_t *tile, int row, int cb) {
+    const int addr = row * 128 + ((((cb >> 4) ^ (row & 7)) << 4) | (cb & 15));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(tile + addr));
+  };
+
+  v16f acc = v16f{};
+  issue(0);
+  issue(1);
+  for (int step = 0; step < nsteps; ++step) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");  // this step's 4 loads are done
+    __builtin_amdgcn_sched_barrier(0);
+    issue(step + 2);
+    const uint8_t *tp = smem + (step % kGradStages) * kGradStageBytes;
+    const uint8_t *tq = tp + kGradStageBytes / 2;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r0 = 16 * kk + trow;
+      const v4s a_lo = tr_read(tp, r0, cbyte[0]), a_hi = tr_read(tp, r0 + 4, cbyte[0]);
+      const v4s b_lo = tr_read(tq, r0, cbyte[1]), b_hi = tr_read(tq, r0 + 4, cbyte[1]);
+      const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the zero-fill loads past the last step
+
+  // acc element r: a = wa*32 + 8*(r/4) + 4*(l/32) + r%4, b = wb*32 + l%32
+  float *dst = partials + (int64_t)split * pa * qb;
+  const int64_t b = b0 + wb * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t a = a0 + wa * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (a < pa && b < qb) dst[a * qb + b] = acc[r];
+  }
 }
 
 __global__ void lora_grad_reduce_kernel(const float *__restrict__ partials, int splits, int64_t count, float scale,
