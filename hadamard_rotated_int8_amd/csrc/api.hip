@@ -257,13 +257,13 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
 
   if (r > 0) {
     float *part = reinterpret_cast<float *>(ws_at(workspace, L.part));
-    if (want_ga) SDNQ_LAUNCH(launch_lora_grad(x, k, gr, r, m, 1.0f, part, grad_a, s));  // x^T g_r
+    if (want_ga) SDNQ_LAUNCH(launch_lora_grad(x, k, gr, r, m, 1.0f, false, part, grad_a, s));  // x^T g_r
     if (want_gb) {
       tx = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tx));
       at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
       SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));
       SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, 1.0f, tx, s));                  // t = x A
-      SDNQ_LAUNCH(launch_lora_grad(tx, r, dy, n, m, lora_scale, part, grad_b, s));  // scale * t^T dY
+      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, r, m, lora_scale, true, part, grad_b, s));  // scale * (dY^T t)^T
     }
   }
   return SDNQ_OK;

@@ -103,24 +103,32 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restri
 }
 
 // ----------------------------------------------------------- lora_grad --
-// Workgroup tile: 64 (a) x 64 (b) outputs, 4 wavefronts of 32 x 32 (one
-// v_mfma_f32_32x32x16_bf16 accumulator each), over one split of at most 1024
-// tokens, 64 tokens per step.  The contraction runs over tokens, the slow index
-// of both P and Q, so the tiles are staged row-major in LDS (direct-to-LDS
-// buffer loads, 3-stage ring) and the MFMA operands are read with
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the
-// address of 4 consecutive bf16 of token row (j / 4), column quad (j % 4), and
-// lane l receives column (l % 16) of those 4 token rows.  So lane l gets 4
-// consecutive tokens of one column, which is the operand layout (two reads give
-// the 8 tokens of a 16-token MFMA step).
-// LDS rows are 128 bytes (64 bf16); 16-byte chunk c of row t is stored at chunk
-// c ^ (t & 7) so the transposing reads spread over the banks.
-constexpr int kGradTile = 64;
+// partial[split][a][b] = sum over the split's tokens t of P[t, a] * Q[t, b], with
+// P the wide operand (x or dY: a over 3072-ish features) and Q the narrow one
+// (g_r or t: b over the rank).  Workgroup tile: 128 (a) x 64 (b), 4 wavefronts
+// of 32 (a) x 64 (b) (two v_mfma_f32_32x32x16_bf16 accumulators each), over one
+// split of at most 1024 tokens, 64 tokens per step.
+// The contraction runs over tokens, the slow index of both P and Q, so the
+// tiles are staged row-major in LDS (direct-to-LDS buffer loads, a 3-stage
+// ring) and the MFMA operands are read with ds_read_b64_tr_b16: within each group of
+// 16 lanes, lane j supplies the address of 4 consecutive bf16 of token row
+// (j / 4), column quad (j % 4), and lane l receives column (l % 16) of those 4
+// token rows.  So lane l gets 4 consecutive tokens of one column, which is the
+// operand layout (two reads give the 8 tokens of a 16-token MFMA step).
+// LDS sub-tiles are 64 token rows x 64 columns (128-byte rows); 16-byte chunk c
+// of row t is stored at chunk c ^ (t & 7) so the transposing reads spread over
+// the banks.  The P tile is two such sub-tiles side by side (256 contiguous
+// bytes of each token row), the Q tile one.
+constexpr int kGradA = 128;  // P columns per workgroup
+constexpr int kGradB = 64;   // Q columns per workgroup
 constexpr int kGradTokens = 64;
 constexpr int kGradStages = 3;
-constexpr int kGradStageBytes = 2 * kGradTokens * kGradTile * 2;  // P tile then Q tile
+constexpr int kGradSub = kGradTokens * 64 * 2;               // one 64 x 64 bf16 sub-tile, 8 KB
+constexpr int kGradStageBytes = (kGradA / 64 + 1) * kGradSub;  // P sub-tiles then the Q sub-tile
+constexpr int kGradBlocks = kGradStageBytes / 1024;          // 1 KB direct loads per stage
 constexpr int kMaxSplits = 16;
 constexpr int64_t kTokensPerSplit = 1024;
+static_assert(kGradBlocks % 4 == 0, "every wavefront issues the same number of loads");
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -130,11 +138,13 @@ __global__ __launch_bounds__(256) void lora_grad_partial_kernel(const uint16_t *
                                                                 const uint16_t *__restrict__ q, int64_t qb,
                                                                 int64_t m, int64_t tokens_per_split,
                                                                 float *__restrict__ partials) {
+  constexpr int LPW = kGradBlocks / 4;  // loads per wavefront per step
+  constexpr int PSUB = kGradA / 64;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGradStages * kGradStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t a0 = (int64_t)blockIdx.x * kGradTile;
-  const int64_t b0 = (int64_t)blockIdx.y * kGradTile;
+  const int64_t a0 = (int64_t)blockIdx.x * kGradA;
+  const int64_t b0 = (int64_t)blockIdx.y * kGradB;
   const int split = blockIdx.z;
   const int64_t tb = split * tokens_per_split;
   int64_t te = tb + tokens_per_split;
@@ -142,97 +152,109 @@ __global__ __launch_bounds__(256) void lora_grad_partial_kernel(const uint16_t *
   te = te > tb ? te : tb;  // an empty split reads nothing (num_records 0) and writes zeros
   const int nsteps = (int)((te - tb + kGradTokens - 1) / kGradTokens);
 
-  // Loads: per step 16 KB = 16 blocks of 1 KB (8 token rows x 128 B); wavefront w
-  // issues blocks w, w + 4, w + 8, w + 12 (the first two of P, the last two of Q).
-  // Lane i of a block lands in LDS slot i: row 8 * blk + i / 8, stored chunk i % 8,
-  // which holds logical chunk (i % 8) ^ (row & 7).  Rows past the split and
-  // columns past the matrix read as zero.
+  // Loads: block B of a stage (1 KB = 8 token rows x 128 B of one sub-tile) is
+  // issued by wavefront B % 4.  Blocks 0 .. 8*PSUB-1 are P (sub-tile B / 8), the
+  // rest Q.  Lane i of a block lands in LDS slot i: row 8 * (B % 8) + i / 8,
+  // stored chunk i % 8, which holds logical chunk (i % 8) ^ (row & 7).  Rows past
+  // the split and columns past the matrix read as zero.
   const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(p + tb * pa), 0, (int)((te - tb) * pa * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(q + tb * qb), 0, (int)((te - tb) * qb * 2), 0x00020000);
-  unsigned off[4];
-  bool ok[4];
+  unsigned off[LPW];
+  bool ok[LPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int blk = 4 * (u & 1) + wave;  // block within its operand, 0..7
-    const int row = 8 * blk + (lane >> 3);
+  for (int u = 0; u < LPW; ++u) {
+    const int blk = 4 * u + wave;
+    const bool isp = blk < 8 * PSUB;
+    const int row = 8 * (blk % 8) + (lane >> 3);
     const int chunk = (lane & 7) ^ (row & 7);
-    const int64_t col = (u < 2 ? a0 : b0) + 8 * chunk;
-    const int64_t width = u < 2 ? pa : qb;
+    const int64_t col = isp ? a0 + 64 * (blk / 8) + 8 * chunk : b0 + 8 * chunk;
+    const int64_t width = isp ? pa : qb;
     ok[u] = col < width;
     off[u] = (unsigned)((row * width + col) * 2);
   }
   auto issue = [&](int step) {
     uint8_t *base = smem + (step % kGradStages) * kGradStageBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t width = u < 2 ? pa : qb;
+    for (int u = 0; u < LPW; ++u) {
+      const int blk = 4 * u + wave;
+      const bool isp = blk < 8 * PSUB;
+      const int64_t width = isp ? pa : qb;
       const unsigned step_off = (unsigned)((int64_t)step * kGradTokens * width * 2);
       const unsigned o = ok[u] ? off[u] + step_off : 0x80000000u;
-      uint8_t *dst = base + (u < 2 ? 0 : kGradStageBytes / 2) + (4 * (u & 1) + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(u < 2 ? rs_p : rs_q, (lds_void *)dst, 16, o, 0, 0, 0);
+      uint8_t *dst = base + blk * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isp ? rs_p : rs_q, (lds_void *)dst, 16, o, 0, 0, 0);
     }
   };
 
-  // Transposing operand reads: wavefront (wa, wb) multiplies columns wa*32.. of P
-  // by columns wb*32.. of Q.  Lane l, group G = l / 16, j = l % 16: token row
-  // 8 * (G / 2) + 4 * h + j / 4 of the 16-token step, column quad j % 4 of
-  // the 16 columns 16 * (G % 2) of its 32.
-  const int wa = wave & 1, wb = wave >> 1;
+  // Transposing operand reads.  Wavefront w multiplies P columns 32 w .. 32 w + 31
+  // (sub-tile w / 2) by all 64 Q columns.  Lane l, group G = l / 16, j = l % 16:
+  // token row 8 * (G / 2) + 4 * h + j / 4 of the 16-token step, column quad
+  // j % 4 of the 16 columns 16 * (G % 2) of a 32-column block.
   const int G = lane >> 4, jl = lane & 15;
   const int trow = 8 * (G >> 1) + (jl >> 2);
-  int cbyte[2];
-#pragma unroll
-  for (int o2 = 0; o2 < 2; ++o2) {
-    const int col = (o2 == 0 ? wa : wb) * 32 + 16 * (G & 1) + 4 * (jl & 3);
-    cbyte[o2] = col * 2;  // byte offset in the (unswizzled) 128-byte row
-  }
+  const int qcol = 16 * (G & 1) + 4 * (jl & 3);
+  const int pbyte = 2 * (32 * (wave & 1) + qcol);  // in the wavefront's P sub-tile
+  const int psub = (wave >> 1) * kGradSub;
   auto tr_read = [&](const uint8_t *tile, int row, int cb) {
     const int addr = row * 128 + ((((cb >> 4) ^ (row & 7)) << 4) | (cb & 15));
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(tile + addr));
   };
+  auto cat = [](v4s lo, v4s hi) {
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
-  v16f acc = v16f{};
-  issue(0);
-  issue(1);
+  v16f acc[2] = {v16f{}, v16f{}};
+#pragma unroll
+  for (int t = 0; t < kGradStages - 1; ++t) issue(t);
   for (int step = 0; step < nsteps; ++step) {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");  // this step's 4 loads are done
+    // the loads of the kGradStages - 2 later steps may still be in flight
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kGradStages - 2) * LPW) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue(step + 2);
-    const uint8_t *tp = smem + (step % kGradStages) * kGradStageBytes;
-    const uint8_t *tq = tp + kGradStageBytes / 2;
+    issue(step + kGradStages - 1);
+    const uint8_t *tile = smem + (step % kGradStages) * kGradStageBytes;
+    const uint8_t *tp = tile + psub;
+    const uint8_t *tq = tile + PSUB * kGradSub;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < kGradTokens / 16; ++kk) {
       const int r0 = 16 * kk + trow;
-      const v4s a_lo = tr_read(tp, r0, cbyte[0]), a_hi = tr_read(tp, r0 + 4, cbyte[0]);
-      const v4s b_lo = tr_read(tq, r0, cbyte[1]), b_hi = tr_read(tq, r0 + 4, cbyte[1]);
-      const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      const v8bf av = cat(tr_read(tp, r0, pbyte), tr_read(tp, r0 + 4, pbyte));
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int qb2 = 2 * (32 * jb + qcol);
+        const v8bf bv = cat(tr_read(tq, r0, qb2), tr_read(tq, r0 + 4, qb2));
+        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[jb], 0, 0, 0);
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the zero-fill loads past the last step
 
-  // acc element r: a = wa*32 + 8*(r/4) + 4*(l/32) + r%4, b = wb*32 + l%32
+  // acc[jb] element r: a = 32 w + 8*(r/4) + 4*(l/32) + r%4, b = 32 jb + l%32
   float *dst = partials + (int64_t)split * pa * qb;
-  const int64_t b = b0 + wb * 32 + (lane & 31);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t a = a0 + wa * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (a < pa && b < qb) dst[a * qb + b] = acc[r];
+  for (int jb = 0; jb < 2; ++jb) {
+    const int64_t b = b0 + 32 * jb + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t a = a0 + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (a < pa && b < qb) dst[a * qb + b] = acc[jb][r];
+    }
   }
 }
 
-__global__ void lora_grad_reduce_kernel(const float *__restrict__ partials, int splits, int64_t count, float scale,
-                                        uint16_t *__restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// out = bf16(scale * sum over splits of partial), in split order; the partials
+// are [pa][qb]; out is [pa][qb], or [qb][pa] when transposed.
+__global__ void lora_grad_reduce_kernel(const float *__restrict__ partials, int splits, int64_t pa, int64_t qb,
+                                        float scale, int transposed, uint16_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // index into the partials
+  const int64_t count = pa * qb;
   if (i >= count) return;
   float s = partials[i];
   for (int k = 1; k < splits; ++k) s += partials[(int64_t)k * count + i];
   const __bf16 b = (__bf16)(scale * s);
-  out[i] = __builtin_bit_cast(uint16_t, b);
+  out[transposed ? (i % qb) * pa + i / qb : i] = __builtin_bit_cast(uint16_t, b);
 }
 
 __global__ void fill_zero_u16_kernel(uint16_t *__restrict__ out, int64_t count) {
@@ -361,18 +383,17 @@ int lora_grad_splits(int64_t m) {
 }
 
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m, float scale,
-                            float *partials, uint16_t *out, hipStream_t stream) {
+                            bool transposed, float *partials, uint16_t *out, hipStream_t stream) {
   const int splits = lora_grad_splits(m);
   int64_t per = (m + splits - 1) / splits;
   per = (per + kGradTokens - 1) / kGradTokens * kGradTokens;
-  const dim3 grid((unsigned)((pa + kGradTile - 1) / kGradTile), (unsigned)((qb + kGradTile - 1) / kGradTile),
-                  (unsigned)splits);
+  const dim3 grid((unsigned)((pa + kGradA - 1) / kGradA), (unsigned)((qb + kGradB - 1) / kGradB), (unsigned)splits);
   hipLaunchKernelGGL(lora_grad_partial_kernel, grid, dim3(256), 0, stream, p, pa, q, qb, m, per, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t count = pa * qb;
   hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
-                     partials, splits, count, scale, out);
+                     partials, splits, pa, qb, scale, transposed ? 1 : 0, out);
   return hipGetLastError();
 }
 

@@ -77,9 +77,10 @@ hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const ui
                             int rank, float scale, uint16_t *out, hipStream_t stream);
 
 // Token reduction: part[s, a, b] = sum over the tokens of split s of p[t, a] * q[t, b]
-// (p [m, pa], q [m, qb] bf16), then out[a, b] = bf16(scale * sum_s part[s, a, b]).
+// (p [m, pa] the wide operand, q [m, qb] the narrow one, qb <= 128; bf16), then
+// out[a, b] (or out[b, a] when transposed) = bf16(scale * sum_s part[s, a, b]).
 int lora_grad_splits(int64_t m);
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
-                            float scale, float *partials, uint16_t *out, hipStream_t stream);
+                            float scale, bool transposed, float *partials, uint16_t *out, hipStream_t stream);
 
 }  // namespace sdnq
