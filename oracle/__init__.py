@@ -73,8 +73,15 @@ def _load():
                                            p, p, p, p, p]
     lib.oracle_qlinear_backward_input.argtypes = [p, i64, i64, p, p, i64, i32, p, p, p, i32,
                                                   ctypes.c_double, p, p, p, p, p, p, p]
+    lib.oracle_e4m3_encode.argtypes = [p, i64, p]
+    lib.oracle_e4m3_decode.argtypes = [p, i64, p]
+    lib.oracle_rotate_quantize_fp8.argtypes = [p, i64, i64, i32, p, p, p]
+    lib.oracle_gemm_fp8.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_qlinear_forward_fp8.argtypes = [p, i64, i64, p, p, i64, i32, p, p, i32, ctypes.c_double,
+                                               p, p, p, p, p]
     for name in ("oracle_fwht_unnormalized", "oracle_rotate", "oracle_rotate_quantize",
-                 "oracle_gemm_i8", "oracle_qlinear_forward", "oracle_qlinear_backward_input"):
+                 "oracle_gemm_i8", "oracle_qlinear_forward", "oracle_qlinear_backward_input",
+                 "oracle_rotate_quantize_fp8", "oracle_gemm_fp8", "oracle_qlinear_forward_fp8"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -228,3 +235,74 @@ def qlinear_backward_input(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: in
         _ptr(out.get("qdy")), _ptr(out.get("sdy")), _ptr(out.get("acc")), _ptr(out.get("dxbase")))
     _check(rc, "qlinear_backward_input")
     return out
+
+
+# ------------------------------------------------------------- FP8 (E4M3) --
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 codes (uint8) of binary32 values with |v| <= 448, round half to even."""
+    a = _c(v, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _load().oracle_e4m3_encode(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    """Values (fp64) of E4M3 codes (NaN codes excluded)."""
+    a = _c(c, np.uint8)
+    out = np.empty(a.shape, np.float64)
+    _load().oracle_e4m3_decode(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def rotate_quantize_fp8(x_bf16: np.ndarray, g: int, col_scale: np.ndarray | None = None):
+    """Rotate then quantize each row to E4M3: returns (codes uint8 [rows, cols], scales f32 [rows])."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    cs = None if col_scale is None else _c(col_scale, np.float32)
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows,), np.float32)
+    _check(_load().oracle_rotate_quantize_fp8(_ptr(x), rows, cols, g, _ptr(cs), _ptr(q), _ptr(s)),
+           "rotate_quantize_fp8")
+    return q, s
+
+
+def gemm_fp8(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Exact E4M3 matmul C = dec(A) dec(B)^T in fp64 (a [m, k], b [n, k] uint8 codes)."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("contraction lengths differ")
+    c = np.empty((m, n), np.float64)
+    _check(_load().oracle_gemm_fp8(_ptr(a), _ptr(b), m, n, k, _ptr(c)), "gemm_fp8")
+    return c
+
+
+def qlinear_forward_fp8(x: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
+                        lora_a: np.ndarray | None = None, lora_b: np.ndarray | None = None,
+                        lora_scale: float = 0.0, intermediates: bool = True) -> dict:
+    """FP8 forward of the layer for every row of x.  Returns y (bf16 bits) and, with
+    ``intermediates``, qx (E4M3 codes), sx, acc (exact fp64) and base (fp32)."""
+    x = _c(x, np.uint16)
+    qw = _c(qw, np.uint8)
+    sw = _c(sw, np.float32)
+    m, k = x.shape
+    n = qw.shape[0]
+    if qw.shape[1] != k or sw.shape != (n,):
+        raise ValueError("shape mismatch")
+    la = None if lora_a is None else _c(lora_a, np.uint16)
+    lb = None if lora_b is None else _c(lora_b, np.uint16)
+    rank = 0 if la is None else la.shape[1]
+    out = {"y": np.empty((m, n), np.uint16)}
+    if intermediates:
+        out.update(qx=np.empty((m, k), np.uint8), sx=np.empty((m,), np.float32),
+                   acc=np.empty((m, n), np.float64), base=np.empty((m, n), np.float32))
+    rc = _load().oracle_qlinear_forward_fp8(
+        _ptr(x), m, k, _ptr(qw), _ptr(sw), n, g, _ptr(la), _ptr(lb), rank, float(lora_scale),
+        _ptr(out["y"]), _ptr(out.get("qx")), _ptr(out.get("sx")), _ptr(out.get("acc")),
+        _ptr(out.get("base")))
+    _check(rc, "qlinear_forward_fp8")
+    return out
+

@@ -39,6 +39,14 @@
  *  - the LoRA side path sees the unrotated x; A is [K,r], B is [r,N]; its terms are
  *    computed in fp64 from the bf16 values with no intermediate rounding.
  *
+ * FP8 variant (the float8_e4m3fn quantized matmul that the SDNQ README lists next
+ * to INT8): the same rotation and absmax, with s = fl32(a/448), r = fl32(448/a),
+ * v = fl32(y*r) clamped to [-448, 448] and each v encoded in OCP FP8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinities, 0x7F/0xFF = NaN, largest finite 448) with round half to even.  The
+ * product of two E4M3 values has at most 8 significant bits between 2^-18 and
+ * 2^17.6, so the fp64 sum over K <= 65536 of them is exact.
+ *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -fPIC -shared.
  * x86-64 floats use SSE: every float operation below is one IEEE binary32
  * operation rounded to nearest even.  OpenMP only splits independent rows or
@@ -164,6 +172,59 @@ static void quantize_row(const float *y, int64_t cols, int8_t *q, float *s)
         if (t < -127.0f)
             t = -127.0f;
         q[i] = (int8_t)t;
+    }
+}
+
+/* ---------------------------------------------------------- fp8 e4m3 -- */
+
+/* Value of an E4M3 code: exponent field 0 holds subnormals m/8 * 2^-6, fields
+ * 1..15 hold (1 + m/8) * 2^(e-7).  0x7F and 0xFF (NaN) are never produced here. */
+static double e4m3_decode(uint8_t c)
+{
+    int e = (c >> 3) & 15, mant = c & 7;
+    double v = e == 0 ? ldexp(mant / 8.0, -6) : ldexp(1.0 + mant / 8.0, e - 7);
+    return (c & 0x80) ? -v : v;
+}
+
+/* E4M3 code of a finite binary32 v with |v| <= 448, rounded to nearest, ties to
+ * even.  Scaling by a power of two is exact in double, so the only rounding is
+ * the nearbyint of the mantissa (default rounding mode: half to even). */
+static uint8_t e4m3_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a < 0x1p-6) {                      /* subnormal binade, steps of 2^-9 */
+        double r = nearbyint(ldexp(a, 9)); /* 0 .. 8; 8 is the smallest normal 0x08 */
+        return (uint8_t)(sign | (uint8_t)r);
+    }
+    int ex;
+    frexp(a, &ex);                         /* a in [2^(ex-1), 2^ex) */
+    int eu = ex - 1;                       /* unbiased exponent */
+    double r = nearbyint(ldexp(a, 3 - eu)); /* 8 .. 16 mantissa units */
+    if (r >= 16.0) {
+        r = 8.0;
+        eu += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)((eu + 7) << 3) | (uint8_t)(r - 8.0));
+}
+
+/* The FP8 counterpart of quantize_row: s = fl32(a/448), codes e4m3(clamp(fl32(y*r))). */
+static void quantize_row_fp8(const float *y, int64_t cols, uint8_t *q, float *s)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < cols; i++)
+        a = fmaxf(a, fabsf(y[i]));
+    *s = a / 448.0f;
+    float up = (a < 0x1p-100f) ? 0x1p100f : 1.0f;
+    float as = a * up;
+    float r = (as > 0.0f) ? 448.0f / as : 0.0f;
+    for (int64_t i = 0; i < cols; i++) {
+        float t = (y[i] * up) * r;
+        if (t > 448.0f)
+            t = 448.0f;
+        if (t < -448.0f)
+            t = -448.0f;
+        q[i] = e4m3_encode(t);
     }
 }
 
@@ -529,4 +590,134 @@ int oracle_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n,
     if (alloc_fail)
         return ORACLE_ERR_ARG;
     return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
+/* ------------------------------------------------------- fp8 exports -- */
+
+void oracle_e4m3_encode(const float *v, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = e4m3_encode(v[i]);
+}
+
+void oracle_e4m3_decode(const uint8_t *c, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = e4m3_decode(c[i]);
+}
+
+/* Rotate, then quantize each row to E4M3 codes: q[rows, cols] and s[rows]. */
+int oracle_rotate_quantize_fp8(const uint16_t *x, int64_t rows, int64_t cols, int g,
+                               const float *col_scale, uint8_t *q, float *s)
+{
+    if (!x || !q || !s || rows < 0 || cols < 0 || !is_pow2_upto256(g) || cols % g != 0)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel
+    {
+        float *y = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+        if (!y) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ARG;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < rows; m++) {
+                rotate_row(x + m * cols, cols, g, col_scale, y);
+                quantize_row_fp8(y, cols, q + m * cols, s + m);
+            }
+            free(y);
+        }
+    }
+    return err;
+}
+
+/* E4M3 matmul, exact: c[i,j] = sum_t dec(a[i,t]) * dec(b[j,t]) in fp64 (a[m,k], b[n,k]). */
+int oracle_gemm_fp8(const uint8_t *a, const uint8_t *b, int64_t m, int64_t n, int64_t k, double *c)
+{
+    if (!a || !b || !c || m < 0 || n < 0 || k < 0 || k > 65536)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t j = 0; j < n; j++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < k; t++)
+                acc += e4m3_decode(a[i * k + t]) * e4m3_decode(b[j * k + t]);
+            c[i * n + j] = acc;
+        }
+    return ORACLE_OK;
+}
+
+/* FP8 forward, the same steps as oracle_qlinear_forward with the E4M3 quantizer:
+ *   q_x, s_x   = rotate + per-token E4M3 quantization (x row, block g)
+ *   acc[m,n]   = sum_k dec(q_x[m,k]) * dec(qw[n,k])          (exact, fp64)
+ *   base[m,n]  = fl32(fl32(acc) * fl32(s_x[m] * s_w[n]))
+ *   y[m,n]     = bf16_rne(base + lora_scale * ((x A) B)[m,n])  (LoRA in fp64)
+ * Every *_out pointer may be NULL. */
+int oracle_qlinear_forward_fp8(const uint16_t *x, int64_t m, int64_t k,
+                               const uint8_t *qw, const float *sw, int64_t n, int g,
+                               const uint16_t *lora_a, const uint16_t *lora_b, int rank, double lora_scale,
+                               uint16_t *y, uint8_t *qx_out, float *sx_out, double *acc_out, float *base_out)
+{
+    if (!x || !qw || !sw || !y || m < 0 || k <= 0 || k > 65536 || n < 0 || !is_pow2_upto256(g) || k % g != 0)
+        return ORACLE_ERR_ARG;
+    int use_lora = lora_a && lora_b && rank > 0;
+    int alloc_fail = 0;
+#pragma omp parallel
+    {
+        float *yr = (float *)malloc(sizeof(float) * (size_t)k);
+        uint8_t *qr = (uint8_t *)malloc((size_t)k);
+        double *dq = (double *)malloc(sizeof(double) * (size_t)k);
+        double *t = (double *)malloc(sizeof(double) * (size_t)(rank > 0 ? rank : 1));
+        if (!yr || !qr || !dq || !t) {
+#pragma omp atomic write
+            alloc_fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < m; i++) {
+                const uint16_t *xr = x + i * k;
+                float sx;
+                rotate_row(xr, k, g, NULL, yr);
+                quantize_row_fp8(yr, k, qr, &sx);
+                for (int64_t kk = 0; kk < k; kk++)
+                    dq[kk] = e4m3_decode(qr[kk]);
+                if (qx_out)
+                    memcpy(qx_out + i * k, qr, (size_t)k);
+                if (sx_out)
+                    sx_out[i] = sx;
+                if (use_lora) {
+                    for (int j = 0; j < rank; j++)
+                        t[j] = 0.0;
+                    for (int64_t kk = 0; kk < k; kk++) {
+                        double xv = (double)bf16_decode(xr[kk]);
+                        for (int j = 0; j < rank; j++)
+                            t[j] += xv * (double)bf16_decode(lora_a[kk * rank + j]);
+                    }
+                }
+                for (int64_t j = 0; j < n; j++) {
+                    const uint8_t *wr = qw + j * k;
+                    double acc = 0.0;
+                    for (int64_t kk = 0; kk < k; kk++)
+                        acc += dq[kk] * e4m3_decode(wr[kk]);
+                    float base = (float)acc * (sx * sw[j]);
+                    if (acc_out)
+                        acc_out[i * n + j] = acc;
+                    if (base_out)
+                        base_out[i * n + j] = base;
+                    double out = (double)base;
+                    if (use_lora) {
+                        double l = 0.0;
+                        for (int r = 0; r < rank; r++)
+                            l += t[r] * (double)bf16_decode(lora_b[(int64_t)r * n + j]);
+                        out += l * lora_scale;
+                    }
+                    y[i * n + j] = bf16_encode_f64(out);
+                }
+            }
+        }
+        free(yr);
+        free(qr);
+        free(dq);
+        free(t);
+    }
+    return alloc_fail ? ORACLE_ERR_ARG : ORACLE_OK;
 }

@@ -37,6 +37,13 @@ MUTANTS = {
     "bf16_truncation": ("double rq = nearbyint(q);", "double rq = floor(q);"),
     "weight_scale_index": ("float base = (float)(int32_t)acc * (sx * sw[j]);",
                            "float base = (float)(int32_t)acc * (sx * sw[i % n]);"),
+    "e4m3_truncation": ("double r = nearbyint(ldexp(a, 3 - eu));", "double r = floor(ldexp(a, 3 - eu));"),
+    "e4m3_subnormal_step": ("double r = nearbyint(ldexp(a, 9));", "double r = nearbyint(ldexp(a, 10));"),
+    "e4m3_exponent_bias": ("(uint8_t)((eu + 7) << 3)", "(uint8_t)((eu + 8) << 3)"),
+    "fp8_scale_over_240": ("*s = a / 448.0f;", "*s = a / 240.0f;"),
+    "fp8_no_tiny_row_rescale": ("float up = (a < 0x1p-100f) ? 0x1p100f : 1.0f;\n    float as = a * up;\n    float r = (as > 0.0f) ? 448.0f / as : 0.0f;",
+                                "float up = 1.0f;\n    float as = a * up;\n    float r = (as > 0.0f) ? 448.0f / as : 0.0f;"),
+    "fp8_weight_index": ("acc += dq[kk] * e4m3_decode(wr[kk]);", "acc += dq[kk] * e4m3_decode(wr[(kk + 1) % k]);"),
 }
 
 

@@ -454,3 +454,123 @@ def test_argument_errors():
         oracle.rotate_quantize(np.zeros((2, 100), np.uint16), 64)    # cols % g != 0
     with pytest.raises(ValueError):
         oracle.rotate_quantize(np.zeros((2, 96), np.uint16), 96)     # g not a power of two
+
+
+# ------------------------------------------------------------ FP8 (E4M3) --
+# The FP8 variant of the quantized matmul (float8_e4m3fn, listed next to INT8 in
+# the SDNQ README's feature list and SDNQConfig example): the same rotation and
+# absmax with a /448 scale and OCP E4M3 codes, round half to even.
+
+def torch_e4m3(v) -> np.ndarray:
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def torch_e4m3_value(c) -> np.ndarray:
+    return torch.from_numpy(np.asarray(c, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+FINITE_CODES = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+
+
+def test_e4m3_decode_matches_torch_and_closed_form():
+    got = oracle.e4m3_decode(FINITE_CODES)
+    assert np.array_equal(got, torch_e4m3_value(FINITE_CODES))
+    d = dict(zip(FINITE_CODES.tolist(), got.tolist()))
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0       # largest finite
+    assert d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9  # smallest normal, smallest subnormal
+    assert d[0x38] == 1.0 and d[0x00] == 0.0
+
+
+def test_e4m3_encode_matches_torch_on_codes_midpoints_and_neighbours():
+    vals = np.sort(np.unique(np.abs(oracle.e4m3_decode(FINITE_CODES))))
+    mids = (vals[:-1] + vals[1:]) / 2                        # exact in binary32
+    pts = np.concatenate([vals, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                          np.nextafter(mids.astype(np.float32), np.float32(1e9))]).astype(np.float32)
+    pts = pts[np.abs(pts) <= 448]
+    pts = np.concatenate([pts, -pts])
+    rng = np.random.default_rng(8)
+    rnd = (rng.uniform(-1, 1, 20000) * np.exp2(rng.integers(-14, 9, 20000))).astype(np.float32)
+    rnd = rnd[np.abs(rnd) <= 448]
+    for v in (pts, rnd):
+        assert np.array_equal(oracle.e4m3_encode(v), torch_e4m3(v))
+
+
+def test_e4m3_ties_go_to_even_codes():
+    # 1 + 1/16 lies halfway between 1 (0x38, even) and 1.125 (0x39); 3 * 2^-10
+    # halfway between 2^-9 (0x01) and 2^-8 (0x02); 248 between 240 (0x77) and 256 (0x78).
+    assert oracle.e4m3_encode(np.array([1.0625, 3 * 2.0 ** -10, 248.0], np.float32)).tolist() == [0x38, 0x02, 0x78]
+
+
+@pytest.mark.parametrize("g", [1, 64, 256])
+def test_fp8_quantization_matches_a_library_encoder_of_the_rotated_row(g):
+    """Codes = torch's e4m3 encoding of fl32(y * fl32(448 / a)), y the oracle's
+    (separately pinned) rotation; scales = fl32(a / 448)."""
+    rng = np.random.default_rng(g)
+    x = bf(rng.standard_normal((7, 512)) * np.exp2(rng.integers(-8, 8, (7, 1))))
+    q, s = oracle.rotate_quantize_fp8(x, g)
+    y = oracle.rotate(x, g)
+    a = np.abs(y).max(axis=1).astype(np.float32)
+    assert np.array_equal(s, (a / np.float32(448)).astype(np.float32))
+    r = (np.float32(448) / a).astype(np.float32)
+    t = np.clip((y * r[:, None]).astype(np.float32), -448, 448)
+    assert np.array_equal(q, torch_e4m3(t))
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_fp8_quantization_error_bound_and_full_scale_code(g):
+    rng = np.random.default_rng(3 + g)
+    x = bf(synth.outlier_activations(rng, 16, 1024, channels=(5, 700)))
+    q, s = oracle.rotate_quantize_fp8(x, g)
+    y = oracle.rotate(x, g).astype(np.float64)
+    deq = oracle.e4m3_decode(q) * s[:, None].astype(np.float64)
+    # half an E4M3 ulp: 2^-4 relative for normals, 2^-10 of the row scale in the subnormal range
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * (1 + 1e-6) + 1e-30
+    assert np.all(np.abs(deq - y) <= bound)
+    assert np.all(np.any((q & 0x7F) == 0x7E, axis=1))     # every row reaches +-448
+
+
+def test_fp8_all_zero_and_tiny_rows():
+    x = np.zeros((2, 256), np.uint16)
+    x[1, 3] = bf(np.array([2.0 ** -120], np.float32))[0]      # absmax below 2^-100
+    x[1, 5] = bf(np.array([2.0 ** -121], np.float32))[0]
+    q, s = oracle.rotate_quantize_fp8(x, 256)
+    assert s[0] == 0 and np.all(q[0] == 0)
+    # rotated values are (+-2^-120 +- 2^-121) / 16: magnitudes a = 3 * 2^-125 and a / 3
+    a = np.float32(3 * 2.0 ** -125)
+    assert s[1] == np.float32(a / np.float32(448))
+    # the row is scaled by 2^100 (exact) before r = 448 / a, so 448 / 3 stays finite
+    small = np.float32(np.float32(a * np.float32(2.0 ** 100) / 3) * np.float32(np.float32(448) / np.float32(a * np.float32(2.0 ** 100))))
+    assert sorted(set((q[1] & 0x7F).tolist())) == sorted({0x7E, int(torch_e4m3([small])[0])})
+
+
+def test_gemm_fp8_brute_force_python_loops():
+    rng = np.random.default_rng(11)
+    codes = FINITE_CODES
+    a = rng.choice(codes, (5, 24))
+    b = rng.choice(codes, (4, 24))
+    c = oracle.gemm_fp8(a, b)
+    av, bv = torch_e4m3_value(a), torch_e4m3_value(b)
+    for i in range(5):
+        for j in range(4):
+            exact = sum(Fraction(float(av[i, t])) * Fraction(float(bv[j, t])) for t in range(24))
+            assert Fraction(float(c[i, j])) == exact
+
+
+def test_fp8_forward_dequant_and_lora_terms():
+    inp = synth.make_linear(12, 512, 48, seed=4, lora_rank=16)
+    qw, sw = oracle.rotate_quantize_fp8(inp["w"], 128)
+    out = oracle.qlinear_forward_fp8(inp["x"], qw, sw, 128, inp["lora_a"], inp["lora_b"], 0.5)
+    qx, sx = oracle.rotate_quantize_fp8(inp["x"], 128)
+    assert np.array_equal(out["qx"], qx) and np.array_equal(out["sx"], sx)
+    assert np.array_equal(out["acc"], oracle.gemm_fp8(qx, qw))
+    base = (out["acc"].astype(np.float32) * (sx[:, None] * sw[None, :]).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(out["base"], base)
+    xf = torch.from_numpy(synth.bf16_bits_to_f32(inp["x"]).astype(np.float64))
+    la = torch.from_numpy(synth.bf16_bits_to_f32(inp["lora_a"]).astype(np.float64))
+    lb = torch.from_numpy(synth.bf16_bits_to_f32(inp["lora_b"]).astype(np.float64))
+    ref = base.astype(np.float64) + 0.5 * (xf @ la @ lb).numpy()
+    assert np.array_equal(out["y"], oracle.bf16_from_f64(ref))
+    # the quantized product approximates the unquantized fp64 product
+    wf = synth.bf16_bits_to_f32(inp["w"]).astype(np.float64)
+    exact = synth.bf16_bits_to_f32(inp["x"]).astype(np.float64) @ wf.T
+    assert np.linalg.norm(base - exact) / np.linalg.norm(exact) < 0.06
