@@ -11,12 +11,17 @@ from ._binding import (  # noqa: F401
     SDNQ_OK,
     SdnqError,
     lib,
+    sdnq_gemm_fp8_f32,
     sdnq_gemm_i8_i32,
     sdnq_qlinear_backward_input,
     sdnq_qlinear_forward,
+    sdnq_qlinear_forward_fp8,
+    sdnq_qlinear_forward_fp8_quantized,
     sdnq_qlinear_forward_quantized,
     sdnq_rotate_quantize_act,
+    sdnq_rotate_quantize_act_fp8,
     sdnq_rotate_quantize_weight,
+    sdnq_rotate_quantize_weight_fp8,
     sdnq_workspace_bytes,
     status_string,
 )

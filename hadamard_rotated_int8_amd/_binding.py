@@ -45,6 +45,11 @@ def lib() -> ctypes.CDLL:
         "sdnq_qlinear_forward_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
         "sdnq_qlinear_backward_input": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
         "sdnq_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p, sz, p],
+        "sdnq_rotate_quantize_weight_fp8": [p, i64, i64, i32, p, p, p],
+        "sdnq_rotate_quantize_act_fp8": [p, i64, i64, i32, p, p, p, p],
+        "sdnq_qlinear_forward_fp8": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p, sz, p],
+        "sdnq_qlinear_forward_fp8_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
+        "sdnq_gemm_fp8_f32": [p, p, i64, i64, i64, p, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -98,35 +103,63 @@ def sdnq_workspace_bytes(m: int, n: int, k: int, rank: int = 0, is_backward: boo
     return int(lib().sdnq_workspace_bytes(m, n, k, rank, int(bool(is_backward))))
 
 
-def sdnq_rotate_quantize_weight(w: torch.Tensor, g: int):
-    """W [n, k] bf16 -> (qw [n, k] int8, w_scale [n] fp32)."""
+def _rotate_quantize_weight(name, code_dtype, w, g):
     _need(w, torch.bfloat16, 2, "w")
     n, k = w.shape
-    qw = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    qw = torch.empty((n, k), dtype=code_dtype, device=w.device)
     sw = torch.empty((n,), dtype=torch.float32, device=w.device)
-    _check(lib().sdnq_rotate_quantize_weight(_ptr(w), n, k, g, _ptr(qw), _ptr(sw), _stream(w.device)),
-           "sdnq_rotate_quantize_weight")
+    _check(getattr(lib(), name)(_ptr(w), n, k, g, _ptr(qw), _ptr(sw), _stream(w.device)), name)
     return qw, sw
 
 
-def sdnq_rotate_quantize_act(x: torch.Tensor, g: int, col_scale: torch.Tensor | None = None):
-    """x [m, k] bf16 -> (qx [m, k] int8, x_scale [m] fp32)."""
+def _rotate_quantize_act(name, code_dtype, x, g, col_scale):
     _need(x, torch.bfloat16, 2, "x")
     if col_scale is not None:
         _need(col_scale, torch.float32, 1, "col_scale")
     m, k = x.shape
-    qx = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    qx = torch.empty((m, k), dtype=code_dtype, device=x.device)
     sx = torch.empty((m,), dtype=torch.float32, device=x.device)
-    _check(lib().sdnq_rotate_quantize_act(_ptr(x), m, k, g, _ptr(col_scale), _ptr(qx), _ptr(sx),
-                                          _stream(x.device)), "sdnq_rotate_quantize_act")
+    _check(getattr(lib(), name)(_ptr(x), m, k, g, _ptr(col_scale), _ptr(qx), _ptr(sx), _stream(x.device)), name)
     return qx, sx
+
+
+def sdnq_rotate_quantize_weight(w: torch.Tensor, g: int):
+    """W [n, k] bf16 -> (qw [n, k] int8, w_scale [n] fp32)."""
+    return _rotate_quantize_weight("sdnq_rotate_quantize_weight", torch.int8, w, g)
+
+
+def sdnq_rotate_quantize_act(x: torch.Tensor, g: int, col_scale: torch.Tensor | None = None):
+    """x [m, k] bf16 -> (qx [m, k] int8, x_scale [m] fp32)."""
+    return _rotate_quantize_act("sdnq_rotate_quantize_act", torch.int8, x, g, col_scale)
+
+
+def sdnq_rotate_quantize_weight_fp8(w: torch.Tensor, g: int):
+    """W [n, k] bf16 -> (qw [n, k] E4M3 codes as uint8, w_scale [n] fp32)."""
+    return _rotate_quantize_weight("sdnq_rotate_quantize_weight_fp8", torch.uint8, w, g)
+
+
+def sdnq_rotate_quantize_act_fp8(x: torch.Tensor, g: int, col_scale: torch.Tensor | None = None):
+    """x [m, k] bf16 -> (qx [m, k] E4M3 codes as uint8, x_scale [m] fp32)."""
+    return _rotate_quantize_act("sdnq_rotate_quantize_act_fp8", torch.uint8, x, g, col_scale)
 
 
 def sdnq_qlinear_forward(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale=0.0, out=None,
                          workspace=None):
     """y [m, n] bf16 = dequant(rotq(x) . qw^T) + lora_scale * (x lora_a) lora_b."""
+    return _forward("sdnq_qlinear_forward", torch.int8, x, qw, w_scale, g, lora_a, lora_b, lora_scale, out,
+                    workspace)
+
+
+def sdnq_qlinear_forward_fp8(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale=0.0, out=None,
+                             workspace=None):
+    """The FP8 forward: qw are E4M3 codes (uint8) from sdnq_rotate_quantize_weight_fp8."""
+    return _forward("sdnq_qlinear_forward_fp8", torch.uint8, x, qw, w_scale, g, lora_a, lora_b, lora_scale, out,
+                    workspace)
+
+
+def _forward(name, code_dtype, x, qw, w_scale, g, lora_a, lora_b, lora_scale, out, workspace):
     _need(x, torch.bfloat16, 2, "x")
-    _need(qw, torch.int8, 2, "qw")
+    _need(qw, code_dtype, 2, "qw")
     _need(w_scale, torch.float32, 1, "w_scale")
     m, k = x.shape
     n = qw.shape[0]
@@ -138,18 +171,29 @@ def sdnq_qlinear_forward(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     nb = sdnq_workspace_bytes(m, n, k, rank, False)
     ws = _workspace(nb, x.device, workspace)
-    _check(lib().sdnq_qlinear_forward(_ptr(x), m, k, _ptr(qw), _ptr(w_scale), n, g, _ptr(lora_a), _ptr(lora_b),
-                                      rank, float(lora_scale), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
-           "sdnq_qlinear_forward")
+    _check(getattr(lib(), name)(_ptr(x), m, k, _ptr(qw), _ptr(w_scale), n, g, _ptr(lora_a), _ptr(lora_b),
+                                rank, float(lora_scale), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)), name)
     return y
 
 
 def sdnq_qlinear_forward_quantized(qx, x_scale, qw, w_scale, t=None, lora_b=None, lora_scale=0.0, out=None,
                                    workspace=None):
     """y [m, n] bf16 from pre-quantized activations (qx, x_scale)."""
-    _need(qx, torch.int8, 2, "qx")
+    return _forward_quantized("sdnq_qlinear_forward_quantized", torch.int8, qx, x_scale, qw, w_scale, t, lora_b,
+                              lora_scale, out, workspace)
+
+
+def sdnq_qlinear_forward_fp8_quantized(qx, x_scale, qw, w_scale, t=None, lora_b=None, lora_scale=0.0, out=None,
+                                       workspace=None):
+    """The FP8 forward from E4M3 activations (qx, x_scale from sdnq_rotate_quantize_act_fp8)."""
+    return _forward_quantized("sdnq_qlinear_forward_fp8_quantized", torch.uint8, qx, x_scale, qw, w_scale, t,
+                              lora_b, lora_scale, out, workspace)
+
+
+def _forward_quantized(name, code_dtype, qx, x_scale, qw, w_scale, t, lora_b, lora_scale, out, workspace):
+    _need(qx, code_dtype, 2, "qx")
     _need(x_scale, torch.float32, 1, "x_scale")
-    _need(qw, torch.int8, 2, "qw")
+    _need(qw, code_dtype, 2, "qw")
     _need(w_scale, torch.float32, 1, "w_scale")
     m, k = qx.shape
     n = qw.shape[0]
@@ -161,10 +205,9 @@ def sdnq_qlinear_forward_quantized(qx, x_scale, qw, w_scale, t=None, lora_b=None
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=qx.device)
     nb = sdnq_workspace_bytes(m, n, k, rank, False)
     ws = _workspace(nb, qx.device, workspace) if rank else workspace
-    _check(lib().sdnq_qlinear_forward_quantized(_ptr(qx), _ptr(x_scale), m, k, _ptr(qw), _ptr(w_scale), n,
-                                                _ptr(t), _ptr(lora_b), rank, float(lora_scale), _ptr(y),
-                                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(qx.device)),
-           "sdnq_qlinear_forward_quantized")
+    _check(getattr(lib(), name)(_ptr(qx), _ptr(x_scale), m, k, _ptr(qw), _ptr(w_scale), n, _ptr(t), _ptr(lora_b),
+                                rank, float(lora_scale), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream(qx.device)), name)
     return y
 
 
@@ -207,3 +250,17 @@ def sdnq_gemm_i8_i32(a, b, b_layout: int = 0, workspace=None):
     _check(lib().sdnq_gemm_i8_i32(_ptr(a), _ptr(b), m, n, k, b_layout, _ptr(c), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(a.device)), "sdnq_gemm_i8_i32")
     return c
+
+
+def sdnq_gemm_fp8_f32(a, b):
+    """fp32-accumulated E4M3 product a [m,k] . b [n,k]^T (codes as uint8)."""
+    _need(a, torch.uint8, 2, "a")
+    _need(b, torch.uint8, 2, "b")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("contraction lengths differ")
+    c = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _check(lib().sdnq_gemm_fp8_f32(_ptr(a), _ptr(b), m, n, k, _ptr(c), _stream(a.device)), "sdnq_gemm_fp8_f32")
+    return c
+

@@ -142,10 +142,14 @@ sdnq_status_t sdnq_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, 
   return launched(launch_rotate_quantize(x, m, k, g, col_scale, qx, x_scale, (hipStream_t)stream));
 }
 
-sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_scale, int64_t m, int64_t k,
-                                             const int8_t *qw, const float *w_scale, int64_t n, const uint16_t *t,
-                                             const uint16_t *lora_b, int32_t rank, float lora_scale, uint16_t *y,
-                                             void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+sdnq_status_t forward_quantized(bool fp8, const int8_t *qx, const float *x_scale, int64_t m, int64_t k,
+                                const int8_t *qw, const float *w_scale, int64_t n, const uint16_t *t,
+                                const uint16_t *lora_b, int32_t rank, float lora_scale, uint16_t *y,
+                                void *workspace, size_t workspace_bytes, void *stream) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!qx || !x_scale || !y)) return SDNQ_ERR_INVALID_ARG;
   SDNQ_TRY(check_feature(k));
@@ -161,7 +165,7 @@ sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_sc
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   GemmArgs ga{};
-  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k;
+  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k; ga.fp8 = fp8;
   ga.row_scale = x_scale; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
   if (r > 0) {
     uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
@@ -171,10 +175,9 @@ sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_sc
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
 
-sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
-                                   int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b,
-                                   int32_t rank, float lora_scale, uint16_t *y, void *workspace,
-                                   size_t workspace_bytes, void *stream) {
+sdnq_status_t forward(bool fp8, const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
+                      int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                      float lora_scale, uint16_t *y, void *workspace, size_t workspace_bytes, void *stream) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!x || !y)) return SDNQ_ERR_INVALID_ARG;
   SDNQ_TRY(check_feature(k));
@@ -191,10 +194,13 @@ sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, cons
   (void)hipGetLastError();
   int8_t *qx = reinterpret_cast<int8_t *>(ws_at(workspace, L.qx));
   float *sx = reinterpret_cast<float *>(ws_at(workspace, L.sx));
-  SDNQ_LAUNCH(launch_rotate_quantize(x, m, k, g, nullptr, qx, sx, s));
+  if (fp8)
+    SDNQ_LAUNCH(launch_rotate_quantize_fp8(x, m, k, g, nullptr, reinterpret_cast<uint8_t *>(qx), sx, s));
+  else
+    SDNQ_LAUNCH(launch_rotate_quantize(x, m, k, g, nullptr, qx, sx, s));
 
   GemmArgs ga{};
-  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k;
+  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k; ga.fp8 = fp8;
   ga.row_scale = sx; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
   if (r > 0) {
     uint16_t *t = reinterpret_cast<uint16_t *>(ws_at(workspace, L.t));
@@ -206,6 +212,26 @@ sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, cons
     ga.lora_t = t; ga.lora_r = bt; ga.rank = r;
   }
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+sdnq_status_t sdnq_qlinear_forward_quantized(const int8_t *qx, const float *x_scale, int64_t m, int64_t k,
+                                             const int8_t *qw, const float *w_scale, int64_t n, const uint16_t *t,
+                                             const uint16_t *lora_b, int32_t rank, float lora_scale, uint16_t *y,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_quantized(false, qx, x_scale, m, k, qw, w_scale, n, t, lora_b, rank, lora_scale, y, workspace,
+                           workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
+                                   int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b,
+                                   int32_t rank, float lora_scale, uint16_t *y, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  return forward(false, x, m, k, qw, w_scale, n, g, lora_a, lora_b, rank, lora_scale, y, workspace,
+                 workspace_bytes, stream);
 }
 
 sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw,
@@ -291,6 +317,56 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
   GemmArgs ga{};
   ga.a = a; ga.b = bb; ga.m = m; ga.n = n; ga.k = k; ga.c_i32 = c; ga.g = 1;
   return launched(launch_gemm_i8(Epilogue::kInt32, ga, s));
+}
+
+// ---------------------------------------------------------------- FP8 --
+sdnq_status_t sdnq_rotate_quantize_weight_fp8(const uint16_t *w, int64_t n, int64_t k, int32_t g, uint8_t *qw,
+                                              float *w_scale, void *stream) {
+  SDNQ_TRY(check_rotq(w, n, k, g, nullptr, qw, w_scale));
+  if (n == 0) return SDNQ_OK;
+  (void)hipGetLastError();
+  return launched(launch_rotate_quantize_fp8(w, n, k, g, nullptr, qw, w_scale, (hipStream_t)stream));
+}
+
+sdnq_status_t sdnq_rotate_quantize_act_fp8(const uint16_t *x, int64_t m, int64_t k, int32_t g,
+                                           const float *col_scale, uint8_t *qx, float *x_scale, void *stream) {
+  SDNQ_TRY(check_rotq(x, m, k, g, col_scale, qx, x_scale));
+  if (m == 0) return SDNQ_OK;
+  (void)hipGetLastError();
+  return launched(launch_rotate_quantize_fp8(x, m, k, g, col_scale, qx, x_scale, (hipStream_t)stream));
+}
+
+sdnq_status_t sdnq_qlinear_forward_fp8(const uint16_t *x, int64_t m, int64_t k, const uint8_t *qw,
+                                       const float *w_scale, int64_t n, int32_t g, const uint16_t *lora_a,
+                                       const uint16_t *lora_b, int32_t rank, float lora_scale, uint16_t *y,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  return forward(true, x, m, k, reinterpret_cast<const int8_t *>(qw), w_scale, n, g, lora_a, lora_b, rank,
+                 lora_scale, y, workspace, workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_qlinear_forward_fp8_quantized(const uint8_t *qx, const float *x_scale, int64_t m, int64_t k,
+                                                 const uint8_t *qw, const float *w_scale, int64_t n,
+                                                 const uint16_t *t, const uint16_t *lora_b, int32_t rank,
+                                                 float lora_scale, uint16_t *y, void *workspace,
+                                                 size_t workspace_bytes, void *stream) {
+  return forward_quantized(true, reinterpret_cast<const int8_t *>(qx), x_scale, m, k,
+                           reinterpret_cast<const int8_t *>(qw), w_scale, n, t, lora_b, rank, lora_scale, y,
+                           workspace, workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_gemm_fp8_f32(const uint8_t *a, const uint8_t *b, int64_t m, int64_t n, int64_t k, float *c,
+                                void *stream) {
+  if (!b || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!a || !c)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(k));
+  SDNQ_TRY(check_feature(n));
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return SDNQ_ERR_INVALID_ARG;
+  if (m == 0) return SDNQ_OK;
+  (void)hipGetLastError();
+  GemmArgs ga{};
+  ga.a = reinterpret_cast<const int8_t *>(a); ga.b = reinterpret_cast<const int8_t *>(b);
+  ga.m = m; ga.n = n; ga.k = k; ga.c_i32 = reinterpret_cast<int32_t *>(c); ga.g = 1; ga.fp8 = true;
+  return launched(launch_gemm_i8(Epilogue::kInt32, ga, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -12,6 +12,13 @@
 // where rot_g is the normalized block Walsh-Hadamard rotation along the output
 // columns (the same transform as the forward's, which is its own inverse).
 //
+// FP8 (E4M3 x E4M3, the float8_e4m3fn quantized matmul of the same pages): the
+// same tiles and loads, one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 tile and
+// 64-byte k-tile with fp32 accumulation, and the forward epilogue's scales.
+// Its A and B fragments pair up 64 k positions of a tile the same way (the
+// two 16-byte halves the int8 path reads for its two 32-deep steps), so the
+// contraction is the full 64-k dot product.
+//
 // Tiling.  A workgroup of 8 wavefronts (two per SIMD, so one hides the other's
 // waits) computes a 256 x 256 output tile; K is consumed 64 bytes at a time
 // through a 4-stage LDS ring (4 x 32 KB) filled by buffer loads that write LDS
@@ -126,8 +133,21 @@ struct TileCfg {
   static_assert(BN_ % 32 == 0 && BM / 16 == 16, "A groups fill load slots 0 and 1");
 };
 
-template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA>
+template <bool FP8>
+struct AccOf {
+  typedef v16i type;
+};
+template <>
+struct AccOf<true> {
+  typedef v16f type;
+};
+__device__ __forceinline__ float acc_f32(int v) { return (float)v; }
+__device__ __forceinline__ float acc_f32(float v) { return v; }
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  static_assert(!FP8 || EPI != Epilogue::kBackward, "FP8 runs the forward only");
   using Cfg = TileCfg<BN>;
   constexpr int kStageBytes = Cfg::kStageBytes;
   constexpr int LPW = Cfg::kLoadsPerWave;
@@ -207,18 +227,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     for (int j = 0; j < SN; ++j) f.b[j] = *reinterpret_cast<const v4i *>(base + BM * BK + (wn * TN + j * 32) * BK);
   };
 
-  v16i acc[SM][SN];
+  typedef typename AccOf<FP8>::type AccT;
+  AccT acc[SM][SN];
 #pragma unroll
   for (int i = 0; i < SM; ++i)
 #pragma unroll
-    for (int j = 0; j < SN; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < SN; ++j) acc[i][j] = AccT{};
 
+  // FP8: one MFMA per tile over both 16-byte halves (64 k positions)
+  auto mfma8_all = [&](const Frags &f0, const Frags &f1) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+          const v8i bv = __builtin_shufflevector(f0.b[j], f1.b[j], 0, 1, 2, 3, 4, 5, 6, 7);
+          const v8i av = __builtin_shufflevector(f0.a[i], f1.a[i], 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+        }
+    }
+  };
   auto mfma_all = [&](const Frags &f) {
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
       for (int j = 0; j < SN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+        if constexpr (!FP8) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
 
   // ---- pipeline: tiles kt+1..kt+3 are in flight while tile kt is consumed.
@@ -232,6 +266,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   Frags f0, f1;
   read_frags(0, 0, f0);
 
+  if constexpr (FP8) {
+    // Iteration kt: wait for tile kt+1, barrier | load tile kt+3 | read both
+    // halves of tile kt+1 | MFMA tile kt (both halves, read one iteration ago).
+    read_frags(0, 1, f1);
+    constexpr int R = 2 * (SM + SN);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_loads_and_barrier<LPW>();
+      issue_loads(kt + 3);
+      Frags g0, g1;
+      read_frags(kt + 1, 0, g0);
+      read_frags(kt + 1, 1, g1);
+      mfma8_all(f0, f1);
+#pragma unroll
+      for (int u = 0; u < SM * SN; ++u) {
+        if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      // 1 global->LDS load
+        __builtin_amdgcn_sched_group_barrier(0x100, R / (SM * SN), 0);                    // LDS reads
+        if (u < R % (SM * SN)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // 1 MFMA
+      }
+      f0 = g0;
+      f1 = g1;
+    }
+  } else
   for (int kt = 0; kt < nk; ++kt) {
     read_frags(kt, 1, f1);
     mfma_all(f0);
@@ -269,7 +326,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         for (int q4 = 0; q4 < 4; ++q4) {
           const int64_t n = n0 + wn * TN + j * 32 + 8 * q4 + 4 * half;
           if (n < N) {
-            v4i o = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+            v4i o;
+            if constexpr (FP8) {  // the fp32 accumulators' bits
+              o = v4i{__float_as_int(acc[i][j][4 * q4]), __float_as_int(acc[i][j][4 * q4 + 1]),
+                      __float_as_int(acc[i][j][4 * q4 + 2]), __float_as_int(acc[i][j][4 * q4 + 3])};
+            } else {
+              o = v4i{acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+            }
             *reinterpret_cast<v4i *>(args.c_i32 + m * N + n) = o;
           }
         }
@@ -292,10 +355,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
           int64_t n = nb + 8 * q4;
           n = n < N ? n : N - 4;
           const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
-          o[i][j][4 * q4 + 0] = (float)acc[i][j][4 * q4 + 0] * (sx * sw.x);
-          o[i][j][4 * q4 + 1] = (float)acc[i][j][4 * q4 + 1] * (sx * sw.y);
-          o[i][j][4 * q4 + 2] = (float)acc[i][j][4 * q4 + 2] * (sx * sw.z);
-          o[i][j][4 * q4 + 3] = (float)acc[i][j][4 * q4 + 3] * (sx * sw.w);
+          o[i][j][4 * q4 + 0] = acc_f32(acc[i][j][4 * q4 + 0]) * (sx * sw.x);
+          o[i][j][4 * q4 + 1] = acc_f32(acc[i][j][4 * q4 + 1]) * (sx * sw.y);
+          o[i][j][4 * q4 + 2] = acc_f32(acc[i][j][4 * q4 + 2]) * (sx * sw.z);
+          o[i][j][4 * q4 + 3] = acc_f32(acc[i][j][4 * q4 + 3]) * (sx * sw.w);
         }
       }
     }
@@ -338,10 +401,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
           int64_t n = nb + 8 * q4;
           n = n < N ? n : N - 4;
           const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
-          o[4 * q4 + 0] = (float)acc[i][j][4 * q4 + 0] * (sx * sw.x);
-          o[4 * q4 + 1] = (float)acc[i][j][4 * q4 + 1] * (sx * sw.y);
-          o[4 * q4 + 2] = (float)acc[i][j][4 * q4 + 2] * (sx * sw.z);
-          o[4 * q4 + 3] = (float)acc[i][j][4 * q4 + 3] * (sx * sw.w);
+          o[4 * q4 + 0] = acc_f32(acc[i][j][4 * q4 + 0]) * (sx * sw.x);
+          o[4 * q4 + 1] = acc_f32(acc[i][j][4 * q4 + 1]) * (sx * sw.y);
+          o[4 * q4 + 2] = acc_f32(acc[i][j][4 * q4 + 2]) * (sx * sw.z);
+          o[4 * q4 + 3] = acc_f32(acc[i][j][4 * q4 + 3]) * (sx * sw.w);
         }
         if (m < M) {
 #pragma unroll
@@ -372,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 #pragma unroll
       for (int j = 0; j < SN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) z[j][r] = (float)acc[i][j][r] * sdy;
+        for (int r = 0; r < 16; ++r) z[j][r] = acc_f32(acc[i][j][r]) * sdy;
 
       if constexpr (G > 1) {
         // h = 1, 2: register bits 0-1
@@ -485,11 +548,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   }
 }
 
-template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA>
+template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8 = false>
 hipError_t launch_typed(const GemmArgs &args, hipStream_t stream) {
   const int tiles_m = (int)((args.m + BM - 1) / BM);
   const int tiles_n = (int)((args.n + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<EPI, BN, WAVES_M, G, LORA>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_i8_kernel<EPI, BN, WAVES_M, G, LORA, FP8>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
                      stream, args, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -519,19 +582,24 @@ int gemm_cu_count() {
 // column-rounds wins (ties go to 256): e.g. 4096 x 10240 takes 2 rounds of
 // 256 x 320 tiles instead of 2.5 (so 3) of 256 x 256, and 4096 x 3072 one round
 // of 256 x 192 instead of 0.75 of 256 x 256.
-int gemm_tile_n(int64_t m, int64_t n) {
+// (FP8 keeps two fragment sets of both halves live, which 320 columns do not fit.)
+int gemm_tile_n(int64_t m, int64_t n, bool fp8) {
   const int64_t cus = gemm_cu_count();
   const int64_t tiles_m = (m + BM - 1) / BM;
   auto cost = [&](int bn) { return (tiles_m * ((n + bn - 1) / bn) + cus - 1) / cus * bn; };
   int best = 256;
   for (int bn : {320, 192})
-    if (cost(bn) < cost(best)) best = bn;
+    if ((bn != 320 || !fp8) && cost(bn) < cost(best)) best = bn;
   return best;
 }
 
 template <Epilogue EPI, bool LORA>
 hipError_t launch_forward_like(const GemmArgs &args, hipStream_t stream) {
-  switch (gemm_tile_n(args.m, args.n)) {
+  if (args.fp8) {
+    if (gemm_tile_n(args.m, args.n, true) == 192) return launch_typed<EPI, 192, 4, 1, LORA, true>(args, stream);
+    return launch_typed<EPI, 256, 2, 1, LORA, true>(args, stream);
+  }
+  switch (gemm_tile_n(args.m, args.n, false)) {
     case 320: return launch_typed<EPI, 320, 4, 1, LORA>(args, stream);
     case 192: return launch_typed<EPI, 192, 4, 1, LORA>(args, stream);
     default: return launch_typed<EPI, 256, 2, 1, LORA>(args, stream);
@@ -547,6 +615,7 @@ hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream
       return args.rank > 0 ? launch_forward_like<Epilogue::kForward, true>(args, stream)
                            : launch_forward_like<Epilogue::kForward, false>(args, stream);
     case Epilogue::kBackward:
+      if (args.fp8) return hipErrorInvalidValue;
       switch (args.g) {
         case 1: return launch_backward<1>(args, stream);
         case 64: return launch_backward<64>(args, stream);

@@ -23,6 +23,12 @@
 // its absmax is known (one workgroup holds `rows_per_wg` complete rows at a
 // time and walks over row groups persistently, prefetching the next group).
 //
+// FP8 variant (the float8_e4m3fn quantized matmul listed next to INT8 in "SDNQ:
+// SD.Next Quantization Engine"): s = fl32(a / 448), r = fl32(448 / a), and each
+// fl32(y * r), clamped to +-448, is converted by v_cvt_pk_fp8_f32 (OCP E4M3,
+// round half to even; it would give NaN from 464 up, which the clamp rules out);
+// an exact zero is stored as +0, a nonzero value that rounds to zero keeps its sign.
+//
 // Cross-lane stages keep a per-lane sign: the upper lane of a pair computes
 // fma(partner, -1, self) = self - partner = -(a - b), which rounds exactly like
 // a - b up to the sign; the sign of every lane is (-1)^popcount(l4) after both
@@ -88,7 +94,7 @@ __device__ __forceinline__ void dpp_stage_xor2(float (&r)[8], float m) {
                : "v"(m));
 }
 
-template <int G, bool COLSCALE, int MAXT>
+template <int G, bool COLSCALE, int MAXT, bool FP8>
 __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
     int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg, int64_t groups) {
@@ -238,13 +244,14 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
 
     // g = 64, 256: norm_const is a power of two, so a = fl32(max|u| * c) = max|fl32(u * c)|.
     if constexpr (G == 64 || G == 256) a = a * norm_const<G>();
-    const float s = a / 127.0f;
+    constexpr float kQMax = FP8 ? 448.0f : 127.0f;
+    const float s = a / kQMax;
     // Rows with a < 2^-100 are scaled by 2^100 (exact) before r = 127/a is formed,
     // which would otherwise overflow binary32.
     const bool tiny = a < 0x1p-100f;
     const float up = tiny ? 0x1p100f : 1.0f;
     const float as = a * up;
-    const float r = (as > 0.0f) ? 127.0f / as : 0.0f;
+    const float r = (as > 0.0f) ? kQMax / as : 0.0f;
     if (row_ok && qt == 0) scale[row] = s;
 
     // Multiplier turning the stored value into fl32(y * r).
@@ -274,16 +281,29 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t e0 = base + 32 * i;
-        uint32_t c[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float t = v[i][j] * mult;
-          c[j] = code_bits(t);
-        }
         const unsigned off = (e0 < cols) ? (unsigned)(r_local * cols + e0) : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(v2u, (v2u){pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])}), rq, off,
-            0, 0);
+        v2u packed;
+        if constexpr (FP8) {
+          float t[8];
+#pragma unroll
+          // + 0.0f stores an exact zero as +0: the per-lane sign trick can leave -0
+          // where the butterfly cancels exactly
+          for (int j = 0; j < 8; ++j) t[j] = fminf(fmaxf(v[i][j] * mult, -448.0f), 448.0f) + 0.0f;
+          // bytes 0-1 then 2-3 of each dword, in value order
+          packed[0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+              t[2], t[3], __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false), true);
+          packed[1] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+              t[6], t[7], __builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], 0, false), true);
+        } else {
+          uint32_t c[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float t = v[i][j] * mult;
+            c[j] = code_bits(t);
+          }
+          packed = (v2u){pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(packed, rq, off, 0, 0);
       }
     }
   }
@@ -311,14 +331,15 @@ int pick_rows_per_wg(int t_row, int max_threads) {
 
 // Resident workgroups per CU for a kernel at a block size (cached; the launch
 // configuration only depends on the kernel and the block size).
-template <int G, bool CS, int MAXT>
+template <int G, bool CS, int MAXT, bool FP8>
 int blocks_per_cu(int threads) {
   static int cached_threads[kMaxThreads / 4 + 1];
   static int cached_blocks[kMaxThreads / 4 + 1];
   const int slot = threads / 4;
   if (cached_threads[slot] == threads) return cached_blocks[slot];
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT>, threads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8>, threads, 0) !=
+          hipSuccess ||
       n < 1)
     n = 1;
   cached_blocks[slot] = n;
@@ -338,30 +359,47 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int G, bool CS, int MAXT>
+template <int G, bool CS, int MAXT, bool FP8>
 hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
                         float *scale, int t_row, int rpw, hipStream_t stream) {
   const int threads = rpw * t_row;
   const int64_t groups = (rows + rpw - 1) / rpw;
-  int64_t blocks = (int64_t)cu_count() * blocks_per_cu<G, CS, MAXT>(threads);
+  int64_t blocks = (int64_t)cu_count() * blocks_per_cu<G, CS, MAXT, FP8>(threads);
   if (blocks > groups) blocks = groups;
-  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT>), dim3((unsigned)blocks), dim3(threads), 0, stream, x, rows, cols,
-                     col_scale, q, scale, t_row, rpw, groups);
+  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8>), dim3((unsigned)blocks), dim3(threads), 0, stream, x, rows,
+                     cols, col_scale, q, scale, t_row, rpw, groups);
   return hipGetLastError();
 }
 
 // Rows of up to 32768 values run in workgroups of at most 512 threads (up to 256
 // VGPRs per lane, room for the prefetch buffer); longer rows need up to 1024.
-template <int G, bool CS>
+template <int G, bool CS, bool FP8>
 hipError_t launch_typed(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale,
                         int8_t *q, float *scale, hipStream_t stream) {
   const int t_row = 4 * (int)((cols + 255) / 256);
   if (t_row <= 512) {
     const int rpw = pick_rows_per_wg(t_row, 512);
-    return launch_sized<G, CS, 512>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);
+    return launch_sized<G, CS, 512, FP8>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);
   }
   const int rpw = pick_rows_per_wg(t_row, kMaxThreads);
-  return launch_sized<G, CS, kMaxThreads>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);
+  return launch_sized<G, CS, kMaxThreads, FP8>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);
+}
+
+template <bool FP8>
+hipError_t launch_any(const uint16_t *x, int64_t rows, int64_t cols, int g, const float *col_scale, int8_t *q,
+                      float *scale, hipStream_t stream) {
+  const bool cs = col_scale != nullptr;
+  switch (g) {
+    case 1: return cs ? launch_typed<1, true, FP8>(x, rows, cols, col_scale, q, scale, stream)
+                      : launch_typed<1, false, FP8>(x, rows, cols, col_scale, q, scale, stream);
+    case 64: return cs ? launch_typed<64, true, FP8>(x, rows, cols, col_scale, q, scale, stream)
+                       : launch_typed<64, false, FP8>(x, rows, cols, col_scale, q, scale, stream);
+    case 128: return cs ? launch_typed<128, true, FP8>(x, rows, cols, col_scale, q, scale, stream)
+                        : launch_typed<128, false, FP8>(x, rows, cols, col_scale, q, scale, stream);
+    case 256: return cs ? launch_typed<256, true, FP8>(x, rows, cols, col_scale, q, scale, stream)
+                        : launch_typed<256, false, FP8>(x, rows, cols, col_scale, q, scale, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -369,18 +407,12 @@ hipError_t launch_typed(const uint16_t *x, int64_t rows, int64_t cols, const flo
 hipError_t launch_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
                                   const float *col_scale, int8_t *q, float *scale,
                                   hipStream_t stream) {
-  const bool cs = col_scale != nullptr;
-  switch (g) {
-    case 1: return cs ? launch_typed<1, true>(x, rows, cols, col_scale, q, scale, stream)
-                      : launch_typed<1, false>(x, rows, cols, col_scale, q, scale, stream);
-    case 64: return cs ? launch_typed<64, true>(x, rows, cols, col_scale, q, scale, stream)
-                       : launch_typed<64, false>(x, rows, cols, col_scale, q, scale, stream);
-    case 128: return cs ? launch_typed<128, true>(x, rows, cols, col_scale, q, scale, stream)
-                        : launch_typed<128, false>(x, rows, cols, col_scale, q, scale, stream);
-    case 256: return cs ? launch_typed<256, true>(x, rows, cols, col_scale, q, scale, stream)
-                        : launch_typed<256, false>(x, rows, cols, col_scale, q, scale, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any<false>(x, rows, cols, g, col_scale, q, scale, stream);
+}
+
+hipError_t launch_rotate_quantize_fp8(const uint16_t *x, int64_t rows, int64_t cols, int g,
+                                      const float *col_scale, uint8_t *q, float *scale, hipStream_t stream) {
+  return launch_any<true>(x, rows, cols, g, col_scale, reinterpret_cast<int8_t *>(q), scale, stream);
 }
 
 }  // namespace sdnq

@@ -36,6 +36,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 hipError_t launch_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
                                   const float *col_scale, int8_t *q, float *scale,
                                   hipStream_t stream);
+// The same with the FP8 (E4M3) quantizer: s = a / 448, codes e4m3(clamp(y * r, +-448)).
+hipError_t launch_rotate_quantize_fp8(const uint16_t *x, int64_t rows, int64_t cols, int g,
+                                      const float *col_scale, uint8_t *q, float *scale, hipStream_t stream);
 
 // G2 epilogue selector.
 enum class Epilogue { kInt32, kForward, kBackward };
@@ -55,6 +58,8 @@ struct GemmArgs {
   int rank;
   int g;                  // backward: inverse rotation block along n (1, 64, 128, 256)
   uint16_t *out_bf16;     // [m, n]
+  bool fp8;               // a and b hold E4M3 codes (forward and the accumulator export only);
+                          // the kInt32 epilogue then stores the fp32 accumulators' bits
 };
 
 hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream);

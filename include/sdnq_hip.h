@@ -145,6 +145,52 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
                                int32_t b_layout, int32_t *c, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- FP8 ------
+ * The FP8 variant of the quantized matmul ("SDNQ: SD.Next Quantization Engine":
+ * INT8 and FP8 quantized matmul; the SDNQConfig example's matmul dtype
+ * float8_e4m3fn).  Same rotation and row absmax as the INT8 path, with
+ *   s = fl32(a/448), r = fl32(448/a), code = E4M3(clamp(fl32(y*r), -448, 448)),
+ * E4M3 being the OCP FP8 format (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, largest finite 448), rounded to nearest, ties to even.  Codes
+ * are passed as uint8_t bit patterns.  The GEMM accumulates the products of the
+ * decoded codes in fp32 (MFMA order), so its results match the exact sum within
+ * fp32 accumulation error rather than bit for bit.  Shapes, alignment, limits,
+ * errors and workspace sizes are those of the INT8 entry points. */
+
+/* Weight preparation: qw[n,k] E4M3 codes, w_scale[n] fp32. */
+sdnq_status_t sdnq_rotate_quantize_weight_fp8(const uint16_t *w, int64_t n, int64_t k, int32_t g,
+                                              uint8_t *qw, float *w_scale, void *stream);
+
+/* Per-token activation quantization: qx[m,k] E4M3 codes, x_scale[m] fp32
+ * (col_scale as for sdnq_rotate_quantize_act, nullable). */
+sdnq_status_t sdnq_rotate_quantize_act_fp8(const uint16_t *x, int64_t m, int64_t k, int32_t g,
+                                           const float *col_scale, uint8_t *qx, float *x_scale,
+                                           void *stream);
+
+/* Forward: y[m,n] = bf16( fp32(dec(rotq8(x)) . dec(qw)^T) * x_scale[m] * w_scale[n]
+ *                         + lora_scale * ((x lora_a) lora_b)[m,n] ),
+ * arguments as for sdnq_qlinear_forward with E4M3 weight codes.
+ * workspace: at least sdnq_workspace_bytes(m, n, k, rank, 0) bytes. */
+sdnq_status_t sdnq_qlinear_forward_fp8(const uint16_t *x, int64_t m, int64_t k,
+                                       const uint8_t *qw, const float *w_scale, int64_t n, int32_t g,
+                                       const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                       float lora_scale, uint16_t *y,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward from E4M3 activations (qx, x_scale from sdnq_rotate_quantize_act_fp8 with
+ * the weight's g), arguments as for sdnq_qlinear_forward_quantized. */
+sdnq_status_t sdnq_qlinear_forward_fp8_quantized(const uint8_t *qx, const float *x_scale, int64_t m,
+                                                 int64_t k, const uint8_t *qw, const float *w_scale,
+                                                 int64_t n, const uint16_t *t, const uint16_t *lora_b,
+                                                 int32_t rank, float lora_scale, uint16_t *y,
+                                                 void *workspace, size_t workspace_bytes,
+                                                 void *stream);
+
+/* Diagnostics: the FP8 GEMM with an fp32 store instead of the epilogue:
+ * c[m,n] = sum_k dec(a[m,k]) * dec(b[n,k]), fp32 accumulation. */
+sdnq_status_t sdnq_gemm_fp8_f32(const uint8_t *a, const uint8_t *b, int64_t m, int64_t n, int64_t k,
+                                float *c, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,7 +43,9 @@
  * to INT8): the same rotation and absmax, with s = fl32(a/448), r = fl32(448/a),
  * v = fl32(y*r) clamped to [-448, 448] and each v encoded in OCP FP8 E4M3
  * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
- * infinities, 0x7F/0xFF = NaN, largest finite 448) with round half to even.  The
+ * infinities, 0x7F/0xFF = NaN, largest finite 448) with round half to even; an
+ * exact zero is stored as +0 (0x00), while nonzero values that round to zero
+ * keep their sign.  The
  * product of two E4M3 values has at most 8 significant bits between 2^-18 and
  * 2^17.6, so the fp64 sum over K <= 65536 of them is exact.
  *
@@ -219,7 +221,10 @@ static void quantize_row_fp8(const float *y, int64_t cols, uint8_t *q, float *s)
     float as = a * up;
     float r = (as > 0.0f) ? 448.0f / as : 0.0f;
     for (int64_t i = 0; i < cols; i++) {
-        float t = (y[i] * up) * r;
+        /* + 0.0f stores an exact zero as +0 (0x00): the sign of a zero that the
+         * butterfly's cancellations produce depends on evaluation order, not on the
+         * data.  Nonzero values that round to zero keep their sign. */
+        float t = (y[i] * up) * r + 0.0f;
         if (t > 448.0f)
             t = 448.0f;
         if (t < -448.0f)

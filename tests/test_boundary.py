@@ -32,7 +32,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("sdnq_rotate_quantize_weight", "sdnq_rotate_quantize_act", "sdnq_qlinear_forward",
               "sdnq_qlinear_backward_input", "sdnq_qlinear_forward_quantized", "sdnq_workspace_bytes",
-              "sdnq_status_string", "sdnq_gemm_i8_i32"):
+              "sdnq_status_string", "sdnq_gemm_i8_i32", "sdnq_rotate_quantize_weight_fp8",
+              "sdnq_rotate_quantize_act_fp8", "sdnq_qlinear_forward_fp8", "sdnq_qlinear_forward_fp8_quantized",
+              "sdnq_gemm_fp8_f32"):
         assert n in names
 
 
@@ -173,3 +175,19 @@ def test_binding_rejects_wrong_types_before_calling():
         h.sdnq_rotate_quantize_act(torch.zeros(4, 256, dtype=torch.float32), 256)
     with pytest.raises((TypeError, ValueError)):
         h.sdnq_rotate_quantize_act(torch.zeros(4, 256, dtype=torch.bfloat16), 256)  # CPU tensor
+
+
+@no_gpu
+def test_fp8_entry_points_validate_like_the_int8_ones():
+    L = h.lib()
+    assert L.sdnq_rotate_quantize_act_fp8(A, 4, 256, 32, None, B, C, None) == UNSUPPORTED
+    assert L.sdnq_rotate_quantize_act_fp8(A + 8, 4, 256, 256, None, B, C, None) == INVALID
+    assert L.sdnq_rotate_quantize_weight_fp8(A, 0, 256, 256, B, C, None) == OK
+    assert L.sdnq_qlinear_forward_fp8(A, 4, 256, B, C, 256, 7, None, None, 0, 1.0, D, W, WS, None) == UNSUPPORTED
+    assert L.sdnq_qlinear_forward_fp8(A, 4, 256, B, C, 256, 256, None, None, 0, 1.0, D, None, 0, None) == WORKSPACE
+    assert L.sdnq_qlinear_forward_fp8_quantized(A, C, 4, 256, B, C, 200, None, None, 0, 1.0, D, None, 0,
+                                                None) == UNSUPPORTED
+    assert L.sdnq_gemm_fp8_f32(A, B, 4, 30, 32, C, None) == UNSUPPORTED
+    assert L.sdnq_gemm_fp8_f32(None, B, 4, 32, 32, C, None) == INVALID
+    assert L.sdnq_gemm_fp8_f32(A, B, 0, 32, 32, C, None) == OK
+

@@ -44,6 +44,7 @@ MUTANTS = {
     "fp8_no_tiny_row_rescale": ("float up = (a < 0x1p-100f) ? 0x1p100f : 1.0f;\n    float as = a * up;\n    float r = (as > 0.0f) ? 448.0f / as : 0.0f;",
                                 "float up = 1.0f;\n    float as = a * up;\n    float r = (as > 0.0f) ? 448.0f / as : 0.0f;"),
     "fp8_weight_index": ("acc += dq[kk] * e4m3_decode(wr[kk]);", "acc += dq[kk] * e4m3_decode(wr[(kk + 1) % k]);"),
+    "fp8_signed_zero": ("float t = (y[i] * up) * r + 0.0f;", "float t = (y[i] * up) * r;"),
 }
 
 

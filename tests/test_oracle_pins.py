@@ -512,7 +512,7 @@ def test_fp8_quantization_matches_a_library_encoder_of_the_rotated_row(g):
     a = np.abs(y).max(axis=1).astype(np.float32)
     assert np.array_equal(s, (a / np.float32(448)).astype(np.float32))
     r = (np.float32(448) / a).astype(np.float32)
-    t = np.clip((y * r[:, None]).astype(np.float32), -448, 448)
+    t = np.clip((y * r[:, None]).astype(np.float32), -448, 448) + np.float32(0)  # exact zeros as +0
     assert np.array_equal(q, torch_e4m3(t))
 
 
@@ -527,6 +527,19 @@ def test_fp8_quantization_error_bound_and_full_scale_code(g):
     bound = np.maximum(np.abs(y) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * (1 + 1e-6) + 1e-30
     assert np.all(np.abs(deq - y) <= bound)
     assert np.all(np.any((q & 0x7F) == 0x7E, axis=1))     # every row reaches +-448
+
+
+def test_fp8_exact_zeros_are_stored_as_positive_zero():
+    """A block of -0 inputs rotates to zeros of both signs; every code is 0x00.
+    A small negative value that rounds to zero keeps its sign (0x80)."""
+    x = np.full((1, 256), 0x8000, np.uint16)                  # bf16 -0.0
+    x[0, 0] = bf(np.array([1.0], np.float32))[0]
+    x[0, 1] = bf(np.array([-1.0], np.float32))[0]            # y has exact zeros from cancellation
+    q, s = oracle.rotate_quantize_fp8(x, 2)
+    assert set(q[0, 2:].tolist()) == {0x00}
+    x = bf(np.array([[448.0, -1e-4] + [0.0] * 14], np.float32))
+    q, s = oracle.rotate_quantize_fp8(x, 1)
+    assert q[0, 1] == 0x80 and q[0, 2] == 0x00
 
 
 def test_fp8_all_zero_and_tiny_rows():
