@@ -109,8 +109,9 @@ def cpu_baseline(inp, target_s: float) -> dict:
 def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     """Whole-call timings (HIP events on the launch stream) of the other steps of
     the layer, each on its own workload: weight preparation, the attention
-    projection forward, the QuaRot-style forward with LoRA (g = 64 and 128) and
-    the PEFT backward (input gradient + LoRA gradients)."""
+    projection forward, the QuaRot-style forward with LoRA (g = 64 and 128), the
+    PEFT backward (input gradient + LoRA gradients) and the FP8 (E4M3) variant of
+    the MLP step."""
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
 
@@ -165,6 +166,40 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     rows["peft_backward_16384x3072x3072_g256_r64"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
                                                       "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
                                                       "note": "dX through the int8 weight + LoRA dX, dA, dB"}
+    del x, w, dy, la, lb, ws
+    # FP8 variant of the MLP step (same workload, E4M3 codes, fp32 MFMA accumulation)
+    inp = synth.make_config("mlp")
+    x, hh = to_dev_bf16(torch, inp["x"]), to_dev_bf16(torch, inp["h"])
+    qwu, swu = h.sdnq_rotate_quantize_weight_fp8(to_dev_bf16(torch, inp["w_up"]), 256)
+    qwd, swd = h.sdnq_rotate_quantize_weight_fp8(to_dev_bf16(torch, inp["w_down"]), 256)
+    qx = torch.empty((M, K_UP), dtype=torch.uint8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    qh = torch.empty((M, K_DOWN), dtype=torch.uint8, device=dev)
+    sh = torch.empty((M,), dtype=torch.float32, device=dev)
+    yu = torch.empty((M, N_UP), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((M, N_DOWN), dtype=torch.bfloat16, device=dev)
+    L = h.lib()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    gemm_up = lambda: L.sdnq_qlinear_forward_fp8_quantized(P(qx), P(sx), M, K_UP, P(qwu), P(swu), N_UP, None, None,
+                                                           0, 0.0, P(yu), None, 0, sp)
+    gemm_down = lambda: L.sdnq_qlinear_forward_fp8_quantized(P(qh), P(sh), M, K_DOWN, P(qwd), P(swd), N_DOWN,
+                                                             None, None, 0, 0.0, P(yd), None, 0, sp)
+
+    def step8():
+        L.sdnq_rotate_quantize_act_fp8(P(x), M, K_UP, G, None, P(qx), P(sx), sp)
+        gemm_up()
+        L.sdnq_rotate_quantize_act_fp8(P(hh), M, K_DOWN, G, None, P(qh), P(sh), sp)
+        gemm_down()
+    ops = 2.0 * M * (N_UP * K_UP + N_DOWN * K_DOWN)
+    us = timed(step8)
+    t_up, t_down = timed(gemm_up), timed(gemm_down)
+    gemm_tops = ops / (t_up + t_down) / 1e6
+    rows["fp8_mlp_step_4096tok_g256"] = {
+        "us": round(us, 2), "TFLOP/s": round(ops / us / 1e6, 1), "pct_of_fp8_peak": round(ops / us / 1e6 / 50.0, 2),
+        "gemm_up_us": round(t_up, 2), "gemm_down_us": round(t_down, 2),
+        "gemm_TFLOP/s": round(gemm_tops, 1), "gemm_pct_of_fp8_peak": round(gemm_tops / 50.0, 2),
+        "note": "E4M3 codes, fp32 MFMA accumulation; back-to-back GEMM launches; fp8 dense peak 5.0 PFLOP/s"}
     return rows
 
 

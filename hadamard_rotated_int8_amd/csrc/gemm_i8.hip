@@ -266,7 +266,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   Frags f0, f1;
   read_frags(0, 0, f0);
 
-  if constexpr (FP8) {
+  if constexpr (FP8 && BN == 320) {
+    // Ten accumulator tiles leave room for three fragment sets only.  Iteration
+    // kt: read the second half of tile kt | wait for tile kt+1, barrier | load
+    // tile kt+3 | read the first half of tile kt+1 | MFMA tile kt.
+    for (int kt = 0; kt < nk; ++kt) {
+      read_frags(kt, 1, f1);
+      wait_loads_and_barrier<LPW>();
+      issue_loads(kt + 3);
+      Frags g0;
+      read_frags(kt + 1, 0, g0);
+      mfma8_all(f0, f1);
+#pragma unroll
+      for (int u = 0; u < SM * SN; ++u) {
+        if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // 1 global->LDS load
+        if (u < SM + SN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+      }
+      f0 = g0;
+    }
+  } else if constexpr (FP8) {
     // Iteration kt: wait for tile kt+1, barrier | load tile kt+3 | read both
     // halves of tile kt+1 | MFMA tile kt (both halves, read one iteration ago).
     read_frags(0, 1, f1);
@@ -589,15 +608,18 @@ int gemm_tile_n(int64_t m, int64_t n, bool fp8) {
   auto cost = [&](int bn) { return (tiles_m * ((n + bn - 1) / bn) + cus - 1) / cus * bn; };
   int best = 256;
   for (int bn : {320, 192})
-    if ((bn != 320 || !fp8) && cost(bn) < cost(best)) best = bn;
+    if (cost(bn) < cost(best)) best = bn;
   return best;
 }
 
 template <Epilogue EPI, bool LORA>
 hipError_t launch_forward_like(const GemmArgs &args, hipStream_t stream) {
   if (args.fp8) {
-    if (gemm_tile_n(args.m, args.n, true) == 192) return launch_typed<EPI, 192, 4, 1, LORA, true>(args, stream);
-    return launch_typed<EPI, 256, 2, 1, LORA, true>(args, stream);
+    switch (gemm_tile_n(args.m, args.n, true)) {
+      case 320: return launch_typed<EPI, 320, 4, 1, LORA, true>(args, stream);
+      case 192: return launch_typed<EPI, 192, 4, 1, LORA, true>(args, stream);
+      default: return launch_typed<EPI, 256, 2, 1, LORA, true>(args, stream);
+    }
   }
   switch (gemm_tile_n(args.m, args.n, false)) {
     case 320: return launch_typed<EPI, 320, 4, 1, LORA>(args, stream);

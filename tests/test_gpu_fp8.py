@@ -118,9 +118,10 @@ def abs_sum(a, b):
     return np.abs(oracle.e4m3_decode(a)) @ np.abs(oracle.e4m3_decode(b)).T + 1e-30
 
 
-# 4000 x 3840 selects 256-column tiles, the small grids 192-column tiles (256 CUs)
+# 4000 x 3840 selects 256-column tiles, 4000 x 5104 320-column tiles, the small
+# grids 192-column tiles (on 256 CUs)
 @pytest.mark.parametrize("m,n,k", [(64, 512, 512), (300, 640, 400), (1, 16, 16), (257, 272, 4096),
-                                   (40, 48, 144), (4000, 3840, 80)])
+                                   (40, 48, 144), (4000, 3840, 80), (4000, 5104, 80)])
 def test_fp8_gemm_within_accumulation_bound(m, n, k):
     rng = np.random.default_rng(m + n + k)
     a = rng.choice(FINITE_CODES, (m, k))
@@ -166,6 +167,14 @@ def test_fp8_forward_with_lora(g, rank, scale):
     err = rel_l2(y, ref["y"])
     say(f"    rel-L2 {err:.3e}")
     assert err < REL_L2
+
+
+@pytest.mark.parametrize("m,n", [(4000, 3840), (4000, 5104)])
+def test_fp8_forward_every_tile_width(m, n):
+    y, ref = forward8_case(m, 256, n, 256, seed=m + n)
+    assert rel_l2(y, ref["y"]) < REL_L2
+    y, ref = forward8_case(m, 256, n, 128, rank=32, seed=m + n + 1, scale=0.5)
+    assert rel_l2(y, ref["y"]) < REL_L2
 
 
 def test_fp8_forward_quantized_entry_matches_forward():
