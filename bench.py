@@ -110,8 +110,8 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     """Whole-call timings (HIP events on the launch stream) of the other steps of
     the layer, each on its own workload: weight preparation, the attention
     projection forward, the QuaRot-style forward with LoRA (g = 64 and 128), the
-    PEFT backward (input gradient + LoRA gradients) and the FP8 (E4M3) variant of
-    the MLP step."""
+    PEFT backward (input gradient + LoRA gradients), the full fine-tuning weight
+    gradient and the FP8 (E4M3) variant of the MLP step."""
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
 
@@ -166,6 +166,13 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     rows["peft_backward_16384x3072x3072_g256_r64"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
                                                       "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
                                                       "note": "dX through the int8 weight + LoRA dX, dA, dB"}
+    wws = torch.empty(h.sdnq_weight_grad_workspace_bytes(c.m, c.n, c.k), dtype=torch.uint8, device=dev)
+    dw = torch.empty((c.n, c.k), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda: h.sdnq_qlinear_weight_grad(dy, x, 256, out=dw, workspace=wws))
+    rows["weight_grad_16384x3072x3072_g256"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+                                                "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
+                                                "note": "dW = dY^T x, both quantized per feature along the tokens"}
+    del wws, dw
     del x, w, dy, la, lb, ws
     # FP8 variant of the MLP step (same workload, E4M3 codes, fp32 MFMA accumulation)
     inp = synth.make_config("mlp")

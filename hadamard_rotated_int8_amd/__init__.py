@@ -22,6 +22,8 @@ from ._binding import (  # noqa: F401
     sdnq_rotate_quantize_act_fp8,
     sdnq_rotate_quantize_weight,
     sdnq_rotate_quantize_weight_fp8,
+    sdnq_qlinear_weight_grad,
+    sdnq_weight_grad_workspace_bytes,
     sdnq_workspace_bytes,
     status_string,
 )

@@ -50,6 +50,7 @@ def lib() -> ctypes.CDLL:
         "sdnq_qlinear_forward_fp8": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p, sz, p],
         "sdnq_qlinear_forward_fp8_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
         "sdnq_gemm_fp8_f32": [p, p, i64, i64, i64, p, p],
+        "sdnq_qlinear_weight_grad": [p, p, i64, i64, i64, i32, p, p, sz, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.sdnq_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.sdnq_workspace_bytes.restype = sz
+    L.sdnq_weight_grad_workspace_bytes.argtypes = [i64, i64, i64]
+    L.sdnq_weight_grad_workspace_bytes.restype = sz
     L.sdnq_status_string.argtypes = [ctypes.c_int]
     L.sdnq_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -263,4 +266,23 @@ def sdnq_gemm_fp8_f32(a, b):
     c = torch.empty((m, n), dtype=torch.float32, device=a.device)
     _check(lib().sdnq_gemm_fp8_f32(_ptr(a), _ptr(b), m, n, k, _ptr(c), _stream(a.device)), "sdnq_gemm_fp8_f32")
     return c
+
+
+def sdnq_weight_grad_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().sdnq_weight_grad_workspace_bytes(m, n, k))
+
+
+def sdnq_qlinear_weight_grad(dy, x, g, out=None, workspace=None):
+    """dw [n, k] bf16 = dequant(Q_g(dy^T) . Q_g(x^T)^T): quantized along the tokens."""
+    _need(dy, torch.bfloat16, 2, "dy")
+    _need(x, torch.bfloat16, 2, "x")
+    m, n = dy.shape
+    if x.shape[0] != m:
+        raise ValueError("dy and x must have the same number of tokens")
+    k = x.shape[1]
+    dw = out if out is not None else torch.empty((n, k), dtype=torch.bfloat16, device=dy.device)
+    ws = _workspace(sdnq_weight_grad_workspace_bytes(m, n, k), dy.device, workspace)
+    _check(lib().sdnq_qlinear_weight_grad(_ptr(dy), _ptr(x), m, n, k, g, _ptr(dw), _ptr(ws), ws.numel(),
+                                          _stream(dy.device)), "sdnq_qlinear_weight_grad")
+    return dw
 

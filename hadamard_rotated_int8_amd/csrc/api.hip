@@ -64,6 +64,23 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   return L;
 }
 
+// Weight gradient: a bf16 transpose buffer (dy^T, then x^T) and the two quantized
+// transposed operands with their per-feature scales.
+struct WgradLayout {
+  size_t tbuf, qdy, sdy, qx, sx, total;
+};
+WgradLayout wgrad_layout(int64_t m, int64_t n, int64_t k) {
+  WgradLayout L{};
+  size_t off = 0;
+  L.tbuf = off; off += align_up((size_t)(n > k ? n : k) * (size_t)m * 2);
+  L.qdy = off; off += align_up((size_t)n * (size_t)m);
+  L.sdy = off; off += align_up((size_t)n * 4);
+  L.qx = off; off += align_up((size_t)k * (size_t)m);
+  L.sx = off; off += align_up((size_t)k * 4);
+  L.total = off;
+  return L;
+}
+
 char *ws_at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 sdnq_status_t launched(hipError_t e) { return e == hipSuccess ? SDNQ_OK : SDNQ_ERR_LAUNCH; }
@@ -317,6 +334,45 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
   GemmArgs ga{};
   ga.a = a; ga.b = bb; ga.m = m; ga.n = n; ga.k = k; ga.c_i32 = c; ga.g = 1;
   return launched(launch_gemm_i8(Epilogue::kInt32, ga, s));
+}
+
+// ----------------------------------------------------- weight gradient --
+size_t sdnq_weight_grad_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n <= 0 || k <= 0) return 0;
+  return wgrad_layout(m, n, k).total;
+}
+
+sdnq_status_t sdnq_qlinear_weight_grad(const uint16_t *dy, const uint16_t *x, int64_t m, int64_t n, int64_t k,
+                                       int32_t g, uint16_t *dw, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+  if (!dw || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!dy || !x)) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_feature(k));
+  if (!valid_group(g)) return SDNQ_ERR_UNSUPPORTED;
+  if (m > 0) {
+    SDNQ_TRY(check_feature(m));  // the tokens are the contraction here
+    if (m % g != 0) return SDNQ_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(dw)) return SDNQ_ERR_INVALID_ARG;
+  const WgradLayout L = wgrad_layout(m, n, k);
+  if (m > 0 && (!workspace || workspace_bytes < L.total || !aligned16(workspace))) return SDNQ_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (m == 0) return launched(launch_fill_zero_u16(dw, n * k, s));  // empty sum
+  uint16_t *tbuf = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tbuf));
+  int8_t *qdy = reinterpret_cast<int8_t *>(ws_at(workspace, L.qdy));
+  float *sdy = reinterpret_cast<float *>(ws_at(workspace, L.sdy));
+  int8_t *qx = reinterpret_cast<int8_t *>(ws_at(workspace, L.qx));
+  float *sx = reinterpret_cast<float *>(ws_at(workspace, L.sx));
+  SDNQ_LAUNCH(launch_transpose_u16(dy, m, n, tbuf, s));                   // dy^T [n, m]
+  SDNQ_LAUNCH(launch_rotate_quantize(tbuf, n, m, g, nullptr, qdy, sdy, s));  // per feature, along tokens
+  SDNQ_LAUNCH(launch_transpose_u16(x, m, k, tbuf, s));                    // x^T [k, m]
+  SDNQ_LAUNCH(launch_rotate_quantize(tbuf, k, m, g, nullptr, qx, sx, s));
+  GemmArgs ga{};
+  ga.a = qdy; ga.b = qx; ga.m = n; ga.n = k; ga.k = m;
+  ga.row_scale = sdy; ga.col_scale = sx; ga.out_bf16 = dw; ga.g = 1;
+  return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
 
 // ---------------------------------------------------------------- FP8 --

@@ -263,6 +263,49 @@ __global__ void fill_zero_u16_kernel(uint16_t *__restrict__ out, int64_t count) 
 }
 
 // ---------------------------------------------------------- transposes --
+// bf16 transpose of a rows x cols matrix whose sides are multiples of 8, in
+// 64 x 64 tiles: 16-byte row chunks in, LDS with an 8-byte row pad, 16-byte
+// column chunks (gathered 2 bytes at a time from LDS) out.
+constexpr int kT16 = 64;
+constexpr int kT16Pitch = kT16 + 4;  // in uint16
+
+__global__ __launch_bounds__(256) void transpose_u16_kernel(const uint16_t *__restrict__ in, int64_t rows,
+                                                            int64_t cols, uint16_t *__restrict__ out) {
+  __shared__ __align__(16) uint16_t tile[kT16 * kT16Pitch];
+  const int64_t r0 = (int64_t)blockIdx.y * kT16, c0 = (int64_t)blockIdx.x * kT16;
+  const int tid = threadIdx.x;
+  v4u v[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // item = (row, chunk of 8 columns)
+    const int item = tid + 256 * i, r = item >> 3, ch = item & 7;
+    const bool ok = r0 + r < rows && c0 + 8 * ch < cols;
+    v[i] = ok ? *reinterpret_cast<const v4u *>(in + (r0 + r) * cols + c0 + 8 * ch) : v4u{};
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int item = tid + 256 * i, r = item >> 3, ch = item & 7;
+    uint32_t *d = reinterpret_cast<uint32_t *>(tile + r * kT16Pitch + 8 * ch);
+    d[0] = v[i][0];
+    d[1] = v[i][1];
+    d[2] = v[i][2];
+    d[3] = v[i][3];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // item = (output row = input column c, chunk of 8 input rows)
+    const int item = tid + 256 * i, c = item >> 3, ch = item & 7;
+    if (c0 + c < cols && r0 + 8 * ch < rows) {
+      v4u o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint16_t *src = tile + (8 * ch + 2 * w) * kT16Pitch + c;
+        o[w] = (uint32_t)src[0] | ((uint32_t)src[kT16Pitch] << 16);
+      }
+      *reinterpret_cast<v4u *>(out + (c0 + c) * rows + r0 + 8 * ch) = o;
+    }
+  }
+}
+
 template <typename T, int TILE>
 __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in, int64_t rows, int64_t cols,
                                                         T *__restrict__ out) {
@@ -411,6 +454,11 @@ hipError_t launch_transpose_i8(const int8_t *in, int64_t rows, int64_t cols, int
 }
 
 hipError_t launch_transpose_u16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream) {
+  if (rows % 8 == 0 && cols % 8 == 0) {
+    const dim3 grid((unsigned)((cols + kT16 - 1) / kT16), (unsigned)((rows + kT16 - 1) / kT16));
+    hipLaunchKernelGGL(transpose_u16_kernel, grid, dim3(256), 0, stream, in, rows, cols, out);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
   hipLaunchKernelGGL((transpose_kernel<uint16_t, 32>), grid, dim3(256), 0, stream, in, rows, cols, out);
   return hipGetLastError();

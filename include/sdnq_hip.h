@@ -145,6 +145,25 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
                                int32_t b_layout, int32_t *c, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Weight gradient through the quantized matmul (full fine-tuning: "SDNQ: SD.Next
+ * Quantization Engine", the training example runs the quantized matmul in the
+ * backward pass and the feature list includes full-parameter quantized training):
+ *   dw[n,k] = bf16( fp32(q_dy . q_x^T) * s_dy[n] * s_x[k] )
+ * where the contraction runs over the m tokens, so both operands are quantized
+ * along the tokens: (q_dy, s_dy) = sdnq_rotate_quantize_act applied to the rows of
+ * dy^T [n,m] and (q_x, s_x) to the rows of x^T [k,m], each rotated with block g
+ * along the tokens (the rotation is orthogonal along the contracted axis, so it
+ * cancels in the product) and quantized with one scale per feature.
+ * dy[m,n], x[m,k] bf16 (the layer's output gradient and input); dw[n,k] bf16.
+ * m is a contraction length here: a multiple of 16, at most 65536, m % g == 0;
+ * m == 0 writes zeros.  workspace: sdnq_weight_grad_workspace_bytes(m, n, k). */
+sdnq_status_t sdnq_qlinear_weight_grad(const uint16_t *dy, const uint16_t *x, int64_t m, int64_t n, int64_t k,
+                                       int32_t g, uint16_t *dw, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+/* Workspace size in bytes for sdnq_qlinear_weight_grad; 0 on invalid sizes. */
+size_t sdnq_weight_grad_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
 /* ---------------------------------------------------------------- FP8 ------
  * The FP8 variant of the quantized matmul ("SDNQ: SD.Next Quantization Engine":
  * INT8 and FP8 quantized matmul; the SDNQConfig example's matmul dtype

@@ -306,3 +306,21 @@ def qlinear_forward_fp8(x: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
     _check(rc, "qlinear_forward_fp8")
     return out
 
+
+# -------------------------------------------------------- weight gradient --
+
+def qlinear_weight_grad(dy: np.ndarray, x: np.ndarray, g: int, intermediates: bool = False) -> dict:
+    """Weight gradient through the quantized matmul, contracting over the tokens:
+    q_dy, s_dy = rotate (block g along the tokens) + per-feature quantization of
+    the rows of dy^T [n, m]; q_x, s_x likewise for x^T [k, m]; then
+    dw[n, k] = bf16(fl32(fl32(sum_t q_dy q_x) * fl32(s_dy[n] * s_x[k]))), i.e. the
+    forward's steps with dy^T as the activations and x^T as the weight."""
+    dyt = np.ascontiguousarray(_c(dy, np.uint16).T)
+    xt = np.ascontiguousarray(_c(x, np.uint16).T)
+    qx, sx = rotate_quantize(xt, g)
+    out = qlinear_forward(dyt, qx, sx, g, intermediates=intermediates)
+    res = {"dw": out["y"]}
+    if intermediates:
+        res.update(q_dy=out["qx"], s_dy=out["sx"], q_x=qx, s_x=sx, acc=out["acc"])
+    return res
+

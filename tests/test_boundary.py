@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "sdnq_qlinear_backward_input", "sdnq_qlinear_forward_quantized", "sdnq_workspace_bytes",
               "sdnq_status_string", "sdnq_gemm_i8_i32", "sdnq_rotate_quantize_weight_fp8",
               "sdnq_rotate_quantize_act_fp8", "sdnq_qlinear_forward_fp8", "sdnq_qlinear_forward_fp8_quantized",
-              "sdnq_gemm_fp8_f32"):
+              "sdnq_gemm_fp8_f32", "sdnq_qlinear_weight_grad", "sdnq_weight_grad_workspace_bytes"):
         assert n in names
 
 
@@ -190,4 +190,18 @@ def test_fp8_entry_points_validate_like_the_int8_ones():
     assert L.sdnq_gemm_fp8_f32(A, B, 4, 30, 32, C, None) == UNSUPPORTED
     assert L.sdnq_gemm_fp8_f32(None, B, 4, 32, 32, C, None) == INVALID
     assert L.sdnq_gemm_fp8_f32(A, B, 0, 32, 32, C, None) == OK
+
+
+@no_gpu
+def test_weight_grad_validation():
+    L = h.lib()
+    f = lambda m=64, n=256, k=256, g=64, dy=A, x=B, dw=D, ws=W, wsb=WS: L.sdnq_qlinear_weight_grad(
+        dy, x, m, n, k, g, dw, ws, wsb, None)
+    assert f(m=-1) == INVALID and f(dw=None) == INVALID and f(dy=None) == INVALID
+    assert f(m=40) == UNSUPPORTED          # tokens are the contraction: a multiple of 16 ...
+    assert f(m=96, g=64) == UNSUPPORTED    # ... and of g
+    assert f(n=100) == UNSUPPORTED and f(g=3) == UNSUPPORTED
+    assert f(ws=None) == WORKSPACE and f(wsb=100) == WORKSPACE
+    assert f(m=64, g=64, wsb=h.sdnq_weight_grad_workspace_bytes(64, 256, 256) - 1) == WORKSPACE
+    assert h.sdnq_weight_grad_workspace_bytes(16384, 3072, 3072) >= 16384 * 3072 * 4
 

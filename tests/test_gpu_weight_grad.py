@@ -1,0 +1,88 @@
+"""GPU parity of the weight gradient through the quantized matmul (full
+fine-tuning), through the C ABI, against the CPU oracle: bf16 transposes, the
+per-feature rotate+quantize along the tokens and the exact int32 GEMM with the
+fp32 dequantization are all deterministic, so dW is compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_int8_amd as h
+import oracle
+from hadamard_rotated_int8_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def d_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def h_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    h.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def inputs(m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    dy = synth.to_bf16_bits((rng.standard_normal((m, n)) * 1e-3).astype(np.float32))
+    x = synth.to_bf16_bits(synth.outlier_activations(rng, m, k))
+    return dy, x
+
+
+@pytest.mark.parametrize("g", [1, 64, 128, 256])
+@pytest.mark.parametrize("m,n,k", [(512, 256, 256), (768, 272, 400), (256, 16, 48), (1280, 640, 3072)])
+def test_weight_grad_bit_exact(m, n, k, g):
+    if m % g:
+        pytest.skip("m must be a multiple of g")
+    dy, x = inputs(m, n, k, m + n + k + g)
+    say(f"  weight_grad m={m} n={n} k={k} g={g}")
+    dw = h.sdnq_qlinear_weight_grad(d_bf16(dy), d_bf16(x), g)
+    torch.cuda.synchronize()
+    ref = oracle.qlinear_weight_grad(dy, x, g)["dw"]
+    got = h_bits(dw)
+    assert np.array_equal(got, ref), f"{np.mean(got != ref):.4f} of the outputs differ"
+
+
+def test_weight_grad_empty_batch_is_zero():
+    dy = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((0, 32), dtype=torch.bfloat16, device=DEV)
+    dw = h.sdnq_qlinear_weight_grad(dy, x, 256, out=torch.full((64, 32), 7.0, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw).item() == 0
+
+
+def test_weight_grad_peft_size_sampled_rows():
+    """16384 tokens, 3072 x 3072: all of x's codes and scales, and sampled rows of dW."""
+    c = synth.CONFIGS["peft"]
+    inp = synth.make_config("peft")
+    m, n, k = c.m, c.n, c.k
+    say(f"  weight_grad m={m} n={n} k={k} g=256")
+    ws = torch.empty(h.sdnq_weight_grad_workspace_bytes(m, n, k), dtype=torch.uint8, device=DEV)
+    dw = h.sdnq_qlinear_weight_grad(d_bf16(inp["dy"]), d_bf16(inp["x"]), 256, workspace=ws)
+    torch.cuda.synchronize()
+    oracle.set_num_threads(16)
+    xt = np.ascontiguousarray(inp["x"].T)
+    qx, sx = oracle.rotate_quantize(xt, 256)
+    # the workspace holds q_x [k, m] and s_x [k] after the bf16 transpose buffer and q_dy, s_dy
+    al = lambda v: (v + 255) // 256 * 256
+    off = al(max(n, k) * m * 2) + al(n * m) + al(n * 4)
+    assert np.array_equal(ws[off: off + k * m].view(k, m).cpu().numpy().view(np.int8), qx)
+    sx_gpu = ws[off + al(k * m): off + al(k * m) + 4 * k].cpu().numpy().view(np.float32)
+    assert np.array_equal(sx_gpu.view(np.uint32), sx.view(np.uint32))
+    rows = np.array([0, 1, 1000, 2047, 3071])
+    dyt = np.ascontiguousarray(inp["dy"].T)[rows]
+    ref = oracle.qlinear_forward(dyt, qx, sx, 256, intermediates=False)["y"]
+    assert np.array_equal(h_bits(dw)[rows], ref)

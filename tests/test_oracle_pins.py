@@ -587,3 +587,49 @@ def test_fp8_forward_dequant_and_lora_terms():
     wf = synth.bf16_bits_to_f32(inp["w"]).astype(np.float64)
     exact = synth.bf16_bits_to_f32(inp["x"]).astype(np.float64) @ wf.T
     assert np.linalg.norm(base - exact) / np.linalg.norm(exact) < 0.06
+
+
+# ----------------------------------------------------------- weight gradient --
+# Full fine-tuning through the quantized matmul ("SDNQ: SD.Next Quantization
+# Engine": quantized matmul in the backward pass, full-parameter quantized
+# training): dW = dY^T x contracts over the tokens, so both operands are
+# quantized per feature along the tokens, rotated with block g along the tokens.
+
+def _wgrad_inputs(m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    dy = bf(rng.standard_normal((m, n)) * 1e-3)
+    x = bf(synth.outlier_activations(rng, m, k, channels=(3, k - 5)))
+    return dy, x
+
+
+@pytest.mark.parametrize("g", [1, 64, 256])
+def test_weight_grad_approximates_the_exact_product(g):
+    dy, x = _wgrad_inputs(512, 48, 80, 21 + g)
+    out = oracle.qlinear_weight_grad(dy, x, g)
+    exact = synth.bf16_bits_to_f32(dy).astype(np.float64).T @ synth.bf16_bits_to_f32(x).astype(np.float64)
+    got = synth.bf16_bits_to_f32(out["dw"]).astype(np.float64)
+    assert np.linalg.norm(got - exact) / np.linalg.norm(exact) < 0.03
+
+
+def test_weight_grad_rotation_along_tokens_cancels():
+    """(dY^T H)(x^T H)^T = dY^T x: the unquantized rotated operands give the exact
+    product up to binary32 rounding."""
+    dy, x = _wgrad_inputs(256, 32, 48, 5)
+    ry = oracle.rotate(np.ascontiguousarray(dy.T), 256).astype(np.float64)
+    rx = oracle.rotate(np.ascontiguousarray(x.T), 256).astype(np.float64)
+    exact = synth.bf16_bits_to_f32(dy).astype(np.float64).T @ synth.bf16_bits_to_f32(x).astype(np.float64)
+    assert np.abs(ry @ rx.T - exact).max() <= 1e-5 * np.abs(exact).max()
+
+
+def test_weight_grad_brute_force_on_codes():
+    """Python loops over the per-feature codes of the transposed operands."""
+    dy, x = _wgrad_inputs(64, 5, 6, 9)
+    out = oracle.qlinear_weight_grad(dy, x, 64, intermediates=True)
+    qd, sd = oracle.rotate_quantize(np.ascontiguousarray(dy.T), 64)
+    qx, sx = oracle.rotate_quantize(np.ascontiguousarray(x.T), 64)
+    assert np.array_equal(out["q_dy"], qd) and np.array_equal(out["q_x"], qx)
+    for i in range(5):
+        for j in range(6):
+            acc = sum(int(qd[i, t]) * int(qx[j, t]) for t in range(64))
+            v = np.float32(np.float32(acc) * np.float32(sd[i] * sx[j]))
+            assert out["dw"][i, j] == oracle.bf16_from_f64(np.array([float(v)]))[0]
