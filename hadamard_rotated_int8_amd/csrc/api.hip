@@ -3,9 +3,25 @@
 // call that fails writes nothing.  See sdnq_hip.h for the contract.
 #include <string.h>
 
+#include <atomic>
+
 #include "sdnq_internal.hpp"
 
 using namespace sdnq;
+
+namespace sdnq {
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace sdnq
 
 namespace {
 

@@ -582,19 +582,6 @@ hipError_t launch_backward(const GemmArgs &args, hipStream_t stream) {
                        : launch_typed<Epilogue::kBackward, 256, 8, G, false>(args, stream);
 }
 
-int gemm_cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
-                                                hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
-
 // Output tile width along N for the forward and int32 epilogues.  One workgroup
 // fills a compute unit, so a launch runs in ceil(tiles / CUs) rounds, each as
 // long as one tile (proportional to its width).  The width with the fewest
@@ -603,7 +590,7 @@ int gemm_cu_count() {
 // of 256 x 192 instead of 0.75 of 256 x 256.
 // (FP8 keeps two fragment sets of both halves live, which 320 columns do not fit.)
 int gemm_tile_n(int64_t m, int64_t n, bool fp8) {
-  const int64_t cus = gemm_cu_count();
+  const int64_t cus = device_cu_count();
   const int64_t tiles_m = (m + BM - 1) / BM;
   auto cost = [&](int bn) { return (tiles_m * ((n + bn - 1) / bn) + cus - 1) / cus * bn; };
   int best = 256;

@@ -33,6 +33,8 @@
 // fma(partner, -1, self) = self - partner = -(a - b), which rounds exactly like
 // a - b up to the sign; the sign of every lane is (-1)^popcount(l4) after both
 // stages and is folded into the normalization multiply.
+#include <atomic>
+
 #include "sdnq_internal.hpp"
 
 namespace sdnq {
@@ -329,34 +331,21 @@ int pick_rows_per_wg(int t_row, int max_threads) {
   return best_r;
 }
 
-// Resident workgroups per CU for a kernel at a block size (cached; the launch
-// configuration only depends on the kernel and the block size).
+// Resident workgroups per CU for a kernel at a block size, cached per block size
+// (one atomic word holding both, so concurrent callers read a consistent pair).
 template <int G, bool CS, int MAXT, bool FP8>
 int blocks_per_cu(int threads) {
-  static int cached_threads[kMaxThreads / 4 + 1];
-  static int cached_blocks[kMaxThreads / 4 + 1];
-  const int slot = threads / 4;
-  if (cached_threads[slot] == threads) return cached_blocks[slot];
+  static std::atomic<uint64_t> cache[kMaxThreads / 4 + 1];
+  std::atomic<uint64_t> &slot = cache[threads / 4];
+  const uint64_t c = slot.load(std::memory_order_relaxed);
+  if ((int)(c >> 32) == threads) return (int)(c & 0xffffffffu);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8>, threads, 0) !=
           hipSuccess ||
       n < 1)
     n = 1;
-  cached_blocks[slot] = n;
-  cached_threads[slot] = threads;
+  slot.store(((uint64_t)(uint32_t)threads << 32) | (uint32_t)n, std::memory_order_relaxed);
   return n;
-}
-
-int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 template <int G, bool CS, int MAXT, bool FP8>
@@ -364,7 +353,7 @@ hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const flo
                         float *scale, int t_row, int rpw, hipStream_t stream) {
   const int threads = rpw * t_row;
   const int64_t groups = (rows + rpw - 1) / rpw;
-  int64_t blocks = (int64_t)cu_count() * blocks_per_cu<G, CS, MAXT, FP8>(threads);
+  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8>(threads);
   if (blocks > groups) blocks = groups;
   hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8>), dim3((unsigned)blocks), dim3(threads), 0, stream, x, rows,
                      cols, col_scale, q, scale, t_row, rpw, groups);

@@ -32,6 +32,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ------------------------------------------------------------------ launches --
 // Each returns hipSuccess or the launch error; arguments are validated by the caller.
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
 // G1: rotate (block g) + per-row absmax int8 quantization of a bf16 [rows, cols] matrix.
 hipError_t launch_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
                                   const float *col_scale, int8_t *q, float *scale,
