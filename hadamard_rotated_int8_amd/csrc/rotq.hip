@@ -311,9 +311,21 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
   }
 }
 
-// Rows per workgroup: the count with the fewest idle lanes in the last wavefront,
-// then the one closest to 256 threads.
+// Rows per workgroup.  Smaller workgroups wait on fewer wavefronts at the per-group
+// barrier, which measured faster even with some idle lanes: a [4096, 10240] matrix
+// (160 lanes per row) took 24.7 us at one row per workgroup (three wavefronts, a
+// sixth of the lanes idle) against 30.5 us at two rows (five full wavefronts).  So
+// the fewest wavefronts that hold whole rows (as many as fit) with at most a fifth
+// of the lanes idle; failing that, the count with the fewest idle lanes, then the
+// one closest to 256 threads.
 int pick_rows_per_wg(int t_row, int max_threads) {
+  for (int waves = 1; 64 * waves <= max_threads; ++waves) {
+    int r = 64 * waves / t_row;
+    if (r > kMaxRowsPerWg) r = kMaxRowsPerWg;
+    if (r < 1) continue;
+    const int threads = r * t_row;
+    if (5 * (64 * waves - threads) <= 64 * waves) return r;
+  }
   int best_r = 1;
   double best_waste = 2.0;
   int best_dist = 1 << 30;
