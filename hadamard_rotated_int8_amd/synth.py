@@ -56,6 +56,25 @@ def outlier_activations(rng: np.random.Generator, m: int, k: int, channels=None,
     return x
 
 
+def planted_lowrank_weight(rng: np.random.Generator, n: int, k: int, std: float = 0.02, planted: int = 16,
+                           lead: float = 4.0, decay: float = 0.7) -> np.ndarray:
+    """W [n, k] (binary32) = N(0, std) plus a planted part sum_i s_i u_i v_i^T with
+    u_i ~ N(0, 1/n) [n], v_i ~ N(0, 1/k) [k] (nearly unit, nearly orthogonal) and
+    s_i = lead * std * (sqrt(n) + sqrt(k)) * decay^i: a few singular directions well
+    above the noise's edge, std * (sqrt(n) + sqrt(k)), then decaying into it.
+    Drawn in the order noise, u, v."""
+    w = gaussian(rng, (n, k), std)
+    u = rng.standard_normal((n, planted), dtype=np.float32) / np.float32(np.sqrt(n))
+    v = rng.standard_normal((k, planted), dtype=np.float32) / np.float32(np.sqrt(k))
+    s = (lead * std * (np.sqrt(n) + np.sqrt(k)) * decay ** np.arange(planted)).astype(np.float32)
+    return w + (u * s) @ v.T
+
+
+def gaussian_test_matrix(rng: np.random.Generator, k: int, rank: int) -> np.ndarray:
+    """The random test matrix of the low-rank split: N(0, 1) [k, rank], binary32."""
+    return rng.standard_normal((k, rank), dtype=np.float32)
+
+
 @dataclass(frozen=True)
 class LinearConfig:
     """One workload: activation rows m, in-features k, out-features n."""
@@ -89,6 +108,9 @@ CONFIGS = {
                            note="QuaRot-style blocks + LoRA r=32: x [8192,3072], W [3072,3072]"),
     "peft": LinearConfig("peft", 16384, 3072, 3072, lora_rank=64, lora_alpha=32.0, backward=True,
                          note="PEFT step: x, dY [16384,3072], W [3072,3072], LoRA r=64"),
+    "svd": LinearConfig("svd", 4096, 3072, 3072, extra={"rank": 32, "steps": 8},
+                        note="low-rank split r=32, 8 steps (the SDNQConfig defaults) on the attention "
+                             "shape: x [4096,3072]; W [3072,3072] N(0,0.02) + 16 planted directions"),
 }
 
 
@@ -121,5 +143,12 @@ def make_config(name: str, seed: int = 0) -> dict:
         if name == "mlp_down":
             return {"x": h, "w": w_down}
         return {"x": x, "w_up": w_up, "h": h, "w_down": w_down}
+    if name == "svd":
+        c = CONFIGS["svd"]
+        rng = np.random.default_rng(seed)
+        x = to_bf16_bits(outlier_activations(rng, c.m, c.k))
+        w = to_bf16_bits(planted_lowrank_weight(rng, c.n, c.k))
+        omega = gaussian_test_matrix(rng, c.k, c.extra["rank"])
+        return {"x": x, "w": w, "omega": omega}
     c = CONFIGS[name]
     return make_linear(c.m, c.k, c.n, seed, c.outlier_channels, c.lora_rank, c.backward)

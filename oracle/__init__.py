@@ -68,6 +68,7 @@ def _load():
     lib.oracle_f32_from_bf16.argtypes = [p, i64, p]
     lib.oracle_rotate.argtypes = [p, i64, i64, i32, p, p]
     lib.oracle_rotate_quantize.argtypes = [p, i64, i64, i32, p, p, p]
+    lib.oracle_rotate_quantize_f32.argtypes = [p, i64, i64, i32, p, p]
     lib.oracle_gemm_i8.argtypes = [p, p, i64, i64, i64, i32, p]
     lib.oracle_qlinear_forward.argtypes = [p, i64, i64, p, p, i64, i32, p, p, i32, ctypes.c_double,
                                            p, p, p, p, p]
@@ -79,7 +80,7 @@ def _load():
     lib.oracle_gemm_fp8.argtypes = [p, p, i64, i64, i64, p]
     lib.oracle_qlinear_forward_fp8.argtypes = [p, i64, i64, p, p, i64, i32, p, p, i32, ctypes.c_double,
                                                p, p, p, p, p]
-    for name in ("oracle_fwht_unnormalized", "oracle_rotate", "oracle_rotate_quantize",
+    for name in ("oracle_fwht_unnormalized", "oracle_rotate", "oracle_rotate_quantize", "oracle_rotate_quantize_f32",
                  "oracle_gemm_i8", "oracle_qlinear_forward", "oracle_qlinear_backward_input",
                  "oracle_rotate_quantize_fp8", "oracle_gemm_fp8", "oracle_qlinear_forward_fp8"):
         getattr(lib, name).restype = i32
@@ -157,6 +158,17 @@ def rotate_quantize(x_bf16: np.ndarray, g: int, col_scale: np.ndarray | None = N
     s = np.empty((rows,), np.float32)
     _check(_load().oracle_rotate_quantize(_ptr(x), rows, cols, g, _ptr(cs), _ptr(q), _ptr(s)),
            "rotate_quantize")
+    return q, s
+
+
+def rotate_quantize_f32(x_f32: np.ndarray, g: int):
+    """Rotate then quantize rows given as binary32 values (no bf16 decode, no column
+    scale): returns (codes int8 [rows, cols], scales f32 [rows])."""
+    x = _c(x_f32, np.float32)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows,), np.float32)
+    _check(_load().oracle_rotate_quantize_f32(_ptr(x), rows, cols, g, _ptr(q), _ptr(s)), "rotate_quantize_f32")
     return q, s
 
 
@@ -324,3 +336,58 @@ def qlinear_weight_grad(dy: np.ndarray, x: np.ndarray, g: int, intermediates: bo
         res.update(q_dy=out["qx"], s_dy=out["sx"], q_x=qx, s_x=sx, acc=out["acc"])
     return res
 
+
+
+# ------------------------------------------------------ low-rank (SVD) split --
+#
+# "SDNQ: SD.Next Quantization Engine" lists SVD quantization next to the Hadamard
+# rotation for quantized weights and the quantized matmul, and its SDNQConfig
+# example carries use_svd, svd_rank=32 and svd_steps=8.  The SD.Next dev commit
+# log ("automatic/commits/branch/dev/cli") calls the factorization a seeded SVD
+# truncation and notes that a weight quantized with it dequantizes off the plain
+# integer grid: the stored weight is integer codes plus low-rank factors.  The
+# pages do not print the algorithm; the reading taken here is the randomized
+# range finder with subspace iteration (Halko, Martinsson and Tropp, 2011,
+# algorithms 4.1 and 4.4):
+#   Q = orth(W omega)                        omega [K, r] Gaussian, seeded, an input
+#   repeat svd_steps times: Z = orth(W^T Q); Q = orth(W Z)
+#   low-rank part L = Q (Q^T W);  factors svd_a = W^T Q [K, r], svd_b = Q^T [r, N]
+#   both rounded to bf16; residual R = fl32(W - svd_b^T svd_a^T) with the rounded
+#   factors (the quantizer sees exactly what the factors leave out)
+#   the residual is rotated and quantized like any weight (rotate_quantize_f32)
+#   at run time y = dequant(q(xH) q(RH)^T) + (x svd_a) svd_b: the LoRA side term
+#   with scale 1 on the unrotated x.
+# orth() is a reduced QR (numpy's Householder QR): only the span of Q matters,
+# so any orthonormal basis of the same span gives the same L.
+
+def _orth(y: np.ndarray) -> np.ndarray:
+    q, _ = np.linalg.qr(y, mode="reduced")
+    return q
+
+
+def svd_lowrank_split(w_bf16: np.ndarray, omega: np.ndarray, steps: int) -> dict:
+    """Low-rank split of a bf16 weight [N, K] with rank r = omega.shape[1] and
+    `steps` subspace iterations, in fp64.  Returns q [N, r] (fp64, orthonormal),
+    svd_a [K, r] and svd_b [r, N] (bf16 bits) and the residual [N, K] (binary32)."""
+    w = f32_from_bf16(w_bf16).astype(np.float64)
+    om = np.asarray(omega, np.float64)
+    if om.ndim != 2 or om.shape[0] != w.shape[1] or not 1 <= om.shape[1] <= min(w.shape):
+        raise ValueError("omega must be [K, r] with 1 <= r <= min(N, K)")
+    if steps < 0:
+        raise ValueError("steps must be >= 0")
+    q = _orth(w @ om)
+    for _ in range(steps):
+        z = _orth(w.T @ q)
+        q = _orth(w @ z)
+    a_bits = bf16_from_f64(w.T @ q)
+    b_bits = bf16_from_f64(np.ascontiguousarray(q.T))
+    lr = f32_from_bf16(b_bits).astype(np.float64).T @ f32_from_bf16(a_bits).astype(np.float64).T
+    return {"q": q, "svd_a": a_bits, "svd_b": b_bits, "residual": (w - lr).astype(np.float32)}
+
+
+def svd_quantize_weight(w_bf16: np.ndarray, g: int, omega: np.ndarray, steps: int) -> dict:
+    """Low-rank split, then rotate + row-wise int8 quantization of the residual.
+    Returns the split's fields plus qw [N, K] int8 and sw [N] f32."""
+    out = svd_lowrank_split(w_bf16, omega, steps)
+    out["qw"], out["sw"] = rotate_quantize_f32(out["residual"], g)
+    return out

@@ -310,6 +310,41 @@ int oracle_rotate_quantize(const uint16_t *x, int64_t rows, int64_t cols, int g,
     return err;
 }
 
+/* Rotate, then quantize rows given as binary32 values: the same steps as
+ * oracle_rotate_quantize without the bf16 decode (and with no column scale).
+ * The low-rank split forms its residual weight in binary32 and quantizes it
+ * through this path. */
+int oracle_rotate_quantize_f32(const float *x, int64_t rows, int64_t cols, int g, int8_t *q, float *s)
+{
+    if (!x || !q || !s || rows < 0 || cols < 0 || !is_pow2_upto256(g) || cols % g != 0)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel
+    {
+        float *y = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+        if (!y) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ARG;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < rows; m++) {
+                for (int64_t i = 0; i < cols; i++)
+                    y[i] = x[m * cols + i];
+                if (g > 1) {
+                    float c = norm_const(g);
+                    for (int64_t b = 0; b < cols; b += g)
+                        fwht_block(y + b, g);
+                    for (int64_t i = 0; i < cols; i++)
+                        y[i] = y[i] * c;
+                }
+                quantize_row(y, cols, q + m * cols, s + m);
+            }
+            free(y);
+        }
+    }
+    return err;
+}
+
 /* Integer matmul with exact int64 accumulation, stored as int32.
  *   b_layout 0: a[m,k], b[n,k]  ->  c[i,j] = sum_t a[i,t] * b[j,t]
  *   b_layout 1: a[m,k], b[k,n]  ->  c[i,j] = sum_t a[i,t] * b[t,j]

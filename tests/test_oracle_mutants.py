@@ -45,6 +45,21 @@ MUTANTS = {
                                 "float up = 1.0f;\n    float as = a * up;\n    float r = (as > 0.0f) ? 448.0f / as : 0.0f;"),
     "fp8_weight_index": ("acc += dq[kk] * e4m3_decode(wr[kk]);", "acc += dq[kk] * e4m3_decode(wr[(kk + 1) % k]);"),
     "fp8_signed_zero": ("float t = (y[i] * up) * r + 0.0f;", "float t = (y[i] * up) * r;"),
+    "f32_input_no_normalization": ("                    for (int64_t i = 0; i < cols; i++)\n                        y[i] = y[i] * c;",
+                                   "                    for (int64_t i = 0; i < cols; i++)\n                        y[i] = y[i];"),
+}
+
+# Mistakes planted in the Python part of the oracle (the low-rank split).
+PY_MUTANTS = {
+    "svd_no_subspace_iteration": ("    for _ in range(steps):", "    for _ in range(0):"),
+    "svd_residual_against_unrounded_factors": (
+        "    lr = f32_from_bf16(b_bits).astype(np.float64).T @ f32_from_bf16(a_bits).astype(np.float64).T",
+        "    lr = q @ (q.T @ w)"),
+    "svd_residual_sign": ('"residual": (w - lr).astype(np.float32)', '"residual": (lr - w).astype(np.float32)'),
+    "svd_one_sided_iteration": ("        z = _orth(w.T @ q)\n        q = _orth(w @ z)",
+                                "        z = _orth(w.T @ q)\n        q = _orth(w @ om)"),
+    "svd_factor_b_not_orthonormal": ("    b_bits = bf16_from_f64(np.ascontiguousarray(q.T))",
+                                     "    b_bits = bf16_from_f64(np.ascontiguousarray((w @ om).T))"),
 }
 
 
@@ -61,6 +76,32 @@ def _run(name, tmp):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode
+
+
+def _run_py(name, tmp):
+    """Copy the oracle package with one planted mistake in its Python source and run
+    the pins against the copy (it loads the unmodified C library)."""
+    old, new = PY_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert src.count(old) == 1, name
+    pkg = os.path.join(tmp, name, "oracle")
+    os.makedirs(pkg)
+    with open(os.path.join(pkg, "__init__.py"), "w") as f:
+        f.write(src.replace(old, new, 1))
+    env = dict(os.environ, SDNQ_ORACLE_LIB=oracle.build(force=False), OMP_NUM_THREADS="1",
+               PYTHONPATH=os.pathsep.join([os.path.join(tmp, name), ROOT]))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=os.path.join(tmp, name), env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+@pytest.mark.slow
+def test_every_planted_python_mistake_is_caught(tmp_path):
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = dict(ex.map(lambda n: _run_py(n, str(tmp_path)), sorted(PY_MUTANTS)))
+    survivors = [n for n, rc in results.items() if rc == 0]
+    assert not survivors, f"pins did not catch: {survivors}"
 
 
 @pytest.mark.slow

@@ -633,3 +633,145 @@ def test_weight_grad_brute_force_on_codes():
             acc = sum(int(qd[i, t]) * int(qx[j, t]) for t in range(64))
             v = np.float32(np.float32(acc) * np.float32(sd[i] * sx[j]))
             assert out["dw"][i, j] == oracle.bf16_from_f64(np.array([float(v)]))[0]
+
+
+# ------------------------------------------------------ low-rank (SVD) split --
+# Reading: randomized range finder with subspace iteration (Halko, Martinsson and
+# Tropp 2011); factors bf16(W^T Q) [K, r] and bf16(Q^T) [r, N]; residual in
+# binary32 against the rounded factors, then rotate + quantize.
+
+def _exact_rank4_weight(n=96, k=128, seed=3):
+    """W = U V^T with U, V entries in {-1, 0, 1} / 8: every entry is a multiple of
+    2^-6 no larger than 4 * 2^-6, so W is exactly representable in bf16 and has
+    rank 4 (checked)."""
+    rng = np.random.default_rng(seed)
+    u = rng.integers(-1, 2, (n, 4)).astype(np.float64) / 8
+    v = rng.integers(-1, 2, (k, 4)).astype(np.float64) / 8
+    w = u @ v.T
+    assert np.linalg.matrix_rank(w) == 4
+    bits = oracle.bf16_from_f64(w)
+    assert np.array_equal(synth.bf16_bits_to_f32(bits).astype(np.float64), w)
+    return bits, w
+
+
+@pytest.mark.parametrize("steps", [0, 3])
+def test_svd_recovers_an_exactly_low_rank_weight(steps):
+    """range(W omega) = range(W) for a Gaussian omega when rank(W) <= r, so the
+    projection Q Q^T W is W itself up to fp64 rounding, with or without iterations."""
+    bits, w = _exact_rank4_weight()
+    omega = np.random.default_rng(1).standard_normal((w.shape[1], 6))
+    q = oracle.svd_lowrank_split(bits, omega, steps)["q"]
+    assert np.abs(w - q @ (q.T @ w)).max() <= 1e-12 * np.abs(w).max()
+
+
+def test_svd_q_is_orthonormal_and_the_residual_orthogonal_to_it():
+    d = synth.make_config("tiny")
+    w = synth.bf16_bits_to_f32(d["w"]).astype(np.float64)
+    omega = np.random.default_rng(2).standard_normal((w.shape[1], 16))
+    q = oracle.svd_lowrank_split(d["w"], omega, 2)["q"]
+    assert q.shape == (w.shape[0], 16)
+    assert np.abs(q.T @ q - np.eye(16)).max() <= 1e-12
+    assert np.abs(q.T @ (w - q @ (q.T @ w))).max() <= 1e-12 * np.abs(w).max()
+
+
+def _planted(n, k, lead, decay, seed, planted=12):
+    rng = np.random.default_rng(seed)
+    return synth.to_bf16_bits(synth.planted_lowrank_weight(rng, n, k, planted=planted, lead=lead, decay=decay))
+
+
+def test_svd_with_a_spectral_gap_finds_the_top_singular_subspace():
+    """Eckart-Young: no rank-r matrix is closer to W in Frobenius norm than the
+    truncated SVD (computed here with LAPACK).  With a clear gap after the planted
+    directions the subspace iteration reaches that optimum and that subspace."""
+    bits = _planted(256, 320, lead=20.0, decay=0.9, seed=4, planted=8)
+    w = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    u, s, _ = np.linalg.svd(w)
+    assert s[7] > 5 * s[8]
+    omega = np.random.default_rng(5).standard_normal((w.shape[1], 8))
+    q = oracle.svd_lowrank_split(bits, omega, 8)["q"]
+    err = np.linalg.norm(w - q @ (q.T @ w))
+    opt = np.sqrt((s[8:] ** 2).sum())
+    assert opt <= err <= opt * (1 + 1e-9)
+    assert np.abs(q @ q.T - u[:, :8] @ u[:, :8].T).max() <= 1e-8
+
+
+def test_svd_subspace_iterations_approach_the_optimum():
+    """Without a clear gap the range finder alone (steps = 0) is measurably worse
+    than the truncated SVD; the iterations close most of that distance."""
+    bits = _planted(256, 320, lead=1.5, decay=0.85, seed=6, planted=24)
+    w = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    s = np.linalg.svd(w, compute_uv=False)
+    opt = np.sqrt((s[16:] ** 2).sum())
+    omega = np.random.default_rng(7).standard_normal((w.shape[1], 16))
+    errs = []
+    for steps in (0, 1, 2, 4, 8):
+        q = oracle.svd_lowrank_split(bits, omega, steps)["q"]
+        errs.append(np.linalg.norm(w - q @ (q.T @ w)))
+    assert errs[0] > 1.05 * opt
+    assert all(b < a for a, b in zip(errs, errs[1:]))
+    assert errs[-1] <= 1.005 * opt
+
+
+def test_svd_factors_and_residual_add_back_to_the_weight():
+    """svd_b^T svd_a^T is the projection Q Q^T W up to the bf16 rounding of the two
+    factors, and the binary32 residual is W minus exactly that rounded product
+    (one rounding to binary32)."""
+    d = synth.make_config("tiny")
+    w = synth.bf16_bits_to_f32(d["w"]).astype(np.float64)
+    omega = np.random.default_rng(8).standard_normal((w.shape[1], 32))
+    out = oracle.svd_lowrank_split(d["w"], omega, 8)
+    a = synth.bf16_bits_to_f32(out["svd_a"]).astype(np.float64)
+    b = synth.bf16_bits_to_f32(out["svd_b"]).astype(np.float64)
+    assert a.shape == (w.shape[1], 32) and b.shape == (32, w.shape[0])
+    lr = b.T @ a.T
+    proj = out["q"] @ (out["q"].T @ w)
+    assert np.linalg.norm(lr - proj) <= 2 ** -7 * np.linalg.norm(proj)
+    r = out["residual"].astype(np.float64)
+    exact = w - lr
+    half_ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64) / 2
+    assert np.all(np.abs(r - exact) <= half_ulp + 1e-300)
+
+
+def test_rotate_quantize_f32_agrees_with_the_bf16_path_on_bf16_values():
+    d = synth.make_config("tiny")
+    for g in (1, 64, 256):
+        q1, s1 = oracle.rotate_quantize(d["w"], g)
+        q2, s2 = oracle.rotate_quantize_f32(synth.bf16_bits_to_f32(d["w"]), g)
+        assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+def test_rotate_quantize_f32_keeps_binary32_precision():
+    """Values that bf16 cannot hold: the codes stay within half a step of the exact
+    rotated values (fp64 Sylvester product), so the low mantissa bits are used."""
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((8, 256)) * (1 + 2.0 ** -12)).astype(np.float32)
+    q, s = oracle.rotate_quantize_f32(x, 256)
+    h = scipy.linalg.hadamard(256).astype(np.float64) / 16.0
+    y = x.astype(np.float64) @ h.T
+    for i in range(8):
+        assert s[i] == np.float32(np.abs(y[i]).max().astype(np.float32) / np.float32(127)) or \
+            abs(float(s[i]) - np.abs(y[i]).max() / 127) <= 1e-6 * float(s[i])
+        assert np.abs(q[i] * float(s[i]) - y[i]).max() <= 0.5 * float(s[i]) * (1 + 1e-5)
+    # a bf16 truncation of the inputs moves some code
+    qt, _ = oracle.rotate_quantize(synth.to_bf16_bits(x), 256)
+    assert not np.array_equal(q, qt)
+
+
+def test_svd_split_lowers_the_forward_error_on_a_planted_weight():
+    """With a few dominant singular directions, quantizing only the residual (and
+    adding the bf16 factors back) approximates x W^T better than quantizing W."""
+    c = synth.CONFIGS["tiny"]
+    x = synth.make_config("tiny")["x"]
+    bits = _planted(c.n, c.k, lead=20.0, decay=0.6, seed=10, planted=8)
+    w = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    exact = xf @ w.T
+    qw, sw = oracle.rotate_quantize(bits, 256)
+    plain = synth.bf16_bits_to_f32(oracle.qlinear_forward(x, qw, sw, 256)["y"]).astype(np.float64)
+    omega = np.random.default_rng(11).standard_normal((c.k, 32))
+    sv = oracle.svd_quantize_weight(bits, 256, omega, 8)
+    y = oracle.qlinear_forward(x, sv["qw"], sv["sw"], 256, sv["svd_a"], sv["svd_b"], 1.0)["y"]
+    svd = synth.bf16_bits_to_f32(y).astype(np.float64)
+    e_plain = np.linalg.norm(plain - exact) / np.linalg.norm(exact)
+    e_svd = np.linalg.norm(svd - exact) / np.linalg.norm(exact)
+    assert e_svd < 0.5 * e_plain
