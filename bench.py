@@ -111,7 +111,8 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     the layer, each on its own workload: weight preparation, the attention
     projection forward, the QuaRot-style forward with LoRA (g = 64 and 128), the
     PEFT backward (input gradient + LoRA gradients), the full fine-tuning weight
-    gradient and the FP8 (E4M3) variant of the MLP step."""
+    gradient, the FP8 (E4M3) variant of the MLP step, and the low-rank (SVD)
+    split with the forward that uses it."""
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
 
@@ -207,6 +208,27 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
         "gemm_up_us": round(t_up, 2), "gemm_down_us": round(t_down, 2),
         "gemm_TFLOP/s": round(gemm_tops, 1), "gemm_pct_of_fp8_peak": round(gemm_tops / 50.0, 2),
         "note": "E4M3 codes, fp32 MFMA accumulation; back-to-back GEMM launches; fp8 dense peak 5.0 PFLOP/s"}
+    del x, hh, qwu, qwd, qx, qh, yu, yd
+    # low-rank (SVD) split: offline preparation of W [3072, 3072] (rank 32, 8 steps),
+    # then the forward with the factors as the LoRA term
+    sv = synth.make_config("svd")
+    c = synth.CONFIGS["svd"]
+    r, steps = c.extra["rank"], c.extra["steps"]
+    x, w = to_dev_bf16(torch, sv["x"]), to_dev_bf16(torch, sv["w"])
+    omega = torch.from_numpy(sv["omega"]).to(dev)
+    sws = torch.empty(h.sdnq_svd_workspace_bytes(c.n, c.k, r), dtype=torch.uint8, device=dev)
+    us = timed(lambda: h.sdnq_svd_quantize_weight(w, 256, omega, steps, workspace=sws))
+    rows["svd_split_prep_3072x3072_r32_s8_g256"] = {
+        "us": round(us, 2), "note": "offline: randomized range finder, 8 subspace iterations, fp64 thin products"}
+    qw, sw, sa, sb = h.sdnq_svd_quantize_weight(w, 256, omega, steps, workspace=sws)
+    del sws
+    ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, r, False), dtype=torch.uint8, device=dev)
+    y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda: h.sdnq_qlinear_forward(x, qw, sw, 256, sa, sb, 1.0, out=y, workspace=ws))
+    ops = 2.0 * c.m * c.n * c.k
+    rows["svd_forward_4096x3072x3072_g256_r32"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+                                                   "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
+                                                   "note": "int8 residual + bf16 rank-32 factors in the epilogue"}
     return rows
 
 

@@ -22,6 +22,9 @@ from ._binding import (  # noqa: F401
     sdnq_rotate_quantize_act_fp8,
     sdnq_rotate_quantize_weight,
     sdnq_rotate_quantize_weight_fp8,
+    sdnq_svd_quantize_weight,
+    sdnq_svd_workspace_bytes,
+    sdnq_svd_workspace_q_offset,
     sdnq_qlinear_weight_grad,
     sdnq_weight_grad_workspace_bytes,
     sdnq_workspace_bytes,

@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
         "sdnq_qlinear_forward_fp8_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
         "sdnq_gemm_fp8_f32": [p, p, i64, i64, i64, p, p],
         "sdnq_qlinear_weight_grad": [p, p, i64, i64, i64, i32, p, p, sz, p],
+        "sdnq_svd_quantize_weight": [p, i64, i64, i32, i32, i32, p, p, p, p, p, p, sz, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
     L.sdnq_workspace_bytes.restype = sz
     L.sdnq_weight_grad_workspace_bytes.argtypes = [i64, i64, i64]
     L.sdnq_weight_grad_workspace_bytes.restype = sz
+    L.sdnq_svd_workspace_bytes.argtypes = [i64, i64, i32]
+    L.sdnq_svd_workspace_bytes.restype = sz
+    L.sdnq_svd_workspace_q_offset.argtypes = [i64, i64, i32]
+    L.sdnq_svd_workspace_q_offset.restype = sz
     L.sdnq_status_string.argtypes = [ctypes.c_int]
     L.sdnq_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -286,3 +291,34 @@ def sdnq_qlinear_weight_grad(dy, x, g, out=None, workspace=None):
                                           _stream(dy.device)), "sdnq_qlinear_weight_grad")
     return dw
 
+
+
+def sdnq_svd_workspace_bytes(n: int, k: int, rank: int) -> int:
+    return int(lib().sdnq_svd_workspace_bytes(n, k, rank))
+
+
+def sdnq_svd_workspace_q_offset(n: int, k: int, rank: int) -> int:
+    return int(lib().sdnq_svd_workspace_q_offset(n, k, rank))
+
+
+def sdnq_svd_quantize_weight(w, g, omega, steps: int, workspace=None):
+    """Low-rank split of w [n, k] (bf16) with the test matrix omega [k, rank] (fp32),
+    then rotate + int8 quantization of the residual.  Returns (qw, w_scale, svd_a
+    [k, rank] bf16, svd_b [rank, n] bf16); the layer runs as sdnq_qlinear_forward
+    with lora_a=svd_a, lora_b=svd_b, lora_scale=1."""
+    _need(w, torch.bfloat16, 2, "w")
+    _need(omega, torch.float32, 2, "omega")
+    n, k = w.shape
+    if omega.shape[0] != k:
+        raise ValueError("omega must be [k, rank]")
+    rank = omega.shape[1]
+    dev = w.device
+    qw = torch.empty((n, k), dtype=torch.int8, device=dev)
+    sw = torch.empty((n,), dtype=torch.float32, device=dev)
+    svd_a = torch.empty((k, rank), dtype=torch.bfloat16, device=dev)
+    svd_b = torch.empty((rank, n), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(sdnq_svd_workspace_bytes(n, k, rank), dev, workspace)
+    _check(lib().sdnq_svd_quantize_weight(_ptr(w), n, k, g, rank, steps, _ptr(omega), _ptr(qw), _ptr(sw),
+                                          _ptr(svd_a), _ptr(svd_b), _ptr(ws), ws.numel(), _stream(dev)),
+           "sdnq_svd_quantize_weight")
+    return qw, sw, svd_a, svd_b

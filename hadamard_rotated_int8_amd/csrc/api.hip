@@ -34,6 +34,8 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool valid_group(int32_t g) { return g == 1 || g == 64 || g == 128 || g == 256; }
 
+constexpr int32_t kMaxSvdSteps = 64;
+
 bool valid_rank(int32_t rank) { return rank >= 16 && rank <= 128 && rank % 16 == 0; }
 
 sdnq_status_t check_feature(int64_t d) {
@@ -439,6 +441,38 @@ sdnq_status_t sdnq_gemm_fp8_f32(const uint8_t *a, const uint8_t *b, int64_t m, i
   ga.a = reinterpret_cast<const int8_t *>(a); ga.b = reinterpret_cast<const int8_t *>(b);
   ga.m = m; ga.n = n; ga.k = k; ga.c_i32 = reinterpret_cast<int32_t *>(c); ga.g = 1; ga.fp8 = true;
   return launched(launch_gemm_i8(Epilogue::kInt32, ga, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------ low-rank (SVD) split --
+size_t sdnq_svd_workspace_bytes(int64_t n, int64_t k, int32_t rank) {
+  if (check_feature(n) != SDNQ_OK || check_feature(k) != SDNQ_OK) return 0;
+  if (!(rank == 16 || rank == 32 || rank == 64) || rank > n || rank > k) return 0;
+  return svd_workspace_bytes(n, k, rank);
+}
+
+size_t sdnq_svd_workspace_q_offset(int64_t n, int64_t k, int32_t rank) {
+  if (sdnq_svd_workspace_bytes(n, k, rank) == 0) return 0;
+  return svd_workspace_q_offset(n, k, rank);
+}
+
+sdnq_status_t sdnq_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int32_t g, int32_t rank,
+                                       int32_t steps, const float *omega, int8_t *qw, float *w_scale,
+                                       uint16_t *svd_a, uint16_t *svd_b, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+  if (!w || !omega || !qw || !w_scale || !svd_a || !svd_b) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_feature(k));
+  if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
+  if (!(rank == 16 || rank == 32 || rank == 64) || rank > n || rank > k) return SDNQ_ERR_UNSUPPORTED;
+  if (steps < 0 || steps > kMaxSvdSteps) return SDNQ_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(omega) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(svd_a) ||
+      !aligned16(svd_b))
+    return SDNQ_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < svd_workspace_bytes(n, k, rank))
+    return SDNQ_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return launched(launch_svd_quantize_weight(w, n, k, g, rank, steps, omega, qw, w_scale, svd_a, svd_b, workspace,
+                                             (hipStream_t)stream));
 }
 
 }  // extern "C"

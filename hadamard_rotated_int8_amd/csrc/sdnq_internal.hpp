@@ -91,4 +91,14 @@ int lora_grad_splits(int64_t m);
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
                             float scale, bool transposed, float *partials, uint16_t *out, hipStream_t stream);
 
+// Low-rank (SVD) split of w [n, k] with rank in {16, 32, 64}, then rotate + int8
+// quantization of the binary32 residual.  The workspace holds the residual [n, k]
+// (binary32) at offset 0 and the orthonormal basis Q [n, rank] (fp64) at
+// svd_workspace_q_offset() when the call returns.
+size_t svd_workspace_bytes(int64_t n, int64_t k, int rank);
+size_t svd_workspace_q_offset(int64_t n, int64_t k, int rank);
+hipError_t launch_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int g, int rank, int steps,
+                                      const float *omega, int8_t *qw, float *w_scale, uint16_t *svd_a,
+                                      uint16_t *svd_b, void *workspace, hipStream_t stream);
+
 }  // namespace sdnq

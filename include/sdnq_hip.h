@@ -210,6 +210,41 @@ sdnq_status_t sdnq_qlinear_forward_fp8_quantized(const uint8_t *qx, const float 
 sdnq_status_t sdnq_gemm_fp8_f32(const uint8_t *a, const uint8_t *b, int64_t m, int64_t n, int64_t k,
                                 float *c, void *stream);
 
+/* ------------------------------------------------- low-rank (SVD) split ------
+ * SVD quantization ("SDNQ: SD.Next Quantization Engine": SVD quantization next to
+ * the Hadamard rotation; SDNQConfig use_svd, svd_rank = 32, svd_steps = 8; the
+ * SD.Next dev-branch commit log: a seeded SVD truncation, so the quantized weight
+ * is integer codes plus low-rank factors).  The pages give no algorithm; this is
+ * the randomized range finder with subspace iteration:
+ *   Q = orth(w omega); `steps` times: Z = orth(w^T Q), Q = orth(w Z);
+ *   svd_a[k,rank] = bf16(w^T Q), svd_b[rank,n] = bf16(Q^T)   (round to nearest even)
+ *   residual[n,k] = fl32(w - svd_b^T svd_a^T)   (fp64 sum of the rounded factors)
+ *   qw[n,k], w_scale[n] = rotation (block g) + row quantization of the residual,
+ *   with the binary32 steps of sdnq_rotate_quantize_weight.
+ * orth() is an orthonormal basis of the same span (computed in fp64 by shifted
+ * CholeskyQR; where w omega is rank-deficient, the extra columns are arbitrary
+ * directions that add nothing to the projection Q Q^T w).
+ * The layer then runs as sdnq_qlinear_forward(x, ..., qw, w_scale, n, g,
+ * lora_a = svd_a, lora_b = svd_b, rank, lora_scale = 1, ...).
+ * w[n,k] bf16; omega[k,rank] fp32, the random test matrix (N(0,1) entries; the
+ * caller draws it, so the split is reproducible from its seed); rank in {16, 32,
+ * 64} and at most min(n, k); 0 <= steps <= 64; n and k multiples of 16, at most
+ * 65536; k % g == 0.  Offline weight preparation: it reads w about 2 (steps + 1)
+ * times and runs small fp64 kernels in between.
+ * workspace: sdnq_svd_workspace_bytes(n, k, rank) bytes, 16-byte aligned.  When
+ * the call's work has completed, the workspace holds the binary32 residual [n,k]
+ * at offset 0 and Q [n,rank] (fp64) at sdnq_svd_workspace_q_offset(n, k, rank). */
+sdnq_status_t sdnq_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int32_t g, int32_t rank,
+                                       int32_t steps, const float *omega, int8_t *qw, float *w_scale,
+                                       uint16_t *svd_a, uint16_t *svd_b, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+/* Workspace size in bytes for sdnq_svd_quantize_weight; 0 on invalid sizes. */
+size_t sdnq_svd_workspace_bytes(int64_t n, int64_t k, int32_t rank);
+
+/* Byte offset of Q [n,rank] (fp64) in that workspace; 0 on invalid sizes. */
+size_t sdnq_svd_workspace_q_offset(int64_t n, int64_t k, int32_t rank);
+
 #ifdef __cplusplus
 }
 #endif

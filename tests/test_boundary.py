@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
               "sdnq_qlinear_backward_input", "sdnq_qlinear_forward_quantized", "sdnq_workspace_bytes",
               "sdnq_status_string", "sdnq_gemm_i8_i32", "sdnq_rotate_quantize_weight_fp8",
               "sdnq_rotate_quantize_act_fp8", "sdnq_qlinear_forward_fp8", "sdnq_qlinear_forward_fp8_quantized",
-              "sdnq_gemm_fp8_f32", "sdnq_qlinear_weight_grad", "sdnq_weight_grad_workspace_bytes"):
+              "sdnq_gemm_fp8_f32", "sdnq_qlinear_weight_grad", "sdnq_weight_grad_workspace_bytes",
+              "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset"):
         assert n in names
 
 
@@ -205,3 +206,32 @@ def test_weight_grad_validation():
     assert f(m=64, g=64, wsb=h.sdnq_weight_grad_workspace_bytes(64, 256, 256) - 1) == WORKSPACE
     assert h.sdnq_weight_grad_workspace_bytes(16384, 3072, 3072) >= 16384 * 3072 * 4
 
+
+
+@no_gpu
+def test_svd_split_validation():
+    L = h.lib()
+    E = 0x60000
+
+    def f(w=A, n=256, k=256, g=256, rank=32, steps=8, omega=B, qw=C, sw=D, a=E, b=W, ws=0x70000,
+          wsb=None):
+        if wsb is None:
+            wsb = h.sdnq_svd_workspace_bytes(n, k, rank) or WS
+        return L.sdnq_svd_quantize_weight(w, n, k, g, rank, steps, omega, qw, sw, a, b, ws, wsb, None)
+    assert f(w=None) == INVALID and f(omega=None) == INVALID and f(b=None) == INVALID
+    assert f(n=0) == INVALID and f(k=-16) == INVALID
+    assert f(n=100) == UNSUPPORTED and f(g=32) == UNSUPPORTED and f(k=320, g=256) == UNSUPPORTED
+    assert f(rank=48) == UNSUPPORTED and f(rank=128) == UNSUPPORTED    # ranks 16, 32, 64 only
+    assert f(n=32, k=256, rank=64) == UNSUPPORTED                     # rank above min(n, k)
+    assert f(steps=-1) == INVALID and f(steps=65) == INVALID
+    assert f(omega=B + 4) == INVALID and f(a=E + 8) == INVALID
+    assert f(ws=None) == WORKSPACE
+    assert f(wsb=h.sdnq_svd_workspace_bytes(256, 256, 32) - 1) == WORKSPACE
+
+
+def test_svd_workspace_bytes():
+    f = h.sdnq_svd_workspace_bytes
+    n, k, r = 3072, 3072, 32
+    assert f(n, k, r) >= n * k * 4 + n * k * 2 + n * r * 8   # residual, W^T, Q
+    assert h.sdnq_svd_workspace_q_offset(n, k, r) >= n * k * 4
+    assert f(n, k, 48) == 0 and f(n, 100, r) == 0 and f(16, 256, 32) == 0
