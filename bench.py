@@ -23,6 +23,7 @@ import argparse
 import ctypes
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -72,6 +73,20 @@ def measured_traffic():
         return [int(kv["up_bytes"]), int(kv["down_bytes"])]
     except (OSError, KeyError, ValueError):
         return None
+
+
+def environment(torch) -> dict:
+    """Device, ROCm and clock information recorded with the numbers (rocm-smi's
+    current clocks, read after the timed region; None where unavailable)."""
+    env = {"device": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values())) if r.returncode == 0 else {}
+        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() and ("sclk" in k or "mclk" in k
+                                                                                   or "fclk" in k)}
+    except Exception:  # the tool may be missing or print something else
+        env["clocks"] = None
+    return env
 
 
 def to_dev_bf16(torch, bits):
@@ -311,8 +326,24 @@ def main():
             c()
             evs[i][j + 1].record(stream)
     torch.cuda.synchronize()
-    in_step_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
-                           for i in range(args.steps)]).mean(axis=0)
+    in_step_all = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                            for i in range(args.steps)])
+    in_step_ms = in_step_all.mean(axis=0)
+
+    # cold launches: a 1 GiB read before each one evicts the operands from the
+    # 256 MB MALL without leaving dirty lines behind
+    scrub = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    cold = np.zeros((min(args.steps, 20), 4))
+    for i in range(cold.shape[0]):
+        for j, c in enumerate(calls):
+            scrub.max()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold[i, j] = e0.elapsed_time(e1)
+    del scrub
 
     # per-kernel launch duration: HIP events on the launch stream around K
     # back-to-back launches of each kernel (same inputs as in the step)
@@ -370,6 +401,13 @@ def main():
                                      "timing": "HIP events between the kernels of whole steps"},
         "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
         "kernel_in_step_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, in_step_ms)},
+        "kernel_in_step_median_min_us": {k: [round(float(np.median(in_step_all[:, j])) * 1e3, 2),
+                                             round(float(in_step_all[:, j].min()) * 1e3, 2)]
+                                         for j, k in enumerate(kernels)},
+        "kernel_cold_median_min_us": {k: [round(float(np.median(cold[:, j])) * 1e3, 2),
+                                          round(float(cold[:, j].min()) * 1e3, 2)]
+                                      for j, k in enumerate(kernels)},
+        "env": environment(torch),
     }
     if not args.no_rows:
         out["rows"] = measure_rows(torch, h, synth)
