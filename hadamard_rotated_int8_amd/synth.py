@@ -76,6 +76,56 @@ def gaussian_test_matrix(rng: np.random.Generator, k: int, rank: int) -> np.ndar
 
 
 @dataclass(frozen=True)
+class AttentionConfig:
+    """One attention workload in SDPA's layout: q [batch, heads_q, seq_q, head_dim],
+    k and v [batch, heads_kv, seq_k, head_dim]."""
+    name: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seq_q: int
+    seq_k: int
+    head_dim: int
+    causal: bool = False
+    note: str = ""
+
+
+# flux.1 joint attention: 3072 wide = 24 heads of 128, 4608 joint tokens (the SD.Next
+# dev-branch commit log's block geometry); a causal grouped-query text-encoder
+# stand-in for the commit log's causal gqa text-encoder preset; a small case.
+ATTENTION_CONFIGS = {
+    "attn_tiny": AttentionConfig("attn_tiny", 1, 4, 2, 200, 176, 128, causal=True,
+                                 note="ragged tiles, gqa, causal"),
+    "attn_flux": AttentionConfig("attn_flux", 1, 24, 24, 4608, 4608, 128,
+                                 note="flux.1 joint attention: 24 heads x 128, 4608 tokens"),
+    "attn_te": AttentionConfig("attn_te", 2, 16, 4, 1024, 1024, 128, causal=True,
+                               note="causal gqa text encoder: 16 query heads over 4 key/value heads"),
+}
+
+
+def make_attention(name: str, seed: int = 0) -> dict:
+    """q, k, v (bf16 bits) of a named attention workload, drawn in the order q, k, v:
+    q ~ N(0, 1) with 1 % of the head channels x20 (outlier channels, as for the
+    linear layer's activations); k the same plus a per-(head, channel) offset
+    N(0, 4) shared by all tokens (the channel-wise bias that K smoothing removes);
+    v ~ N(0, 1)."""
+    c = ATTENTION_CONFIGS[name]
+    rng = np.random.default_rng(seed)
+
+    def act(heads, seq):
+        x = rng.standard_normal((c.batch, heads, seq, c.head_dim), dtype=np.float32)
+        count = max(1, int(round(0.01 * c.head_dim)))
+        ch = np.sort(rng.permutation(c.head_dim)[:count])
+        x[..., ch] *= np.float32(20.0)
+        return x
+    q = act(c.heads_q, c.seq_q)
+    k = act(c.heads_kv, c.seq_k)
+    k += rng.standard_normal((c.batch, c.heads_kv, 1, c.head_dim), dtype=np.float32) * np.float32(4.0)
+    v = rng.standard_normal((c.batch, c.heads_kv, c.seq_k, c.head_dim), dtype=np.float32)
+    return {"q": to_bf16_bits(q), "k": to_bf16_bits(k), "v": to_bf16_bits(v)}
+
+
+@dataclass(frozen=True)
 class LinearConfig:
     """One workload: activation rows m, in-features k, out-features n."""
     name: str

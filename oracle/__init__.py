@@ -391,3 +391,90 @@ def svd_quantize_weight(w_bf16: np.ndarray, g: int, omega: np.ndarray, steps: in
     out = svd_lowrank_split(w_bf16, omega, steps)
     out["qw"], out["sw"] = rotate_quantize_f32(out["residual"], g)
     return out
+
+
+# ---------------------------------------------------- int8 attention (QK^T) --
+#
+# "SDNQ: SD.Next Quantization Engine", the SDPA-replacement example: the
+# attention takes query/key/value in SDPA's layout with is_causal, scale and
+# enable_gqa, runs Q K^T as an int8 quantized matmul (matmul_dtype "int8"),
+# keeps P V unquantized (pv_matmul_dtype "disabled"), smooths K (smooth_k), can
+# rotate Q and K with a Hadamard block (use_hadamard, hadamard_group_size 256),
+# and quantizes in fp32 (quantize_fp32).  Readings (the pages give the options,
+# not the arithmetic):
+#   * q [B, Hq, Sq, D], k and v [B, Hkv, Sk, D]; query head h reads key/value
+#     head h // (Hq / Hkv) (grouped-query attention);
+#   * smooth_k subtracts from K its mean over the key tokens, per batch, head and
+#     channel (the softmax of each query row is unchanged by a shift common to
+#     all keys); the mean is fl32(sum / Sk) with the sum taken in fp64 in token
+#     order; K' = fl32(k - mean);
+#   * the rotation block along the head dimension is min(g, D) (g <= 1: none),
+#     with the butterfly, normalization and per-row int8 quantizer of the
+#     linear layer, one scale per token of Q and of K;
+#   * scores = fp64(int Q K^T) * s_q[i] * s_k[j] * scale, scale = 1/sqrt(D) by
+#     default; is_causal masks keys j > i (top-left aligned, as SDPA);
+#   * softmax and P V in fp64 on the bf16 values of v, one rounding to bf16.
+
+def attention_k_mean(k_bf16: np.ndarray) -> np.ndarray:
+    """Per (batch, head, channel) mean of k [B, H, S, D] over the tokens:
+    fl32(fp64 sum in token order / S), as binary32 [B, H, D]."""
+    kf = f32_from_bf16(k_bf16).astype(np.float64)
+    total = np.cumsum(kf, axis=2)[:, :, -1, :]
+    return (total / kf.shape[2]).astype(np.float32)
+
+
+def attention_block(g: int, d: int) -> int:
+    return 1 if g <= 1 else min(g, d)
+
+
+def attention_prep(x_bf16: np.ndarray, g: int, offset: np.ndarray | None = None):
+    """Codes int8 [B, H, S, D] and scales f32 [B, H, S] of each token row, rotated
+    with block min(g, D); offset [B, H, D] (binary32) is subtracted first."""
+    b, hh, s, d = x_bf16.shape
+    blk = attention_block(g, d)
+    if offset is None:
+        q, sc = rotate_quantize(np.ascontiguousarray(x_bf16).reshape(-1, d), blk)
+    else:
+        xf = f32_from_bf16(x_bf16) - np.asarray(offset, np.float32)[:, :, None, :]
+        q, sc = rotate_quantize_f32(xf.astype(np.float32).reshape(-1, d), blk)
+    return q.reshape(b, hh, s, d), sc.reshape(b, hh, s)
+
+
+def attention_int8(q: np.ndarray, k: np.ndarray, v: np.ndarray, is_causal: bool = False,
+                   scale: float | None = None, smooth_k: bool = True, g: int = 256,
+                   intermediates: bool = False, q_rows: np.ndarray | None = None) -> dict:
+    """Int8-QK^T attention of bf16 q [B, Hq, Sq, D], k, v [B, Hkv, Sk, D]:
+    returns out (bf16 bits [B, Hq, Sq, D]) and, with intermediates, the codes,
+    scales, K mean and the fp64 output before rounding.  q_rows (query token
+    indices) restricts the work and the outputs to those rows of every head."""
+    bsz, hq, sq, d = q.shape
+    hkv, sk = k.shape[1], k.shape[2]
+    if k.shape != (bsz, hkv, sk, d) or v.shape != k.shape or hq % hkv != 0:
+        raise ValueError("q [B, Hq, Sq, D], k and v [B, Hkv, Sk, D] with Hq % Hkv == 0")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(sq) if q_rows is None else np.asarray(q_rows, np.int64)
+    q = np.ascontiguousarray(np.asarray(q)[:, :, rows, :])
+    sq = len(rows)
+    qc, qs = attention_prep(q, g)
+    mean = attention_k_mean(k) if smooth_k else None
+    kc, ks = attention_prep(k, g, mean)
+    vf = f32_from_bf16(v).astype(np.float64)
+    rep = hq // hkv
+    o = np.empty((bsz, hq, sq, d), np.float64)
+    mask = (np.arange(sk)[None, :] > rows[:, None]) if is_causal else None
+    for b in range(bsz):
+        for h in range(hq):
+            hk = h // rep
+            acc = qc[b, h].astype(np.int64) @ kc[b, hk].astype(np.int64).T
+            s = acc.astype(np.float64) * (qs[b, h].astype(np.float64)[:, None] *
+                                          ks[b, hk].astype(np.float64)[None, :]) * scale
+            if mask is not None:
+                s[mask] = -np.inf
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            o[b, h] = (p @ vf[b, hk]) / p.sum(axis=1, keepdims=True)
+    res = {"out": bf16_from_f64(o)}
+    if intermediates:
+        res.update(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks, k_mean=mean, o=o)
+    return res

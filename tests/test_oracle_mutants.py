@@ -60,6 +60,16 @@ PY_MUTANTS = {
                                 "        z = _orth(w.T @ q)\n        q = _orth(w @ om)"),
     "svd_factor_b_not_orthonormal": ("    b_bits = bf16_from_f64(np.ascontiguousarray(q.T))",
                                      "    b_bits = bf16_from_f64(np.ascontiguousarray((w @ om).T))"),
+    "attn_mean_divides_by_head_dim": ("    return (total / kf.shape[2]).astype(np.float32)",
+                                      "    return (total / kf.shape[3]).astype(np.float32)"),
+    "attn_causal_off_by_one": ("    mask = (np.arange(sk)[None, :] > rows[:, None]) if is_causal else None",
+                               "    mask = (np.arange(sk)[None, :] >= rows[:, None]) if is_causal else None"),
+    "attn_gqa_modulo": ("            hk = h // rep", "            hk = h % hkv"),
+    "attn_smoothing_adds": ("        xf = f32_from_bf16(x_bf16) - np.asarray(offset, np.float32)[:, :, None, :]",
+                            "        xf = f32_from_bf16(x_bf16) + np.asarray(offset, np.float32)[:, :, None, :]"),
+    "attn_half_head_block": ("    return 1 if g <= 1 else min(g, d)", "    return 1 if g <= 1 else min(g, d) // 2"),
+    "attn_scale_dropped": ("                                          ks[b, hk].astype(np.float64)[None, :]) * scale",
+                           "                                          ks[b, hk].astype(np.float64)[None, :])"),
 }
 
 

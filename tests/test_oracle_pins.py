@@ -775,3 +775,120 @@ def test_svd_split_lowers_the_forward_error_on_a_planted_weight():
     e_plain = np.linalg.norm(plain - exact) / np.linalg.norm(exact)
     e_svd = np.linalg.norm(svd - exact) / np.linalg.norm(exact)
     assert e_svd < 0.5 * e_plain
+
+
+# ---------------------------------------------------- int8 attention (QK^T) --
+# Reading: per-token int8 Q and K rotated along the head dimension with block
+# min(g, D); K smoothed by its per-channel mean over the key tokens; fp64 softmax
+# and P V; grouped-query heads h -> h // (Hq / Hkv); top-left causal mask.
+
+def _attn_inputs(b, hq, hkv, sq, sk, d, seed):
+    rng = np.random.default_rng(seed)
+    q = synth.to_bf16_bits(rng.standard_normal((b, hq, sq, d)).astype(np.float32))
+    k = synth.to_bf16_bits((rng.standard_normal((b, hkv, sk, d)) + rng.standard_normal((b, hkv, 1, d)) * 3)
+                           .astype(np.float32))
+    v = synth.to_bf16_bits(rng.standard_normal((b, hkv, sk, d)).astype(np.float32))
+    return q, k, v
+
+
+def _f64(bits):
+    return torch.from_numpy(synth.bf16_bits_to_f32(bits).astype(np.float64))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_core_is_sdpa_on_the_dequantized_codes(causal):
+    """Softmax, P V, the scale, the causal mask and the head grouping, against
+    torch's scaled_dot_product_attention in fp64 on q_codes * s_q, k_codes * s_k
+    (the rotation leaves every score q . k unchanged, so SDPA may see the
+    rotated, dequantized operands)."""
+    q, k, v = _attn_inputs(2, 4, 2, 40, 56, 64, 12)
+    r = oracle.attention_int8(q, k, v, causal, 0.3, True, 64, intermediates=True)
+    qh = torch.from_numpy(r["q_codes"].astype(np.float64) * r["q_scales"].astype(np.float64)[..., None])
+    kh = torch.from_numpy(r["k_codes"].astype(np.float64) * r["k_scales"].astype(np.float64)[..., None])
+    ref = torch.nn.functional.scaled_dot_product_attention(qh, kh, _f64(v), is_causal=causal, scale=0.3,
+                                                           enable_gqa=True).numpy()
+    assert np.abs(r["o"] - ref).max() <= 1e-12
+
+
+def test_attention_causal_brute_force():
+    q, k, v = _attn_inputs(1, 1, 1, 5, 7, 64, 13)
+    r = oracle.attention_int8(q, k, v, True, None, False, 64, intermediates=True)
+    vf = synth.bf16_bits_to_f32(v)[0, 0].astype(np.float64)
+    for i in range(5):
+        s = []
+        for j in range(i + 1):
+            acc = sum(int(r["q_codes"][0, 0, i, t]) * int(r["k_codes"][0, 0, j, t]) for t in range(64))
+            s.append(acc * float(r["q_scales"][0, 0, i]) * float(r["k_scales"][0, 0, j]) / 8.0)
+        mx = max(s)
+        p = [np.exp(x - mx) for x in s]
+        o = sum(p[j] * vf[j] for j in range(i + 1)) / sum(p)
+        assert np.abs(o - r["o"][0, 0, i]).max() <= 1e-12
+
+
+def test_attention_k_mean_is_the_exact_mean_rounded_once():
+    """Values n/16 with |n| < 128 (exact in bf16): every fp64 partial sum is
+    exact, so the mean is the exact rational mean rounded once to binary32."""
+    rng = np.random.default_rng(14)
+    kf = rng.integers(-127, 128, (1, 2, 37, 64)).astype(np.float64) / 16
+    k = oracle.bf16_from_f64(kf)
+    assert np.array_equal(synth.bf16_bits_to_f32(k).astype(np.float64), kf)
+    mean = oracle.attention_k_mean(k)
+    for h in range(2):
+        for c in range(64):
+            exact = Fraction(int(round(kf[0, h, :, c].sum() * 16)), 16 * 37)
+            assert mean[0, h, c] == nearest_f32(exact)
+
+
+def test_attention_smoothing_ignores_a_key_offset_common_to_all_tokens():
+    """Adding the same per-channel constant to every key token leaves the smoothed
+    K, so its codes and the output, unchanged.  With 64 tokens of values n/16 and
+    integer offsets every step is exact (the mean divides by a power of two), so
+    the invariance holds bit for bit."""
+    rng = np.random.default_rng(15)
+    kf = rng.integers(-64, 64, (1, 2, 64, 64)).astype(np.float64) / 16
+    off = rng.integers(-7, 8, (1, 2, 1, 64)).astype(np.float64)
+    q, _, v = _attn_inputs(1, 2, 2, 24, 64, 64, 16)
+    a = oracle.attention_int8(q, oracle.bf16_from_f64(kf), v, False, None, True, 64, intermediates=True)
+    b = oracle.attention_int8(q, oracle.bf16_from_f64(kf + off), v, False, None, True, 64, intermediates=True)
+    assert np.array_equal(a["k_codes"], b["k_codes"]) and np.array_equal(a["k_scales"], b["k_scales"])
+    assert np.array_equal(a["out"], b["out"])
+    c = oracle.attention_int8(q, oracle.bf16_from_f64(kf + off), v, False, None, False, 64, intermediates=True)
+    assert not np.array_equal(a["k_codes"], c["k_codes"])
+
+
+def test_attention_gqa_equals_repeated_key_value_heads():
+    q, k, v = _attn_inputs(1, 6, 2, 30, 40, 64, 17)
+    a = oracle.attention_int8(q, k, v, True, None, True, 64)["out"]
+    b = oracle.attention_int8(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), True, None, True, 64)["out"]
+    assert np.array_equal(a, b)
+
+
+def test_attention_approximates_exact_attention_and_rotation_and_smoothing_help():
+    """The method's premise on the outlier workload: against fp64 SDPA on the bf16
+    inputs, the Hadamard rotation lowers the error and K smoothing lowers it
+    further; the full method stays within 3 %."""
+    d = synth.make_attention("attn_tiny")
+    c = synth.ATTENTION_CONFIGS["attn_tiny"]
+    ref = torch.nn.functional.scaled_dot_product_attention(_f64(d["q"]), _f64(d["k"]), _f64(d["v"]),
+                                                           is_causal=c.causal, enable_gqa=True).numpy()
+
+    def err(g, smooth):
+        o = synth.bf16_bits_to_f32(oracle.attention_int8(d["q"], d["k"], d["v"], c.causal, None, smooth, g)["out"])
+        return np.linalg.norm(o.astype(np.float64) - ref) / np.linalg.norm(ref)
+    e_plain, e_rot, e_full = err(1, False), err(256, False), err(256, True)
+    assert e_full < e_rot < e_plain
+    assert e_full < 0.03
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_rotation_block_is_the_whole_head(d):
+    """g = 256 rotates each head row as one block of D (min(g, D)): a one-hot row
+    becomes flat, so all D codes are +-127; with g = 1 only one code is nonzero."""
+    q = np.zeros((1, 1, 2, d), np.float64)
+    q[0, 0, 0, 3] = 1.0
+    q[0, 0, 1, d - 1] = -2.0
+    bits = oracle.bf16_from_f64(q)
+    codes, _ = oracle.attention_prep(bits, 256)
+    assert np.all(np.abs(codes[0, 0]) == 127)
+    codes1, _ = oracle.attention_prep(bits, 1)
+    assert np.count_nonzero(codes1[0, 0, 0]) == 1 and np.count_nonzero(codes1[0, 0, 1]) == 1
