@@ -11,6 +11,9 @@ from ._binding import (  # noqa: F401
     SDNQ_OK,
     SdnqError,
     lib,
+    sdnq_attention_int8,
+    sdnq_attention_workspace_bytes,
+    sdnq_attention_workspace_offset,
     sdnq_gemm_fp8_f32,
     sdnq_gemm_i8_i32,
     sdnq_qlinear_backward_input,

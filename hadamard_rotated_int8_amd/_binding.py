@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         "sdnq_gemm_fp8_f32": [p, p, i64, i64, i64, p, p],
         "sdnq_qlinear_weight_grad": [p, p, i64, i64, i64, i32, p, p, sz, p],
         "sdnq_svd_quantize_weight": [p, i64, i64, i32, i32, i32, p, p, p, p, p, p, sz, p],
+        "sdnq_attention_int8": [p, p, p, i64, i64, i64, i64, i64, i64, i32, ctypes.c_float, i32, i32, p, p, sz, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.sdnq_svd_workspace_bytes.restype = sz
     L.sdnq_svd_workspace_q_offset.argtypes = [i64, i64, i32]
     L.sdnq_svd_workspace_q_offset.restype = sz
+    L.sdnq_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+    L.sdnq_attention_workspace_bytes.restype = sz
+    L.sdnq_attention_workspace_offset.argtypes = [i64, i64, i64, i64, i64, i64, i32]
+    L.sdnq_attention_workspace_offset.restype = sz
     L.sdnq_status_string.argtypes = [ctypes.c_int]
     L.sdnq_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -322,3 +327,30 @@ def sdnq_svd_quantize_weight(w, g, omega, steps: int, workspace=None):
                                           _ptr(svd_a), _ptr(svd_b), _ptr(ws), ws.numel(), _stream(dev)),
            "sdnq_svd_quantize_weight")
     return qw, sw, svd_a, svd_b
+
+
+def sdnq_attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim) -> int:
+    return int(lib().sdnq_attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim))
+
+
+def sdnq_attention_workspace_offset(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, which: int) -> int:
+    return int(lib().sdnq_attention_workspace_offset(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, which))
+
+
+def sdnq_attention_int8(q, k, v, is_causal: bool = False, scale: float | None = None, smooth_k: bool = True,
+                        hadamard_group: int = 256, out=None, workspace=None):
+    """Int8-QK^T attention of q [B, Hq, Sq, D], k, v [B, Hkv, Sk, D] (bf16, SDPA's layout)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, 4, nm)
+    bsz, hq, sq, d = q.shape
+    hkv, sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (bsz, hkv, sk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, Sk, D] matching q's batch and head_dim")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    o = out if out is not None else torch.empty_like(q)
+    ws = _workspace(sdnq_attention_workspace_bytes(bsz, hq, hkv, sq, sk, d), q.device, workspace)
+    _check(lib().sdnq_attention_int8(_ptr(q), _ptr(k), _ptr(v), bsz, hq, hkv, sq, sk, d, int(bool(is_causal)),
+                                     float(scale), int(bool(smooth_k)), int(hadamard_group), _ptr(o), _ptr(ws),
+                                     ws.numel(), _stream(q.device)), "sdnq_attention_int8")
+    return o

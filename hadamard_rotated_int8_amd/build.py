@@ -34,13 +34,19 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-file device flags.  attn.hip: keep MFMA accumulators in ordinary VGPRs.  Its
+# online softmax rescales the output accumulators with VALU multiplies, which
+# cost an accumulator-register read and write around each multiply otherwise.
+FILE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature and says so.
     noise = ("packed-fp32-ops", "unknown target feature", "warning generated", "warnings generated")

@@ -1,6 +1,7 @@
 // C ABI of libsdnq_hip: argument validation, workspace carving and the launch
 // sequence of each entry point.  Every check runs before the first launch, so a
 // call that fails writes nothing.  See sdnq_hip.h for the contract.
+#include <math.h>
 #include <string.h>
 
 #include <atomic>
@@ -473,6 +474,51 @@ sdnq_status_t sdnq_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, 
   (void)hipGetLastError();
   return launched(launch_svd_quantize_weight(w, n, k, g, rank, steps, omega, qw, w_scale, svd_a, svd_b, workspace,
                                              (hipStream_t)stream));
+}
+
+// ------------------------------------------------------- int8 attention --
+static sdnq_status_t check_attention(const void *q, const void *k, const void *v, int64_t bsz, int64_t hq, int64_t hkv,
+                                     int64_t sq, int64_t sk, int64_t d, float scale, int32_t g, const void *out) {
+  if (!q || !k || !v || !out) return SDNQ_ERR_INVALID_ARG;
+  if (bsz <= 0 || hq <= 0 || hkv <= 0 || sq <= 0 || sk <= 0) return SDNQ_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return SDNQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDNQ_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SDNQ_ERR_UNSUPPORTED;
+  if (hq % hkv != 0 || sk % 16 != 0 || sq > (1 << 20) || sk > (1 << 20)) return SDNQ_ERR_UNSUPPORTED;
+  if (bsz * hq > (1 << 16) || bsz * hkv > (1 << 16)) return SDNQ_ERR_UNSUPPORTED;
+  if (!(g == 0 || g == 1 || g == 64 || g == 128 || g == 256)) return SDNQ_ERR_UNSUPPORTED;
+  return SDNQ_OK;
+}
+
+size_t sdnq_attention_workspace_bytes(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
+                                      int64_t seq_k, int64_t head_dim) {
+  static const int probe[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  if (check_attention(probe, probe, probe, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, 1.0f, 256, probe) !=
+      SDNQ_OK)
+    return 0;
+  return attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim);
+}
+
+size_t sdnq_attention_workspace_offset(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
+                                       int64_t seq_k, int64_t head_dim, int32_t which) {
+  if (which < 0 || which > 4 || sdnq_attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim) == 0)
+    return 0;
+  size_t off[5];
+  attention_workspace_offsets(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, off);
+  return off[which];
+}
+
+sdnq_status_t sdnq_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t batch,
+                                  int64_t heads_q, int64_t heads_kv, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                                  int32_t is_causal, float scale, int32_t smooth_k, int32_t hadamard_group,
+                                  uint16_t *out, void *workspace, size_t workspace_bytes, void *stream) {
+  SDNQ_TRY(check_attention(q, k, v, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, scale, hadamard_group, out));
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim))
+    return SDNQ_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return launched(launch_attention_int8(q, k, v, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, is_causal != 0,
+                                        scale, smooth_k != 0, hadamard_group, out, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

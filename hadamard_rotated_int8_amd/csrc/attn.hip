@@ -1,0 +1,481 @@
+// Int8 Q K^T attention with K smoothing and a Hadamard rotation of the head rows.
+//
+// What it computes ("SDNQ: SD.Next Quantization Engine", the SDPA-replacement
+// example: matmul_dtype int8 for Q K^T, pv_matmul_dtype disabled, smooth_k,
+// use_hadamard with hadamard_group_size, quantize_fp32; SDPA's is_causal, scale
+// and enable_gqa).  Readings, the pages giving the options only:
+//   q [B, Hq, Sq, D], k and v [B, Hkv, Sk, D]; query head h reads head
+//   h / (Hq / Hkv) of k and v.
+//   smooth_k: mean[b, h, c] = fl32(sum_j k[b, h, j, c] / Sk), the sum in fp64 over
+//   blocks of 64 tokens (each block in token order, then the block sums in
+//   block order); K' = fl32(k - mean).
+//   Q and K' rows are rotated with block min(g, D) (the linear layer's butterfly
+//   and normalization) and quantized per token with its int8 quantizer.
+//   scores s_ij = fp32(int32 q_i . k_j) * s_q[i] * s_k[j] * scale, keys j > i
+//   masked when causal (top-left aligned); softmax; P V with P rounded to bf16 and
+//   fp32 accumulation (online, flash-attention style); bf16 output.
+//
+// Kernels:
+//  - attn_kmean_partial / attn_kmean_finish: the blocked fp64 sum, then the mean;
+//  - attn_prep_kernel: one wavefront per row of D values (D/64 per lane), the
+//    butterfly across lanes with shuffles, absmax by a wavefront reduction;
+//  - attn_vt_kernel: V [BH, Sk, D] -> V^T [BH, D, Sk] (64 x 64 LDS tiles);
+//  - attn_fwd_kernel: 128 query rows per workgroup (4 wavefronts x 32), 64 keys
+//    per step, K codes and V^T double-buffered in LDS.  S = K Q^T per wavefront
+//    with v_mfma_i32_32x32x32_i8 (lane l: query l % 32, keys 8 (r / 4) +
+//    4 (l / 32) + r % 4 in register r); P V with v_mfma_f32_32x32x16_bf16, whose
+//    contraction index is mapped to the keys so that each lane's own registers
+//    8c .. 8c + 7 form its P operand: lane group g = l / 32 takes keys
+//    16c + 4g + {0..3} and 16c + 8 + 4g + {0..3}, read from V^T as two 8-byte
+//    runs.  exp2 with the log2(e) folded into the query scale.
+#include <math.h>
+
+#include "sdnq_internal.hpp"
+
+namespace sdnq {
+namespace {
+
+constexpr int kMeanBlock = 64;       // tokens per block of the K-mean sum
+constexpr int kBM = 128;             // query rows per workgroup
+constexpr int kBN = 64;              // keys per step
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128))
+
+__device__ __forceinline__ float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// part[bh, blk, c] = sum_{j in block blk} k[bh, j, c] in token order (fp64)
+__global__ __launch_bounds__(256) void attn_kmean_partial(const uint16_t *__restrict__ k, int64_t bh_count,
+                                                          int64_t sk, int d, double *__restrict__ part) {
+  const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= bh_count * nblk * d) return;
+  const int c = (int)(idx % d);
+  const int64_t blk = (idx / d) % nblk, bh = idx / (d * nblk);
+  const int64_t j0 = blk * kMeanBlock, j1 = j0 + kMeanBlock < sk ? j0 + kMeanBlock : sk;
+  const uint16_t *p = k + (bh * sk) * d + c;
+  double s = 0.0;
+  for (int64_t j = j0; j < j1; ++j) s += (double)bf16_f32(p[j * d]);
+  part[idx] = s;
+}
+
+// mean[bh, c] = fl32((sum over blocks in order) / sk)
+__global__ __launch_bounds__(256) void attn_kmean_finish(const double *__restrict__ part, int64_t bh_count,
+                                                         int64_t sk, int d, float *__restrict__ mean) {
+  const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= bh_count * d) return;
+  const int c = (int)(idx % d);
+  const int64_t bh = idx / d;
+  double s = 0.0;
+  for (int64_t b = 0; b < nblk; ++b) s += part[(bh * nblk + b) * d + c];
+  mean[idx] = (float)(s / (double)sk);
+}
+
+template <int G>
+__device__ __forceinline__ float norm_const() {
+  if constexpr (G == 64) return 0.125f;
+  else if constexpr (G == 128) return kInvSqrt128;
+  else return 1.0f;
+}
+
+// One wavefront per row of D values; lane l holds elements VPL*l .. VPL*l + VPL-1.
+// Rows of x: [rows, D] with rows = bh * seq; offset [bh, D] (binary32) subtracted
+// first when given.  Codes [rows, D], scales [rows].
+template <int D, int G, bool OFFSET>
+__global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t seq,
+                                                        const float *__restrict__ offset, int8_t *__restrict__ codes,
+                                                        float *__restrict__ scale) {
+  constexpr int VPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // a whole wavefront leaves together
+  float v[VPL];
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) {
+    v[e] = bf16_f32(x[row * D + VPL * lane + e]);
+    if constexpr (OFFSET) v[e] = v[e] - offset[(row / seq) * D + VPL * lane + e];
+  }
+  if constexpr (G > 1) {
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1) {
+      if (h < VPL) {  // both elements of the pair in this lane
+#pragma unroll
+        for (int e = 0; e < VPL; ++e)
+          if ((e & h) == 0) {
+            const float a = v[e], b = v[e + h];
+            v[e] = a + b;
+            v[e + h] = a - b;
+          }
+      } else {
+        const int hl = h / VPL;
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) {
+          const float p = __shfl_xor(v[e], hl);
+          v[e] = (lane & hl) ? p - v[e] : v[e] + p;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) v[e] = v[e] * norm_const<G>();
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) a = fmaxf(a, fabsf(v[e]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  const float up = a < 0x1p-100f ? 0x1p100f : 1.0f;
+  const float as = a * up;
+  const float r = as > 0.0f ? 127.0f / as : 0.0f;
+  if (lane == 0) scale[row] = a / 127.0f;
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) {
+    float t = rintf((v[e] * up) * r);
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    codes[row * D + VPL * lane + e] = (int8_t)(int)t;
+  }
+}
+
+// vt[bh, c, j] = v[bh, j, c]; 64 x 64 tiles through LDS, grid (ceil(sk/64), D/64, bh)
+__global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t *__restrict__ v, int64_t sk, int d,
+                                                      uint16_t *__restrict__ vt) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t bh = blockIdx.z;
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const uint16_t *src = v + bh * sk * d;
+  uint16_t *dst = vt + bh * (int64_t)d * sk;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int jj = e / 64, cc = e % 64;
+    tile[jj][cc] = j0 + jj < sk ? src[(j0 + jj) * d + c0 + cc] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int cc = e / 64, jj = e % 64;
+    if (j0 + jj < sk) dst[(int64_t)(c0 + cc) * sk + j0 + jj] = tile[jj][cc];
+  }
+}
+
+// Block index -> (head, query tile): each XCD takes a contiguous run of the
+// logical order (heads outermost), so the K and V of a head stay in one L2.
+__device__ __forceinline__ void attn_coords(int nq, int &bh, int &qt) {
+  const int nblk = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q = nblk >> 3, rmd = nblk & 7;
+  const int logical = xcd * q + (xcd < rmd ? xcd : rmd) + local;
+  bh = logical / nq;
+  qt = logical % nq;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr unsigned kOutOfRange = 0x80000000u;  // any offset past num_records reads as zero
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict__ qc, const float *__restrict__ qs,
+                                                       const int8_t *__restrict__ kc, const float *__restrict__ ks,
+                                                       const uint16_t *__restrict__ vt, int hq, int hkv, int64_t sq,
+                                                       int64_t sk, float scale_log2, uint16_t *__restrict__ out) {
+  // LDS tiles, filled by direct global -> LDS loads (16 bytes per lane, 1 KB per
+  // wavefront instruction), 16-byte chunks XOR-swizzled by row instead of padded:
+  //   K codes [64 keys][D bytes]: chunk c of row r stored at c ^ (r % CPR);
+  //   V^T     [D rows][64 keys] bf16 (128-byte rows): chunk c of row d at c ^ (d % 8).
+  constexpr int CPR = D / 16;                 // 16-byte chunks per K row
+  constexpr int KB = kBN * D;                 // K tile bytes
+  constexpr int VB = D * kBN * 2;             // V^T tile bytes
+  constexpr int KSLOTS = KB / 1024 / 4;       // K loads per wavefront per tile
+  constexpr int VSLOTS = VB / 1024 / 4;       // V^T loads per wavefront per tile
+  constexpr int KS = D / 32;                  // 32-deep k-steps of Q K^T
+  constexpr int DT = D / 32;                  // 32-wide output column tiles of P V
+  __shared__ __attribute__((aligned(1024))) int8_t k_lds[2][KB];
+  __shared__ __attribute__((aligned(1024))) int8_t v_lds[2][VB];
+  __shared__ __attribute__((aligned(16))) float ks_lds[2][kBN];
+
+  const int nq = (int)((sq + kBM - 1) / kBM);
+  int bh, qt;
+  attn_coords(nq, bh, qt);
+  if (CAUSAL) qt = nq - 1 - qt;  // the longest rows first
+  const int b = bh / hq, h = bh % hq;
+  const int64_t bhk = (int64_t)b * hkv + h / (hq / hkv);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t q0 = (int64_t)qt * kBM;
+  const int64_t my_row = q0 + 32 * wave + (lane & 31);
+  const int my_row32 = (int)my_row, sk32 = (int)sk;  // both below 2^20
+
+  // Q fragments: lane holds row my_row, bytes 32 s + 16 g .. + 15
+  v4i qf[KS];
+  const bool row_ok = my_row < sq;
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = row_ok ? *reinterpret_cast<const v4i *>(qc + (bh * sq + my_row) * D + 32 * s + 16 * g) : v4i{0, 0, 0, 0};
+  const float qscale = row_ok ? qs[bh * sq + my_row] * scale_log2 : 0.0f;
+
+  // buffer resources over this head's K codes, K scales and V^T: rows past sk
+  // lie past num_records and read as zero; V^T chunks past sk get an
+  // out-of-range offset (the next row would follow otherwise)
+  const __amdgpu_buffer_rsrc_t rs_k =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(kc + bhk * sk * D), 0, (int)(sk * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_s =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(ks + bhk * sk), 0, (int)(sk * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_v =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vt + bhk * (int64_t)D * sk), 0, (int)(D * sk * 2), 0x00020000);
+  // per-lane parts of the load offsets
+  unsigned koff[KSLOTS], voff[VSLOTS];
+  int vkey[VSLOTS];
+#pragma unroll
+  for (int j = 0; j < KSLOTS; ++j) {
+    const int slot = j * 4 + wave;
+    const int row = slot * (64 / CPR) + lane / CPR;
+    const int lc = (lane % CPR) ^ (row % CPR);
+    koff[j] = (unsigned)(row * D + 16 * lc);
+  }
+#pragma unroll
+  for (int j = 0; j < VSLOTS; ++j) {
+    const int slot = j * 4 + wave;
+    const int d = slot * 8 + lane / 8;
+    const int lc = (lane % 8) ^ (d % 8);
+    vkey[j] = 8 * lc;
+    voff[j] = (unsigned)((d * sk32 + 8 * lc) * 2);
+  }
+  auto issue = [&](int64_t t, int buf) {
+    const int k0 = (int)(t * kBN);
+#pragma unroll
+    for (int j = 0; j < KSLOTS; ++j) {
+      const unsigned off = koff[j] + (unsigned)(k0 * D);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (lds_void *)(k_lds[buf] + 1024 * (j * 4 + wave)), 16, off, 0,
+                                               0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VSLOTS; ++j) {
+      const unsigned off = (k0 + vkey[j] < sk32) ? voff[j] + (unsigned)(k0 * 2) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lds_void *)(v_lds[buf] + 1024 * (j * 4 + wave)), 16, off, 0,
+                                               0, 0);
+    }
+    if (wave == 0) {
+      const unsigned off = (unsigned)((k0 + lane) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void *)ks_lds[buf], 4, off, 0, 0, 0);
+    }
+  };
+
+  v16f o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = v16f{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  int64_t n_tiles = (sk + kBN - 1) / kBN;
+  if (CAUSAL) {
+    const int64_t last = (q0 + kBM - 1) / kBN + 1;
+    if (last < n_tiles) n_tiles = last;
+  }
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int buf = (int)(t & 1);
+    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);  // buf ^ 1 was released by the last barrier
+    const int k032 = (int)(t * kBN);
+    const int8_t *kt = k_lds[buf];
+    const int8_t *vtile = v_lds[buf];
+    // two 32-key halves, each with its own online-softmax update
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // S = K Q^T: lane: query l % 32, key 32 u + 8 (r / 4) + 4 g + r % 4 in register r
+      v16i sacc = v16i{};
+      const int krow = 32 * u + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int lc = (2 * s + g) ^ (krow % CPR);
+        const v4i kf = *reinterpret_cast<const v4i *>(kt + krow * D + 16 * lc);
+        sacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], sacc, 0, 0, 0);
+      }
+      float sv[16];
+      const bool edge = (k032 + 32 * u + 32 > sk32) || (CAUSAL && k032 + 32 * u + 31 > (int)q0 + 32 * wave);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int kk = 32 * u + 8 * r4 + 4 * g;
+        const float4 kq = *reinterpret_cast<const float4 *>(&ks_lds[buf][kk]);
+        const float kv[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * r4 + e] = (float)sacc[4 * r4 + e] * (kv[e] * qscale);
+        if (edge) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k032 + kk + e;
+            if (key >= sk32 || (CAUSAL && key > my_row32)) sv[4 * r4 + e] = -INFINITY;
+          }
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      // m_new is finite from the first half on: key 0 is valid for every row
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float psum = 0.0f;
+      v8bf pf[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(sv[8 * c + e] - m_new);
+          psum += p[e];
+        }
+        v4u packed;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) packed[w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+        pf[c] = __builtin_bit_cast(v8bf, packed);
+      }
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // rescale the running output only when some row's maximum moved (alpha is
+      // exactly 1 otherwise)
+      if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) o[i] = o[i] * alpha;
+      }
+      // O += P V: V^T operand of lane l: row d = 32 dt + l % 32, keys 32 u + 16 c +
+      // 4 g + {0..3} (logical chunk 4 u + 2 c) and + 8 (chunk 4 u + 2 c + 1)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + (lane & 31);
+        const int8_t *vrow = vtile + d * (kBN * 2) + 8 * g;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const v2u lo = *reinterpret_cast<const v2u *>(vrow + 16 * ((4 * u + 2 * c) ^ (d % 8)));
+          const v2u hi = *reinterpret_cast<const v2u *>(vrow + 16 * ((4 * u + 2 * c + 1) ^ (d % 8)));
+          const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vv), pf[c], o[dt], 0, 0, 0);
+        }
+      }
+    }
+    // tile t + 1 has landed and every wavefront is done with tile t
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+
+  // out[bh, row, d] = bf16(o / l); lane holds d = 32 dt + 8 (r / 4) + 4 g + r % 4
+  if (!row_ok) return;
+  const float inv = 1.0f / l_run;
+  uint16_t *orow = out + (bh * sq + my_row) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      v2u pk = {pack_bf16x2(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv),
+                pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv)};
+      *reinterpret_cast<v2u *>(orow + 32 * dt + 8 * r4 + 4 * g) = pk;
+    }
+}
+
+struct AttnLayout {
+  size_t qc, qs, kc, ks, kmean, kpart, vt, total;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+AttnLayout attn_layout(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d) {
+  AttnLayout L{};
+  const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
+  size_t off = 0;
+  L.qc = off; off += align256((size_t)(bsz * hq * sq * d));
+  L.qs = off; off += align256((size_t)(bsz * hq * sq) * 4);
+  L.kc = off; off += align256((size_t)(bsz * hkv * sk * d));
+  L.ks = off; off += align256((size_t)(bsz * hkv * sk) * 4);
+  L.kmean = off; off += align256((size_t)(bsz * hkv * d) * 4);
+  L.kpart = off; off += align256((size_t)(bsz * hkv * nblk * d) * 8);
+  L.vt = off; off += align256((size_t)(bsz * hkv * sk * d) * 2);
+  L.total = off;
+  return L;
+}
+
+template <int D, int G>
+hipError_t launch_prep(const uint16_t *x, int64_t rows, int64_t seq, const float *offset, int8_t *codes, float *scale,
+                       hipStream_t s) {
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (offset)
+    hipLaunchKernelGGL((attn_prep_kernel<D, G, true>), dim3(blocks), dim3(256), 0, s, x, rows, seq, offset, codes,
+                       scale);
+  else
+    hipLaunchKernelGGL((attn_prep_kernel<D, G, false>), dim3(blocks), dim3(256), 0, s, x, rows, seq, offset, codes,
+                       scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t prep_any(int block, const uint16_t *x, int64_t rows, int64_t seq, const float *offset, int8_t *codes,
+                    float *scale, hipStream_t s) {
+  switch (block) {
+    case 1: return launch_prep<D, 1>(x, rows, seq, offset, codes, scale, s);
+    case 64: return launch_prep<D, 64>(x, rows, seq, offset, codes, scale, s);
+    case 128:
+      if constexpr (D >= 128) return launch_prep<D, 128>(x, rows, seq, offset, codes, scale, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t attention_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t bsz, int64_t hq, int64_t hkv,
+                       int64_t sq, int64_t sk, bool causal, float scale, bool smooth_k, int g, uint16_t *out,
+                       void *ws, hipStream_t s) {
+  const AttnLayout L = attn_layout(bsz, hq, hkv, sq, sk, D);
+  char *base = static_cast<char *>(ws);
+  int8_t *qc = reinterpret_cast<int8_t *>(base + L.qc);
+  float *qs = reinterpret_cast<float *>(base + L.qs);
+  int8_t *kc = reinterpret_cast<int8_t *>(base + L.kc);
+  float *ks = reinterpret_cast<float *>(base + L.ks);
+  float *kmean = reinterpret_cast<float *>(base + L.kmean);
+  double *kpart = reinterpret_cast<double *>(base + L.kpart);
+  uint16_t *vt = reinterpret_cast<uint16_t *>(base + L.vt);
+  const int block = g <= 1 ? 1 : (g < D ? g : D);
+  const int64_t bhk = bsz * hkv;
+  hipError_t e;
+  if (smooth_k) {
+    const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
+    const int64_t np = bhk * nblk * D, nm = bhk * D;
+    hipLaunchKernelGGL(attn_kmean_partial, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s, k, bhk, sk, D, kpart);
+    hipLaunchKernelGGL(attn_kmean_finish, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s, kpart, bhk, sk, D,
+                       kmean);
+  }
+  if ((e = prep_any<D>(block, q, bsz * hq * sq, sq, nullptr, qc, qs, s)) != hipSuccess) return e;
+  if ((e = prep_any<D>(block, k, bhk * sk, sk, smooth_k ? kmean : nullptr, kc, ks, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_vt_kernel, dim3((unsigned)((sk + 63) / 64), D / 64, (unsigned)bhk), dim3(256), 0, s, v, sk,
+                     D, vt);
+  const int64_t nq = (sq + kBM - 1) / kBM;
+  const unsigned blocks = (unsigned)(nq * bsz * hq);
+  const float sl = scale * kLog2e;
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3(blocks), dim3(256), 0, s, qc, qs, kc, ks, vt, (int)hq,
+                       (int)hkv, sq, sk, sl, out);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), dim3(blocks), dim3(256), 0, s, qc, qs, kc, ks, vt, (int)hq,
+                       (int)hkv, sq, sk, sl, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attention_workspace_bytes(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d) {
+  return attn_layout(bsz, hq, hkv, sq, sk, d).total;
+}
+
+void attention_workspace_offsets(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d,
+                                 size_t *offsets) {
+  const AttnLayout L = attn_layout(bsz, hq, hkv, sq, sk, d);
+  offsets[0] = L.qc;
+  offsets[1] = L.qs;
+  offsets[2] = L.kc;
+  offsets[3] = L.ks;
+  offsets[4] = L.kmean;
+}
+
+hipError_t launch_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t bsz, int64_t hq,
+                                 int64_t hkv, int64_t sq, int64_t sk, int64_t d, bool causal, float scale,
+                                 bool smooth_k, int g, uint16_t *out, void *workspace, hipStream_t stream) {
+  if (d == 64) return attention_d<64>(q, k, v, bsz, hq, hkv, sq, sk, causal, scale, smooth_k, g, out, workspace, stream);
+  if (d == 128)
+    return attention_d<128>(q, k, v, bsz, hq, hkv, sq, sk, causal, scale, smooth_k, g, out, workspace, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdnq

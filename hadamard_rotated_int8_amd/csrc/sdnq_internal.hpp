@@ -22,11 +22,11 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+// fp32 -> bf16 bits, round to nearest even: one v_cvt_pk_bf16_f32 for the pair.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
 }
 
 // ------------------------------------------------------------------ launches --
@@ -100,5 +100,16 @@ size_t svd_workspace_q_offset(int64_t n, int64_t k, int rank);
 hipError_t launch_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int g, int rank, int steps,
                                       const float *omega, int8_t *qw, float *w_scale, uint16_t *svd_a,
                                       uint16_t *svd_b, void *workspace, hipStream_t stream);
+
+// Int8 Q K^T attention (q [B, Hq, Sq, D], k, v [B, Hkv, Sk, D] bf16, D in {64, 128},
+// Sk % 16 == 0).  The workspace holds, in order, q codes [B, Hq, Sq, D], q scales,
+// k codes [B, Hkv, Sk, D], k scales and the K mean [B, Hkv, D] at the offsets
+// attention_workspace_offsets() returns, then scratch.
+size_t attention_workspace_bytes(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d);
+void attention_workspace_offsets(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d,
+                                 size_t *offsets);
+hipError_t launch_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t bsz, int64_t hq,
+                                 int64_t hkv, int64_t sq, int64_t sk, int64_t d, bool causal, float scale,
+                                 bool smooth_k, int g, uint16_t *out, void *workspace, hipStream_t stream);
 
 }  // namespace sdnq

@@ -245,6 +245,43 @@ size_t sdnq_svd_workspace_bytes(int64_t n, int64_t k, int32_t rank);
 /* Byte offset of Q [n,rank] (fp64) in that workspace; 0 on invalid sizes. */
 size_t sdnq_svd_workspace_q_offset(int64_t n, int64_t k, int32_t rank);
 
+/* ------------------------------------------------------ int8 attention ------
+ * The quantized attention of "SDNQ: SD.Next Quantization Engine" (its
+ * SDPA-replacement example: Q K^T as an int8 quantized matmul, P V unquantized,
+ * smooth_k, use_hadamard with hadamard_group_size, quantize_fp32, and SDPA's
+ * is_causal, scale and enable_gqa).  The pages name the options only; readings:
+ *  - q[batch, heads_q, seq_q, head_dim], k and v[batch, heads_kv, seq_k, head_dim],
+ *    out like q, all bf16; query head h reads key/value head h / (heads_q / heads_kv);
+ *  - smooth_k != 0: K minus its mean over the key tokens per (batch, head,
+ *    channel), mean = fl32(sum / seq_k) with the sum in fp64 over blocks of 64
+ *    tokens (each in token order, then the block sums in order), K' = fl32(k - mean);
+ *  - hadamard_group g in {64, 128, 256}: Q and K' rows are rotated with block
+ *    min(g, head_dim) (the butterfly and normalization above); g = 0 or 1: none;
+ *  - Q and K' are quantized per token (one scale per row over head_dim) with the
+ *    row quantization above;
+ *  - scores = fp32(int32 q . k) * s_q * s_k * scale (scale > 0; the usual value is
+ *    1/sqrt(head_dim)); is_causal != 0 masks keys j > i (top-left aligned);
+ *  - softmax, then P V with P rounded to bf16 and fp32 accumulation; bf16 out.
+ * head_dim in {64, 128}; seq_k a multiple of 16; seq_q, seq_k <= 2^20;
+ * batch * heads <= 65536; heads_q % heads_kv == 0.
+ * workspace: sdnq_attention_workspace_bytes(...) bytes, 16-byte aligned.  When the
+ * work has completed it holds the q codes [batch, heads_q, seq_q, head_dim] (int8),
+ * q scales (fp32), k codes, k scales and the K mean [batch, heads_kv, head_dim]
+ * (fp32) at sdnq_attention_workspace_offset(..., which = 0 .. 4). */
+sdnq_status_t sdnq_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t batch,
+                                  int64_t heads_q, int64_t heads_kv, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                                  int32_t is_causal, float scale, int32_t smooth_k, int32_t hadamard_group,
+                                  uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace size in bytes for sdnq_attention_int8; 0 on invalid sizes. */
+size_t sdnq_attention_workspace_bytes(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
+                                      int64_t seq_k, int64_t head_dim);
+
+/* Byte offset in that workspace of: 0 q codes, 1 q scales, 2 k codes, 3 k scales,
+ * 4 K mean; 0 on invalid arguments. */
+size_t sdnq_attention_workspace_offset(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
+                                       int64_t seq_k, int64_t head_dim, int32_t which);
+
 #ifdef __cplusplus
 }
 #endif

@@ -406,7 +406,8 @@ def svd_quantize_weight(w_bf16: np.ndarray, g: int, omega: np.ndarray, steps: in
 #     head h // (Hq / Hkv) (grouped-query attention);
 #   * smooth_k subtracts from K its mean over the key tokens, per batch, head and
 #     channel (the softmax of each query row is unchanged by a shift common to
-#     all keys); the mean is fl32(sum / Sk) with the sum taken in fp64 in token
+#     all keys); the mean is fl32(sum / Sk) with the sum taken in fp64 over blocks
+#     of 64 tokens, each block in token order, then the block sums in block
 #     order; K' = fl32(k - mean);
 #   * the rotation block along the head dimension is min(g, D) (g <= 1: none),
 #     with the butterfly, normalization and per-row int8 quantizer of the
@@ -416,10 +417,13 @@ def svd_quantize_weight(w_bf16: np.ndarray, g: int, omega: np.ndarray, steps: in
 #   * softmax and P V in fp64 on the bf16 values of v, one rounding to bf16.
 
 def attention_k_mean(k_bf16: np.ndarray) -> np.ndarray:
-    """Per (batch, head, channel) mean of k [B, H, S, D] over the tokens:
-    fl32(fp64 sum in token order / S), as binary32 [B, H, D]."""
+    """Per (batch, head, channel) mean of k [B, H, S, D] over the tokens as
+    binary32 [B, H, D]: fl32(sum / S), the fp64 sum taken block by block (64
+    tokens, in token order), then over the blocks in order."""
     kf = f32_from_bf16(k_bf16).astype(np.float64)
-    total = np.cumsum(kf, axis=2)[:, :, -1, :]
+    total = np.zeros(kf.shape[:2] + kf.shape[3:], np.float64)
+    for b0 in range(0, kf.shape[2], 64):
+        total = total + np.cumsum(kf[:, :, b0:b0 + 64, :], axis=2)[:, :, -1, :]
     return (total / kf.shape[2]).astype(np.float32)
 
 

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
               "sdnq_status_string", "sdnq_gemm_i8_i32", "sdnq_rotate_quantize_weight_fp8",
               "sdnq_rotate_quantize_act_fp8", "sdnq_qlinear_forward_fp8", "sdnq_qlinear_forward_fp8_quantized",
               "sdnq_gemm_fp8_f32", "sdnq_qlinear_weight_grad", "sdnq_weight_grad_workspace_bytes",
-              "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset"):
+              "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset",
+              "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset"):
         assert n in names
 
 
@@ -235,3 +236,30 @@ def test_svd_workspace_bytes():
     assert f(n, k, r) >= n * k * 4 + n * k * 2 + n * r * 8   # residual, W^T, Q
     assert h.sdnq_svd_workspace_q_offset(n, k, r) >= n * k * 4
     assert f(n, k, 48) == 0 and f(n, 100, r) == 0 and f(16, 256, 32) == 0
+
+
+@no_gpu
+def test_attention_validation():
+    L = h.lib()
+
+    def f(q=A, k=B, v=C, b=1, hq=4, hkv=2, sq=64, sk=64, d=128, causal=0, scale=0.1, smooth=1, g=256, out=D,
+          ws=W, wsb=WS):
+        return L.sdnq_attention_int8(q, k, v, b, hq, hkv, sq, sk, d, causal, scale, smooth, g, out, ws, wsb, None)
+    assert f(q=None) == INVALID and f(out=None) == INVALID and f(b=0) == INVALID and f(sq=0) == INVALID
+    assert f(scale=0.0) == INVALID and f(scale=-1.0) == INVALID and f(scale=float("nan")) == INVALID
+    assert f(q=A + 8) == INVALID and f(out=D + 2) == INVALID
+    assert f(d=96) == UNSUPPORTED and f(d=256) == UNSUPPORTED
+    assert f(hkv=3) == UNSUPPORTED and f(sk=40) == UNSUPPORTED and f(g=32) == UNSUPPORTED
+    assert f(ws=None) == WORKSPACE
+    assert f(wsb=h.sdnq_attention_workspace_bytes(1, 4, 2, 64, 64, 128) - 1) == WORKSPACE
+
+
+def test_attention_workspace():
+    f = h.sdnq_attention_workspace_bytes
+    b, hq, hkv, s, d = 1, 24, 24, 4608, 128
+    n = f(b, hq, hkv, s, s, d)
+    assert n >= b * hq * s * d + b * hkv * s * d + b * hkv * s * d * 2   # q and k codes, V^T
+    offs = [h.sdnq_attention_workspace_offset(b, hq, hkv, s, s, d, i) for i in range(5)]
+    assert offs == sorted(offs) and offs[0] == 0 and offs[1] >= b * hq * s * d and all(o % 256 == 0 for o in offs)
+    assert f(1, 4, 3, 64, 64, 128) == 0 and f(1, 4, 2, 64, 40, 128) == 0 and f(1, 4, 2, 64, 64, 80) == 0
+    assert h.sdnq_attention_workspace_offset(1, 4, 2, 64, 64, 128, 5) == 0

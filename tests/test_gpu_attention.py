@@ -1,0 +1,141 @@
+"""GPU parity of the int8-QK^T attention against the oracle.
+
+Bit-exact: the q and k codes and scales and the K mean that the entry point
+leaves in its workspace (both sides take every rounding decision on the same
+binary32 values in the same order).  Within 1e-2 relative L2 per head: the
+output (the GPU accumulates P V in fp32 from bf16 P with exp2; the oracle
+computes softmax and P V in fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_int8_amd as h
+import oracle
+from hadamard_rotated_int8_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    h.lib()
+    oracle.set_num_threads(16)
+    yield
+    torch.cuda.synchronize()
+
+
+def d_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def h_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(q, k, v, causal, smooth, g, scale=None):
+    b, hq, sq, d = q.shape
+    hkv, sk = k.shape[1], k.shape[2]
+    say(f"  attention B={b} Hq={hq} Hkv={hkv} Sq={sq} Sk={sk} D={d} causal={causal} smooth={smooth} g={g}")
+    ws = torch.empty(h.sdnq_attention_workspace_bytes(b, hq, hkv, sq, sk, d), dtype=torch.uint8, device=DEV)
+    out = h.sdnq_attention_int8(d_bf16(q), d_bf16(k), d_bf16(v), causal, scale, smooth, g, workspace=ws)
+    torch.cuda.synchronize()
+    off = [h.sdnq_attention_workspace_offset(b, hq, hkv, sq, sk, d, i) for i in range(5)]
+    nq, nk = b * hq * sq, b * hkv * sk
+    res = {
+        "out": h_bits(out),
+        "q_codes": ws[off[0]: off[0] + nq * d].cpu().numpy().view(np.int8).reshape(b, hq, sq, d),
+        "q_scales": ws[off[1]: off[1] + 4 * nq].cpu().numpy().view(np.float32).reshape(b, hq, sq),
+        "k_codes": ws[off[2]: off[2] + nk * d].cpu().numpy().view(np.int8).reshape(b, hkv, sk, d),
+        "k_scales": ws[off[3]: off[3] + 4 * nk].cpu().numpy().view(np.float32).reshape(b, hkv, sk),
+        "k_mean": ws[off[4]: off[4] + 4 * b * hkv * d].cpu().numpy().view(np.float32).reshape(b, hkv, d),
+    }
+    return res
+
+
+def rel_l2_per_head(got_bits, ref_bits):
+    g = synth.bf16_bits_to_f32(got_bits).astype(np.float64)
+    r = synth.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    num = np.sqrt(((g - r) ** 2).sum(axis=(-2, -1)))
+    den = np.sqrt((r ** 2).sum(axis=(-2, -1)))
+    return (num / den).max()
+
+
+def check(q, k, v, causal, smooth, g, q_rows=None, scale=None):
+    got = run(q, k, v, causal, smooth, g, scale)
+    ref = oracle.attention_int8(q, k, v, causal, scale, smooth, g, intermediates=True, q_rows=q_rows)
+    rows = slice(None) if q_rows is None else np.asarray(q_rows)
+    assert np.array_equal(got["k_codes"], ref["k_codes"]), "k codes"
+    assert np.array_equal(got["k_scales"].view(np.uint32), ref["k_scales"].view(np.uint32)), "k scales"
+    if smooth:
+        assert np.array_equal(got["k_mean"].view(np.uint32), ref["k_mean"].view(np.uint32)), "k mean"
+    assert np.array_equal(got["q_codes"][:, :, rows], ref["q_codes"]), "q codes"
+    assert np.array_equal(got["q_scales"][:, :, rows].view(np.uint32), ref["q_scales"].view(np.uint32)), "q scales"
+    err = rel_l2_per_head(got["out"][:, :, rows], ref["out"])
+    say(f"    output rel-L2 (worst head) {err:.3e}")
+    assert np.all(np.isfinite(synth.bf16_bits_to_f32(got["out"])))
+    assert err < REL_L2
+    return got, ref
+
+
+def inputs(b, hq, hkv, sq, sk, d, seed, bias=3.0):
+    rng = np.random.default_rng(seed)
+    q = synth.to_bf16_bits(rng.standard_normal((b, hq, sq, d)).astype(np.float32))
+    k = synth.to_bf16_bits((rng.standard_normal((b, hkv, sk, d)) + rng.standard_normal((b, hkv, 1, d)) * bias)
+                           .astype(np.float32))
+    v = synth.to_bf16_bits(rng.standard_normal((b, hkv, sk, d)).astype(np.float32))
+    return q, k, v
+
+
+def test_attention_tiny_config():
+    c = synth.ATTENTION_CONFIGS["attn_tiny"]
+    d = synth.make_attention("attn_tiny")
+    check(d["q"], d["k"], d["v"], c.causal, True, 256)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("smooth,g", [(True, 256), (False, 256), (True, 64), (True, 1), (False, 0)])
+def test_attention_options(d, causal, smooth, g):
+    q, k, v = inputs(1, 4, 2, 150, 208, d, 30 + d + int(causal))
+    check(q, k, v, causal, smooth, g)
+
+
+@pytest.mark.parametrize("sq,sk", [(1, 16), (17, 16), (128, 64), (129, 80), (300, 1024)])
+def test_attention_ragged_and_tiny_lengths(sq, sk):
+    q, k, v = inputs(2, 2, 1, sq, sk, 128, 40 + sq)
+    check(q, k, v, True, True, 256)
+    check(q, k, v, False, True, 256, scale=0.05)
+
+
+def test_attention_text_encoder_config():
+    c = synth.ATTENTION_CONFIGS["attn_te"]
+    d = synth.make_attention("attn_te")
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(c.seq_q - 4, c.seq_q),
+                                     np.random.default_rng(5).choice(c.seq_q, 24, replace=False)]))
+    check(d["q"], d["k"], d["v"], True, True, 256, q_rows=rows)
+
+
+def test_attention_flux_full_size():
+    """flux.1 joint attention (24 heads x 128, 4608 tokens): every code and scale,
+    and the output on sampled query rows of every head; then the error against
+    exact fp64 attention on the same sampled rows."""
+    c = synth.ATTENTION_CONFIGS["attn_flux"]
+    d = synth.make_attention("attn_flux")
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(c.seq_q - 4, c.seq_q),
+                                     np.random.default_rng(6).choice(c.seq_q, 24, replace=False)]))
+    got, ref = check(d["q"], d["k"], d["v"], False, True, 256, q_rows=rows)
+    f = lambda b: torch.from_numpy(synth.bf16_bits_to_f32(b).astype(np.float64))
+    exact = torch.nn.functional.scaled_dot_product_attention(f(d["q"][:, :, rows]), f(d["k"]), f(d["v"])).numpy()
+    o = synth.bf16_bits_to_f32(got["out"][:, :, rows]).astype(np.float64)
+    err = np.linalg.norm(o - exact) / np.linalg.norm(exact)
+    say(f"    error vs exact attention {err:.3e}")
+    assert err < 0.03

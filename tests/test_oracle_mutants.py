@@ -62,6 +62,7 @@ PY_MUTANTS = {
                                      "    b_bits = bf16_from_f64(np.ascontiguousarray((w @ om).T))"),
     "attn_mean_divides_by_head_dim": ("    return (total / kf.shape[2]).astype(np.float32)",
                                       "    return (total / kf.shape[3]).astype(np.float32)"),
+    "attn_mean_drops_a_block": ("    for b0 in range(0, kf.shape[2], 64):", "    for b0 in range(64, kf.shape[2], 64):"),
     "attn_causal_off_by_one": ("    mask = (np.arange(sk)[None, :] > rows[:, None]) if is_causal else None",
                                "    mask = (np.arange(sk)[None, :] >= rows[:, None]) if is_causal else None"),
     "attn_gqa_modulo": ("            hk = h // rep", "            hk = h % hkv"),

@@ -826,17 +826,18 @@ def test_attention_causal_brute_force():
 
 
 def test_attention_k_mean_is_the_exact_mean_rounded_once():
-    """Values n/16 with |n| < 128 (exact in bf16): every fp64 partial sum is
-    exact, so the mean is the exact rational mean rounded once to binary32."""
+    """Values n/16 with |n| < 128 (exact in bf16), 150 tokens (three blocks of the
+    summation): every fp64 partial sum is exact, so the mean is the exact
+    rational mean divided in fp64 and rounded to binary32."""
     rng = np.random.default_rng(14)
-    kf = rng.integers(-127, 128, (1, 2, 37, 64)).astype(np.float64) / 16
+    kf = rng.integers(-127, 128, (1, 2, 150, 64)).astype(np.float64) / 16
     k = oracle.bf16_from_f64(kf)
     assert np.array_equal(synth.bf16_bits_to_f32(k).astype(np.float64), kf)
     mean = oracle.attention_k_mean(k)
     for h in range(2):
         for c in range(64):
-            exact = Fraction(int(round(kf[0, h, :, c].sum() * 16)), 16 * 37)
-            assert mean[0, h, c] == nearest_f32(exact)
+            exact = Fraction(int(round(kf[0, h, :, c].sum() * 16)), 16 * 150)
+            assert mean[0, h, c] == np.float32(float(exact))
 
 
 def test_attention_smoothing_ignores_a_key_offset_common_to_all_tokens():
