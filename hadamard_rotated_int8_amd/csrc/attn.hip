@@ -17,8 +17,9 @@
 //
 // Kernels:
 //  - attn_kmean_partial / attn_kmean_finish: the blocked fp64 sum, then the mean;
-//  - attn_prep_kernel: one wavefront per row of D values (D/64 per lane), the
-//    butterfly across lanes with shuffles, absmax by a wavefront reduction;
+//  - attn_prep_kernel: sixteen lanes per row of D values (D/16 per lane), the
+//    butterfly in registers and across the row's lanes with shuffles, absmax by
+//    a 16-lane reduction;
 //  - attn_vt_kernel: V [BH, Sk, D] -> V^T [BH, D, Sk] (64 x 64 LDS tiles);
 //  - attn_fwd_kernel: 128 query rows per workgroup (4 wavefronts x 32), 64 keys
 //    per step, K codes and V^T double-buffered in LDS.  S = K Q^T per wavefront
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(256) void attn_kmean_partial(const uint16_t *__rest
   const int64_t j0 = blk * kMeanBlock, j1 = j0 + kMeanBlock < sk ? j0 + kMeanBlock : sk;
   const uint16_t *p = k + (bh * sk) * d + c;
   double s = 0.0;
+#pragma unroll 16
   for (int64_t j = j0; j < j1; ++j) s += (double)bf16_f32(p[j * d]);
   part[idx] = s;
 }
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(256) void attn_kmean_finish(const double *__restric
   const int c = (int)(idx % d);
   const int64_t bh = idx / d;
   double s = 0.0;
+#pragma unroll 8
   for (int64_t b = 0; b < nblk; ++b) s += part[(bh * nblk + b) * d + c];
   mean[idx] = (float)(s / (double)sk);
 }
@@ -78,22 +81,46 @@ __device__ __forceinline__ float norm_const() {
   else return 1.0f;
 }
 
-// One wavefront per row of D values; lane l holds elements VPL*l .. VPL*l + VPL-1.
-// Rows of x: [rows, D] with rows = bh * seq; offset [bh, D] (binary32) subtracted
-// first when given.  Codes [rows, D], scales [rows].
+// Sixteen lanes per row of D values, four rows per wavefront; lane l of a row
+// holds elements VPL*l .. VPL*l + VPL-1 (16 bytes of bf16 for D = 128).  Rows of
+// x: [rows, D] with rows = bh * seq; offset [bh, D] (binary32) subtracted first
+// when given.  Codes [rows, D], scales [rows].
 template <int D, int G, bool OFFSET>
 __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t seq,
                                                         const float *__restrict__ offset, int8_t *__restrict__ codes,
                                                         float *__restrict__ scale) {
-  constexpr int VPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;  // a whole wavefront leaves together
+  constexpr int VPL = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool ok = row < rows;  // lanes of a missing row still take part in the shuffles
   float v[VPL];
+  if constexpr (VPL == 8) {
+    const v4u raw = ok ? *reinterpret_cast<const v4u *>(x + row * D + 8 * l16) : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int e = 0; e < VPL; ++e) {
-    v[e] = bf16_f32(x[row * D + VPL * lane + e]);
-    if constexpr (OFFSET) v[e] = v[e] - offset[(row / seq) * D + VPL * lane + e];
+    for (int w = 0; w < 4; ++w) {
+      v[2 * w] = bf16_lo(raw[w]);
+      v[2 * w + 1] = bf16_hi(raw[w]);
+    }
+  } else {
+    const v2u raw = ok ? *reinterpret_cast<const v2u *>(x + row * D + 4 * l16) : v2u{0u, 0u};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      v[2 * w] = bf16_lo(raw[w]);
+      v[2 * w + 1] = bf16_hi(raw[w]);
+    }
+  }
+  if constexpr (OFFSET) {
+    if (ok) {
+      const float *o = offset + (row / seq) * D + VPL * l16;
+#pragma unroll
+      for (int e = 0; e < VPL; e += 4) {
+        const float4 f = *reinterpret_cast<const float4 *>(o + e);
+        v[e] = v[e] - f.x;
+        v[e + 1] = v[e + 1] - f.y;
+        v[e + 2] = v[e + 2] - f.z;
+        v[e + 3] = v[e + 3] - f.w;
+      }
+    }
   }
   if constexpr (G > 1) {
 #pragma unroll
@@ -107,11 +134,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
             v[e + h] = a - b;
           }
       } else {
-        const int hl = h / VPL;
+        const int hl = h / VPL;  // 1, 2, 4, 8: within the row's 16 lanes
 #pragma unroll
         for (int e = 0; e < VPL; ++e) {
           const float p = __shfl_xor(v[e], hl);
-          v[e] = (lane & hl) ? p - v[e] : v[e] + p;
+          v[e] = (l16 & hl) ? p - v[e] : v[e] + p;
         }
       }
     }
@@ -122,20 +149,36 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
 #pragma unroll
   for (int e = 0; e < VPL; ++e) a = fmaxf(a, fabsf(v[e]));
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
   const float up = a < 0x1p-100f ? 0x1p100f : 1.0f;
   const float as = a * up;
   const float r = as > 0.0f ? 127.0f / as : 0.0f;
-  if (lane == 0) scale[row] = a / 127.0f;
+  if (!ok) return;
+  if (l16 == 0) scale[row] = a / 127.0f;
+  uint32_t packed[VPL / 4];
 #pragma unroll
-  for (int e = 0; e < VPL; ++e) {
-    float t = rintf((v[e] * up) * r);
-    t = fminf(fmaxf(t, -127.0f), 127.0f);
-    codes[row * D + VPL * lane + e] = (int8_t)(int)t;
+  for (int w = 0; w < VPL / 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float t = rintf((v[4 * w + e] * up) * r);
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      word |= ((uint32_t)(int)t & 0xFFu) << (8 * e);
+    }
+    packed[w] = word;
   }
+  if constexpr (VPL == 8)
+    *reinterpret_cast<v2u *>(codes + row * D + 8 * l16) = v2u{packed[0], packed[1]};
+  else
+    *reinterpret_cast<uint32_t *>(codes + row * D + 4 * l16) = packed[0];
 }
 
-// vt[bh, c, j] = v[bh, j, c]; 64 x 64 tiles through LDS, grid (ceil(sk/64), D/64, bh)
+// vt[bh, c, p] = v[bh, key(p), c]: V^T with the keys of every 16-key group stored
+// in the order 0-3, 8-11, 4-7, 12-15, so that the 8 keys one lane feeds to the
+// P V product are 16 contiguous bytes.  64 x 64 tiles through LDS, grid
+// (ceil(sk/64), D/64, bh); sk is a multiple of 16.
+__device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
 __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t *__restrict__ v, int64_t sk, int d,
                                                       uint16_t *__restrict__ vt) {
   __shared__ uint16_t tile[64][66];
@@ -150,8 +193,8 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t *__restrict
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int cc = e / 64, jj = e % 64;
-    if (j0 + jj < sk) dst[(int64_t)(c0 + cc) * sk + j0 + jj] = tile[jj][cc];
+    const int cc = e / 64, pp = e % 64;
+    if (j0 + pp < sk) dst[(int64_t)(c0 + cc) * sk + j0 + pp] = tile[vt_key(pp)][cc];
   }
 }
 
@@ -177,7 +220,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
   // LDS tiles, filled by direct global -> LDS loads (16 bytes per lane, 1 KB per
   // wavefront instruction), 16-byte chunks XOR-swizzled by row instead of padded:
   //   K codes [64 keys][D bytes]: chunk c of row r stored at c ^ (r % CPR);
-  //   V^T     [D rows][64 keys] bf16 (128-byte rows): chunk c of row d at c ^ (d % 8).
+  //   V^T     [D rows][64 key positions] bf16 (128-byte rows, keys permuted within
+  //           16-key groups as attn_vt_kernel stores them): chunk c of row d at
+  //           c ^ (d % 8).
   constexpr int CPR = D / 16;                 // 16-byte chunks per K row
   constexpr int KB = kBN * D;                 // K tile bytes
   constexpr int VB = D * kBN * 2;             // V^T tile bytes
@@ -294,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
         const float4 kq = *reinterpret_cast<const float4 *>(&ks_lds[buf][kk]);
         const float kv[4] = {kq.x, kq.y, kq.z, kq.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[4 * r4 + e] = (float)sacc[4 * r4 + e] * (kv[e] * qscale);
+        for (int e = 0; e < 4; ++e) sv[4 * r4 + e] = (float)sacc[4 * r4 + e] * kv[e];
         if (edge) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -303,13 +348,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
           }
         }
       }
+      // sv holds acc * s_k (the row's positive factor s_q * scale * log2 e is
+      // applied inside the exponent, after the max)
       float mx = sv[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * qscale;
       const float m_new = fmaxf(m_run, mx);
       // m_new is finite from the first half on: key 0 is valid for every row
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float neg_m = -m_new;
       float psum = 0.0f;
       v8bf pf[2];
 #pragma unroll
@@ -317,7 +365,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(sv[8 * c + e] - m_new);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * c + e], qscale, neg_m));
           psum += p[e];
         }
         v4u packed;
@@ -335,17 +383,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
         for (int i = 0; i < DT; ++i) o[i] = o[i] * alpha;
       }
       // O += P V: V^T operand of lane l: row d = 32 dt + l % 32, keys 32 u + 16 c +
-      // 4 g + {0..3} (logical chunk 4 u + 2 c) and + 8 (chunk 4 u + 2 c + 1)
+      // 4 g + {0..3, 8..11}, i.e. stored positions 32 u + 16 c + 8 g .. + 7, one
+      // logical 16-byte chunk 4 u + 2 c + g
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + (lane & 31);
-        const int8_t *vrow = vtile + d * (kBN * 2) + 8 * g;
+        const int8_t *vrow = vtile + d * (kBN * 2);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const v2u lo = *reinterpret_cast<const v2u *>(vrow + 16 * ((4 * u + 2 * c) ^ (d % 8)));
-          const v2u hi = *reinterpret_cast<const v2u *>(vrow + 16 * ((4 * u + 2 * c + 1) ^ (d % 8)));
-          const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vv), pf[c], o[dt], 0, 0, 0);
+          const v8bf vv = *reinterpret_cast<const v8bf *>(vrow + 16 * ((4 * u + 2 * c + g) ^ (d % 8)));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pf[c], o[dt], 0, 0, 0);
         }
       }
     }
@@ -391,7 +438,7 @@ AttnLayout attn_layout(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t
 template <int D, int G>
 hipError_t launch_prep(const uint16_t *x, int64_t rows, int64_t seq, const float *offset, int8_t *codes, float *scale,
                        hipStream_t s) {
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  const unsigned blocks = (unsigned)((rows + 15) / 16);
   if (offset)
     hipLaunchKernelGGL((attn_prep_kernel<D, G, true>), dim3(blocks), dim3(256), 0, s, x, rows, seq, offset, codes,
                        scale);
