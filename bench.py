@@ -53,7 +53,8 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_mlp_4096tok_hbm_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc", "gemm_i8.hip")
+# the GEMM kernel's sources: its own file and the shared device header it includes
+GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc", f) for f in ("gemm_i8.hip", "sdnq_internal.hpp")]
 
 
 def measured_traffic():
@@ -67,7 +68,7 @@ def measured_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in GEMM_SOURCES)).hexdigest()
         if kv.get("source_sha256") != sha:
             return None
         return [int(kv["up_bytes"]), int(kv["down_bytes"])]
@@ -126,8 +127,8 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     the layer, each on its own workload: weight preparation, the attention
     projection forward, the QuaRot-style forward with LoRA (g = 64 and 128), the
     PEFT backward (input gradient + LoRA gradients), the full fine-tuning weight
-    gradient, the FP8 (E4M3) variant of the MLP step, and the low-rank (SVD)
-    split with the forward that uses it."""
+    gradient, the FP8 (E4M3) variant of the MLP step, the low-rank (SVD)
+    split with the forward that uses it, and the int8-QK^T attention."""
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
 
@@ -244,6 +245,26 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     rows["svd_forward_4096x3072x3072_g256_r32"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
                                                    "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
                                                    "note": "int8 residual + bf16 rank-32 factors in the epilogue"}
+    del x, w, omega, qw, sw, sa, sb, ws, y
+    # int8-QK^T attention: flux.1 joint attention and a causal grouped-query text encoder
+    for name in ("attn_flux", "attn_te"):
+        ac = synth.ATTENTION_CONFIGS[name]
+        ai = synth.make_attention(name)
+        q, k, v = (to_dev_bf16(torch, ai[t]) for t in ("q", "k", "v"))
+        aws = torch.empty(h.sdnq_attention_workspace_bytes(ac.batch, ac.heads_q, ac.heads_kv, ac.seq_q, ac.seq_k,
+                                                           ac.head_dim), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        us = timed(lambda: h.sdnq_attention_int8(q, k, v, ac.causal, None, True, 256, out=o, workspace=aws))
+        pairs = ac.seq_q * ac.seq_k * (0.5 if ac.causal else 1.0)
+        ops = 4.0 * ac.batch * ac.heads_q * pairs * ac.head_dim
+        ref_us = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=ac.causal,
+                                                                                enable_gqa=True))
+        rows[f"attention_int8_{name[5:]}_{ac.batch}x{ac.heads_q}x{ac.seq_q}x{ac.head_dim}"] = {
+            "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+            "torch_sdpa_bf16_us": round(ref_us, 2),
+            "note": "whole call (K mean, rotate+quantize of Q and K, V transpose, int8 QK^T / bf16 PV kernel); "
+                    "ops = 2 (QK^T) + 2 (PV) per query-key pair and head dimension"}
+        del q, k, v, aws, o
     return rows
 
 
