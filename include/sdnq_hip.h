@@ -263,7 +263,8 @@ size_t sdnq_svd_workspace_q_offset(int64_t n, int64_t k, int32_t rank);
  *    1/sqrt(head_dim)); is_causal != 0 masks keys j > i (top-left aligned);
  *  - softmax, then P V with P rounded to bf16 and fp32 accumulation; bf16 out.
  * head_dim in {64, 128}; seq_k a multiple of 16; seq_q, seq_k <= 2^20;
- * batch * heads <= 65536; heads_q % heads_kv == 0.
+ * batch * heads_q and batch * heads_kv <= 65535; batch * heads * seq <= 2^31 for
+ * q and for k; heads_q % heads_kv == 0.
  * workspace: sdnq_attention_workspace_bytes(...) bytes, 16-byte aligned.  When the
  * work has completed it holds the q codes [batch, heads_q, seq_q, head_dim] (int8),
  * q scales (fp32), k codes, k scales and the K mean [batch, heads_kv, head_dim]

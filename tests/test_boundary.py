@@ -250,6 +250,8 @@ def test_attention_validation():
     assert f(q=A + 8) == INVALID and f(out=D + 2) == INVALID
     assert f(d=96) == UNSUPPORTED and f(d=256) == UNSUPPORTED
     assert f(hkv=3) == UNSUPPORTED and f(sk=40) == UNSUPPORTED and f(g=32) == UNSUPPORTED
+    assert f(b=65536, hq=1, hkv=1) == UNSUPPORTED                      # grid z of the V transpose
+    assert f(b=4096, hq=16, hkv=16, sq=1 << 16, sk=1 << 16) == UNSUPPORTED  # 2^32 rows
     assert f(ws=None) == WORKSPACE
     assert f(wsb=h.sdnq_attention_workspace_bytes(1, 4, 2, 64, 64, 128) - 1) == WORKSPACE
 
