@@ -83,15 +83,15 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   return L;
 }
 
-// Weight gradient: a bf16 transpose buffer (dy^T, then x^T) and the two quantized
+// Weight gradient: the per-feature absmax words of dy and x, then the two quantized
 // transposed operands with their per-feature scales.
 struct WgradLayout {
-  size_t tbuf, qdy, sdy, qx, sx, total;
+  size_t colmax, qdy, sdy, qx, sx, total;
 };
 WgradLayout wgrad_layout(int64_t m, int64_t n, int64_t k) {
   WgradLayout L{};
   size_t off = 0;
-  L.tbuf = off; off += align_up((size_t)(n > k ? n : k) * (size_t)m * 2);
+  L.colmax = off; off += align_up((size_t)(n + k) * 4);
   L.qdy = off; off += align_up((size_t)n * (size_t)m);
   L.sdy = off; off += align_up((size_t)n * 4);
   L.qx = off; off += align_up((size_t)k * (size_t)m);
@@ -379,15 +379,13 @@ sdnq_status_t sdnq_qlinear_weight_grad(const uint16_t *dy, const uint16_t *x, in
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (m == 0) return launched(launch_fill_zero_u16(dw, n * k, s));  // empty sum
-  uint16_t *tbuf = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tbuf));
+  uint32_t *colmax = reinterpret_cast<uint32_t *>(ws_at(workspace, L.colmax));
   int8_t *qdy = reinterpret_cast<int8_t *>(ws_at(workspace, L.qdy));
   float *sdy = reinterpret_cast<float *>(ws_at(workspace, L.sdy));
   int8_t *qx = reinterpret_cast<int8_t *>(ws_at(workspace, L.qx));
   float *sx = reinterpret_cast<float *>(ws_at(workspace, L.sx));
-  SDNQ_LAUNCH(launch_transpose_u16(dy, m, n, tbuf, s));                   // dy^T [n, m]
-  SDNQ_LAUNCH(launch_rotate_quantize(tbuf, n, m, g, nullptr, qdy, sdy, s));  // per feature, along tokens
-  SDNQ_LAUNCH(launch_transpose_u16(x, m, k, tbuf, s));                    // x^T [k, m]
-  SDNQ_LAUNCH(launch_rotate_quantize(tbuf, k, m, g, nullptr, qx, sx, s));
+  // per feature, rotated along the tokens: the codes of dy^T [n, m] and x^T [k, m]
+  SDNQ_LAUNCH(launch_colq_pair(dy, n, qdy, sdy, x, k, qx, sx, m, g, colmax, s));
   GemmArgs ga{};
   ga.a = qdy; ga.b = qx; ga.m = n; ga.n = k; ga.k = m;
   ga.row_scale = sdy; ga.col_scale = sx; ga.out_bf16 = dw; ga.g = 1;

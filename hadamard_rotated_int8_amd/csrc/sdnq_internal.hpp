@@ -91,6 +91,13 @@ int lora_grad_splits(int64_t m);
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
                             float scale, bool transposed, float *partials, uint16_t *out, hipStream_t stream);
 
+// Rotate (block g along the tokens) + per-feature int8 quantization of two
+// operands sharing the token count m, each x [m, f] bf16 read as it is: q [f, m]
+// (the codes of x^T) and scale [f].  colmax [f0 + f1] is scratch (zeroed here).
+// m is a multiple of 16 and of g, f0 and f1 of 16 (f1 may be 0).
+hipError_t launch_colq_pair(const uint16_t *x0, int64_t f0, int8_t *q0, float *s0, const uint16_t *x1, int64_t f1,
+                            int8_t *q1, float *s1, int64_t m, int g, uint32_t *colmax, hipStream_t stream);
+
 // Low-rank (SVD) split of w [n, k] with rank in {16, 32, 64}, then rotate + int8
 // quantization of the binary32 residual.  The workspace holds the residual [n, k]
 // (binary32) at offset 0 and the orthonormal basis Q [n, rank] (fp64) at

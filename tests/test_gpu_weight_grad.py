@@ -43,7 +43,8 @@ def inputs(m, n, k, seed):
 
 
 @pytest.mark.parametrize("g", [1, 64, 128, 256])
-@pytest.mark.parametrize("m,n,k", [(512, 256, 256), (768, 272, 400), (256, 16, 48), (1280, 640, 3072)])
+@pytest.mark.parametrize("m,n,k", [(512, 256, 256), (768, 272, 400), (256, 16, 48), (1280, 640, 3072),
+                                   (400, 80, 48), (320, 96, 144), (16, 32, 16)])
 def test_weight_grad_bit_exact(m, n, k, g):
     if m % g:
         pytest.skip("m must be a multiple of g")
@@ -76,9 +77,15 @@ def test_weight_grad_peft_size_sampled_rows():
     oracle.set_num_threads(16)
     xt = np.ascontiguousarray(inp["x"].T)
     qx, sx = oracle.rotate_quantize(xt, 256)
-    # the workspace holds q_x [k, m] and s_x [k] after the bf16 transpose buffer and q_dy, s_dy
+    # the workspace holds, after a per-feature absmax scratch of n + k words,
+    # q_dy [n, m], s_dy [n], q_x [k, m], s_x [k]
     al = lambda v: (v + 255) // 256 * 256
-    off = al(max(n, k) * m * 2) + al(n * m) + al(n * 4)
+    o_dy = al((n + k) * 4)
+    qdy, sdy = oracle.rotate_quantize(np.ascontiguousarray(inp["dy"].T), 256)
+    assert np.array_equal(ws[o_dy: o_dy + n * m].view(n, m).cpu().numpy().view(np.int8), qdy)
+    sdy_gpu = ws[o_dy + al(n * m): o_dy + al(n * m) + 4 * n].cpu().numpy().view(np.float32)
+    assert np.array_equal(sdy_gpu.view(np.uint32), sdy.view(np.uint32))
+    off = o_dy + al(n * m) + al(n * 4)
     assert np.array_equal(ws[off: off + k * m].view(k, m).cpu().numpy().view(np.int8), qx)
     sx_gpu = ws[off + al(k * m): off + al(k * m) + 4 * k].cpu().numpy().view(np.float32)
     assert np.array_equal(sx_gpu.view(np.uint32), sx.view(np.uint32))
