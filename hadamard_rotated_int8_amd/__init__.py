@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     sdnq_svd_workspace_bytes,
     sdnq_svd_workspace_q_offset,
     sdnq_qlinear_weight_grad,
+    sdnq_weight_grad_workspace_offset,
     sdnq_weight_grad_workspace_bytes,
     sdnq_workspace_bytes,
     status_string,

@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.sdnq_workspace_bytes.restype = sz
     L.sdnq_weight_grad_workspace_bytes.argtypes = [i64, i64, i64]
     L.sdnq_weight_grad_workspace_bytes.restype = sz
+    L.sdnq_weight_grad_workspace_offset.argtypes = [i64, i64, i64, i32]
+    L.sdnq_weight_grad_workspace_offset.restype = sz
     L.sdnq_svd_workspace_bytes.argtypes = [i64, i64, i32]
     L.sdnq_svd_workspace_bytes.restype = sz
     L.sdnq_svd_workspace_q_offset.argtypes = [i64, i64, i32]
@@ -280,6 +282,10 @@ def sdnq_gemm_fp8_f32(a, b):
 
 def sdnq_weight_grad_workspace_bytes(m: int, n: int, k: int) -> int:
     return int(lib().sdnq_weight_grad_workspace_bytes(m, n, k))
+
+
+def sdnq_weight_grad_workspace_offset(m: int, n: int, k: int, which: int) -> int:
+    return int(lib().sdnq_weight_grad_workspace_offset(m, n, k, which))
 
 
 def sdnq_qlinear_weight_grad(dy, x, g, out=None, workspace=None):

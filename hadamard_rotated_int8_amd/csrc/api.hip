@@ -357,8 +357,16 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
 
 // ----------------------------------------------------- weight gradient --
 size_t sdnq_weight_grad_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m < 0 || n <= 0 || k <= 0) return 0;
+  if (m < 0 || check_feature(n) != SDNQ_OK || check_feature(k) != SDNQ_OK) return 0;
+  if (m > 0 && check_feature(m) != SDNQ_OK) return 0;
   return wgrad_layout(m, n, k).total;
+}
+
+size_t sdnq_weight_grad_workspace_offset(int64_t m, int64_t n, int64_t k, int32_t which) {
+  if (which < 0 || which > 3 || sdnq_weight_grad_workspace_bytes(m, n, k) == 0) return 0;
+  const WgradLayout L = wgrad_layout(m, n, k);
+  const size_t off[4] = {L.qdy, L.sdy, L.qx, L.sx};
+  return off[which];
 }
 
 sdnq_status_t sdnq_qlinear_weight_grad(const uint16_t *dy, const uint16_t *x, int64_t m, int64_t n, int64_t k,
@@ -384,6 +392,7 @@ sdnq_status_t sdnq_qlinear_weight_grad(const uint16_t *dy, const uint16_t *x, in
   float *sdy = reinterpret_cast<float *>(ws_at(workspace, L.sdy));
   int8_t *qx = reinterpret_cast<int8_t *>(ws_at(workspace, L.qx));
   float *sx = reinterpret_cast<float *>(ws_at(workspace, L.sx));
+  SDNQ_LAUNCH(launch_fill_zero_u16(reinterpret_cast<uint16_t *>(colmax), 2 * (n + k), s));
   // per feature, rotated along the tokens: the codes of dy^T [n, m] and x^T [k, m]
   SDNQ_LAUNCH(launch_colq_pair(dy, n, qdy, sdy, x, k, qx, sx, m, g, colmax, s));
   GemmArgs ga{};

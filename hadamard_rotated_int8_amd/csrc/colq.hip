@@ -218,8 +218,6 @@ hipError_t launch_colq_pair(const uint16_t *x0, int64_t f0, int8_t *q0, float *s
   if ((m + kTok - 1) / kTok > 65535) return hipErrorInvalidValue;
   const ColqOperand a{x0, f0, (f0 + kFeat - 1) / kFeat, colmax, q0, s0};
   const ColqOperand b{x1, f1, (f1 + kFeat - 1) / kFeat, colmax + f0, q1, s1};
-  hipError_t e = launch_fill_zero_u16(reinterpret_cast<uint16_t *>(colmax), 2 * (f0 + f1), stream);
-  if (e != hipSuccess) return e;
   switch (g) {
     case 1: return launch_colq_g<1>(a, b, m, stream);
     case 64: return launch_colq_g<64>(a, b, m, stream);

@@ -93,7 +93,7 @@ hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, in
 
 // Rotate (block g along the tokens) + per-feature int8 quantization of two
 // operands sharing the token count m, each x [m, f] bf16 read as it is: q [f, m]
-// (the codes of x^T) and scale [f].  colmax [f0 + f1] is scratch (zeroed here).
+// (the codes of x^T) and scale [f].  colmax [f0 + f1] is scratch, zero on entry.
 // m is a multiple of 16 and of g, f0 and f1 of 16 (f1 may be 0).
 hipError_t launch_colq_pair(const uint16_t *x0, int64_t f0, int8_t *q0, float *s0, const uint16_t *x1, int64_t f1,
                             int8_t *q1, float *s1, int64_t m, int g, uint32_t *colmax, hipStream_t stream);

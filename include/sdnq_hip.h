@@ -164,6 +164,11 @@ sdnq_status_t sdnq_qlinear_weight_grad(const uint16_t *dy, const uint16_t *x, in
 /* Workspace size in bytes for sdnq_qlinear_weight_grad; 0 on invalid sizes. */
 size_t sdnq_weight_grad_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
+/* Byte offset in that workspace of: 0 q_dy [n,m] (int8), 1 s_dy [n] (fp32),
+ * 2 q_x [k,m] (int8), 3 s_x [k] (fp32), which hold the quantized operands once the
+ * call has completed; 0 on invalid arguments. */
+size_t sdnq_weight_grad_workspace_offset(int64_t m, int64_t n, int64_t k, int32_t which);
+
 /* ---------------------------------------------------------------- FP8 ------
  * The FP8 variant of the quantized matmul ("SDNQ: SD.Next Quantization Engine":
  * INT8 and FP8 quantized matmul; the SDNQConfig example's matmul dtype

@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
               "sdnq_status_string", "sdnq_gemm_i8_i32", "sdnq_rotate_quantize_weight_fp8",
               "sdnq_rotate_quantize_act_fp8", "sdnq_qlinear_forward_fp8", "sdnq_qlinear_forward_fp8_quantized",
               "sdnq_gemm_fp8_f32", "sdnq_qlinear_weight_grad", "sdnq_weight_grad_workspace_bytes",
+              "sdnq_weight_grad_workspace_offset",
               "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset",
               "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset"):
         assert n in names
@@ -206,6 +207,14 @@ def test_weight_grad_validation():
     assert f(ws=None) == WORKSPACE and f(wsb=100) == WORKSPACE
     assert f(m=64, g=64, wsb=h.sdnq_weight_grad_workspace_bytes(64, 256, 256) - 1) == WORKSPACE
     assert h.sdnq_weight_grad_workspace_bytes(16384, 3072, 3072) >= 16384 * 3072 * 2   # codes of dy^T and x^T
+    for m, n, k in ((16384, 3072, 3072), (64, 256, 256), (2048, 2000, 3008)):
+        total = h.sdnq_weight_grad_workspace_bytes(m, n, k)
+        off = [h.sdnq_weight_grad_workspace_offset(m, n, k, i) for i in range(4)]
+        ends = [off[0] + n * m, off[1] + 4 * n, off[2] + k * m, off[3] + 4 * k]
+        assert all(o % 256 == 0 for o in off) and off[0] > 0
+        assert all(ends[i] <= off[i + 1] for i in range(3)) and ends[3] <= total
+    assert h.sdnq_weight_grad_workspace_offset(64, 256, 256, 4) == 0
+    assert h.sdnq_weight_grad_workspace_offset(64, 100, 256, 0) == 0
 
 
 

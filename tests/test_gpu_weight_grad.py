@@ -1,7 +1,7 @@
 """GPU parity of the weight gradient through the quantized matmul (full
-fine-tuning), through the C ABI, against the CPU oracle: bf16 transposes, the
-per-feature rotate+quantize along the tokens and the exact int32 GEMM with the
-fp32 dequantization are all deterministic, so dW is compared bit for bit."""
+fine-tuning), through the C ABI, against the CPU oracle: the per-feature
+rotate+quantize along the tokens and the exact int32 GEMM with the fp32
+dequantization are all deterministic, so dW is compared bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -77,19 +77,39 @@ def test_weight_grad_peft_size_sampled_rows():
     oracle.set_num_threads(16)
     xt = np.ascontiguousarray(inp["x"].T)
     qx, sx = oracle.rotate_quantize(xt, 256)
-    # the workspace holds, after a per-feature absmax scratch of n + k words,
-    # q_dy [n, m], s_dy [n], q_x [k, m], s_x [k]
-    al = lambda v: (v + 255) // 256 * 256
-    o_dy = al((n + k) * 4)
+    off = [h.sdnq_weight_grad_workspace_offset(m, n, k, i) for i in range(4)]
     qdy, sdy = oracle.rotate_quantize(np.ascontiguousarray(inp["dy"].T), 256)
-    assert np.array_equal(ws[o_dy: o_dy + n * m].view(n, m).cpu().numpy().view(np.int8), qdy)
-    sdy_gpu = ws[o_dy + al(n * m): o_dy + al(n * m) + 4 * n].cpu().numpy().view(np.float32)
+    assert np.array_equal(ws[off[0]: off[0] + n * m].view(n, m).cpu().numpy().view(np.int8), qdy)
+    sdy_gpu = ws[off[1]: off[1] + 4 * n].cpu().numpy().view(np.float32)
     assert np.array_equal(sdy_gpu.view(np.uint32), sdy.view(np.uint32))
-    off = o_dy + al(n * m) + al(n * 4)
-    assert np.array_equal(ws[off: off + k * m].view(k, m).cpu().numpy().view(np.int8), qx)
-    sx_gpu = ws[off + al(k * m): off + al(k * m) + 4 * k].cpu().numpy().view(np.float32)
+    assert np.array_equal(ws[off[2]: off[2] + k * m].view(k, m).cpu().numpy().view(np.int8), qx)
+    sx_gpu = ws[off[3]: off[3] + 4 * k].cpu().numpy().view(np.float32)
     assert np.array_equal(sx_gpu.view(np.uint32), sx.view(np.uint32))
     rows = np.array([0, 1, 1000, 2047, 3071])
     dyt = np.ascontiguousarray(inp["dy"].T)[rows]
     ref = oracle.qlinear_forward(dyt, qx, sx, 256, intermediates=False)["y"]
     assert np.array_equal(h_bits(dw)[rows], ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(16384, 3072, 3072), (2048, 2000, 3008), (4096, 2896, 3008)])
+def test_weight_grad_matches_forward_gemm_on_its_codes(m, n, k):
+    """dW against sdnq_qlinear_forward_quantized on the codes the call left in its
+    workspace (the same int32 GEMM and epilogue through the forward entry point),
+    at sizes too large for the oracle's int64 matmul, with ragged tile edges along
+    both output axes."""
+    rng = np.random.default_rng(m + n + k)
+    dy = synth.to_bf16_bits((rng.standard_normal((m, n)) * 1e-3).astype(np.float32))
+    x = synth.to_bf16_bits(synth.outlier_activations(rng, m, k))
+    say(f"  weight_grad m={m} n={n} k={k} g=256 against the forward GEMM")
+    ws = torch.empty(h.sdnq_weight_grad_workspace_bytes(m, n, k), dtype=torch.uint8, device=DEV)
+    dw = h.sdnq_qlinear_weight_grad(d_bf16(dy), d_bf16(x), 256, workspace=ws)
+    off = [h.sdnq_weight_grad_workspace_offset(m, n, k, i) for i in range(4)]
+    qdy = ws[off[0]: off[0] + n * m].view(torch.int8).view(n, m)
+    sdy = ws[off[1]: off[1] + 4 * n].view(torch.float32)
+    qx = ws[off[2]: off[2] + k * m].view(torch.int8).view(k, m)
+    sx = ws[off[3]: off[3] + 4 * k].view(torch.float32)
+    whole = h.sdnq_qlinear_forward_quantized(qdy, sdy, qx, sx)
+    torch.cuda.synchronize()
+    got, ref = h_bits(dw), h_bits(whole)
+    assert np.array_equal(got, ref), f"{np.mean(got != ref):.6f} of the outputs differ"
+    assert np.count_nonzero(ref) > 0.9 * ref.size
