@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings of the other workloads")
+    ap.add_argument("--no-smi", action="store_true",
+                    help="do not start rocm-smi for the clock record (under a profiler that preloads into children)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 256 MiB device-to-device copy first (scales the HBM byte counters)")
     return ap.parse_args()
@@ -76,10 +78,13 @@ def measured_traffic():
         return None
 
 
-def environment(torch) -> dict:
+def environment(torch, query_smi: bool = True) -> dict:
     """Device, ROCm and clock information recorded with the numbers (rocm-smi's
     current clocks, read after the timed region; None where unavailable)."""
     env = {"device": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
+    if not query_smi:
+        env["clocks"] = None
+        return env
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         card = next(iter(json.loads(r.stdout).values())) if r.returncode == 0 else {}
@@ -428,7 +433,7 @@ def main():
         "kernel_cold_median_min_us": {k: [round(float(np.median(cold[:, j])) * 1e3, 2),
                                           round(float(cold[:, j].min()) * 1e3, 2)]
                                       for j, k in enumerate(kernels)},
-        "env": environment(torch),
+        "env": environment(torch, not args.no_smi),
     }
     if not args.no_rows:
         out["rows"] = measure_rows(torch, h, synth)
