@@ -441,10 +441,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       }
     }
   } else {
-    // Backward: WAVES_M = 8, so one wavefront holds all 256 output columns of
-    // its 32 tokens: column c = 32*j + 8*(r/4) + 4*half + (r%4) of the tile,
-    // i.e. bits 0-1 = r%4, bit 2 = lane half, bits 3-4 = r/4, bits 5-7 = j.
-    static_assert(WAVES_M == 8 && SN == 8, "backward epilogue needs full-width wavefront tiles");
+    // Backward.  A wavefront holds TN = 256 / WAVES_N consecutive output columns
+    // of its tokens: column c = wn*TN + 32*j + 8*(r/4) + 4*half + (r%4) of the
+    // tile, i.e. bits 0-1 = r%4, bit 2 = lane half, bits 3-4 = r/4, then j.
+    // WAVES_M = 8: all 256 columns.  WAVES_M = 4 (4 x 2 wavefronts, the forward's
+    // fragment traffic): 128 columns, enough for g <= 128.  Every stage runs in
+    // the wavefront's registers.
+    static_assert((WAVES_M == 8 && SN == 8) || (WAVES_M == 4 && SN == 4 && BN == 256 && G <= 128),
+                  "backward epilogue: the rotation block lies within a wavefront's columns");
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         int64_t nrow[SN];
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
-          const int64_t nr = n0 + j * 32 + (lane & 31);
+          const int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
           nrow[j] = nr < N ? nr : N - 1;
         }
         lora_all<1, SN>(args.lora_t, args.lora_r, mrow, nrow, args.rank, lane, ot);
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         if (m < M) {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int64_t n = n0 + j * 32 + 8 * q4 + 4 * half;
+            const int64_t n = n0 + wn * TN + j * 32 + 8 * q4 + 4 * half;
             if (n < N) {
               uint2 packed;
               packed.x = pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]);
@@ -576,10 +580,14 @@ hipError_t launch_typed(const GemmArgs &args, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Backward tiles: 4 x 2 wavefronts where the rotation block fits in a
+// wavefront's 128 columns, else 8 x 1 (all 256 columns per wavefront).  The
+// 4 x 2 layout at g = 256 with the h = 128 stage through LDS measured slower.
 template <int G>
 hipError_t launch_backward(const GemmArgs &args, hipStream_t stream) {
-  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 256, 8, G, true>(args, stream)
-                       : launch_typed<Epilogue::kBackward, 256, 8, G, false>(args, stream);
+  constexpr int kWavesM = G <= 128 ? 4 : 8;
+  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 256, kWavesM, G, true>(args, stream)
+                       : launch_typed<Epilogue::kBackward, 256, kWavesM, G, false>(args, stream);
 }
 
 // Output tile width along N for the forward and int32 epilogues.  One workgroup
