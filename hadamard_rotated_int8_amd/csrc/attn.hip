@@ -28,7 +28,8 @@
 //    contraction index is mapped to the keys so that each lane's own registers
 //    8c .. 8c + 7 form its P operand: lane group g = l / 32 takes keys
 //    16c + 4g + {0..3} and 16c + 8 + 4g + {0..3}, read from V^T as two 8-byte
-//    runs.  exp2 with the log2(e) folded into the query scale.
+//    runs.  exp2 with the log2(e) folded into the query scale; the softmax offset
+//    is lazy (it moves only when a row maximum grows by more than 2^8).
 #include <math.h>
 
 #include "sdnq_internal.hpp"
@@ -40,6 +41,7 @@ constexpr int kMeanBlock = 64;       // tokens per block of the K-mean sum
 constexpr int kBM = 128;             // query rows per workgroup
 constexpr int kBN = 64;              // keys per step
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.0f;    // the softmax offset moves when the maximum grows past 2^8
 constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128))
 
 __device__ __forceinline__ float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -354,11 +356,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * qscale;
-      const float m_new = fmaxf(m_run, mx);
-      // m_new is finite from the first half on: key 0 is valid for every row
+      // Lazy reference: the exponent's offset m_run moves only when the row's
+      // maximum exceeds it by more than kLazyLog2, so p <= 2^kLazyLog2 and the
+      // running output is rescaled rarely.  softmax is unchanged: numerator and
+      // denominator share the offset.  The first half moves it (key 0 is valid
+      // for every row, so it is finite from then on).
+      const float m_new = mx > m_run + kLazyLog2 ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       const float neg_m = -m_new;
-      float psum = 0.0f;
+      float psum2[2] = {0.0f, 0.0f};
       v8bf pf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -366,17 +372,18 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const int8_t *__restrict_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * c + e], qscale, neg_m));
-          psum += p[e];
+          psum2[c] += p[e];
         }
         v4u packed;
 #pragma unroll
         for (int w = 0; w < 4; ++w) packed[w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
         pf[c] = __builtin_bit_cast(v8bf, packed);
       }
+      float psum = psum2[0] + psum2[1];
       psum += __shfl_xor(psum, 32);
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      // rescale the running output only when some row's maximum moved (alpha is
+      // rescale the running output only when some row's offset moved (alpha is
       // exactly 1 otherwise)
       if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
