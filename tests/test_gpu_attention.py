@@ -139,3 +139,25 @@ def test_attention_flux_full_size():
     err = np.linalg.norm(o - exact) / np.linalg.norm(exact)
     say(f"    error vs exact attention {err:.3e}")
     assert err < 0.03
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_row_maximum_keeps_growing(causal):
+    """Scores that rise along the keys: every query has a component along one
+    direction u and key j carries t_j u with t_j increasing, so a row's maximum
+    grows by about 2^3 per 32-key step (2^42 over the row) and the softmax
+    offset, which moves when the maximum passes it by 2^8, has to follow it
+    several times; a late key then jumps 2^22 above the rest.  The output must
+    still match the oracle."""
+    rng = np.random.default_rng(77)
+    b, hq, hkv, s, d = 1, 2, 1, 320, 128
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((b, hq, s, d)) * 0.3 + 4.0 * u
+    t = np.linspace(0.0, 60.0, s)
+    k = rng.standard_normal((b, hkv, s, d)) * 0.3 + t[None, None, :, None] * u
+    k[:, :, s - 40, :] += 40.0 * u  # one late key far above the rest
+    v = rng.standard_normal((b, hkv, s, d))
+    qb, kb, vb = (synth.to_bf16_bits(a.astype(np.float32)) for a in (q, k, v))
+    check(qb, kb, vb, causal, True, 256)
+    check(qb, kb, vb, causal, False, 128)
