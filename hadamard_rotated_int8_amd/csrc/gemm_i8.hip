@@ -406,39 +406,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       }
     }
   } else if constexpr (EPI == Epilogue::kForward) {
+    // The dequantized tile goes through LDS (free once the k loop has ended), 128
+    // rows at a time, so that it leaves as whole row segments of BN * 2 bytes in
+    // 16-byte non-temporal stores.  Written through, the output does not linger
+    // dirty in the caches to be written back while the next kernel (the next
+    // layer's rotate+quantize) streams its own data.  Rows are padded by 16
+    // bytes, which spreads the 8-byte writes of 16 consecutive rows over the banks.
+    constexpr int kPitch = BN * 2 + 16;
+    constexpr int kPassRows = BM / 2;
+    static_assert(kPassRows * kPitch <= STAGES * kStageBytes, "staged half tile fits in the ring");
+    static_assert(TM <= kPassRows, "a wavefront's rows lie in one pass");
+    int8_t *const stage = smem;
+    __syncthreads();  // every wavefront is done with its last fragments
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
-      const int64_t mc = m < M ? m : M - 1;
-      const float sx = args.row_scale[mc];
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((wm * TM) / kPassRows == pass) {
 #pragma unroll
-      for (int j = 0; j < SN; ++j) {
-        const int64_t nb = n0 + wn * TN + j * 32 + 4 * half;
-        v16f o;
+        for (int i = 0; i < SM; ++i) {
+          const int row = wm * TM + i * 32 + (lane & 31);
+          const int64_t m = m0 + row;
+          const int64_t mc = m < M ? m : M - 1;
+          const float sx = args.row_scale[mc];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          int64_t n = nb + 8 * q4;
-          n = n < N ? n : N - 4;
-          const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
-          o[4 * q4 + 0] = acc_f32(acc[i][j][4 * q4 + 0]) * (sx * sw.x);
-          o[4 * q4 + 1] = acc_f32(acc[i][j][4 * q4 + 1]) * (sx * sw.y);
-          o[4 * q4 + 2] = acc_f32(acc[i][j][4 * q4 + 2]) * (sx * sw.z);
-          o[4 * q4 + 3] = acc_f32(acc[i][j][4 * q4 + 3]) * (sx * sw.w);
-        }
-        if (m < M) {
+          for (int j = 0; j < SN; ++j) {
+            const int col = wn * TN + j * 32 + 4 * half;
+            v16f o;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int64_t n = nb + 8 * q4;
-            if (n < N) {
-              uint2 packed;
-              packed.x = pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]);
-              packed.y = pack_bf16x2(o[4 * q4 + 2], o[4 * q4 + 3]);
-              *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
+            for (int q4 = 0; q4 < 4; ++q4) {
+              int64_t n = n0 + col + 8 * q4;
+              n = n < N ? n : N - 4;
+              const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
+              o[4 * q4 + 0] = acc_f32(acc[i][j][4 * q4 + 0]) * (sx * sw.x);
+              o[4 * q4 + 1] = acc_f32(acc[i][j][4 * q4 + 1]) * (sx * sw.y);
+              o[4 * q4 + 2] = acc_f32(acc[i][j][4 * q4 + 2]) * (sx * sw.z);
+              o[4 * q4 + 3] = acc_f32(acc[i][j][4 * q4 + 3]) * (sx * sw.w);
             }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const v2u packed{pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]), pack_bf16x2(o[4 * q4 + 2], o[4 * q4 + 3])};
+              *reinterpret_cast<v2u *>(stage + (row - pass * kPassRows) * kPitch + (col + 8 * q4) * 2) = packed;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile at a time: bounds register pressure
           }
         }
-        __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile at a time: bounds register pressure
       }
+      __syncthreads();
+      // 16-byte chunks of the staged rows, row-major: consecutive lanes cover a
+      // row segment contiguously (N is a multiple of 16, so a chunk is whole or
+      // past the end)
+      constexpr int kRowChunks = BN / 8;
+      for (int c = tid; c < kPassRows * kRowChunks; c += kThreads) {
+        const int r = c / kRowChunks, k = c - r * kRowChunks;
+        const int64_t m = m0 + pass * kPassRows + r, n = n0 + 8 * k;
+        if (m < M && n < N)
+          __builtin_nontemporal_store(*reinterpret_cast<const v4u *>(stage + r * kPitch + 16 * k),
+                                      reinterpret_cast<v4u *>(args.out_bf16 + m * N + n));
+      }
+      if (pass == 0) __syncthreads();  // the second half overwrites the staging area
     }
   } else {
     // Backward.  A wavefront holds TN = 256 / WAVES_N consecutive output columns
