@@ -334,6 +334,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   // Accumulator layout (32 x 32 tile, lane l, register r):
   //   token m = l % 32, output column n = 8 * (r / 4) + 4 * (l / 32) + r % 4.
   const int half = lane >> 5;
+
+  // bf16 outputs leave through LDS (free once the k loop has ended), 128 rows at
+  // a time, as whole row segments of BN * 2 bytes in 16-byte non-temporal
+  // stores.  Written through, the output does not linger dirty in the caches to
+  // be written back while the next kernel (the next layer's rotate+quantize)
+  // streams its own data.  Rows are padded by 16 bytes, which spreads the 8-byte
+  // writes of 16 consecutive rows over the banks.
+  constexpr int kPitch = BN * 2 + 16;
+  constexpr int kPassRows = BM / 2;
+  constexpr int kRowChunks = BN / 8;
+  static_assert(kPassRows * kPitch <= STAGES * kStageBytes, "staged half tile fits in the ring");
+  static_assert(TM <= kPassRows, "a wavefront's rows lie in one pass");
+  int8_t *const stage = smem;
+  // stores the staged rows of pass `pass` (N is a multiple of 16, so a 16-byte
+  // chunk is whole or past the end); consecutive lanes cover a row contiguously
+  auto store_pass = [&](int pass) {
+    for (int c = tid; c < kPassRows * kRowChunks; c += kThreads) {
+      const int r = c / kRowChunks, k = c - r * kRowChunks;
+      const int64_t m = m0 + pass * kPassRows + r, n = n0 + 8 * k;
+      if (m < M && n < N)
+        __builtin_nontemporal_store(*reinterpret_cast<const v4u *>(stage + r * kPitch + 16 * k),
+                                    reinterpret_cast<v4u *>(args.out_bf16 + m * N + n));
+    }
+  };
+  // a wavefront's packed outputs pk[i][j][q4]: tile row wm*TM + 32 i + lane % 32,
+  // columns wn*TN + 32 j + 8 q4 + 4 half .. + 3
+  auto stage_and_store = [&](const v2u (&pk)[SM][SN][4]) {
+    __syncthreads();  // every wavefront is done with its last fragments
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((wm * TM) / kPassRows == pass) {
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+          for (int j = 0; j < SN; ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              *reinterpret_cast<v2u *>(stage + (wm * TM + i * 32 + (lane & 31) - pass * kPassRows) * kPitch +
+                                       (wn * TN + j * 32 + 8 * q4 + 4 * half) * 2) = pk[i][j][q4];
+      }
+      __syncthreads();
+      store_pass(pass);
+      if (pass == 0) __syncthreads();  // the second half overwrites the staging area
+    }
+  };
+
   if constexpr (EPI == Epilogue::kInt32) {
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
@@ -387,36 +433,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       nrow[j] = nr < N ? nr : N - 1;
     }
     lora_all<SM, SN>(args.lora_t, args.lora_r, mrow, nrow, args.rank, lane, o);
+    v2u pk[SM][SN][4];
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
-      if (m >= M) continue;
+    for (int i = 0; i < SM; ++i)
 #pragma unroll
-      for (int j = 0; j < SN; ++j) {
+      for (int j = 0; j < SN; ++j)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t n = n0 + wn * TN + j * 32 + 4 * half + 8 * q4;
-          if (n < N) {
-            uint2 packed;
-            packed.x = pack_bf16x2(o[i][j][4 * q4 + 0], o[i][j][4 * q4 + 1]);
-            packed.y = pack_bf16x2(o[i][j][4 * q4 + 2], o[i][j][4 * q4 + 3]);
-            *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
-          }
-        }
-      }
-    }
+        for (int q4 = 0; q4 < 4; ++q4)
+          pk[i][j][q4] = v2u{pack_bf16x2(o[i][j][4 * q4 + 0], o[i][j][4 * q4 + 1]),
+                             pack_bf16x2(o[i][j][4 * q4 + 2], o[i][j][4 * q4 + 3])};
+    stage_and_store(pk);
   } else if constexpr (EPI == Epilogue::kForward) {
-    // The dequantized tile goes through LDS (free once the k loop has ended), 128
-    // rows at a time, so that it leaves as whole row segments of BN * 2 bytes in
-    // 16-byte non-temporal stores.  Written through, the output does not linger
-    // dirty in the caches to be written back while the next kernel (the next
-    // layer's rotate+quantize) streams its own data.  Rows are padded by 16
-    // bytes, which spreads the 8-byte writes of 16 consecutive rows over the banks.
-    constexpr int kPitch = BN * 2 + 16;
-    constexpr int kPassRows = BM / 2;
-    static_assert(kPassRows * kPitch <= STAGES * kStageBytes, "staged half tile fits in the ring");
-    static_assert(TM <= kPassRows, "a wavefront's rows lie in one pass");
-    int8_t *const stage = smem;
+    // Dequantized straight into the staging area, pass by pass (the wavefronts
+    // of the other pass have nothing to keep in registers meanwhile).
     __syncthreads();  // every wavefront is done with its last fragments
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -451,17 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         }
       }
       __syncthreads();
-      // 16-byte chunks of the staged rows, row-major: consecutive lanes cover a
-      // row segment contiguously (N is a multiple of 16, so a chunk is whole or
-      // past the end)
-      constexpr int kRowChunks = BN / 8;
-      for (int c = tid; c < kPassRows * kRowChunks; c += kThreads) {
-        const int r = c / kRowChunks, k = c - r * kRowChunks;
-        const int64_t m = m0 + pass * kPassRows + r, n = n0 + 8 * k;
-        if (m < M && n < N)
-          __builtin_nontemporal_store(*reinterpret_cast<const v4u *>(stage + r * kPitch + 16 * k),
-                                      reinterpret_cast<v4u *>(args.out_bf16 + m * N + n));
-      }
+      store_pass(pass);
       if (pass == 0) __syncthreads();  // the second half overwrites the staging area
     }
   } else {
@@ -473,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     // the wavefront's registers.
     static_assert((WAVES_M == 8 && SN == 8) || (WAVES_M == 4 && SN == 4 && BN == 256 && G <= 128),
                   "backward epilogue: the rotation block lies within a wavefront's columns");
+    v2u pk[SM][SN][4];
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
@@ -577,21 +597,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
         const v16f &o = ot[0][j];
-        if (m < M) {
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int64_t n = n0 + wn * TN + j * 32 + 8 * q4 + 4 * half;
-            if (n < N) {
-              uint2 packed;
-              packed.x = pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]);
-              packed.y = pack_bf16x2(o[4 * q4 + 2], o[4 * q4 + 3]);
-              *reinterpret_cast<uint2 *>(args.out_bf16 + m * N + n) = packed;
-            }
-          }
-        }
+        for (int q4 = 0; q4 < 4; ++q4)
+          pk[i][j][q4] = v2u{pack_bf16x2(o[4 * q4 + 0], o[4 * q4 + 1]), pack_bf16x2(o[4 * q4 + 2], o[4 * q4 + 3])};
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    stage_and_store(pk);
   }
 }
 
