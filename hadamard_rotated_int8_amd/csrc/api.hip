@@ -492,8 +492,8 @@ static sdnq_status_t check_attention(const void *q, const void *k, const void *v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SDNQ_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SDNQ_ERR_UNSUPPORTED;
   if (hq % hkv != 0 || sk % 16 != 0 || sq > (1 << 20) || sk > (1 << 20)) return SDNQ_ERR_UNSUPPORTED;
-  // grid limits: the V transpose runs one z-slice per key/value head (at most
-  // 65535), the prep one workgroup per 16 rows of [batch * heads * seq]
+  // grid limits: with at most 65535 heads and 2^20 tokens the forward's
+  // one-dimensional grid of (head, 128-query tile) stays below 2^31 workgroups
   if (bsz * hq > 65535 || bsz * hkv > 65535) return SDNQ_ERR_UNSUPPORTED;
   if (bsz * hq * sq > (int64_t(1) << 31) || bsz * hkv * sk > (int64_t(1) << 31)) return SDNQ_ERR_UNSUPPORTED;
   if (!(g == 0 || g == 1 || g == 64 || g == 128 || g == 256)) return SDNQ_ERR_UNSUPPORTED;

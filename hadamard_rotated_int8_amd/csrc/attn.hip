@@ -16,11 +16,15 @@
 //   fp32 accumulation (online, flash-attention style); bf16 output.
 //
 // Kernels:
-//  - attn_kmean_partial / attn_kmean_finish: the blocked fp64 sum, then the mean;
-//  - attn_prep_kernel: sixteen lanes per row of D values (D/16 per lane), the
-//    butterfly in registers and across the row's lanes with shuffles, absmax by
-//    a 16-lane reduction;
-//  - attn_vt_kernel: V [BH, Sk, D] -> V^T [BH, D, Sk] (64 x 64 LDS tiles);
+//  - attn_kmean_kernel (with smoothing): the K-mean block sums in fp64, one lane
+//    per head, block and 8 channels;
+//  - attn_prep_kernel: one launch for the rest of the prep: the K prep (with
+//    smoothing each workgroup first finishes its head's mean from the block sums
+//    into LDS), V^T with the keys of each 16-key group reordered, the Q prep,
+//    and the split-tile flags cleared;
+//  - the prep itself: four lanes per row of D values, the butterfly in
+//    registers and, for the two stages that cross lanes, as multiply-adds with
+//    DPP reads; the absmax by DPP reads; the int8 quantizer;
 //  - attn_fwd_kernel: 128 query rows per workgroup (4 wavefronts x 32), 64 keys
 //    per step, K codes and V^T double-buffered in LDS.  S = K Q^T per wavefront
 //    with v_mfma_i32_32x32x32_i8 (lane l: query l % 32, keys 8 (r / 4) +
@@ -33,6 +37,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "sdnq_internal.hpp"
 
@@ -48,35 +53,16 @@ constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128))
 
 __device__ __forceinline__ float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// part[bh, blk, c] = sum_{j in block blk} k[bh, j, c] in token order (fp64)
-__global__ __launch_bounds__(256) void attn_kmean_partial(const uint16_t *__restrict__ k, int64_t bh_count,
-                                                          int64_t sk, int d, double *__restrict__ part) {
-  const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= bh_count * nblk * d) return;
-  const int c = (int)(idx % d);
-  const int64_t blk = (idx / d) % nblk, bh = idx / (d * nblk);
-  const int64_t j0 = blk * kMeanBlock, j1 = j0 + kMeanBlock < sk ? j0 + kMeanBlock : sk;
-  const uint16_t *p = k + (bh * sk) * d + c;
-  double s = 0.0;
-#pragma unroll 16
-  for (int64_t j = j0; j < j1; ++j) s += (double)bf16_f32(p[j * d]);
-  part[idx] = s;
-}
-
-// mean[bh, c] = fl32((sum over blocks in order) / sk)
-__global__ __launch_bounds__(256) void attn_kmean_finish(const double *__restrict__ part, int64_t bh_count,
-                                                         int64_t sk, int d, float *__restrict__ mean) {
-  const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= bh_count * d) return;
-  const int c = (int)(idx % d);
-  const int64_t bh = idx / d;
-  double s = 0.0;
-#pragma unroll 8
-  for (int64_t b = 0; b < nblk; ++b) s += part[(bh * nblk + b) * d + c];
-  mean[idx] = (float)(s / (double)sk);
-}
+// ---- Prep ----------------------------------------------------------------
+// Rows of D values are handled by groups of 4 lanes: lane j of a group holds
+// elements 32a + 8j + b (a < D/32, b < 8), loaded as D/32 runs of 8 bf16.  The
+// butterfly stages h = 1, 2, 4 (bits of b) and h = 32, 64 (bits of a) pair
+// elements inside a lane; h = 8 and 16 pair lane j with lane j ^ 1 and j ^ 2,
+// read with DPP quad permutations.  A workgroup of 256 lanes takes 128 rows, two
+// per group, both loaded (buffer loads: rows past the end read as zero) before
+// either is processed.
+constexpr int kPrepRows = 128;
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
 
 template <int G>
 __device__ __forceinline__ float norm_const() {
@@ -85,121 +71,315 @@ __device__ __forceinline__ float norm_const() {
   else return 1.0f;
 }
 
-// Sixteen lanes per row of D values, four rows per wavefront; lane l of a row
-// holds elements VPL*l .. VPL*l + VPL-1 (16 bytes of bf16 for D = 128).  Rows of
-// x: [rows, D] with rows = bh * seq; offset [bh, D] (binary32) subtracted first
-// when given.  Codes [rows, D], scales [rows].
-template <int D, int G, bool OFFSET>
-__global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t seq,
-                                                        const float *__restrict__ offset, int8_t *__restrict__ codes,
-                                                        float *__restrict__ scale) {
-  constexpr int VPL = D / 16;
-  const int l16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const bool ok = row < rows;  // lanes of a missing row still take part in the shuffles
-  float v[VPL];
-  if constexpr (VPL == 8) {
-    const v4u raw = ok ? *reinterpret_cast<const v4u *>(x + row * D + 8 * l16) : v4u{0u, 0u, 0u, 0u};
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
+
+// One cross-lane butterfly stage on 8 registers: v = fma(v[partner lane], m, v)
+// as one v_fmac_f32 with a quad_perm DPP source; m = +-1, so the product is exact
+// and the result is fl(a + b) or -fl(a - b).  The s_nop gives the two wait states
+// a DPP read needs after a VALU write of its source; inside the block no
+// instruction reads a register that the one before it wrote.
+#define ATTN_FMAC_DPP8(PERM)                                                                    \
+  "s_nop 1\n\t"                                                                                \
+  "v_fmac_f32_dpp %0, %0, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %1, %1, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %2, %2, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %3, %3, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %4, %4, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %5, %5, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %6, %6, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                \
+  "v_fmac_f32_dpp %7, %7, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf"
+
+__device__ __forceinline__ void fmac_dpp_xor1(float (&r)[8], float m) {
+  asm volatile(ATTN_FMAC_DPP8("[1,0,3,2]")
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "v"(m));
+}
+__device__ __forceinline__ void fmac_dpp_xor2(float (&r)[8], float m) {
+  asm volatile(ATTN_FMAC_DPP8("[2,3,0,1]")
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "v"(m));
+}
+
+// Rows [first, first + kPrepRows) of x clipped to `valid` rows: lane group
+// threadIdx.x / 4 reads rows first + g and first + g + 64.
+template <int D>
+__device__ __forceinline__ void prep_load2(const uint16_t *__restrict__ x, int64_t first, int64_t valid,
+                                           v4u (&raw0)[D / 32], v4u (&raw1)[D / 32]) {
+  const int64_t n = valid < kPrepRows ? valid : kPrepRows;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(x + first * D), 0, (int)(n * D * 2), 0x00020000);
+  const int j = threadIdx.x & 3, g = threadIdx.x >> 2;
+#pragma unroll
+  for (int a = 0; a < D / 32; ++a) {
+    raw0[a] = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)((g * D + 32 * a + 8 * j) * 2), 0, 0));
+    raw1[a] = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)(((g + kPrepRows / 2) * D + 32 * a + 8 * j) * 2),
+                                                   0, 0));
+  }
+}
+
+// One row: minus the offset (K smoothing) when given, the rotation with block G,
+// the row absmax across the group's lanes and the int8 quantizer.  Every lane of
+// a group runs this, also for a missing row, so that the DPP reads see live lanes.
+// The cross-lane stages leave y = sigma * v with sigma = +-1 per lane (the lower
+// lane of a pair adds, the upper one takes the difference with a flipped sign);
+// the normalization multiplies by sigma * norm, exactly y * norm.  Codes: rounding
+// to nearest even by adding 1.5 * 2^23 (exact for |t| < 2^22), the code is the low
+// byte; |t| <= 127 (1 + 2^-23) since r = fl(127 / absmax), so no clamp is needed.
+template <int D, int G>
+__device__ __forceinline__ void prep_row(const v4u (&raw)[D / 32], const float *offset, int j, bool ok, int64_t row,
+                                         int8_t *__restrict__ codes, float *__restrict__ scale) {
+  constexpr int NA = D / 32;
+  float v[NA][8];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      v[2 * w] = bf16_lo(raw[w]);
-      v[2 * w + 1] = bf16_hi(raw[w]);
+      v[a][2 * w] = bf16_lo(raw[a][w]);
+      v[a][2 * w + 1] = bf16_hi(raw[a][w]);
     }
-  } else {
-    const v2u raw = ok ? *reinterpret_cast<const v2u *>(x + row * D + 4 * l16) : v2u{0u, 0u};
+  if (offset) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      v[2 * w] = bf16_lo(raw[w]);
-      v[2 * w + 1] = bf16_hi(raw[w]);
-    }
-  }
-  if constexpr (OFFSET) {
-    if (ok) {
-      const float *o = offset + (row / seq) * D + VPL * l16;
-#pragma unroll
-      for (int e = 0; e < VPL; e += 4) {
-        const float4 f = *reinterpret_cast<const float4 *>(o + e);
-        v[e] = v[e] - f.x;
-        v[e + 1] = v[e + 1] - f.y;
-        v[e + 2] = v[e + 2] - f.z;
-        v[e + 3] = v[e + 3] - f.w;
-      }
+    for (int a = 0; a < NA; ++a) {
+      const float4 m0 = *reinterpret_cast<const float4 *>(offset + 32 * a + 8 * j);
+      const float4 m1 = *reinterpret_cast<const float4 *>(offset + 32 * a + 8 * j + 4);
+      v[a][0] = v[a][0] - m0.x; v[a][1] = v[a][1] - m0.y; v[a][2] = v[a][2] - m0.z; v[a][3] = v[a][3] - m0.w;
+      v[a][4] = v[a][4] - m1.x; v[a][5] = v[a][5] - m1.y; v[a][6] = v[a][6] - m1.z; v[a][7] = v[a][7] - m1.w;
     }
   }
   if constexpr (G > 1) {
+    static_assert(G >= 32, "the cross-lane stages are taken whole");
 #pragma unroll
-    for (int h = 1; h < G; h <<= 1) {
-      if (h < VPL) {  // both elements of the pair in this lane
+    for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-        for (int e = 0; e < VPL; ++e)
-          if ((e & h) == 0) {
-            const float a = v[e], b = v[e + h];
-            v[e] = a + b;
-            v[e + h] = a - b;
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          if ((b & h) == 0) {
+            const float lo = v[a][b], hi = v[a][b + h];
+            v[a][b] = lo + hi;
+            v[a][b + h] = lo - hi;
           }
-      } else {
-        const int hl = h / VPL;  // 1, 2, 4, 8: within the row's 16 lanes
+    const float m1 = (j & 1) ? -1.0f : 1.0f, m2 = (j & 2) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) {
-          const float p = __shfl_xor(v[e], hl);
-          v[e] = (l16 & hl) ? p - v[e] : v[e] + p;
-        }
-      }
-    }
+    for (int a = 0; a < NA; ++a) fmac_dpp_xor1(v[a], m1);
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) v[e] = v[e] * norm_const<G>();
+    for (int a = 0; a < NA; ++a) fmac_dpp_xor2(v[a], m2);
+#pragma unroll
+    for (int h = 1; h < NA && 32 * h < G; h <<= 1)
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        if ((a & h) == 0)
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const float lo = v[a][b], hi = v[a + h][b];
+            v[a][b] = lo + hi;
+            v[a + h][b] = lo - hi;
+          }
+    const float sn = (m1 * m2) * norm_const<G>();
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) v[a][b] = v[a][b] * sn;
   }
-  float a = 0.0f;
+  float am = 0.0f;
 #pragma unroll
-  for (int e = 0; e < VPL; ++e) a = fmaxf(a, fabsf(v[e]));
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-  const float up = a < 0x1p-100f ? 0x1p100f : 1.0f;
-  const float as = a * up;
+    for (int b = 0; b < 8; ++b) am = fmaxf(am, fabsf(v[a][b]));
+  am = fmaxf(am, quad_dpp<kQuadXor1>(am));
+  am = fmaxf(am, quad_dpp<kQuadXor2>(am));
+  const float up = am < 0x1p-100f ? 0x1p100f : 1.0f;
+  const float as = am * up;
   const float r = as > 0.0f ? 127.0f / as : 0.0f;
   if (!ok) return;
-  if (l16 == 0) scale[row] = a / 127.0f;
-  uint32_t packed[VPL / 4];
+  if (j == 0) scale[row] = am / 127.0f;
 #pragma unroll
-  for (int w = 0; w < VPL / 4; ++w) {
-    uint32_t word = 0;
+  for (int a = 0; a < NA; ++a) {
+    uint32_t c[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float t = rintf((v[4 * w + e] * up) * r);
-      t = fminf(fmaxf(t, -127.0f), 127.0f);
-      word |= ((uint32_t)(int)t & 0xFFu) << (8 * e);
-    }
-    packed[w] = word;
+    for (int b = 0; b < 8; ++b) c[b] = __float_as_uint(__fadd_rn(__fmul_rn(v[a][b] * up, r), kRoundMagic));
+    // v_perm_b32: selector bytes 0-3 pick the second operand's bytes, 4-7 the first's
+    const uint32_t w0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u), 0x05040100u);
+    const uint32_t w1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[7], c[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u), 0x05040100u);
+    *reinterpret_cast<v2u *>(codes + row * D + 32 * a + 8 * j) = v2u{w0, w1};
   }
-  if constexpr (VPL == 8)
-    *reinterpret_cast<v2u *>(codes + row * D + 8 * l16) = v2u{packed[0], packed[1]};
-  else
-    *reinterpret_cast<uint32_t *>(codes + row * D + 4 * l16) = packed[0];
+}
+
+// kPrepRows consecutive rows from `first` of which `valid` exist, with an offset
+// row of D values (LDS or global) or none.
+template <int D, int G>
+__device__ __forceinline__ void prep_rows(const uint16_t *__restrict__ x, int64_t first, int64_t valid,
+                                          const float *offset, int8_t *__restrict__ codes,
+                                          float *__restrict__ scale) {
+  const int j = threadIdx.x & 3, g = threadIdx.x >> 2;
+  v4u raw0[D / 32], raw1[D / 32];
+  prep_load2<D>(x, first, valid, raw0, raw1);
+  prep_row<D, G>(raw0, offset, j, g < valid, first + g, codes, scale);
+  prep_row<D, G>(raw1, offset, j, g + kPrepRows / 2 < valid, first + g + kPrepRows / 2, codes, scale);
+}
+
+// K-mean partial sums: part[bh, blk, c] = sum of k[bh, j, c] over the tokens j of
+// block blk (kMeanBlock tokens, the last one shorter), in token order, in fp64.
+// One lane per (head, block, 8 channels); a block's tokens are loaded 32 at a
+// time (the count is a multiple of 16, as sk is), then added in order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_kmean_kernel(const uint16_t *__restrict__ k, int64_t bhk, int64_t sk,
+                                                         double *__restrict__ part) {
+  constexpr int CG = D / 8;
+  const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
+  const int64_t unit = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (unit >= bhk * nblk * CG) return;
+  const int cg = (int)(unit % CG);
+  const int64_t hb = unit / CG;  // bh * nblk + blk
+  const int64_t bh = hb / nblk, blk = hb % nblk;
+  const int64_t j0 = blk * kMeanBlock;
+  const int n = (int)(sk - j0 < kMeanBlock ? sk - j0 : kMeanBlock);
+  const uint16_t *p = k + (bh * sk + j0) * D + 8 * cg;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  auto run = [&](int t0, auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    v4u w[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) w[i] = *reinterpret_cast<const v4u *>(p + (int64_t)(t0 + i) * D);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(w[i][e]);
+        acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
+      }
+  };
+  int t0 = 0;
+  for (; t0 + 32 <= n; t0 += 32) run(t0, std::integral_constant<int, 32>{});
+  if (t0 < n) run(t0, std::integral_constant<int, 16>{});
+  double *o = part + hb * D + 8 * cg;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) *reinterpret_cast<double2 *>(o + e) = double2{acc[e], acc[e + 1]};
 }
 
 // vt[bh, c, p] = v[bh, key(p), c]: V^T with the keys of every 16-key group stored
 // in the order 0-3, 8-11, 4-7, 12-15, so that the 8 keys one lane feeds to the
-// P V product are 16 contiguous bytes.  64 x 64 tiles through LDS, grid
-// (ceil(sk/64), D/64, bh); sk is a multiple of 16.
-__device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+// P V product are 16 contiguous bytes.  A lane moves 8 keys x 8 channels: eight
+// 16-byte row loads, an 8 x 8 transpose of 16-bit values with byte permutes,
+// eight 16-byte stores.  Lane l of a wavefront takes positions 8 (l / 8) .. + 7
+// and channels 8 (l % 8) .. + 7 of a 64 x 64 block; a workgroup covers
+// 256 / (D / 64) positions of all D channels.  sk is a multiple of 16, so a
+// lane's 8 positions are all below sk or all past it.
+template <int D>
+__device__ __forceinline__ void vt_block(const uint16_t *__restrict__ v, int64_t sk, int64_t unit,
+                                         uint16_t *__restrict__ vt) {
+  constexpr int CW = D / 64;           // wavefronts across the channels
+  constexpr int PPW = 64 * (4 / CW);   // positions per workgroup
+  const int64_t npb = (sk + PPW - 1) / PPW;
+  const int64_t bh = unit / npb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t p0 = (unit % npb) * PPW + 64 * (wave / CW) + 8 * (lane >> 3);
+  if (p0 >= sk) return;
+  const int c0 = 64 * (wave % CW) + 8 * (lane & 7);
+  const int64_t kb = (p0 & ~(int64_t)15) + ((p0 & 8) >> 1);
+  const uint16_t *src = v + (bh * sk + kb) * D + c0;
+  v4u r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = *reinterpret_cast<const v4u *>(src + (int64_t)((i & 3) + ((i & 4) << 1)) * D);
+  uint16_t *dst = vt + (bh * D + c0) * sk + p0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    v4u o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(r[2 * w + 1][c >> 1], r[2 * w][c >> 1], sel);
+    *reinterpret_cast<v4u *>(dst + (int64_t)c * sk) = o;
+  }
+}
 
-__global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t *__restrict__ v, int64_t sk, int d,
-                                                      uint16_t *__restrict__ vt) {
-  __shared__ uint16_t tile[64][66];
-  const int64_t bh = blockIdx.z;
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  const int c0 = blockIdx.y * 64;
-  const uint16_t *src = v + bh * sk * d;
-  uint16_t *dst = vt + bh * (int64_t)d * sk;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int jj = e / 64, cc = e % 64;
-    tile[jj][cc] = j0 + jj < sk ? src[(j0 + jj) * d + c0 + cc] : (uint16_t)0;
+// K prep with smoothing for kPrepRows keys of head bh from chunk `chunk`: the
+// rows are loaded first; then the head's mean is finished from the partial sums
+// into LDS: the block sums added in block order (32 loads in flight at a time;
+// those past the last block read as +0, which leaves a sum that started at +0
+// unchanged), then one division and one rounding to binary32.  The chunk-0
+// workgroup also stores the mean.
+template <int D, int G>
+__device__ __forceinline__ void prep_k_smooth(const uint16_t *__restrict__ k, int64_t sk, int64_t bh, int64_t chunk,
+                                              const double *__restrict__ kpart, float *__restrict__ kmean,
+                                              int8_t *__restrict__ kc, float *__restrict__ ks, float *smean) {
+  constexpr int kBatch = 32;
+  const int j = threadIdx.x & 3, g = threadIdx.x >> 2;
+  const int64_t first = bh * sk + chunk * kPrepRows, valid = sk - chunk * kPrepRows;
+  v4u raw0[D / 32], raw1[D / 32];
+  prep_load2<D>(k, first, valid, raw0, raw1);
+  if (threadIdx.x < D) {
+    const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kpart + bh * nblk * D), 0, (int)(nblk * D * 8), 0x00020000);
+    double s = 0.0;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kBatch) {
+      double t[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t b = b0 + i;
+        const unsigned off = b < nblk ? (unsigned)((b * D + threadIdx.x) * 8) : 0x80000000u;
+        t[i] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) s += t[i];
+    }
+    const float m = (float)(s / (double)sk);
+    smean[threadIdx.x] = m;
+    if (chunk == 0) kmean[bh * D + threadIdx.x] = m;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int cc = e / 64, pp = e % 64;
-    if (j0 + pp < sk) dst[(int64_t)(c0 + cc) * sk + j0 + pp] = tile[vt_key(pp)][cc];
+  prep_row<D, G>(raw0, smean, j, g < valid, first + g, kc, ks);
+  prep_row<D, G>(raw1, smean, j, g + kPrepRows / 2 < valid, first + g + kPrepRows / 2, kc, ks);
+}
+
+// Everything after the K-mean partial sums, in one launch; workgroups by range:
+// [0, wg_k) the K prep (with smoothing: workgroup (bh, chunk), the mean finished
+// first; these come first so that their wait overlaps the others' work), then
+// wg_vt for V^T, then the Q prep.  The first lanes also clear the split-tile
+// flags of the forward launch.
+struct PrepArgs {
+  const uint16_t *q, *k, *v;
+  int64_t rows_q, bhk, sk;
+  int8_t *qc, *kc;
+  float *qs, *ks;
+  const double *kpart;  // null: no smoothing
+  float *kmean;
+  uint16_t *vt;
+  uint32_t *flags;
+  int64_t nflags;
+  int64_t wg_k, wg_vt;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs p) {
+  __shared__ float smean[D];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < p.nflags; i += (int64_t)gridDim.x * 256)
+    p.flags[i] = 0u;
+  int64_t b = blockIdx.x;
+  if (b < p.wg_k) {
+    if (p.kpart) {
+      const int64_t nchunk = (p.sk + kPrepRows - 1) / kPrepRows;
+      prep_k_smooth<D, G>(p.k, p.sk, b / nchunk, b % nchunk, p.kpart, p.kmean, p.kc, p.ks, smean);
+    } else {
+      prep_rows<D, G>(p.k, b * kPrepRows, p.bhk * p.sk - b * kPrepRows, nullptr, p.kc, p.ks);
+    }
+    return;
   }
+  b -= p.wg_k;
+  if (b < p.wg_vt) {
+    vt_block<D>(p.v, p.sk, b, p.vt);
+    return;
+  }
+  b -= p.wg_vt;
+  prep_rows<D, G>(p.q, b * kPrepRows, p.rows_q - b * kPrepRows, nullptr, p.qc, p.qs);
 }
 
 // Block index -> (head, query tile): each XCD takes a contiguous run of the
@@ -238,7 +418,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
   // wavefront instruction), 16-byte chunks XOR-swizzled by row instead of padded:
   //   K codes [64 keys][D bytes]: chunk c of row r stored at c ^ (r % CPR);
   //   V^T     [D rows][64 key positions] bf16 (128-byte rows, keys permuted within
-  //           16-key groups as attn_vt_kernel stores them): chunk c of row d at
+  //           16-key groups as the prep stores them): chunk c of row d at
   //           c ^ (d % 8).
   constexpr int CPR = D / 16;                 // 16-byte chunks per K row
   constexpr int KB = kBN * D;                 // K tile bytes
@@ -586,27 +766,27 @@ AttnLayout attn_layout(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t
   return L;
 }
 
+// The prep launches: with smoothing the K-mean partial sums, then the fused one.
 template <int D, int G>
-hipError_t launch_prep(const uint16_t *x, int64_t rows, int64_t seq, const float *offset, int8_t *codes, float *scale,
-                       hipStream_t s) {
-  const unsigned blocks = (unsigned)((rows + 15) / 16);
-  if (offset)
-    hipLaunchKernelGGL((attn_prep_kernel<D, G, true>), dim3(blocks), dim3(256), 0, s, x, rows, seq, offset, codes,
-                       scale);
-  else
-    hipLaunchKernelGGL((attn_prep_kernel<D, G, false>), dim3(blocks), dim3(256), 0, s, x, rows, seq, offset, codes,
-                       scale);
+hipError_t launch_prep(const PrepArgs &p, hipStream_t s) {
+  if (p.kpart) {
+    const int64_t nblk = (p.sk + kMeanBlock - 1) / kMeanBlock;
+    const int64_t lanes = p.bhk * nblk * (D / 8);
+    hipLaunchKernelGGL((attn_kmean_kernel<D>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, p.k, p.bhk,
+                       p.sk, const_cast<double *>(p.kpart));
+  }
+  const int64_t wg_q = (p.rows_q + kPrepRows - 1) / kPrepRows;
+  hipLaunchKernelGGL((attn_prep_kernel<D, G>), dim3((unsigned)(p.wg_k + p.wg_vt + wg_q)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t prep_any(int block, const uint16_t *x, int64_t rows, int64_t seq, const float *offset, int8_t *codes,
-                    float *scale, hipStream_t s) {
+hipError_t prep_any(int block, const PrepArgs &p, hipStream_t s) {
   switch (block) {
-    case 1: return launch_prep<D, 1>(x, rows, seq, offset, codes, scale, s);
-    case 64: return launch_prep<D, 64>(x, rows, seq, offset, codes, scale, s);
+    case 1: return launch_prep<D, 1>(p, s);
+    case 64: return launch_prep<D, 64>(p, s);
     case 128:
-      if constexpr (D >= 128) return launch_prep<D, 128>(x, rows, seq, offset, codes, scale, s);
+      if constexpr (D >= 128) return launch_prep<D, 128>(p, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -643,26 +823,9 @@ hipError_t attention_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
   uint16_t *vt = reinterpret_cast<uint16_t *>(base + L.vt);
   const int block = g <= 1 ? 1 : (g < D ? g : D);
   const int64_t bhk = bsz * hkv;
-  hipError_t e;
-  if (smooth_k) {
-    const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
-    const int64_t np = bhk * nblk * D, nm = bhk * D;
-    hipLaunchKernelGGL(attn_kmean_partial, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s, k, bhk, sk, D, kpart);
-    hipLaunchKernelGGL(attn_kmean_finish, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s, kpart, bhk, sk, D,
-                       kmean);
-  }
-  if ((e = prep_any<D>(block, q, bsz * hq * sq, sq, nullptr, qc, qs, s)) != hipSuccess) return e;
-  if ((e = prep_any<D>(block, k, bhk * sk, sk, smooth_k ? kmean : nullptr, kc, ks, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_vt_kernel, dim3((unsigned)((sk + 63) / 64), D / 64, (unsigned)bhk), dim3(256), 0, s, v, sk,
-                     D, vt);
   const int64_t nq = (sq + kBM - 1) / kBM;
   const int64_t tiles = nq * bsz * hq;
   const float sl = scale * kLog2e;
-  if (causal) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, true, false>), dim3((unsigned)tiles), dim3(256), 0, s, qc, qs, kc, ks, vt,
-                       (int)hq, (int)hkv, sq, sk, sl, out, AttnSplit{});
-    return hipGetLastError();
-  }
   // Non-causal: when the tiles overfill the resident workgroups by a little, a
   // last round runs almost empty for nearly a full workgroup's time; split tiles
   // spread the key tiles evenly over exactly the resident workgroups instead.
@@ -670,16 +833,46 @@ hipError_t attention_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
   // so it is used only while the leftover is at most a sixth of a round (flux.1,
   // 864 tiles on 768 workgroups: 357 -> 329 us; 1008 tiles would lose 3 %).
   const int64_t nkt = (sk + kBN - 1) / kBN;
-  const int64_t slots = (int64_t)device_cu_count() * split_blocks_per_cu<D>();
-  const int64_t leftover = tiles % slots;
-  if (tiles > slots && leftover != 0 && 6 * leftover <= slots && tiles <= kMaxSplitTiles && nkt >= 8) {
+  bool split = false;
+  int64_t slots = 0;
+  if (!causal) {
+    slots = (int64_t)device_cu_count() * split_blocks_per_cu<D>();
+    const int64_t leftover = tiles % slots;
+    split = tiles > slots && leftover != 0 && 6 * leftover <= slots && tiles <= kMaxSplitTiles && nkt >= 8;
+  }
+  PrepArgs pa{};
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.rows_q = bsz * hq * sq;
+  pa.bhk = bhk;
+  pa.sk = sk;
+  pa.qc = qc;
+  pa.kc = kc;
+  pa.qs = qs;
+  pa.ks = ks;
+  pa.kpart = smooth_k ? kpart : nullptr;
+  pa.kmean = kmean;
+  pa.vt = vt;
+  pa.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+  pa.nflags = split ? tiles : 0;
+  pa.wg_k = smooth_k ? bhk * ((sk + kPrepRows - 1) / kPrepRows) : (bhk * sk + kPrepRows - 1) / kPrepRows;
+  const int64_t ppw = 64 * (4 / (D / 64));
+  pa.wg_vt = bhk * ((sk + ppw - 1) / ppw);
+  hipError_t e;
+  if ((e = prep_any<D>(block, pa, s)) != hipSuccess) return e;
+  if (causal) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true, false>), dim3((unsigned)tiles), dim3(256), 0, s, qc, qs, kc, ks, vt,
+                       (int)hq, (int)hkv, sq, sk, sl, out, AttnSplit{});
+    return hipGetLastError();
+  }
+  if (split) {
     AttnSplit sp{};
     sp.part_o = reinterpret_cast<float *>(base + L.part_o);
     sp.part_ml = reinterpret_cast<float *>(base + L.part_ml);
-    sp.flags = reinterpret_cast<uint32_t *>(base + L.flags);
+    sp.flags = pa.flags;
     sp.tiles = tiles;
     sp.per = (tiles * nkt + slots - 1) / slots;  // >= nkt since tiles > slots
-    if ((e = launch_fill_zero_u16(reinterpret_cast<uint16_t *>(sp.flags), 2 * tiles, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, false, true>), dim3((unsigned)slots), dim3(256), 0, s, qc, qs, kc, ks, vt,
                        (int)hq, (int)hkv, sq, sk, sl, out, sp);
     return hipGetLastError();
