@@ -274,3 +274,28 @@ def test_attention_workspace():
     assert offs == sorted(offs) and offs[0] == 0 and offs[1] >= b * hq * s * d and all(o % 256 == 0 for o in offs)
     assert f(1, 4, 3, 64, 64, 128) == 0 and f(1, 4, 2, 64, 40, 128) == 0 and f(1, 4, 2, 64, 64, 80) == 0
     assert h.sdnq_attention_workspace_offset(1, 4, 2, 64, 64, 128, 5) == 0
+
+
+def test_product_path_fails_loudly_without_the_library():
+    """With the HIP library absent the entry points raise; nothing falls back to
+    a CPU computation (a fresh interpreter, so no library is loaded yet)."""
+    code = (
+        "import hadamard_rotated_int8_amd._binding as B\n"
+        "B.LIB_PATH = '/nonexistent/libsdnq_hip.so'\n"
+        "import hadamard_rotated_int8_amd as h, torch\n"
+        "try:\n"
+        "    h.sdnq_workspace_bytes(64, 512, 512)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    print('no error')\n")
+    out = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert "raised:" in out.stdout and "is missing" in out.stdout, out.stdout + out.stderr
+
+
+def test_host_tensors_are_rejected():
+    """Host (CPU) tensors are refused before any call: the library computes on the
+    GPU only, and there is no host path to fall back to."""
+    w = torch.zeros(512, 512, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        h.sdnq_rotate_quantize_weight(w, 256)
