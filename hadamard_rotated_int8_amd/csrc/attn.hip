@@ -34,6 +34,7 @@
 //    16c + 4g + {0..3} and 16c + 8 + 4g + {0..3}, read from V^T as two 8-byte
 //    runs.  exp2 with the log2(e) folded into the query scale; the softmax offset
 //    is lazy (it moves only when a row maximum grows by more than 2^8).
+#include <float.h>
 #include <math.h>
 
 #include <atomic>
@@ -474,7 +475,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
     for (int s = 0; s < KS; ++s)
       qf[s] = row_ok ? *reinterpret_cast<const v4i *>(qc + (bh * sq + my_row) * D + 32 * s + 16 * g)
                      : v4i{0, 0, 0, 0};
-    const float qscale = row_ok ? qs[bh * sq + my_row] * scale_log2 : 0.0f;
+    // The row's factor s_q * scale * log2 e, at least FLT_MIN: a zero (or flushed
+    // subnormal) factor would make a masked key's -inf * 0 a NaN; with FLT_MIN the
+    // row's valid scores stay within 2^-126 of zero and masked keys stay at -inf.
+    const float qscale = row_ok ? fmaxf(qs[bh * sq + my_row] * scale_log2, FLT_MIN) : FLT_MIN;
 
     // buffer resources over this head's K codes, K scales and V^T: rows past sk
     // lie past num_records and read as zero; V^T chunks past sk get an
@@ -565,6 +569,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
         const float m_new = mx > m_run + kLazyLog2 ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         const float neg_m = -m_new;
+        // The exponent is one fma of the exact product against the rounded offset.
+        // Once offsets pass 2^14 (a logit of about 10^4) half an ulp of the offset
+        // is no longer small in the exponent, and past 2^31 it would exceed 128 and
+        // turn the row maximum's term into inf or 0; such wavefronts (never with
+        // ordinary inputs) take the rounded product minus the offset, which is
+        // exactly 0 for the maximum.  The vote is a compare on the offset, so the
+        // exponents do not wait for alpha.
+        const bool big = __ballot(fabsf(m_new) > 0x1p14f) != 0;
+        float qf = qscale;
+        if (big) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = __fmul_rn(sv[r], qscale);
+          qf = 1.0f;  // fma(t, 1, -m) = t - m, rounded once
+        }
         float psum2[2] = {0.0f, 0.0f};
         v8bf pf[2];
 #pragma unroll
@@ -572,7 +590,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * c + e], qscale, neg_m));
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * c + e], qf, neg_m));
             psum2[c] += p[e];
           }
           v4u packed;

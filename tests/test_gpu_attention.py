@@ -200,3 +200,36 @@ def test_attention_repeat_runs_are_bit_identical(heads, causal):
         torch.cuda.synchronize()
         diff = (again.view(torch.int16) != first.view(torch.int16))
         assert not diff.any().item(), f"{int(diff.any(-1).sum().item())} rows differ between runs"
+
+
+def stress_rows(d, n, seed):
+    """n rows of d values: the quantizer's edge cases (as the linear layer's stress
+    rows, with the large channel kept at 1e15 so that scores stay finite), then
+    normal rows."""
+    rng = np.random.default_rng(seed)
+    rows = [np.zeros(d, np.float32)]                                        # all-zero row
+    r = rng.standard_normal(d).astype(np.float32); r[17] = 1e15; rows.append(r)   # one large channel
+    r = rng.standard_normal(d).astype(np.float32); r[rng.permutation(d)[:5]] *= 1000; rows.append(r)
+    rows.append((rng.standard_normal(d) * 1e-38).astype(np.float32))      # tiny (normal and subnormal)
+    rows.append((rng.standard_normal(d) * 1e-36).astype(np.float32))
+    r = np.zeros(d, np.float32); r[:4] = [1.0, 2.0 ** -24, -1.0, 2.0 ** -24]; rows.append(r)  # stage order
+    r = (rng.integers(-254, 255, d) / 2.0).astype(np.float32); r[3] = 127.0; rows.append(r)  # ties
+    r = np.zeros(d, np.float32); r[:2] = [1.125, 0.5625]; rows.append(r)  # reciprocal case
+    rows.append(np.full(d, 3.0, np.float32))                               # constant
+    r = np.zeros(d, np.float32); r[d // 2] = 1.0; rows.append(r)           # one-hot
+    rows.append(-np.abs(rng.standard_normal(d)).astype(np.float32))
+    while len(rows) < n:
+        rows.append(rng.standard_normal(d).astype(np.float32))
+    return np.stack(rows[:n])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_attention_prep_stress_rows(d, smooth):
+    """Q and K rows at the quantizer's edge cases: codes, scales and the K mean
+    bit-exact against the oracle, the output within the tolerance."""
+    q = synth.to_bf16_bits(np.stack([stress_rows(d, 24, 50), stress_rows(d, 24, 51)])[None])
+    k = synth.to_bf16_bits(stress_rows(d, 32, 52)[None, None])
+    v = synth.to_bf16_bits(np.random.default_rng(53).standard_normal((1, 1, 32, d)).astype(np.float32))
+    for g in (256, 1):
+        check(q, k, v, False, smooth, g)
