@@ -113,3 +113,37 @@ def test_weight_grad_matches_forward_gemm_on_its_codes(m, n, k):
     got, ref = h_bits(dw), h_bits(whole)
     assert np.array_equal(got, ref), f"{np.mean(got != ref):.6f} of the outputs differ"
     assert np.count_nonzero(ref) > 0.9 * ref.size
+
+
+def stress_columns(m, n, seed):
+    """[m, n]: feature columns (along the tokens) at the quantizer's edge cases,
+    then normal columns."""
+    rng = np.random.default_rng(seed)
+    cols = [np.zeros(m, np.float32)]                                        # all-zero feature
+    c = rng.standard_normal(m).astype(np.float32); c[17] = 1e15; cols.append(c)   # one large token
+    c = rng.standard_normal(m).astype(np.float32); c[rng.permutation(m)[:5]] *= 1000; cols.append(c)
+    cols.append((rng.standard_normal(m) * 1e-38).astype(np.float32))      # tiny (normal and subnormal)
+    cols.append((rng.standard_normal(m) * 1e-36).astype(np.float32))
+    c = np.zeros(m, np.float32); c[:4] = [1.0, 2.0 ** -24, -1.0, 2.0 ** -24]; cols.append(c)  # stage order
+    c = (rng.integers(-254, 255, m) / 2.0).astype(np.float32); c[3] = 127.0; cols.append(c)  # ties
+    c = np.zeros(m, np.float32); c[:2] = [1.125, 0.5625]; cols.append(c)  # reciprocal case
+    cols.append(np.full(m, 3.0, np.float32))                               # constant
+    c = np.zeros(m, np.float32); c[m // 2] = 1.0; cols.append(c)           # one-hot
+    cols.append(-np.abs(rng.standard_normal(m)).astype(np.float32))
+    while len(cols) < n:
+        cols.append(rng.standard_normal(m).astype(np.float32))
+    return np.stack(cols[:n], axis=1)
+
+
+@pytest.mark.parametrize("g", [1, 64, 256])
+def test_weight_grad_stress_columns(g):
+    """dY and x with feature columns at the quantizer's edge cases: dW bit for bit."""
+    m = 512
+    dy = synth.to_bf16_bits(stress_columns(m, 48, 60))
+    x = synth.to_bf16_bits(stress_columns(m, 32, 61))
+    say(f"  weight_grad stress columns m={m} n=48 k=32 g={g}")
+    dw = h.sdnq_qlinear_weight_grad(d_bf16(dy), d_bf16(x), g)
+    torch.cuda.synchronize()
+    ref = oracle.qlinear_weight_grad(dy, x, g)["dw"]
+    got = h_bits(dw)
+    assert np.array_equal(got, ref), f"{np.mean(got != ref):.4f} of the outputs differ"
