@@ -251,8 +251,15 @@ __global__ void lora_grad_reduce_kernel(const float *__restrict__ partials, int 
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // index into the partials
   const int64_t count = pa * qb;
   if (i >= count) return;
-  float s = partials[i];
-  for (int k = 1; k < splits; ++k) s += partials[(int64_t)k * count + i];
+  // all splits' loads in flight first (splits <= kMaxSplits, the same for every
+  // lane), then the sum in split order
+  float t[kMaxSplits];
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) t[k] = k < splits ? partials[(int64_t)k * count + i] : 0.0f;
+  float s = t[0];
+#pragma unroll
+  for (int k = 1; k < kMaxSplits; ++k)
+    if (k < splits) s += t[k];
   const __bf16 b = (__bf16)(scale * s);
   out[transposed ? (i % qb) * pa + i / qb : i] = __builtin_bit_cast(uint16_t, b);
 }
