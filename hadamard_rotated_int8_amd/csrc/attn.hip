@@ -17,7 +17,7 @@
 //
 // Kernels:
 //  - attn_kmean_kernel (with smoothing): the K-mean block sums in fp64, one lane
-//    per head, block and 8 channels;
+//    per head, block and 4 channels;
 //  - attn_prep_kernel: one launch for the rest of the prep: the K prep (with
 //    smoothing each workgroup first finishes its head's mean from the block sums
 //    into LDS), V^T with the keys of each 16-key group reordered, the Q prep,
@@ -229,12 +229,14 @@ __device__ __forceinline__ void prep_rows(const uint16_t *__restrict__ x, int64_
 
 // K-mean partial sums: part[bh, blk, c] = sum of k[bh, j, c] over the tokens j of
 // block blk (kMeanBlock tokens, the last one shorter), in token order, in fp64.
-// One lane per (head, block, 8 channels); a block's tokens are loaded 32 at a
-// time (the count is a multiple of 16, as sk is), then added in order.
+// One lane per (head, block, 4 channels); a whole block's tokens are loaded at
+// once (8 bytes each), then added in order.  A short last block (16, 32 or 48
+// tokens, as sk is a multiple of 16) goes 16 at a time.  The launch has few
+// wavefronts, so registers go to loads in flight rather than occupancy.
 template <int D>
-__global__ __launch_bounds__(256) void attn_kmean_kernel(const uint16_t *__restrict__ k, int64_t bhk, int64_t sk,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void attn_kmean_kernel(const uint16_t *__restrict__ k, int64_t bhk, int64_t sk,
                                                          double *__restrict__ part) {
-  constexpr int CG = D / 8;
+  constexpr int CG = D / 4;
   const int64_t nblk = (sk + kMeanBlock - 1) / kMeanBlock;
   const int64_t unit = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (unit >= bhk * nblk * CG) return;
@@ -243,27 +245,29 @@ __global__ __launch_bounds__(256) void attn_kmean_kernel(const uint16_t *__restr
   const int64_t bh = hb / nblk, blk = hb % nblk;
   const int64_t j0 = blk * kMeanBlock;
   const int n = (int)(sk - j0 < kMeanBlock ? sk - j0 : kMeanBlock);
-  const uint16_t *p = k + (bh * sk + j0) * D + 8 * cg;
-  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  const uint16_t *p = k + (bh * sk + j0) * D + 4 * cg;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
   auto run = [&](int t0, auto nb) {
     constexpr int NB = decltype(nb)::value;
-    v4u w[NB];
+    v2u w[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) w[i] = *reinterpret_cast<const v4u *>(p + (int64_t)(t0 + i) * D);
+    for (int i = 0; i < NB; ++i) w[i] = *reinterpret_cast<const v2u *>(p + (int64_t)(t0 + i) * D);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 2; ++e) {
         acc[2 * e] += (double)bf16_lo(w[i][e]);
         acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
       }
   };
-  int t0 = 0;
-  for (; t0 + 32 <= n; t0 += 32) run(t0, std::integral_constant<int, 32>{});
-  if (t0 < n) run(t0, std::integral_constant<int, 16>{});
-  double *o = part + hb * D + 8 * cg;
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) *reinterpret_cast<double2 *>(o + e) = double2{acc[e], acc[e + 1]};
+  if (n == kMeanBlock) {
+    run(0, std::integral_constant<int, kMeanBlock>{});
+  } else {
+    for (int t0 = 0; t0 < n; t0 += 16) run(t0, std::integral_constant<int, 16>{});
+  }
+  double *o = part + hb * D + 4 * cg;
+  *reinterpret_cast<double2 *>(o) = double2{acc[0], acc[1]};
+  *reinterpret_cast<double2 *>(o + 2) = double2{acc[2], acc[3]};
 }
 
 // vt[bh, c, p] = v[bh, key(p), c]: V^T with the keys of every 16-key group stored
@@ -789,7 +793,7 @@ template <int D, int G>
 hipError_t launch_prep(const PrepArgs &p, hipStream_t s) {
   if (p.kpart) {
     const int64_t nblk = (p.sk + kMeanBlock - 1) / kMeanBlock;
-    const int64_t lanes = p.bhk * nblk * (D / 8);
+    const int64_t lanes = p.bhk * nblk * (D / 4);
     hipLaunchKernelGGL((attn_kmean_kernel<D>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, p.k, p.bhk,
                        p.sk, const_cast<double *>(p.kpart));
   }
