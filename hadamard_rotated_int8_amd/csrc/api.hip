@@ -37,7 +37,13 @@ bool valid_group(int32_t g) { return g == 1 || g == 64 || g == 128 || g == 256; 
 
 constexpr int32_t kMaxSvdSteps = 64;
 
-bool valid_rank(int32_t rank) { return rank >= 16 && rank <= 128 && rank % 16 == 0; }
+constexpr int32_t kMaxRank = 256;
+
+bool valid_rank(int32_t rank) { return rank >= 1 && rank <= kMaxRank; }
+
+// The kernels take LoRA ranks in multiples of 16 (one bf16 MFMA step); other ranks
+// run zero-padded to the next multiple, which adds nothing to any product.
+int32_t padded_rank(int32_t rank) { return (rank + 15) / 16 * 16; }
 
 sdnq_status_t check_feature(int64_t d) {
   if (d <= 0) return SDNQ_ERR_INVALID_ARG;
@@ -46,8 +52,11 @@ sdnq_status_t check_feature(int64_t d) {
 }
 
 // Workspace layouts (each region starts on a 256-byte boundary).
+// With a rank that is not a multiple of 16, the regions marked "padded only" hold
+// the zero-padded copies of the factors (and, in the forward with quantized
+// activations, of the caller's t) and the padded LoRA gradients before cropping.
 struct FwdLayout {
-  size_t qx, sx, t, at, bt, total;
+  size_t qx, sx, t, at, bt, bp, tp, total;
 };
 FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   FwdLayout L{};
@@ -55,16 +64,21 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   L.qx = off; off += align_up((size_t)m * (size_t)k);
   L.sx = off; off += align_up((size_t)m * 4);
   if (rank > 0) {
-    L.t = off; off += align_up((size_t)m * (size_t)rank * 2);
-    L.at = off; off += align_up((size_t)rank * (size_t)k * 2);
-    L.bt = off; off += align_up((size_t)n * (size_t)rank * 2);
+    const size_t rp = (size_t)padded_rank(rank);
+    L.t = off; off += align_up((size_t)m * rp * 2);
+    L.at = off; off += align_up(rp * (size_t)k * 2);
+    L.bt = off; off += align_up((size_t)n * rp * 2);
+    if (rp != (size_t)rank) {
+      L.bp = off; off += align_up(rp * (size_t)n * 2);   // padded only: B [rp, n]
+      L.tp = off; off += align_up((size_t)m * rp * 2);   // padded only: the caller's t [m, rp]
+    }
   }
   L.total = off;
   return L;
 }
 
 struct BwdLayout {
-  size_t qdy, sdy, wt, gr, tx, at, part, total;
+  size_t qdy, sdy, wt, gr, tx, at, part, bp, ap, gap, gbp, total;
 };
 BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   BwdLayout L{};
@@ -73,11 +87,18 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   L.sdy = off; off += align_up((size_t)m * 4);
   L.wt = off; off += align_up((size_t)k * (size_t)n);
   if (rank > 0) {
-    L.gr = off; off += align_up((size_t)m * (size_t)rank * 2);
-    L.tx = off; off += align_up((size_t)m * (size_t)rank * 2);
-    L.at = off; off += align_up((size_t)rank * (size_t)k * 2);
-    const size_t cells = (size_t)rank * (size_t)(k > n ? k : n);
+    const size_t rp = (size_t)padded_rank(rank);
+    L.gr = off; off += align_up((size_t)m * rp * 2);
+    L.tx = off; off += align_up((size_t)m * rp * 2);
+    L.at = off; off += align_up(rp * (size_t)k * 2);
+    const size_t cells = rp * (size_t)(k > n ? k : n);
     L.part = off; off += align_up((size_t)lora_grad_splits(m) * cells * 4);
+    if (rp != (size_t)rank) {
+      L.bp = off; off += align_up(rp * (size_t)n * 2);    // padded only: B [rp, n]
+      L.ap = off; off += align_up((size_t)k * rp * 2);    // padded only: A [k, rp]
+      L.gap = off; off += align_up((size_t)k * rp * 2);   // padded only: dA [k, rp]
+      L.gbp = off; off += align_up(rp * (size_t)n * 2);   // padded only: dB [rp, n]
+    }
   }
   L.total = off;
   return L;
@@ -204,9 +225,19 @@ sdnq_status_t forward_quantized(bool fp8, const int8_t *qx, const float *x_scale
   ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k; ga.fp8 = fp8;
   ga.row_scale = x_scale; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
   if (r > 0) {
+    const int32_t rp = padded_rank(r);
+    const uint16_t *tsrc = t, *bsrc = lora_b;
+    if (rp != r) {
+      uint16_t *tp = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tp));
+      uint16_t *bp = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bp));
+      SDNQ_LAUNCH(launch_copy2d_u16(t, m, r, tp, m, rp, s));        // t [m, r] -> [m, rp]
+      SDNQ_LAUNCH(launch_copy2d_u16(lora_b, r, n, bp, rp, n, s));   // B [r, n] -> [rp, n]
+      tsrc = tp;
+      bsrc = bp;
+    }
     uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
-    SDNQ_LAUNCH(launch_transpose_scale_bf16(lora_b, r, n, lora_scale, bt, s));  // bf16(scale B)^T
-    ga.lora_t = t; ga.lora_r = bt; ga.rank = r;
+    SDNQ_LAUNCH(launch_transpose_scale_bf16(bsrc, rp, n, lora_scale, bt, s));  // bf16(scale B)^T
+    ga.lora_t = tsrc; ga.lora_r = bt; ga.rank = rp;
   }
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
@@ -239,13 +270,21 @@ sdnq_status_t forward(bool fp8, const uint16_t *x, int64_t m, int64_t k, const i
   ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k; ga.fp8 = fp8;
   ga.row_scale = sx; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
   if (r > 0) {
+    const int32_t rp = padded_rank(r);
     uint16_t *t = reinterpret_cast<uint16_t *>(ws_at(workspace, L.t));
     uint16_t *at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
     uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
-    SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));          // A [k, r] -> A^T [r, k]
-    SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, lora_scale, t, s));  // t = bf16(scale * x A)
-    SDNQ_LAUNCH(launch_transpose_u16(lora_b, r, n, bt, s));          // B [r, n] -> B^T [n, r]
-    ga.lora_t = t; ga.lora_r = bt; ga.rank = r;
+    const uint16_t *bsrc = lora_b;
+    SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));           // A [k, r] -> A^T [r, k]
+    if (rp != r) {
+      uint16_t *bp = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bp));
+      SDNQ_LAUNCH(launch_fill_zero_u16(at + (int64_t)r * k, (int64_t)(rp - r) * k, s));  // A^T [rp, k]
+      SDNQ_LAUNCH(launch_copy2d_u16(lora_b, r, n, bp, rp, n, s));                       // B [rp, n]
+      bsrc = bp;
+    }
+    SDNQ_LAUNCH(launch_lora_down(x, m, k, at, rp, lora_scale, t, s));  // t = bf16(scale * x A)
+    SDNQ_LAUNCH(launch_transpose_u16(bsrc, rp, n, bt, s));            // B [rp, n] -> B^T [n, rp]
+    ga.lora_t = t; ga.lora_r = bt; ga.rank = rp;
   }
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
@@ -310,22 +349,39 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
   ga.a = qdy; ga.b = wt; ga.m = m; ga.n = k; ga.k = n;
   ga.row_scale = sdy; ga.out_bf16 = dx; ga.g = g;
   uint16_t *gr = nullptr, *tx = nullptr, *at = nullptr;
+  const int32_t rp = r > 0 ? padded_rank(r) : 0;
+  const bool padded = rp != r;
+  const uint16_t *asrc = lora_a, *bsrc = lora_b;
   if (r > 0) {
+    if (padded) {
+      uint16_t *ap = reinterpret_cast<uint16_t *>(ws_at(workspace, L.ap));
+      uint16_t *bp = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bp));
+      SDNQ_LAUNCH(launch_copy2d_u16(lora_a, k, r, ap, k, rp, s));   // A [k, r] -> [k, rp]
+      SDNQ_LAUNCH(launch_copy2d_u16(lora_b, r, n, bp, rp, n, s));   // B [r, n] -> [rp, n]
+      asrc = ap;
+      bsrc = bp;
+    }
     gr = reinterpret_cast<uint16_t *>(ws_at(workspace, L.gr));
-    SDNQ_LAUNCH(launch_lora_down(dy, m, n, lora_b, r, lora_scale, gr, s));  // g_r = scale * dY B^T
-    ga.lora_t = gr; ga.lora_r = lora_a; ga.rank = r;  // + g_r A^T
+    SDNQ_LAUNCH(launch_lora_down(dy, m, n, bsrc, rp, lora_scale, gr, s));  // g_r = scale * dY B^T
+    ga.lora_t = gr; ga.lora_r = asrc; ga.rank = rp;  // + g_r A^T
   }
   SDNQ_LAUNCH(launch_gemm_i8(Epilogue::kBackward, ga, s));
 
   if (r > 0) {
     float *part = reinterpret_cast<float *>(ws_at(workspace, L.part));
-    if (want_ga) SDNQ_LAUNCH(launch_lora_grad(x, k, gr, r, m, 1.0f, false, part, grad_a, s));  // x^T g_r
+    if (want_ga) {  // x^T g_r
+      uint16_t *dst = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gap)) : grad_a;
+      SDNQ_LAUNCH(launch_lora_grad(x, k, gr, rp, m, 1.0f, false, part, dst, s));
+      if (padded) SDNQ_LAUNCH(launch_copy2d_u16(dst, k, rp, grad_a, k, r, s));
+    }
     if (want_gb) {
       tx = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tx));
       at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
-      SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));
-      SDNQ_LAUNCH(launch_lora_down(x, m, k, at, r, 1.0f, tx, s));                  // t = x A
-      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, r, m, lora_scale, true, part, grad_b, s));  // scale * (dY^T t)^T
+      uint16_t *dst = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gbp)) : grad_b;
+      SDNQ_LAUNCH(launch_transpose_u16(asrc, k, rp, at, s));
+      SDNQ_LAUNCH(launch_lora_down(x, m, k, at, rp, 1.0f, tx, s));                     // t = x A
+      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, rp, m, lora_scale, true, part, dst, s));  // scale * (dY^T t)^T
+      if (padded) SDNQ_LAUNCH(launch_copy2d_u16(dst, rp, n, grad_b, r, n, s));
     }
   }
   return SDNQ_OK;
@@ -511,9 +567,9 @@ size_t sdnq_attention_workspace_bytes(int64_t batch, int64_t heads_q, int64_t he
 
 size_t sdnq_attention_workspace_offset(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
                                        int64_t seq_k, int64_t head_dim, int32_t which) {
-  if (which < 0 || which > 4 || sdnq_attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim) == 0)
+  if (which < 0 || which > 5 || sdnq_attention_workspace_bytes(batch, heads_q, heads_kv, seq_q, seq_k, head_dim) == 0)
     return 0;
-  size_t off[5];
+  size_t off[6];
   attention_workspace_offsets(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, off);
   return off[which];
 }

@@ -401,15 +401,17 @@ __device__ __forceinline__ void attn_coords(int nq, int &bh, int &qt) {
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr unsigned kOutOfRange = 0x80000000u;  // any offset past num_records reads as zero
 
-// Split tiles: partial state of each tile whose key tiles two workgroups share,
-// and a ready flag per tile (zero before the launch).
+// Split tiles: partial state of each tile whose key tiles two workgroups share.
+// flags (zero before the launch): word 0 is the call's hand-over status, then
+// per tile an arrival count and a published flag.
 struct AttnSplit {
   float *part_o;      // [tiles][4 wavefronts][D/32][64 lanes][16] fp32 (in register order)
   float *part_ml;     // [tiles][128 rows][2]: offset, row sum
-  uint32_t *flags;    // [tiles]
+  uint32_t *flags;    // [1 + 2 tiles]
   int64_t tiles;      // query tiles x heads x batch
   int64_t per;        // key tiles per workgroup
 };
+constexpr int kSpinLimit = 1 << 24;  // polls of about 64 clocks: about a second
 constexpr int kSegFull = 0, kSegHead = 1, kSegTail = 2;
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -435,6 +437,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
   __shared__ __attribute__((aligned(1024))) int8_t k_lds[2][KB];
   __shared__ __attribute__((aligned(1024))) int8_t v_lds[2][VB];
   __shared__ __attribute__((aligned(16))) float ks_lds[2][kBN];
+  __shared__ uint32_t first_owner;
 
   const int nq = (int)((sq + kBM - 1) / kBM);
   const int64_t nkt = (sk + kBN - 1) / kBN;  // key tiles of a full row
@@ -462,9 +465,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
   }
 
   // One segment: query tile qt of head bh against key tiles [kb, ke).
-  // kSegFull writes the output; kSegHead hands (o, offset, row sum) of a tile's
-  // first key tiles to the workgroup that runs the rest (kSegTail), which merges
-  // them and writes the output.
+  // kSegFull writes the output.  The two owners of a split tile (kSegHead runs
+  // its first key tiles, kSegTail the rest) meet at the tile's arrival count:
+  // the first to arrive publishes (o, offset, row sum), the second merges them
+  // with its own and writes the output.
   auto segment = [&](int bh, int qt, int64_t kb, int64_t ke, int mode) {
     const int b = bh / hq, h = bh % hq;
     const int64_t bhk = (int64_t)b * hkv + h / (hq / hkv);
@@ -634,11 +638,13 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
     }
 
     if (mode == kSegHead || mode == kSegTail) {
-      // The head's share of a tile (o, the offset and the row sum) goes through
+      // A share of a tile (o, the offset and the row sum) goes through
       // agent-coherent (sc1) stores and loads: written through, read past any
       // cached copy.  No cache-wide write-back or invalidation is needed, which
       // would otherwise empty the XCD's L2 under every other workgroup.
       const int64_t tile = (int64_t)bh * nq + qt;
+      uint32_t *const arrivals = split.flags + 1 + 2 * tile;
+      uint32_t *const published = arrivals + 1;
       const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(split.part_o + tile * (int64_t)kBM * D), 0, kBM * D * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t rs_ml = __builtin_amdgcn_make_buffer_rsrc(
@@ -647,7 +653,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
       const unsigned o_off = (unsigned)((wave * DT * 64 + lane) * 64);
       const unsigned ml_off = (unsigned)((32 * wave + (lane & 31)) * 8);
       constexpr int kSc1 = 16;  // cache policy: agent-coherent
-      if (mode == kSegHead) {
+      if (tid == 0)
+        first_owner = __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+      __syncthreads();
+      if (first_owner) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -659,16 +668,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
                                                           ml_off, 0, kSc1);
         // every wavefront's stores have completed (vmcnt), then one flag store
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (tid == 0) __hip_atomic_store(split.flags + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(published, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
       }
-      // Tail: merge the head's share, both halves against the larger offset.  The
-      // head ran first in its workgroup, which started no later than this one;
-      // the wait is bounded (about a second) all the same, so no wavefront can
-      // spin forever.
+      // Second to arrive: the first owner counted itself in after its key tiles,
+      // so it is running and only its stores remain; it depends on no other
+      // workgroup.  The wait is bounded all the same, so no wavefront can spin
+      // forever; running out marks the call's status word.
       if (tid == 0) {
-        for (int spin = 0; spin < (1 << 24); ++spin) {
-          if (__hip_atomic_load(split.flags + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+        int spin = 0;
+        while (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          if (++spin == kSpinLimit) {
+            __hip_atomic_store(split.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
           __builtin_amdgcn_s_sleep(2);
         }
       }
@@ -686,7 +699,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[dt][4 * c + e] = o[dt][4 * c + e] * a_t + hd[e] * a_h;
         }
-        __builtin_amdgcn_sched_barrier(0);  // one tile of the head's output at a time: bounds registers
+        __builtin_amdgcn_sched_barrier(0);  // one tile of the other share at a time: bounds registers
       }
       l_run = l_run * a_t + l_h * a_h;
     }
@@ -713,10 +726,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
     // Split tiles (non-causal): the tiles' key tiles laid end to end (tiles in
     // the XCD-contiguous order of attn_coords, heads outermost), and workgroup p
     // in that order takes the run [p * per, (p + 1) * per), per >= nkt.  A tile
-    // then has at most two owners: the first runs its head and hands it over,
-    // the second runs the tail and finishes it.  Each workgroup runs its head
-    // segment first, then whole tiles, then its tail segment, so a tail waits
-    // only on a head that its owner ran first.
+    // then has at most two owners, one running its head key tiles and one its
+    // tail; whichever finishes second merges the two shares.  Each workgroup
+    // runs its head segment first, then whole tiles, then its tail segment, so
+    // the head share is usually the one published.
     const int64_t total = split.tiles * nkt;
     const int nblk = gridDim.x, bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3;
@@ -783,7 +796,7 @@ AttnLayout attn_layout(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t
   const int64_t split_tiles = tiles <= kMaxSplitTiles ? tiles : 0;
   L.part_o = off; off += align256((size_t)split_tiles * kBM * d * 4);
   L.part_ml = off; off += align256((size_t)split_tiles * kBM * 2 * 4);
-  L.flags = off; off += align256((size_t)split_tiles * 4);
+  L.flags = off; off += align256((size_t)(1 + 2 * split_tiles) * 4);  // status word, then 2 per split tile
   L.total = off;
   return L;
 }
@@ -814,8 +827,8 @@ hipError_t prep_any(int block, const PrepArgs &p, hipStream_t s) {
   }
 }
 
-// Resident split-tile workgroups per CU (all of them must be resident at once:
-// a tail waits for a head that another workgroup runs).
+// Resident split-tile workgroups per CU (the split deals the key tiles to
+// exactly the workgroups that fit at once; correctness does not depend on it).
 template <int D>
 int split_blocks_per_cu() {
   static std::atomic<int> cached{0};
@@ -877,7 +890,7 @@ hipError_t attention_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
   pa.kmean = kmean;
   pa.vt = vt;
   pa.flags = reinterpret_cast<uint32_t *>(base + L.flags);
-  pa.nflags = split ? tiles : 0;
+  pa.nflags = split ? 1 + 2 * tiles : 1;  // the status word is cleared on every call
   pa.wg_k = smooth_k ? bhk * ((sk + kPrepRows - 1) / kPrepRows) : (bhk * sk + kPrepRows - 1) / kPrepRows;
   const int64_t ppw = 64 * (4 / (D / 64));
   pa.wg_vt = bhk * ((sk + ppw - 1) / ppw);
@@ -918,6 +931,7 @@ void attention_workspace_offsets(int64_t bsz, int64_t hq, int64_t hkv, int64_t s
   offsets[2] = L.kc;
   offsets[3] = L.ks;
   offsets[4] = L.kmean;
+  offsets[5] = L.flags;
 }
 
 hipError_t launch_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t bsz, int64_t hq,

@@ -27,11 +27,10 @@ constexpr int kDownBatch = 4;
 template <int RT, int TT>  // RT = rank / 16, TT = tokens / 16
 __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restrict__ x, int64_t m, int64_t cols,
                                                         const uint16_t *__restrict__ rmat, float scale,
-                                                        uint16_t *__restrict__ out) {
+                                                        uint16_t *__restrict__ out, int64_t out_stride) {
   __shared__ v4f red[4][TT][RT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * (16 * TT);
-  const int rank = RT * 16;
 
   // contraction range of this wavefront, in steps of 32
   const int64_t steps = (cols + 31) / 32;
@@ -96,7 +95,7 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restri
         uint2 packed;
         packed.x = pack_bf16x2(scale * sum[0], scale * sum[1]);
         packed.y = pack_bf16x2(scale * sum[2], scale * sum[3]);
-        *reinterpret_cast<uint2 *>(out + t * rank + r0) = packed;
+        *reinterpret_cast<uint2 *>(out + t * out_stride + r0) = packed;
       }
     }
   }
@@ -269,6 +268,16 @@ __global__ void fill_zero_u16_kernel(uint16_t *__restrict__ out, int64_t count) 
   if (i < count) out[i] = 0;
 }
 
+// out[i, j] = in[i, j] inside in's [in_rows, in_cols], else 0, for out [out_rows, out_cols]:
+// pads a LoRA factor with zero rows or columns, or crops a padded result.
+__global__ void copy2d_u16_kernel(const uint16_t *__restrict__ in, int64_t in_rows, int64_t in_cols,
+                                  uint16_t *__restrict__ out, int64_t out_rows, int64_t out_cols) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= out_rows * out_cols) return;
+  const int64_t i = idx / out_cols, j = idx - i * out_cols;
+  out[idx] = (i < in_rows && j < in_cols) ? in[i * in_cols + j] : (uint16_t)0;
+}
+
 // ---------------------------------------------------------- transposes --
 // bf16 transpose of a rows x cols matrix whose sides are multiples of 8, in
 // 64 x 64 tiles: 16-byte row chunks in, LDS with an 8-byte row pad, 16-byte
@@ -403,12 +412,13 @@ hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t
 
 template <int TT>
 hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
-                              float scale, uint16_t *out, hipStream_t stream) {
+                              float scale, uint16_t *out, int64_t out_stride, hipStream_t stream) {
   const dim3 grid((unsigned)((m + 16 * TT - 1) / (16 * TT)));
   switch (rank / 16) {
-#define SDNQ_DOWN(RT)                                                                                         \
-  case RT:                                                                                                    \
-    hipLaunchKernelGGL((lora_down_kernel<RT, TT>), grid, dim3(256), 0, stream, x, m, cols, rmat, scale, out); \
+#define SDNQ_DOWN(RT)                                                                                           \
+  case RT:                                                                                                      \
+    hipLaunchKernelGGL((lora_down_kernel<RT, TT>), grid, dim3(256), 0, stream, x, m, cols, rmat, scale, out,   \
+                       out_stride);                                                                             \
     break;
     SDNQ_DOWN(1) SDNQ_DOWN(2) SDNQ_DOWN(3) SDNQ_DOWN(4) SDNQ_DOWN(5) SDNQ_DOWN(6) SDNQ_DOWN(7) SDNQ_DOWN(8)
 #undef SDNQ_DOWN
@@ -418,11 +428,20 @@ hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const 
 }
 
 // 64 tokens per workgroup when there are enough tokens to fill the chip that way
-// (the rank x cols factor is then re-read from L2 half as often), else 32.
+// (the rank x cols factor is then re-read from L2 half as often), else 32.  Ranks
+// above kMaxRank run as launches over consecutive slices of at most kMaxRank rows
+// of rmat, each writing its columns of out.
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
                             float scale, uint16_t *out, hipStream_t stream) {
-  if (m >= 16384) return launch_lora_down_t<4>(x, m, cols, rmat, rank, scale, out, stream);
-  return launch_lora_down_t<2>(x, m, cols, rmat, rank, scale, out, stream);
+  if (rank <= 0 || rank % 16) return hipErrorInvalidValue;
+  for (int r0 = 0; r0 < rank; r0 += kMaxRank) {
+    const int rr = rank - r0 < kMaxRank ? rank - r0 : kMaxRank;
+    const hipError_t e = m >= 16384
+        ? launch_lora_down_t<4>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream)
+        : launch_lora_down_t<2>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int lora_grad_splits(int64_t m) {
@@ -444,6 +463,15 @@ hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, in
   const int64_t count = pa * qb;
   hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
                      partials, splits, pa, qb, scale, transposed ? 1 : 0, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy2d_u16(const uint16_t *in, int64_t in_rows, int64_t in_cols, uint16_t *out, int64_t out_rows,
+                             int64_t out_cols, hipStream_t stream) {
+  const int64_t count = out_rows * out_cols;
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy2d_u16_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, in, in_rows,
+                     in_cols, out, out_rows, out_cols);
   return hipGetLastError();
 }
 

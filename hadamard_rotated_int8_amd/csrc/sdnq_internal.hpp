@@ -80,12 +80,18 @@ hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t
 // out[0 .. count) = 0 (16-bit elements)
 hipError_t launch_fill_zero_u16(uint16_t *out, int64_t count, hipStream_t stream);
 
-// out[m, r] = bf16(scale * sum_c x[m, c] * rmat[r, c]); x [m, cols], rmat [rank, cols] bf16.
+// out [out_rows, out_cols] = in [in_rows, in_cols] where both are defined, else 0
+// (16-bit elements): zero-pads a LoRA factor to a rank multiple of 16, or crops a result.
+hipError_t launch_copy2d_u16(const uint16_t *in, int64_t in_rows, int64_t in_cols, uint16_t *out, int64_t out_rows,
+                             int64_t out_cols, hipStream_t stream);
+
+// out[m, r] = bf16(scale * sum_c x[m, c] * rmat[r, c]); x [m, cols], rmat [rank, cols] bf16,
+// rank a multiple of 16 (any number of 128-row slices).
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat,
                             int rank, float scale, uint16_t *out, hipStream_t stream);
 
 // Token reduction: part[s, a, b] = sum over the tokens of split s of p[t, a] * q[t, b]
-// (p [m, pa] the wide operand, q [m, qb] the narrow one, qb <= 128; bf16), then
+// (p [m, pa] the wide operand, q [m, qb] the narrow one, qb a multiple of 16; bf16), then
 // out[a, b] (or out[b, a] when transposed) = bf16(scale * sum_s part[s, a, b]).
 int lora_grad_splits(int64_t m);
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
@@ -110,8 +116,9 @@ hipError_t launch_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, i
 
 // Int8 Q K^T attention (q [B, Hq, Sq, D], k, v [B, Hkv, Sk, D] bf16, D in {64, 128},
 // Sk % 16 == 0).  The workspace holds, in order, q codes [B, Hq, Sq, D], q scales,
-// k codes [B, Hkv, Sk, D], k scales and the K mean [B, Hkv, D] at the offsets
-// attention_workspace_offsets() returns, then scratch.
+// k codes [B, Hkv, Sk, D], k scales, the K mean [B, Hkv, D] and the hand-over
+// status word (uint32) at the six offsets attention_workspace_offsets() returns,
+// then scratch.
 size_t attention_workspace_bytes(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d);
 void attention_workspace_offsets(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d,
                                  size_t *offsets);

@@ -47,6 +47,10 @@
  *    is read, and the only work enqueued is zeroing grad_a / grad_b when the
  *    backward pass requests them (empty sums).
  *  - Alignment: every pointer must be 16-byte aligned.
+ *  - LoRA rank: any rank in [1, 256] with both factors given; rank is ignored
+ *    when both factors are NULL (no adapter).  Ranks that are not a multiple of
+ *    16 run on zero-padded copies of the factors in the workspace (the padding
+ *    adds exact zeros to every sum).
  *  - Non-finite inputs (NaN, Inf) give unspecified outputs; they are not checked.
  */
 #ifndef SDNQ_HIP_H
@@ -63,7 +67,7 @@ typedef enum {
     SDNQ_OK = 0,
     SDNQ_ERR_INVALID_ARG = 1,  /* null required pointer, negative or zero size, misaligned pointer */
     SDNQ_ERR_UNSUPPORTED = 2,  /* g not in {1,64,128,256}, k % g != 0, a feature dimension not a
-                                  multiple of 16 or above 65536, rank not in {16,32,...,128} */
+                                  multiple of 16 or above 65536, LoRA rank outside [1, 256] */
     SDNQ_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than sdnq_workspace_bytes() */
     SDNQ_ERR_LAUNCH = 4        /* a kernel launch was rejected by the HIP runtime */
 } sdnq_status_t;
@@ -258,8 +262,13 @@ size_t sdnq_svd_workspace_q_offset(int64_t n, int64_t k, int32_t rank);
  *  - q[batch, heads_q, seq_q, head_dim], k and v[batch, heads_kv, seq_k, head_dim],
  *    out like q, all bf16; query head h reads key/value head h / (heads_q / heads_kv);
  *  - smooth_k != 0: K minus its mean over the key tokens per (batch, head,
- *    channel), mean = fl32(sum / seq_k) with the sum in fp64 over blocks of 64
- *    tokens (each in token order, then the block sums in order), K' = fl32(k - mean);
+ *    channel), K' = fl32(k - mean).  The mean is the exact mean of the bf16 keys
+ *    rounded once to binary32 wherever a binary64 sum of the channel is exact
+ *    (sum |k| < 2^53 times the finest last-place unit among its nonzero keys,
+ *    which holds for any realistic activations): the sum is taken in binary64
+ *    (64-token blocks, then the block sums), divided once in binary64 and
+ *    rounded to binary32.  Outside that domain the binary64 sum's error bound
+ *    applies;
  *  - hadamard_group g in {64, 128, 256}: Q and K' rows are rotated with block
  *    min(g, head_dim) (the butterfly and normalization above); g = 0 or 1: none;
  *  - Q and K' are quantized per token (one scale per row over head_dim) with the
@@ -273,7 +282,14 @@ size_t sdnq_svd_workspace_q_offset(int64_t n, int64_t k, int32_t rank);
  * workspace: sdnq_attention_workspace_bytes(...) bytes, 16-byte aligned.  When the
  * work has completed it holds the q codes [batch, heads_q, seq_q, head_dim] (int8),
  * q scales (fp32), k codes, k scales and the K mean [batch, heads_kv, head_dim]
- * (fp32) at sdnq_attention_workspace_offset(..., which = 0 .. 4). */
+ * (fp32) at sdnq_attention_workspace_offset(..., which = 0 .. 4), and at which = 5
+ * a uint32 status word: 0, or nonzero if a query tile whose keys two workgroups
+ * shared was finished without the other workgroup's share (its bounded wait ran
+ * out; that wait is only ever on a workgroup already past its key loop, so a
+ * nonzero word means the device stalled a running workgroup for about a second).
+ * Non-causal calls whose query tiles overfill the resident workgroups by at most
+ * a sixth of a round share tiles that way; the result does not depend on which
+ * workgroups are resident together. */
 sdnq_status_t sdnq_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t batch,
                                   int64_t heads_q, int64_t heads_kv, int64_t seq_q, int64_t seq_k, int64_t head_dim,
                                   int32_t is_causal, float scale, int32_t smooth_k, int32_t hadamard_group,
@@ -284,7 +300,7 @@ size_t sdnq_attention_workspace_bytes(int64_t batch, int64_t heads_q, int64_t he
                                       int64_t seq_k, int64_t head_dim);
 
 /* Byte offset in that workspace of: 0 q codes, 1 q scales, 2 k codes, 3 k scales,
- * 4 K mean; 0 on invalid arguments. */
+ * 4 K mean, 5 the status word; 0 on invalid arguments. */
 size_t sdnq_attention_workspace_offset(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
                                        int64_t seq_k, int64_t head_dim, int32_t which);
 

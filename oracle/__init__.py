@@ -14,6 +14,7 @@ bfloat16 bits.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -406,9 +407,9 @@ def svd_quantize_weight(w_bf16: np.ndarray, g: int, omega: np.ndarray, steps: in
 #     head h // (Hq / Hkv) (grouped-query attention);
 #   * smooth_k subtracts from K its mean over the key tokens, per batch, head and
 #     channel (the softmax of each query row is unchanged by a shift common to
-#     all keys); the mean is fl32(sum / Sk) with the sum taken in fp64 over blocks
-#     of 64 tokens, each block in token order, then the block sums in block
-#     order; K' = fl32(k - mean);
+#     all keys); the mean is the exact rational mean of the bf16 keys rounded
+#     once to binary32 (to nearest, ties to even), so it does not depend on any
+#     summation order; K' = fl32(k - mean);
 #   * the rotation block along the head dimension is min(g, D) (g <= 1: none),
 #     with the butterfly, normalization and per-row int8 quantizer of the
 #     linear layer, one scale per token of Q and of K;
@@ -416,15 +417,57 @@ def svd_quantize_weight(w_bf16: np.ndarray, g: int, omega: np.ndarray, steps: in
 #     default; is_causal masks keys j > i (top-left aligned, as SDPA);
 #   * softmax and P V in fp64 on the bf16 values of v, one rounding to bf16.
 
+def _f32_nearest(num: int, den: int) -> float:
+    """The binary32 value nearest to the rational num / den (den > 0), ties to
+    even, as a Python float (exact: at most 24 significant bits).  The value must
+    lie within the binary32 range, which a mean of bf16 values always does."""
+    if num == 0:
+        return 0.0
+    neg, num = num < 0, abs(num)
+    # e = floor(log2(num / den)): start from the bit lengths, correct by one
+    e = num.bit_length() - den.bit_length()
+    if (num << max(0, -e)) < (den << max(0, e)):
+        e -= 1
+    # binary32 keeps 24 significant bits down to 2^-126, then a fixed quantum 2^-149
+    qexp = max(e, -126) - 23
+    n, d = (num, den << qexp) if qexp >= 0 else (num << -qexp, den)
+    qi, r = divmod(n, d)
+    if 2 * r > d or (2 * r == d and qi & 1):
+        qi += 1
+    v = math.ldexp(qi, qexp)
+    return -v if neg else v
+
+
 def attention_k_mean(k_bf16: np.ndarray) -> np.ndarray:
     """Per (batch, head, channel) mean of k [B, H, S, D] over the tokens as
-    binary32 [B, H, D]: fl32(sum / S), the fp64 sum taken block by block (64
-    tokens, in token order), then over the blocks in order."""
-    kf = f32_from_bf16(k_bf16).astype(np.float64)
-    total = np.zeros(kf.shape[:2] + kf.shape[3:], np.float64)
-    for b0 in range(0, kf.shape[2], 64):
-        total = total + np.cumsum(kf[:, :, b0:b0 + 64, :], axis=2)[:, :, -1, :]
-    return (total / kf.shape[2]).astype(np.float32)
+    binary32 [B, H, D]: the exact rational mean, rounded once to nearest (ties to
+    even).
+
+    A bf16 value with exponent field E and mantissa field m is
+    (-1)^sign * sig * 2^(max(E, 1) - 134), with sig = m for E = 0 (subnormal) and
+    128 + m otherwise, so 2^133 times any key is an integer.  The integer sum is
+    formed exactly: the signed sigs are totalled per exponent (at most 255 * S
+    per bucket, exact in binary64 for S <= 2^20), then the buckets are shifted
+    into place and added as Python integers."""
+    kb = np.ascontiguousarray(k_bf16, np.uint16)
+    b, hh, s, d = kb.shape
+    e = ((kb >> 7) & 0xFF).astype(np.int64)
+    if np.any(e == 0xFF):
+        raise ValueError("keys must be finite")
+    sig = (kb & 0x7F).astype(np.int64) + np.where(e > 0, 128, 0)
+    sig = np.where(kb & 0x8000, -sig, sig)
+    pos = np.maximum(e, 1) - 1                               # key = sig * 2^(pos - 133)
+    chan = np.arange(b * hh * d).reshape(b, hh, 1, d)        # one bucket row per (batch, head, channel)
+    idx = (np.broadcast_to(chan, kb.shape) * 254 + pos).ravel()
+    buckets = np.bincount(idx, weights=sig.ravel().astype(np.float64), minlength=b * hh * d * 254)
+    buckets = buckets.reshape(b * hh * d, 254).astype(np.int64)
+    out = np.empty(b * hh * d, np.float32)
+    den = s << 133
+    for c in range(b * hh * d):
+        nz = np.nonzero(buckets[c])[0]
+        total = sum(int(buckets[c, p]) << int(p) for p in nz)
+        out[c] = np.float32(_f32_nearest(total, den))
+    return out.reshape(b, hh, d)
 
 
 def attention_block(g: int, d: int) -> int:

@@ -70,7 +70,12 @@ def test_workspace_bytes():
     assert f(0, 16, 16) == 0 or f(0, 16, 16) >= 0
     assert f(-1, 16, 16) == 0
     assert f(16, 0, 16) == 0
-    assert f(16, 16, 16, 17) == 0   # unsupported rank
+    assert f(16, 16, 16, 257) == 0  # rank above 256
+    assert f(16, 16, 16, -1) == 0
+    # ranks off the multiple of 16 add room for the zero-padded factors
+    for bwd in (False, True):
+        assert f(4096, 3072, 3072, 17, bwd) > f(4096, 3072, 3072, 32, bwd) > f(4096, 3072, 3072, 16, bwd)
+        assert f(4096, 3072, 3072, 1, bwd) > 0 and f(4096, 3072, 3072, 256, bwd) > f(4096, 3072, 3072, 128, bwd)
 
 
 no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer validation runs only without a GPU")
@@ -128,8 +133,10 @@ def test_rotate_quantize_weight_validation():
     (dict(n=200), UNSUPPORTED), (dict(k=300, g=1), UNSUPPORTED), (dict(g=7), UNSUPPORTED),
     (dict(k=192, g=128), UNSUPPORTED),
     (dict(la=0x60000, lb=None, r=32), INVALID), (dict(la=None, lb=0x60000, r=32), INVALID),
-    (dict(la=0x60000, lb=0x70000, r=24), UNSUPPORTED), (dict(la=0x60000, lb=0x70000, r=0), UNSUPPORTED),
-    (dict(la=0x60000, lb=0x70000, r=256), UNSUPPORTED), (dict(la=0x60008, lb=0x70000, r=32), INVALID),
+    (dict(la=0x60000, lb=0x70000, r=257), UNSUPPORTED), (dict(la=0x60000, lb=0x70000, r=0), UNSUPPORTED),
+    (dict(la=0x60000, lb=0x70000, r=-5), UNSUPPORTED), (dict(la=0x60008, lb=0x70000, r=32), INVALID),
+    (dict(m=0, la=0x60000, lb=0x70000, r=1), OK), (dict(m=0, la=0x60000, lb=0x70000, r=24), OK),
+    (dict(m=0, la=0x60000, lb=0x70000, r=200), OK), (dict(m=0, la=0x60000, lb=0x70000, r=256), OK),
     (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(ws=W + 8), WORKSPACE),
     (dict(y=D + 2), INVALID),
     (dict(m=0), OK),
@@ -270,10 +277,11 @@ def test_attention_workspace():
     b, hq, hkv, s, d = 1, 24, 24, 4608, 128
     n = f(b, hq, hkv, s, s, d)
     assert n >= b * hq * s * d + b * hkv * s * d + b * hkv * s * d * 2   # q and k codes, V^T
-    offs = [h.sdnq_attention_workspace_offset(b, hq, hkv, s, s, d, i) for i in range(5)]
+    offs = [h.sdnq_attention_workspace_offset(b, hq, hkv, s, s, d, i) for i in range(6)]
     assert offs == sorted(offs) and offs[0] == 0 and offs[1] >= b * hq * s * d and all(o % 256 == 0 for o in offs)
+    assert offs[5] + 4 <= n                                              # the status word
     assert f(1, 4, 3, 64, 64, 128) == 0 and f(1, 4, 2, 64, 40, 128) == 0 and f(1, 4, 2, 64, 64, 80) == 0
-    assert h.sdnq_attention_workspace_offset(1, 4, 2, 64, 64, 128, 5) == 0
+    assert h.sdnq_attention_workspace_offset(1, 4, 2, 64, 64, 128, 6) == 0
 
 
 def test_product_path_fails_loudly_without_the_library():

@@ -2,7 +2,10 @@
 
 Bit-exact: the q and k codes and scales and the K mean that the entry point
 leaves in its workspace (both sides take every rounding decision on the same
-binary32 values in the same order).  Within 1e-2 relative L2 per head: the
+binary32 values in the same order).  The oracle's K mean is the exact mean
+rounded once; the GPU's binary64 sum reproduces it wherever that sum is exact
+(every realistic key tensor), and elsewhere stays within the summation's error
+bound.  Within 1e-2 relative L2 per head: the
 output (the GPU accumulates P V in fp32 from bf16 P with exp2; the oracle
 computes softmax and P V in fp64).
 """
@@ -58,6 +61,8 @@ def run(q, k, v, causal, smooth, g, scale=None):
         "k_scales": ws[off[3]: off[3] + 4 * nk].cpu().numpy().view(np.float32).reshape(b, hkv, sk),
         "k_mean": ws[off[4]: off[4] + 4 * b * hkv * d].cpu().numpy().view(np.float32).reshape(b, hkv, d),
     }
+    so = h.sdnq_attention_workspace_offset(b, hq, hkv, sq, sk, d, 5)
+    assert int(ws[so: so + 4].cpu().numpy().view(np.uint32)[0]) == 0, "split-tile hand-over status"
     return res
 
 
@@ -69,14 +74,47 @@ def rel_l2_per_head(got_bits, ref_bits):
     return (num / den).max()
 
 
+def kmean_exact_domain(k_bits):
+    """[B, H, D] mask of the channels whose binary64 partial sums are exact in any
+    order: sum|k| < 2^53 * q, q the finest quantum (last place) among the nonzero
+    keys.  There the GPU's mean is the exactly rounded mean (a binary64 sum, one
+    division, one rounding to binary32)."""
+    kf = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
+    e = ((np.asarray(k_bits, np.uint16) >> 7) & 0xFF).astype(np.int64)
+    quantum = np.where(kf != 0, np.exp2(np.maximum(e, 1) - 134.0), np.inf).min(axis=2)
+    return np.abs(kf).sum(axis=2) < 2.0 ** 53 * quantum
+
+
+def kmean_error_bound(k_bits, got_mean):
+    """Bound on |GPU mean - exact mean| for any inputs: the blocked binary64 sum
+    (64-token blocks, then the block sums) errs by at most
+    (63 + blocks) u sum|k| with u = 2^-53, the division by u |S / Sk|, and the
+    binary32 rounding by half a unit in the last place."""
+    kf = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
+    sk = kf.shape[2]
+    n = 63 + (sk + 63) // 64 + 2
+    ulp = np.spacing(np.abs(got_mean.astype(np.float32))).astype(np.float64)
+    return n * 2.0 ** -53 * np.abs(kf).sum(axis=2) / sk + ulp
+
+
 def check(q, k, v, causal, smooth, g, q_rows=None, scale=None):
     got = run(q, k, v, causal, smooth, g, scale)
     ref = oracle.attention_int8(q, k, v, causal, scale, smooth, g, intermediates=True, q_rows=q_rows)
     rows = slice(None) if q_rows is None else np.asarray(q_rows)
-    assert np.array_equal(got["k_codes"], ref["k_codes"]), "k codes"
-    assert np.array_equal(got["k_scales"].view(np.uint32), ref["k_scales"].view(np.uint32)), "k scales"
+    same_mean = np.ones(k.shape[:2], bool)
     if smooth:
-        assert np.array_equal(got["k_mean"].view(np.uint32), ref["k_mean"].view(np.uint32)), "k mean"
+        dom = kmean_exact_domain(k)
+        eq = got["k_mean"].view(np.uint32) == ref["k_mean"].view(np.uint32)
+        assert np.all(eq[dom]), "k mean (exact domain)"
+        err = np.abs(got["k_mean"].astype(np.float64) - ref["k_mean"].astype(np.float64))
+        assert np.all(err <= kmean_error_bound(k, got["k_mean"])), "k mean (outside the exact domain)"
+        same_mean = eq.all(axis=2)
+        if not dom.all():
+            say(f"    {int((~dom).sum())} channels outside the exact-sum domain, {int((~eq).sum())} means differ")
+    # K codes follow from the mean: bit-exact for every head whose mean agrees
+    assert np.array_equal(got["k_codes"][same_mean], ref["k_codes"][same_mean]), "k codes"
+    assert np.array_equal(got["k_scales"][same_mean].view(np.uint32), ref["k_scales"][same_mean].view(np.uint32)), \
+        "k scales"
     assert np.array_equal(got["q_codes"][:, :, rows], ref["q_codes"]), "q codes"
     assert np.array_equal(got["q_scales"][:, :, rows].view(np.uint32), ref["q_scales"].view(np.uint32)), "q scales"
     err = rel_l2_per_head(got["out"][:, :, rows], ref["out"])
@@ -233,3 +271,34 @@ def test_attention_prep_stress_rows(d, smooth):
     v = synth.to_bf16_bits(np.random.default_rng(53).standard_normal((1, 1, 32, d)).astype(np.float32))
     for g in (256, 1):
         check(q, k, v, False, smooth, g)
+
+
+def test_attention_k_mean_outside_the_exact_sum_domain():
+    """Keys for which a binary64 running sum rounds (2^60, 1, -2^60 patterns,
+    2^100 next to ones, bf16 subnormals next to large keys), 256 tokens in four
+    summation blocks: the oracle's mean is exact, the GPU's within the bound of
+    its blocked binary64 sum; a second head of ordinary keys stays bit-exact."""
+    rng = np.random.default_rng(91)
+    b, hkv, s, d = 1, 2, 256, 64
+    k = rng.standard_normal((b, hkv, s, d)) + 3.0 * rng.standard_normal((b, hkv, 1, d))
+    odd = k[0, 1]
+    odd[0::3, 0], odd[1::3, 0], odd[2::3, 0] = 2.0 ** 60, 1.0, -(2.0 ** 60)
+    odd[:, 1] = np.where(np.arange(s) % 2 == 0, 2.0 ** 100, 1.0)
+    odd[:, 2] = rng.integers(-255, 256, s) * 2.0 ** -133
+    odd[7, 2] = 1.0e20
+    odd[:, 3] = rng.standard_normal(s) * 2.0 ** rng.integers(-120, 60, s)
+    kb = synth.to_bf16_bits(k.astype(np.float32))
+    q = synth.to_bf16_bits(rng.standard_normal((b, 2, 64, d)).astype(np.float32))
+    v = synth.to_bf16_bits(rng.standard_normal((b, hkv, s, d)).astype(np.float32))
+    dom = kmean_exact_domain(kb)
+    assert dom[0, 0].all() and not dom[0, 1, :4].any()
+    got = run(q, kb, v, False, True, 256)
+    ref = oracle.attention_int8(q, kb, v, False, None, True, 256, intermediates=True)
+    eq = got["k_mean"].view(np.uint32) == ref["k_mean"].view(np.uint32)
+    assert eq[dom].all()
+    err = np.abs(got["k_mean"].astype(np.float64) - ref["k_mean"].astype(np.float64))
+    bound = kmean_error_bound(kb, got["k_mean"])
+    say(f"    outside the domain: {int((~eq).sum())} means differ, worst error / bound "
+        f"{float((err / bound).max()):.3e}")
+    assert np.all(err <= bound)
+    assert np.array_equal(got["k_codes"][0, 0], ref["k_codes"][0, 0])

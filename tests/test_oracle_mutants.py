@@ -60,9 +60,12 @@ PY_MUTANTS = {
                                 "        z = _orth(w.T @ q)\n        q = _orth(w @ om)"),
     "svd_factor_b_not_orthonormal": ("    b_bits = bf16_from_f64(np.ascontiguousarray(q.T))",
                                      "    b_bits = bf16_from_f64(np.ascontiguousarray((w @ om).T))"),
-    "attn_mean_divides_by_head_dim": ("    return (total / kf.shape[2]).astype(np.float32)",
-                                      "    return (total / kf.shape[3]).astype(np.float32)"),
-    "attn_mean_drops_a_block": ("    for b0 in range(0, kf.shape[2], 64):", "    for b0 in range(64, kf.shape[2], 64):"),
+    "attn_mean_divides_by_head_dim": ("    den = s << 133", "    den = d << 133"),
+    "attn_mean_truncates": ("    if 2 * r > d or (2 * r == d and qi & 1):", "    if False:"),
+    "attn_mean_ties_away": ("    if 2 * r > d or (2 * r == d and qi & 1):", "    if 2 * r >= d:"),
+    "attn_mean_subnormal_keys_get_the_hidden_bit": ("np.where(e > 0, 128, 0)", "128"),
+    "attn_mean_binary64_sum": ("    return out.reshape(b, hh, d)\n",
+                               "    return (f32_from_bf16(kb).astype(np.float64).sum(axis=2) / s).astype(np.float32)\n"),
     "attn_causal_off_by_one": ("    mask = (np.arange(sk)[None, :] > rows[:, None]) if is_causal else None",
                                "    mask = (np.arange(sk)[None, :] >= rows[:, None]) if is_causal else None"),
     "attn_gqa_modulo": ("            hk = h // rep", "            hk = h % hkv"),

@@ -826,9 +826,9 @@ def test_attention_causal_brute_force():
 
 
 def test_attention_k_mean_is_the_exact_mean_rounded_once():
-    """Values n/16 with |n| < 128 (exact in bf16), 150 tokens (three blocks of the
-    summation): every fp64 partial sum is exact, so the mean is the exact
-    rational mean divided in fp64 and rounded to binary32."""
+    """Values n/16 with |n| < 128 (exact in bf16), 150 tokens: the mean is the
+    exact rational mean rounded once to binary32 (here fp64's division is exact
+    enough that numpy's rounding of it is the same number)."""
     rng = np.random.default_rng(14)
     kf = rng.integers(-127, 128, (1, 2, 150, 64)).astype(np.float64) / 16
     k = oracle.bf16_from_f64(kf)
@@ -838,6 +838,58 @@ def test_attention_k_mean_is_the_exact_mean_rounded_once():
         for c in range(64):
             exact = Fraction(int(round(kf[0, h, :, c].sum() * 16)), 16 * 150)
             assert mean[0, h, c] == np.float32(float(exact))
+
+
+def _nearest_f32_brute(exact: Fraction) -> np.float32:
+    """Binary32 nearest to a rational, ties to even, by comparing the neighbours of
+    a first guess exactly."""
+    f = np.float32(float(exact))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda x: (abs(Fraction(float(x)) - exact), int(np.array(x).view(np.uint32)) & 1))
+
+
+def test_attention_k_mean_does_not_depend_on_a_summation_order():
+    """Keys 2^60, 1, -2^60 repeated over 192 tokens: any binary64 running sum
+    loses the ones (2^60 + 1 rounds to 2^60), whatever the blocking; the exact
+    mean is 64 / 192 = 1/3, rounded once."""
+    v = np.zeros((1, 1, 192, 16))
+    v[0, 0, 0::3] = 2.0 ** 60
+    v[0, 0, 1::3] = 1.0
+    v[0, 0, 2::3] = -(2.0 ** 60)
+    v[0, 0, :, 5] = np.roll(v[0, 0, :, 5], 1)          # another token order, the same mean
+    mean = oracle.attention_k_mean(oracle.bf16_from_f64(v))
+    assert np.all(mean == _nearest_f32_brute(Fraction(1, 3)))
+
+
+def test_attention_k_mean_rounds_ties_to_even():
+    """16 tokens (14 ones, a 2, one small key): the exact means 1 + 2^-24 and
+    1 + 3 * 2^-24 lie halfway between binary32 neighbours; ties go to the even
+    significand (1 and 1 + 2^-22)."""
+    v = np.ones((1, 1, 16, 2))
+    v[0, 0, 14] = 2.0
+    v[0, 0, 15, 0] = 2.0 ** -20
+    v[0, 0, 15, 1] = 3 * 2.0 ** -20
+    mean = oracle.attention_k_mean(oracle.bf16_from_f64(v))
+    assert mean[0, 0, 0] == np.float32(1.0)
+    assert mean[0, 0, 1] == np.float32(1.0 + 2.0 ** -22)
+
+
+def test_attention_k_mean_random_and_subnormal_keys_against_exact_rationals():
+    """Keys of every magnitude class, from bf16 subnormals up to 2^100, against the
+    exact Fraction mean rounded by comparing neighbours."""
+    rng = np.random.default_rng(21)
+    s, d = 80, 24
+    mag = 2.0 ** rng.integers(-140, 100, (s, d))
+    kf = rng.standard_normal((s, d)) * mag
+    kf[:, :4] = rng.integers(-255, 256, (s, 4)) * 2.0 ** -133    # bf16 subnormals (and zeros)
+    kf[:, 4] = rng.standard_normal(s) * 2.0 ** -128                # around the normal boundary
+    k = oracle.bf16_from_f64(kf.reshape(1, 1, s, d))
+    exact_keys = synth.bf16_bits_to_f32(k).astype(np.float64)[0, 0]
+    mean = oracle.attention_k_mean(k)[0, 0]
+    for c in range(d):
+        exact = sum((Fraction(float(x)) for x in exact_keys[:, c]), Fraction(0)) / s
+        want = _nearest_f32_brute(exact)
+        assert mean[c].view(np.uint32) == want.view(np.uint32) or (want == 0 and mean[c] == 0), c
 
 
 def test_attention_smoothing_ignores_a_key_offset_common_to_all_tokens():
