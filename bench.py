@@ -54,28 +54,46 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_mlp_4096tok_hbm_traffic.txt")
-# the GEMM kernel's sources: its own file and the shared device header it includes
-GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc", f) for f in ("gemm_i8.hip", "sdnq_internal.hpp")]
+CSRC = os.path.join(ROOT, "hadamard_rotated_int8_amd", "csrc")
+# committed rocprofv3 FETCH_SIZE + WRITE_SIZE summaries, and the sources of the
+# kernel each was taken on (its own file and the shared device header)
+GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_i8_mlp_4096tok_hbm_traffic.txt"),
+                [os.path.join(CSRC, f) for f in ("gemm_i8.hip", "sdnq_internal.hpp")])
+ROTQ_TRAFFIC = (os.path.join(ROOT, "profiles", "rotq_mlp_4096tok_hbm_traffic.txt"),
+                [os.path.join(CSRC, f) for f in ("rotq.hip", "sdnq_internal.hpp")])
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch (up, down) from the committed rocprofv3 counter
-    summary, or None when the GEMM source has changed since it was taken.  The
-    file holds `key: value` lines: source_sha256, up_bytes, down_bytes."""
+def source_sha256(files) -> str:
     import hashlib
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
+
+
+def measured_traffic(which):
+    """HBM bytes per launch (up, down) from a committed rocprofv3 counter summary,
+    or None when the kernel's sources have changed since it was taken.  The file
+    holds `key: value` lines: source_sha256, up_bytes, down_bytes."""
+    path, sources = which
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in GEMM_SOURCES)).hexdigest()
-        if kv.get("source_sha256") != sha:
+        if kv.get("source_sha256") != source_sha256(sources):
             return None
         return [int(kv["up_bytes"]), int(kv["down_bytes"])]
     except (OSError, KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def environment(torch, query_smi: bool = True) -> dict:
@@ -101,7 +119,8 @@ def to_dev_bf16(torch, bits):
 
 def cpu_baseline(inp, target_s: float) -> dict:
     """The oracle (plain C, OpenMP over rows) on a bounded sample of the same
-    workload: the first R token rows of both layers, weights prepared outside."""
+    workload: the first R token rows of both layers, weights prepared outside;
+    on all the threads the oracle uses, then again on one thread."""
     import oracle
     qwu, swu = oracle.rotate_quantize(inp["w_up"], G)
     qwd, swd = oracle.rotate_quantize(inp["w_down"], G)
@@ -112,56 +131,78 @@ def cpu_baseline(inp, target_s: float) -> dict:
         oracle.qlinear_forward(inp["h"][:rows], qwd, swd, G, intermediates=False)
         return time.perf_counter() - t0
 
-    # size the sample from a small probe, then repeat it until about target_s has passed
-    probe = run(64)
-    rows = int(min(M, max(64, 64 * target_s / max(probe, 1e-3))))
-    t, reps = 0.0, 0
-    while reps == 0 or t < 0.6 * target_s:
-        t += run(rows)
-        reps += 1
-    rows_total = rows * reps
-    ops = 2.0 * rows_total * (N_UP * K_UP + N_DOWN * K_DOWN)
-    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+    def sample(target, probe_rows):
+        # size the sample from a small probe, then repeat it until about `target` has passed
+        probe = run(probe_rows)
+        rows = int(min(M, max(probe_rows, probe_rows * target / max(probe, 1e-3))))
+        t, reps = 0.0, 0
+        while reps == 0 or t < 0.6 * target:
+            t += run(rows)
+            reps += 1
+        ops = 2.0 * rows * reps * (N_UP * K_UP + N_DOWN * K_DOWN)
+        return ops / t / 1e12, rows, reps, t
+
+    threads = oracle.num_threads()
+    tops, rows, reps, t = sample(target_s, 64)
+    oracle.set_num_threads(1)
+    try:
+        tops1, rows1, reps1, t1 = sample(0.5 * target_s, 8)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"first {rows} of {M} token rows through both layers, {reps} time(s) (rotate+quantize, "
                       f"exact int GEMM, fp32 dequant, bf16 out); weights prepared outside; {t:.1f} s",
-            "seconds": round(t, 2)}
+            "seconds": round(t, 2),
+            "value_1_thread": round(tops1, 6),
+            "sample_1_thread": f"first {rows1} token rows, {reps1} time(s), {t1:.1f} s"}
 
 
-def measure_rows(torch, h, synth, reps: int = 10) -> dict:
-    """Whole-call timings (HIP events on the launch stream) of the other steps of
-    the layer, each on its own workload: weight preparation, the attention
-    projection forward, the QuaRot-style forward with LoRA (g = 64 and 128), the
-    PEFT backward (input gradient + LoRA gradients), the full fine-tuning weight
-    gradient, the FP8 (E4M3) variant of the MLP step, the low-rank (SVD)
-    split with the forward that uses it, and the int8-QK^T attention."""
+def measure_rows(torch, h, synth, reps: int = 100, warmup: int = 10) -> dict:
+    """Whole-call timings of the other steps of the layer, each on its own
+    workload: weight preparation, the attention projection forward, the
+    QuaRot-style forward with LoRA (g = 64 and 128), the PEFT backward (input
+    gradient + LoRA gradients), the full fine-tuning weight gradient, the FP8
+    (E4M3) variant of the MLP step, the low-rank (SVD) split with the forward
+    that uses it, and the int8-QK^T attention.  Each is `reps` calls after
+    `warmup` untimed ones, every call between two HIP events on the launch
+    stream; `us` is the median, `us_min` the minimum."""
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
+    rows = {}
 
     def timed(fn):
-        for _ in range(3):
+        for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
             fn()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)])
+        return float(np.median(us)), float(us.min())
 
-    rows = {}
+    def row(key, fn, ops=None, extra=None, peak=INT8_PEAK_TOPS, unit="TOPS"):
+        us, us_min = timed(fn)
+        r = {"us": round(us, 2), "us_min": round(us_min, 2)}
+        if ops is not None:
+            r.update({unit: round(ops / us / 1e6, 1), "pct_of_peak": round(ops / us / 1e6 / peak * 100, 2)})
+        r.update(extra or {})
+        rows[key] = r
+        return us
+
     a = synth.make_config("attn")
     x, w = to_dev_bf16(torch, a["x"]), to_dev_bf16(torch, a["w"])
-    us = timed(lambda: h.sdnq_rotate_quantize_weight(w, 256))
     nb = 3072 * 3072 * 3 + 3072 * 4
-    rows["a0_weight_prep_3072x3072_g256"] = {"us": round(us, 2), "GB/s": round(nb / us / 1e3, 1)}
+    us = row("a0_weight_prep_3072x3072_g256", lambda: h.sdnq_rotate_quantize_weight(w, 256))
+    rows["a0_weight_prep_3072x3072_g256"]["GB/s"] = round(nb / us / 1e3, 1)
     qw, sw = h.sdnq_rotate_quantize_weight(w, 256)
     ws = torch.empty(h.sdnq_workspace_bytes(4096, 3072, 3072, 0, False), dtype=torch.uint8, device=dev)
     y = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
-    us = timed(lambda: h.sdnq_qlinear_forward(x, qw, sw, 256, out=y, workspace=ws))
-    ops = 2.0 * 4096 * 3072 * 3072
-    rows["attn_forward_4096x3072x3072_g256"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
-                                                "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2)}
+    row("attn_forward_4096x3072x3072_g256", lambda: h.sdnq_qlinear_forward(x, qw, sw, 256, out=y, workspace=ws),
+        2.0 * 4096 * 3072 * 3072)
     del x, w, ws, y
     q = synth.make_config("quarot")
     c = synth.CONFIGS["quarot"]
@@ -169,13 +210,11 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     la, lb = to_dev_bf16(torch, q["lora_a"]), to_dev_bf16(torch, q["lora_b"])
     ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, c.lora_rank, False), dtype=torch.uint8, device=dev)
     y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
-    ops = 2.0 * c.m * c.n * c.k
     for g in (64, 128):
         qw, sw = h.sdnq_rotate_quantize_weight(w, g)
-        us = timed(lambda: h.sdnq_qlinear_forward(x, qw, sw, g, la, lb, c.lora_scale, out=y, workspace=ws))
-        rows[f"quarot_lora_forward_8192x3072x3072_g{g}_r32"] = {
-            "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
-            "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2)}
+        row(f"quarot_lora_forward_8192x3072x3072_g{g}_r32",
+            lambda: h.sdnq_qlinear_forward(x, qw, sw, g, la, lb, c.lora_scale, out=y, workspace=ws),
+            2.0 * c.m * c.n * c.k)
     del x, w, la, lb, ws, y
     p = synth.make_config("peft")
     c = synth.CONFIGS["peft"]
@@ -183,17 +222,14 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     la, lb = to_dev_bf16(torch, p["lora_a"]), to_dev_bf16(torch, p["lora_b"])
     qw, sw = h.sdnq_rotate_quantize_weight(w, 256)
     ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, c.lora_rank, True), dtype=torch.uint8, device=dev)
-    us = timed(lambda: h.sdnq_qlinear_backward_input(dy, qw, sw, 256, x, la, lb, c.lora_scale, workspace=ws))
     ops = 2.0 * c.m * c.n * c.k
-    rows["peft_backward_16384x3072x3072_g256_r64"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
-                                                      "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
-                                                      "note": "dX through the int8 weight + LoRA dX, dA, dB"}
+    row("peft_backward_16384x3072x3072_g256_r64",
+        lambda: h.sdnq_qlinear_backward_input(dy, qw, sw, 256, x, la, lb, c.lora_scale, workspace=ws), ops,
+        {"note": "dX through the int8 weight + LoRA dX, dA, dB"})
     wws = torch.empty(h.sdnq_weight_grad_workspace_bytes(c.m, c.n, c.k), dtype=torch.uint8, device=dev)
     dw = torch.empty((c.n, c.k), dtype=torch.bfloat16, device=dev)
-    us = timed(lambda: h.sdnq_qlinear_weight_grad(dy, x, 256, out=dw, workspace=wws))
-    rows["weight_grad_16384x3072x3072_g256"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
-                                                "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
-                                                "note": "dW = dY^T x, both quantized per feature along the tokens"}
+    row("weight_grad_16384x3072x3072_g256", lambda: h.sdnq_qlinear_weight_grad(dy, x, 256, out=dw, workspace=wws),
+        ops, {"note": "dW = dY^T x, both quantized per feature along the tokens"})
     del wws, dw
     del x, w, dy, la, lb, ws
     # FP8 variant of the MLP step (same workload, E4M3 codes, fp32 MFMA accumulation)
@@ -221,14 +257,13 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
         L.sdnq_rotate_quantize_act_fp8(P(hh), M, K_DOWN, G, None, P(qh), P(sh), sp)
         gemm_down()
     ops = 2.0 * M * (N_UP * K_UP + N_DOWN * K_DOWN)
-    us = timed(step8)
-    t_up, t_down = timed(gemm_up), timed(gemm_down)
-    gemm_tops = ops / (t_up + t_down) / 1e6
-    rows["fp8_mlp_step_4096tok_g256"] = {
-        "us": round(us, 2), "TFLOP/s": round(ops / us / 1e6, 1), "pct_of_fp8_peak": round(ops / us / 1e6 / 50.0, 2),
-        "gemm_up_us": round(t_up, 2), "gemm_down_us": round(t_down, 2),
-        "gemm_TFLOP/s": round(gemm_tops, 1), "gemm_pct_of_fp8_peak": round(gemm_tops / 50.0, 2),
-        "note": "E4M3 codes, fp32 MFMA accumulation; back-to-back GEMM launches; fp8 dense peak 5.0 PFLOP/s"}
+    (t_up, _), (t_down, _) = timed(gemm_up), timed(gemm_down)
+    gemm_tflops = ops / (t_up + t_down) / 1e6
+    row("fp8_mlp_step_4096tok_g256", step8, ops,
+        {"gemm_up_us": round(t_up, 2), "gemm_down_us": round(t_down, 2), "gemm_TFLOP/s": round(gemm_tflops, 1),
+         "gemm_pct_of_fp8_peak": round(gemm_tflops / 50.0, 2),
+         "note": "E4M3 codes, fp32 MFMA accumulation; GEMM medians timed alone; fp8 dense peak 5.0 PFLOP/s"},
+        peak=5000.0, unit="TFLOP/s")
     del x, hh, qwu, qwd, qx, qh, yu, yd
     # low-rank (SVD) split: offline preparation of W [3072, 3072] (rank 32, 8 steps),
     # then the forward with the factors as the LoRA term
@@ -238,18 +273,15 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
     x, w = to_dev_bf16(torch, sv["x"]), to_dev_bf16(torch, sv["w"])
     omega = torch.from_numpy(sv["omega"]).to(dev)
     sws = torch.empty(h.sdnq_svd_workspace_bytes(c.n, c.k, r), dtype=torch.uint8, device=dev)
-    us = timed(lambda: h.sdnq_svd_quantize_weight(w, 256, omega, steps, workspace=sws))
-    rows["svd_split_prep_3072x3072_r32_s8_g256"] = {
-        "us": round(us, 2), "note": "offline: randomized range finder, 8 subspace iterations, fp64 thin products"}
+    row("svd_split_prep_3072x3072_r32_s8_g256", lambda: h.sdnq_svd_quantize_weight(w, 256, omega, steps, workspace=sws),
+        extra={"note": "offline: randomized range finder, 8 subspace iterations, fp64 thin products"})
     qw, sw, sa, sb = h.sdnq_svd_quantize_weight(w, 256, omega, steps, workspace=sws)
     del sws
     ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, r, False), dtype=torch.uint8, device=dev)
     y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
-    us = timed(lambda: h.sdnq_qlinear_forward(x, qw, sw, 256, sa, sb, 1.0, out=y, workspace=ws))
-    ops = 2.0 * c.m * c.n * c.k
-    rows["svd_forward_4096x3072x3072_g256_r32"] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
-                                                   "pct_of_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS * 100, 2),
-                                                   "note": "int8 residual + bf16 rank-32 factors in the epilogue"}
+    row("svd_forward_4096x3072x3072_g256_r32",
+        lambda: h.sdnq_qlinear_forward(x, qw, sw, 256, sa, sb, 1.0, out=y, workspace=ws), 2.0 * c.m * c.n * c.k,
+        {"note": "int8 residual + bf16 rank-32 factors in the epilogue"})
     del x, w, omega, qw, sw, sa, sb, ws, y
     # int8-QK^T attention: flux.1 joint attention and a causal grouped-query text encoder
     for name in ("attn_flux", "attn_te"):
@@ -259,13 +291,13 @@ def measure_rows(torch, h, synth, reps: int = 10) -> dict:
         aws = torch.empty(h.sdnq_attention_workspace_bytes(ac.batch, ac.heads_q, ac.heads_kv, ac.seq_q, ac.seq_k,
                                                            ac.head_dim), dtype=torch.uint8, device=dev)
         o = torch.empty_like(q)
-        us = timed(lambda: h.sdnq_attention_int8(q, k, v, ac.causal, None, True, 256, out=o, workspace=aws))
         pairs = ac.seq_q * ac.seq_k * (0.5 if ac.causal else 1.0)
         ops = 4.0 * ac.batch * ac.heads_q * pairs * ac.head_dim
-        ref_us = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=ac.causal,
-                                                                                enable_gqa=True))
+        ref_us, _ = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=ac.causal,
+                                                                                   enable_gqa=True))
+        us, us_min = timed(lambda: h.sdnq_attention_int8(q, k, v, ac.causal, None, True, 256, out=o, workspace=aws))
         rows[f"attention_int8_{name[5:]}_{ac.batch}x{ac.heads_q}x{ac.seq_q}x{ac.head_dim}"] = {
-            "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+            "us": round(us, 2), "us_min": round(us_min, 2), "TOPS": round(ops / us / 1e6, 1),
             "torch_sdpa_bf16_us": round(ref_us, 2),
             "note": "whole call (K mean, rotate+quantize of Q and K, V transpose, int8 QK^T / bf16 PV kernel); "
                     "ops = 2 (QK^T) + 2 (PV) per query-key pair and head dimension"}
@@ -395,7 +427,8 @@ def main():
     rot_s = (in_step_ms[0] + in_step_ms[2]) * 1e-3  # in-step: the activations come from HBM, not a warm cache
     rot_gbs = rot_bytes / rot_s / 1e9
 
-    traffic = measured_traffic()
+    traffic = measured_traffic(GEMM_TRAFFIC)
+    rot_traffic = measured_traffic(ROTQ_TRAFFIC)
     out = {
         "metric": "INT8 TOPS of fused Hadamard-quantized linear, % of MI355X INT8 MFMA peak",
         "value": round(tops, 2),
@@ -423,7 +456,10 @@ def main():
                      "per_launch_ops": [ops_up, ops_down]},
         "rotate_quantize_roofline": {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": HBM_PEAK_GBS,
                                      "unit": "GB/s", "frac": round(rot_gbs / HBM_PEAK_GBS, 4),
+                                     "traffic": None if rot_traffic is None else int(sum(rot_traffic) / 2),
+                                     "traffic_per_launch": rot_traffic,
                                      "per_launch_bytes": [M * K_UP * 3 + M * 4, M * K_DOWN * 3 + M * 4],
+                                     "kernel": "rotq_kernel (x [4096, 3840], h [4096, 10240])",
                                      "timing": "HIP events between the kernels of whole steps"},
         "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
         "kernel_in_step_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, in_step_ms)},

@@ -20,18 +20,24 @@
 // contraction is the full 64-k dot product.
 //
 // Tiling.  A workgroup of 8 wavefronts (two per SIMD, so one hides the other's
-// waits) computes a 256 x 256 output tile; K is consumed 64 bytes at a time
-// through a 4-stage LDS ring (4 x 32 KB) filled by buffer loads that write LDS
-// directly, three k-tiles ahead.  Each wavefront owns a (256/WAVES_M) x
-// (256/WAVES_N) sub-tile of eight 32 x 32 MFMA tiles (v_mfma_i32_32x32x32_i8,
-// 128 int32 accumulators).  The MFMA
-// "row" operand is the B side (weight rows, output column n) and the "column"
-// operand the A side (tokens m), so each lane ends up holding, for one token,
-// runs of 4 consecutive output columns: bf16 stores of 8 bytes.
+// waits) computes a 256 x BN output tile; K is consumed 128 bytes at a time (one
+// whole 128-byte cache line of every operand row per k-tile) through a 2-stage
+// LDS ring filled by buffer loads that write LDS directly, one k-tile ahead.
+// Each wavefront owns a (256/WAVES_M) x (BN/WAVES_N) sub-tile of 32 x 32 MFMA
+// tiles (v_mfma_i32_32x32x32_i8, 16 int32 accumulators each), four 32-deep
+// k-steps per k-tile.  The MFMA "row" operand is the B side (weight rows, output
+// column n) and the "column" operand the A side (tokens m), so each lane ends up
+// holding, for one token, runs of 4 consecutive output columns.
 //
-// LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
-// c ^ ((r >> 2) & 3), which makes the 16-byte fragment reads (16 rows, one chunk)
-// conflict-free (the bank-conflict counter reads zero).
+// Why 128-byte k-tiles: the k loop is bound by how fast each compute unit's
+// vector memory path fills LDS (about 55 GB/s per CU, the same whether one tile
+// or all CUs are active, and the same for loads into registers), not by LDS
+// reads.  Fetching whole cache lines per row per k-tile instead of half lines
+// took the 4096 x 3840 x 10240 GEMM from 150 to 136 us.
+//
+// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+// c ^ (r & 7), which makes the 16-byte fragment reads (8 consecutive rows, one
+// logical chunk) conflict-free.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the block index is
 // remapped so that each XCD walks a contiguous run of tiles, ordered in groups
@@ -41,8 +47,9 @@
 namespace sdnq {
 namespace {
 
-constexpr int BM = 256, BK = 64, STAGES = 4;
-constexpr int kThreads = 512;  // 8 wavefronts: two per SIMD
+constexpr int BM = 256, BK = 128, STAGES = 2;
+constexpr int kKSteps = BK / 32;  // 32-deep MFMA steps per k-tile
+constexpr int kThreads = 512;     // 8 wavefronts: two per SIMD
 constexpr int kGroupM = 4;
 constexpr unsigned kOutOfRange = 0x80000000u;  // any offset past num_records reads as zero
 
@@ -118,19 +125,20 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 }
 
 // Tile geometry for an output tile of BM x BN_.  A stage holds the A tile then
-// the B tile, rows of BK bytes, loaded in groups of 16 rows (1 KB, one
+// the B tile, rows of BK bytes, loaded in groups of 8 rows (1 KB, one
 // direct-to-LDS load per wavefront).  The groups are dealt to the 8 wavefronts
-// round-robin; when they do not divide evenly the spare slots load nothing (an
-// out-of-range offset) into a 1 KB dummy area, so every wavefront issues the same
-// number of loads and one vmcnt value fits all.
+// round-robin (the A groups fill the first kASlots slots); when they do not
+// divide evenly the spare slots load nothing (an out-of-range offset) into a
+// 1 KB dummy area.
 template <int BN_>
 struct TileCfg {
   static constexpr int kStageBytes = (BM + BN_) * BK;
-  static constexpr int kGroups = (BM + BN_) / 16;
+  static constexpr int kGroups = (BM + BN_) / 8;
+  static constexpr int kASlots = (BM / 8) / 8;
   static constexpr int kLoadsPerWave = (kGroups + 7) / 8;
   static constexpr bool kDummy = kGroups % 8 != 0;
   static constexpr int kLdsBytes = STAGES * kStageBytes + (kDummy ? 1024 : 0);
-  static_assert(BN_ % 32 == 0 && BM / 16 == 16, "A groups fill load slots 0 and 1");
+  static_assert(BN_ % 32 == 0 && (BM / 8) % 8 == 0, "the A groups fill whole load slots");
 };
 
 template <bool FP8>
@@ -151,6 +159,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   using Cfg = TileCfg<BN>;
   constexpr int kStageBytes = Cfg::kStageBytes;
   constexpr int LPW = Cfg::kLoadsPerWave;
+  constexpr int ASL = Cfg::kASlots;
   constexpr int WAVES_N = 8 / WAVES_M;
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int SM = TM / 32, SN = TN / 32;
@@ -168,12 +177,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
   // ---- direct global -> LDS loads (buffer_load_dwordx4 ... lds)
-  // A stage holds the A tile (256 rows x 64 B) then the B tile (BN rows).  Load
-  // slot j of a wavefront fills the 16-row group 8*j + wave of the stage (slots
-  // 0, 1: A groups; slots 2..: B groups): lane i lands at byte 16*i of that 1 KB
-  // group, i.e. row 16*g + i/4, stored chunk i%4.  Rows are XOR-swizzled (stored
-  // chunk = logical chunk ^ ((row >> 2) & 3)), so lane i fetches logical chunk
-  // c = (i & 3) ^ ((i >> 4) & 3).  Rows past the matrix end lie past the
+  // A stage holds the A tile (256 rows x 128 B) then the B tile (BN rows).  Load
+  // slot j of a wavefront fills the 8-row group 8*j + wave of the stage (slots
+  // below ASL: A groups; the others: B groups): lane i lands at byte 16*i of that
+  // 1 KB group, i.e. row 8*g + i/8, stored chunk i%8.  Rows are XOR-swizzled
+  // (stored chunk = logical chunk ^ (row & 7)), so lane i fetches logical chunk
+  // c = (i & 7) ^ ((i >> 3) & 7).  Rows past the matrix end lie past the
   // buffer's num_records and read as zero, and so do chunks past K (their offset
   // is pushed out of range).
   const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
@@ -182,15 +191,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       __builtin_amdgcn_make_buffer_rsrc((void *)(args.a + m0 * K), 0, (int)(rows_a * K), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_b =
       __builtin_amdgcn_make_buffer_rsrc((void *)(args.b + n0 * K), 0, (int)(rows_b * K), 0x00020000);
-  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const int lc = (lane & 7) ^ ((lane >> 3) & 7);
   // per slot: row group within its operand, or -1 for a spare slot
   int grp[LPW];
   unsigned voff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int g = 8 * j + wave;
-    grp[j] = j < 2 ? g : (g - BM / 16 < BN / 16 ? g - BM / 16 : -1);
-    voff[j] = (unsigned)((16 * (grp[j] < 0 ? 0 : grp[j]) + (lane >> 2)) * K + 16 * lc);
+    grp[j] = j < ASL ? g : (g - BM / 8 < BN / 8 ? g - BM / 8 : -1);
+    voff[j] = (unsigned)((8 * (grp[j] < 0 ? 0 : grp[j]) + (lane >> 3)) * K + 16 * lc);
   }
   int8_t *const dummy = smem + STAGES * kStageBytes;
 
@@ -204,23 +213,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       // wavefront-uniform selects, no branch: a spare slot loads nothing into the dummy area
-      const bool spare = Cfg::kDummy && j >= 2 && grp[j] < 0;
-      int8_t *dst = spare ? dummy : base + (j < 2 ? 0 : BM * BK) + grp[j] * 1024;
+      const bool spare = Cfg::kDummy && j >= ASL && grp[j] < 0;
+      int8_t *dst = spare ? dummy : base + (j < ASL ? 0 : BM * BK) + grp[j] * 1024;
       const unsigned off = spare ? kOutOfRange : ((voff[j] + k0) | oob);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 2 ? rsrc_a : rsrc_b, (lds_void *)dst, 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < ASL ? rsrc_a : rsrc_b, (lds_void *)dst, 16, off, 0, 0, 0);
     }
   };
 
-  // ---- fragment reads: lane l reads row (tile row base + l % 32), logical chunk
-  // 2*kk + l / 32, stored at chunk ^ ((l >> 2) & 3).
+  // ---- fragment reads of k-step kk (0..3) of tile kt: lane l reads row (tile
+  // row base + l % 32), logical chunk 2*kk + l / 32, stored at chunk ^ (l & 7)
+  // (the row base is a multiple of 32).
   const int frow = (lane & 31) * BK;
-  const int fcol0 = 16 * ((0 + (lane >> 5)) ^ ((lane >> 2) & 3));
-  const int fcol1 = 16 * ((2 + (lane >> 5)) ^ ((lane >> 2) & 3));
+  int fcol[kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < kKSteps; ++kk) fcol[kk] = 16 * ((2 * kk + (lane >> 5)) ^ (lane & 7));
   struct Frags {
     v4i a[SM], b[SN];
   };
   auto read_frags = [&](int kt, int kk, Frags &f) {
-    const int8_t *base = smem + (kt & (STAGES - 1)) * kStageBytes + frow + (kk ? fcol1 : fcol0);
+    const int8_t *base = smem + (kt & (STAGES - 1)) * kStageBytes + frow + fcol[kk];
 #pragma unroll
     for (int i = 0; i < SM; ++i) f.a[i] = *reinterpret_cast<const v4i *>(base + (wm * TM + i * 32) * BK);
 #pragma unroll
@@ -255,76 +266,100 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         if constexpr (!FP8) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
 
-  // ---- pipeline: tiles kt+1..kt+3 are in flight while tile kt is consumed.
-  // Iteration kt: read (kt, kk=1) | MFMA (kt, kk=0) | wait for tile kt+1, barrier |
-  // load tile kt+3 into the stage tile kt-1 used | read (kt+1, kk=0) | MFMA (kt, kk=1).
-  // Tiles past the last one are issued too: every lane's offset is then out of
-  // range, so they only write zeros into a free stage.  This keeps the loop body
-  // branch-free and the number of loads in flight constant (4 per tile).
-  for (int t = 0; t < STAGES - 1; ++t) issue_loads(t);
-  wait_loads_and_barrier<2 * LPW>();
+  // ---- pipeline: tile kt+1 lands in the other stage while tile kt is consumed.
+  // Both stages are loaded first; at each k-tile's last step every wavefront
+  // waits for tile kt+1 and for its own LDS reads of tile kt, meets the others at
+  // the barrier, and loads tile kt+2 into the stage tile kt used.  Tiles past the
+  // last one are issued too: every lane's offset is then out of range, so they
+  // only write zeros into a free stage, and the loop body stays branch-free.
+  auto sched = [&](int loads, int reads, int mfmas) {
+#pragma unroll
+    for (int u = 0; u < mfmas; ++u) {
+      if (u < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global->LDS load
+      if (u < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
+    }
+  };
+  auto wait_tile_and_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue_loads(0);
+  issue_loads(1);
+  wait_loads_and_barrier<LPW>();
   Frags f0, f1;
   read_frags(0, 0, f0);
 
   if constexpr (FP8 && BN == 320) {
-    // Ten accumulator tiles leave room for three fragment sets only.  Iteration
-    // kt: read the second half of tile kt | wait for tile kt+1, barrier | load
-    // tile kt+3 | read the first half of tile kt+1 | MFMA tile kt.
+    // Ten accumulator tiles leave room for two fragment sets: each FP8 MFMA
+    // step (two k-steps, both 16-byte halves of 64 k positions) waits for its
+    // own reads, and the other wavefront of the SIMD fills the gap.
+    // Iteration kt: MFMA (kt,0..1) | read (kt,2..3), wait, barrier, load tile
+    // kt+2 | MFMA (kt,2..3) | read (kt+1,0..1).
+    constexpr int T = SM * SN;
+    read_frags(0, 1, f1);
     for (int kt = 0; kt < nk; ++kt) {
-      read_frags(kt, 1, f1);
-      wait_loads_and_barrier<LPW>();
-      issue_loads(kt + 3);
-      Frags g0;
-      read_frags(kt + 1, 0, g0);
       mfma8_all(f0, f1);
-#pragma unroll
-      for (int u = 0; u < SM * SN; ++u) {
-        if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // 1 global->LDS load
-        if (u < SM + SN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
-      }
-      f0 = g0;
+      sched(0, 0, T);
+      read_frags(kt, 2, f0);
+      read_frags(kt, 3, f1);
+      wait_tile_and_barrier();
+      issue_loads(kt + 2);
+      mfma8_all(f0, f1);
+      sched(LPW, 0, T);
+      read_frags(kt + 1, 0, f0);
+      read_frags(kt + 1, 1, f1);
     }
   } else if constexpr (FP8) {
-    // Iteration kt: wait for tile kt+1, barrier | load tile kt+3 | read both
-    // halves of tile kt+1 | MFMA tile kt (both halves, read one iteration ago).
+    // Iteration kt: read (kt,2..3) | MFMA (kt,0..1); wait, barrier, load tile
+    // kt+2 | read (kt+1,0..1) | MFMA (kt,2..3).
     read_frags(0, 1, f1);
-    constexpr int R = 2 * (SM + SN);
+    constexpr int T = SM * SN, R = 2 * (SM + SN);
     for (int kt = 0; kt < nk; ++kt) {
-      wait_loads_and_barrier<LPW>();
-      issue_loads(kt + 3);
       Frags g0, g1;
-      read_frags(kt + 1, 0, g0);
-      read_frags(kt + 1, 1, g1);
+      read_frags(kt, 2, g0);
+      read_frags(kt, 3, g1);
       mfma8_all(f0, f1);
 #pragma unroll
-      for (int u = 0; u < SM * SN; ++u) {
-        if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      // 1 global->LDS load
-        __builtin_amdgcn_sched_group_barrier(0x100, R / (SM * SN), 0);                    // LDS reads
-        if (u < R % (SM * SN)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // 1 MFMA
+      for (int u = 0; u < T; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, R / T, 0);                  // LDS reads
+        if (u < R % T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // 1 MFMA
       }
-      f0 = g0;
-      f1 = g1;
-    }
-  } else
-  for (int kt = 0; kt < nk; ++kt) {
-    read_frags(kt, 1, f1);
-    mfma_all(f0);
+      wait_tile_and_barrier();
+      issue_loads(kt + 2);
+      read_frags(kt + 1, 0, f0);
+      read_frags(kt + 1, 1, f1);
+      mfma8_all(g0, g1);
 #pragma unroll
-    for (int u = 0; u < SM * SN; ++u) {
-      if (u < SM + SN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+      for (int u = 0; u < T; ++u) {
+        if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // 1 global->LDS load
+        __builtin_amdgcn_sched_group_barrier(0x100, R / T, 0);                  // LDS reads
+        if (u < R % T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // 1 MFMA
+      }
     }
-    wait_loads_and_barrier<LPW>();
-    issue_loads(kt + 3);
-    read_frags(kt + 1, 0, f0);
-    mfma_all(f1);
-#pragma unroll
-    for (int u = 0; u < SM * SN; ++u) {
-      if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // 1 global->LDS load
-      if (u < SM + SN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+  } else {
+    // Iteration kt: read (kt,1) | MFMA (kt,0); read (kt,2) | MFMA (kt,1);
+    // read (kt,3) | MFMA (kt,2); wait, barrier, load tile kt+2 | read (kt+1,0) |
+    // MFMA (kt,3).
+    constexpr int T = SM * SN;
+    for (int kt = 0; kt < nk; ++kt) {
+      read_frags(kt, 1, f1);
+      mfma_all(f0);
+      sched(0, SM + SN, T);
+      read_frags(kt, 2, f0);
+      mfma_all(f1);
+      sched(0, SM + SN, T);
+      read_frags(kt, 3, f1);
+      mfma_all(f0);
+      sched(0, SM + SN, T);
+      wait_tile_and_barrier();
+      issue_loads(kt + 2);
+      read_frags(kt + 1, 0, f0);
+      mfma_all(f1);
+      sched(LPW, SM + SN, T);
     }
   }
   // The zero-fill loads of the last iterations may still be landing in LDS.

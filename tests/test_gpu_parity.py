@@ -58,12 +58,15 @@ def max_token_rel(got_bits, ref_bits):
     return float((num / den).max())
 
 
-def assert_close(got_bits, ref_bits, what=""):
-    """Relative L2 over the tensor and for the worst token row, both below 1e-2."""
+def assert_close(got_bits, ref_bits, what="", per_token=True):
+    """Relative L2 over the tensor and, for outputs whose rows are tokens (y, dx),
+    for the worst token row, both below 1e-2.  The LoRA weight gradients are sums
+    over all tokens; their rows are features, compared as one tensor."""
     err, tok = rel_l2(got_bits, ref_bits), max_token_rel(got_bits, ref_bits)
-    say(f"    {what} rel-L2 {err:.3e}  max-token {tok:.3e}")
+    say(f"    {what} rel-L2 {err:.3e}  max-row {tok:.3e}")
     assert err < REL_L2, f"{what} rel-L2 {err:.3e}"
-    assert tok < REL_L2, f"{what} worst token rel-L2 {tok:.3e}"
+    if per_token:
+        assert tok < REL_L2, f"{what} worst token rel-L2 {tok:.3e}"
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -316,8 +319,8 @@ def test_backward_without_lora_is_bit_exact(m, n, k, g):
 
 def assert_lora_grads(dx, ga, gb, ref):
     assert_close(dx, ref["dx"], "dx")
-    assert_close(ga, ref["grad_a"], "grad_a")
-    assert_close(gb, ref["grad_b"], "grad_b")
+    assert_close(ga, ref["grad_a"], "grad_a", per_token=False)
+    assert_close(gb, ref["grad_b"], "grad_b", per_token=False)
 
 
 @pytest.mark.parametrize("g,rank", [(256, 64), (64, 32), (128, 16)])
