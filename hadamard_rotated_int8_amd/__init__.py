@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     sdnq_gemm_i8_i32,
     sdnq_qlinear_backward_input,
     sdnq_qlinear_forward,
+    sdnq_qlinear_forward_noalloc,
+    SDNQ_NOALLOC_SCRATCH_BYTES,
     sdnq_qlinear_forward_fp8,
     sdnq_qlinear_forward_fp8_quantized,
     sdnq_qlinear_forward_quantized,

@@ -42,6 +42,7 @@ def lib() -> ctypes.CDLL:
         "sdnq_rotate_quantize_weight": [p, i64, i64, i32, p, p, p],
         "sdnq_rotate_quantize_act": [p, i64, i64, i32, p, p, p, p],
         "sdnq_qlinear_forward": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p, sz, p],
+        "sdnq_qlinear_forward_noalloc": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p],
         "sdnq_qlinear_forward_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
         "sdnq_qlinear_backward_input": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
         "sdnq_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p, sz, p],
@@ -163,6 +164,29 @@ def sdnq_qlinear_forward(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale
     """y [m, n] bf16 = dequant(rotq(x) . qw^T) + lora_scale * (x lora_a) lora_b."""
     return _forward("sdnq_qlinear_forward", torch.int8, x, qw, w_scale, g, lora_a, lora_b, lora_scale, out,
                     workspace)
+
+
+SDNQ_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def sdnq_qlinear_forward_noalloc(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale=0.0, out=None):
+    """sdnq_qlinear_forward with the library's fixed device scratch array as the
+    workspace (no workspace argument; calls on one device must not overlap)."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(qw, torch.int8, 2, "qw")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    m, k = x.shape
+    n = qw.shape[0]
+    rank = 0
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, torch.bfloat16, 2, "lora_a")
+        _need(lora_b, torch.bfloat16, 2, "lora_b")
+        rank = lora_a.shape[1]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _check(lib().sdnq_qlinear_forward_noalloc(_ptr(x), m, k, _ptr(qw), _ptr(w_scale), n, g, _ptr(lora_a),
+                                              _ptr(lora_b), rank, float(lora_scale), _ptr(y), _stream(x.device)),
+           "sdnq_qlinear_forward_noalloc")
+    return y
 
 
 def sdnq_qlinear_forward_fp8(x, qw, w_scale, g, lora_a=None, lora_b=None, lora_scale=0.0, out=None,

@@ -242,17 +242,24 @@ sdnq_status_t forward_quantized(bool fp8, const int8_t *qx, const float *x_scale
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));
 }
 
-sdnq_status_t forward(bool fp8, const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
-                      int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
-                      float lora_scale, uint16_t *y, void *workspace, size_t workspace_bytes, void *stream) {
+// Every check of the forward except the workspace's; *r is the effective rank.
+sdnq_status_t check_forward(const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
+                            int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                            const uint16_t *y, int32_t *r) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!x || !y)) return SDNQ_ERR_INVALID_ARG;
   SDNQ_TRY(check_feature(k));
   SDNQ_TRY(check_feature(n));
   if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y)) return SDNQ_ERR_INVALID_ARG;
+  return check_lora(lora_a, lora_b, rank, r);
+}
+
+sdnq_status_t forward(bool fp8, const uint16_t *x, int64_t m, int64_t k, const int8_t *qw, const float *w_scale,
+                      int64_t n, int32_t g, const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                      float lora_scale, uint16_t *y, void *workspace, size_t workspace_bytes, void *stream) {
   int32_t r = 0;
-  SDNQ_TRY(check_lora(lora_a, lora_b, rank, &r));
+  SDNQ_TRY(check_forward(x, m, k, qw, w_scale, n, g, lora_a, lora_b, rank, y, &r));
   const FwdLayout L = fwd_layout(m, n, k, r);
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SDNQ_ERR_WORKSPACE;
   if (m == 0) return SDNQ_OK;
@@ -307,6 +314,46 @@ sdnq_status_t sdnq_qlinear_forward(const uint16_t *x, int64_t m, int64_t k, cons
                                    size_t workspace_bytes, void *stream) {
   return forward(false, x, m, k, qw, w_scale, n, g, lora_a, lora_b, rank, lora_scale, y, workspace,
                  workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ forward without allocation --
+// Callers that cannot allocate (code under HIP graph capture, tight serving
+// loops) get the forward's workspace from this fixed device array instead.  The
+// host-side name is only a stand-in: the device address is looked up once per
+// device with hipGetSymbolAddress and that address is what the kernels get.
+namespace {
+constexpr size_t kScratchBytes = SDNQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_addr[kMaxDevices];
+
+// The device address of `scratch` on the current device (nullptr on failure).
+void *scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+sdnq_status_t sdnq_qlinear_forward_noalloc(const uint16_t *x, int64_t m, int64_t k, const int8_t *qw,
+                                           const float *w_scale, int64_t n, int32_t g, const uint16_t *lora_a,
+                                           const uint16_t *lora_b, int32_t rank, float lora_scale, uint16_t *y,
+                                           void *stream) {
+  int32_t r = 0;
+  SDNQ_TRY(check_forward(x, m, k, qw, w_scale, n, g, lora_a, lora_b, rank, y, &r));
+  if (fwd_layout(m, n, k, r).total > kScratchBytes) return SDNQ_ERR_WORKSPACE;
+  void *ws = scratch_on_current_device();
+  if (ws == nullptr) return SDNQ_ERR_LAUNCH;
+  return forward(false, x, m, k, qw, w_scale, n, g, lora_a, lora_b, rank, lora_scale, y, ws, kScratchBytes, stream);
 }
 
 sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw,

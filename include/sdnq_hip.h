@@ -132,6 +132,23 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
                                           uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): sdnq_qlinear_forward
+ * with the same arguments and results, minus the workspace, which comes from a
+ * fixed SDNQ_NOALLOC_SCRATCH_BYTES device array that the library holds on each
+ * device it runs on until the process ends.  Nothing is allocated or freed.
+ * Returns SDNQ_ERR_WORKSPACE, before any launch, when the call would need more
+ * than that (sdnq_workspace_bytes(m, n, k, rank, 0) > SDNQ_NOALLOC_SCRATCH_BYTES),
+ * and SDNQ_ERR_LAUNCH if the array's device address cannot be obtained.  Every
+ * call on a device shares that device's array: calls that overlap on one device
+ * (concurrent streams, other host threads) race and must be serialized by the
+ * caller; consecutive calls on one stream are safe. */
+#define SDNQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sdnq_status_t sdnq_qlinear_forward_noalloc(const uint16_t *x, int64_t m, int64_t k,
+                                           const int8_t *qw, const float *w_scale, int64_t n, int32_t g,
+                                           const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                           float lora_scale, uint16_t *y, void *stream);
+
 /* Workspace size in bytes for sdnq_qlinear_forward(_quantized) (is_backward = 0) or
  * sdnq_qlinear_backward_input (is_backward = 1) at these sizes; 0 on invalid sizes. */
 size_t sdnq_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t rank, int32_t is_backward);

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
               "sdnq_gemm_fp8_f32", "sdnq_qlinear_weight_grad", "sdnq_weight_grad_workspace_bytes",
               "sdnq_weight_grad_workspace_offset",
               "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset",
-              "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset"):
+              "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset",
+              "sdnq_qlinear_forward_noalloc"):
         assert n in names
 
 
@@ -307,3 +308,19 @@ def test_host_tensors_are_rejected():
     w = torch.zeros(512, 512, dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         h.sdnq_rotate_quantize_weight(w, 256)
+
+
+@no_gpu
+def test_noalloc_forward_validation():
+    """Checked before any HIP call: arguments forward() rejects, and a call larger
+    than the fixed scratch array."""
+    L = h.lib()
+
+    def f(x=A, m=4, k=256, qw=B, sw=C, n=256, g=256, la=None, lb=None, r=0, y=D):
+        return L.sdnq_qlinear_forward_noalloc(x, m, k, qw, sw, n, g, la, lb, r, 1.0, y, None)
+    assert f(m=-1) == INVALID and f(x=None) == INVALID and f(k=0) == INVALID
+    assert f(g=32) == UNSUPPORTED and f(n=200) == UNSUPPORTED
+    assert f(la=0x60000, lb=0x70000, r=300) == UNSUPPORTED
+    assert f(m=8192, k=8192 + 256) == WORKSPACE                       # more than 64 MiB of codes
+    assert h.SDNQ_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert f"((size_t)64 << 20)" in open(HEADER).read()
