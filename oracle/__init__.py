@@ -81,9 +81,12 @@ def _load():
     lib.oracle_gemm_fp8.argtypes = [p, p, i64, i64, i64, p]
     lib.oracle_qlinear_forward_fp8.argtypes = [p, i64, i64, p, p, i64, i32, p, p, i32, ctypes.c_double,
                                                p, p, p, p, p]
+    lib.oracle_qlinear_backward_input_fp8.argtypes = [p, i64, i64, p, p, i64, i32, p, p, i32, ctypes.c_double,
+                                                      p, p, p, p, p]
     for name in ("oracle_fwht_unnormalized", "oracle_rotate", "oracle_rotate_quantize", "oracle_rotate_quantize_f32",
                  "oracle_gemm_i8", "oracle_qlinear_forward", "oracle_qlinear_backward_input",
-                 "oracle_rotate_quantize_fp8", "oracle_gemm_fp8", "oracle_qlinear_forward_fp8"):
+                 "oracle_rotate_quantize_fp8", "oracle_gemm_fp8", "oracle_qlinear_forward_fp8",
+                 "oracle_qlinear_backward_input_fp8"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -317,6 +320,38 @@ def qlinear_forward_fp8(x: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
         _ptr(out["y"]), _ptr(out.get("qx")), _ptr(out.get("sx")), _ptr(out.get("acc")),
         _ptr(out.get("base")))
     _check(rc, "qlinear_forward_fp8")
+    return out
+
+
+def qlinear_backward_input_fp8(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, g: int,
+                               x: np.ndarray | None = None, lora_a: np.ndarray | None = None,
+                               lora_b: np.ndarray | None = None, lora_scale: float = 0.0,
+                               want_grads: bool = True, intermediates: bool = True) -> dict:
+    """FP8 input gradient through the E4M3 weight codes qw [n, k] (+ the LoRA
+    input-gradient term and, when x is given and ``want_grads``, the LoRA weight
+    gradients, which do not involve the quantized weight).  With
+    ``intermediates``: qdy (E4M3 codes), sdy, acc (exact fp64) and dxbase."""
+    dy = _c(dy, np.uint16)
+    qw = _c(qw, np.uint8)
+    sw = _c(sw, np.float32)
+    m, n = dy.shape
+    k = qw.shape[1]
+    if qw.shape[0] != n or sw.shape != (n,):
+        raise ValueError("shape mismatch")
+    la = None if lora_a is None else _c(lora_a, np.uint16)
+    lb = None if lora_b is None else _c(lora_b, np.uint16)
+    rank = 0 if la is None else la.shape[1]
+    out = {"dx": np.empty((m, k), np.uint16)}
+    if intermediates:
+        out.update(qdy=np.empty((m, n), np.uint8), sdy=np.empty((m,), np.float32),
+                   acc=np.empty((m, k), np.float64), dxbase=np.empty((m, k), np.float32))
+    rc = _load().oracle_qlinear_backward_input_fp8(
+        _ptr(dy), m, n, _ptr(qw), _ptr(sw), k, g, _ptr(la), _ptr(lb), rank, float(lora_scale),
+        _ptr(out["dx"]), _ptr(out.get("qdy")), _ptr(out.get("sdy")), _ptr(out.get("acc")), _ptr(out.get("dxbase")))
+    _check(rc, "qlinear_backward_input_fp8")
+    if la is not None and want_grads and x is not None:
+        grads = qlinear_backward_input(dy, np.zeros((n, k), np.int8), sw, g, x, la, lb, lora_scale, want_dx=False)
+        out["grad_a"], out["grad_b"] = grads["grad_a"], grads["grad_b"]
     return out
 
 

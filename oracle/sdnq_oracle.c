@@ -761,3 +761,98 @@ int oracle_qlinear_forward_fp8(const uint16_t *x, int64_t m, int64_t k,
     }
     return alloc_fail ? ORACLE_ERR_ARG : ORACLE_OK;
 }
+
+/* FP8 input gradient, the same steps as oracle_qlinear_backward_input with the
+ * E4M3 quantizer (the SDNQ README's quantized training runs the quantized matmul
+ * in the backward pass too, and lists float8_e4m3fn next to int8):
+ *   dY'[m,n]    = fl32(dY * s_w[n])                      (column fold)
+ *   q, s_dy     = per-token E4M3 quantization of dY' (no rotation along n)
+ *   acc[m,k]    = sum_n dec(q[m,n]) * dec(qw[n,k])      (exact, fp64)
+ *   z[m,k]      = fl32(fl32(acc) * s_dy[m])
+ *   dxbase      = the block rotation of z along k, then * fl32(1/sqrt(g))
+ *   dx[m,k]     = bf16_rne(dxbase + ((lora_scale * dY B^T) A^T)[m,k])  (LoRA in fp64)
+ * The LoRA weight gradients do not involve the quantized weight; they are the
+ * ones of oracle_qlinear_backward_input.  Every *_out pointer may be NULL. */
+int oracle_qlinear_backward_input_fp8(const uint16_t *dy, int64_t m, int64_t n, const uint8_t *qw,
+                                      const float *sw, int64_t k, int g, const uint16_t *lora_a,
+                                      const uint16_t *lora_b, int rank, double lora_scale, uint16_t *dx,
+                                      uint8_t *qdy_out, float *sdy_out, double *acc_out, float *dxbase_out)
+{
+    if (!dy || !qw || !sw || !dx || m < 0 || n <= 0 || n > 65536 || k <= 0 || !is_pow2_upto256(g) || k % g != 0)
+        return ORACLE_ERR_ARG;
+    int use_lora = lora_a && lora_b && rank > 0;
+    int alloc_fail = 0;
+#pragma omp parallel
+    {
+        float *yr = (float *)malloc(sizeof(float) * (size_t)n);
+        uint8_t *qr = (uint8_t *)malloc((size_t)n);
+        double *dq = (double *)malloc(sizeof(double) * (size_t)n);
+        float *z = (float *)malloc(sizeof(float) * (size_t)k);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)k);
+        double *gr = (double *)malloc(sizeof(double) * (size_t)(rank > 0 ? rank : 1));
+        if (!yr || !qr || !dq || !z || !acc || !gr) {
+#pragma omp atomic write
+            alloc_fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < m; i++) {
+                float sdy;
+                rotate_row(dy + i * n, n, 1, sw, yr);
+                quantize_row_fp8(yr, n, qr, &sdy);
+                if (qdy_out)
+                    memcpy(qdy_out + i * n, qr, (size_t)n);
+                if (sdy_out)
+                    sdy_out[i] = sdy;
+                for (int64_t j = 0; j < n; j++)
+                    dq[j] = e4m3_decode(qr[j]);
+                for (int64_t kk = 0; kk < k; kk++)
+                    acc[kk] = 0.0;
+                for (int64_t j = 0; j < n; j++) {
+                    const uint8_t *wr = qw + j * k;
+                    for (int64_t kk = 0; kk < k; kk++)
+                        acc[kk] += dq[j] * e4m3_decode(wr[kk]);
+                }
+                for (int64_t kk = 0; kk < k; kk++) {
+                    if (acc_out)
+                        acc_out[i * k + kk] = acc[kk];
+                    z[kk] = (float)acc[kk] * sdy;
+                }
+                if (g > 1) {
+                    float c = norm_const(g);
+                    for (int64_t b = 0; b < k; b += g)
+                        fwht_block(z + b, g);
+                    for (int64_t kk = 0; kk < k; kk++)
+                        z[kk] = z[kk] * c;
+                }
+                if (use_lora) {
+                    /* g_r[r] = lora_scale * sum_j dY[i, j] B[r, j] */
+                    for (int r = 0; r < rank; r++) {
+                        double s = 0.0;
+                        for (int64_t j = 0; j < n; j++)
+                            s += (double)bf16_decode(dy[i * n + j]) * (double)bf16_decode(lora_b[(int64_t)r * n + j]);
+                        gr[r] = s * lora_scale;
+                    }
+                }
+                for (int64_t kk = 0; kk < k; kk++) {
+                    if (dxbase_out)
+                        dxbase_out[i * k + kk] = z[kk];
+                    double out = (double)z[kk];
+                    if (use_lora) {
+                        double l = 0.0;
+                        for (int r = 0; r < rank; r++)
+                            l += gr[r] * (double)bf16_decode(lora_a[kk * rank + r]);
+                        out += l;
+                    }
+                    dx[i * k + kk] = bf16_encode_f64(out);
+                }
+            }
+        }
+        free(yr);
+        free(qr);
+        free(dq);
+        free(z);
+        free(acc);
+        free(gr);
+    }
+    return alloc_fail ? ORACLE_ERR_ARG : ORACLE_OK;
+}

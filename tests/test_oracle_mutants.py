@@ -45,6 +45,16 @@ MUTANTS = {
                                 "float up = 1.0f;\n    float as = a * up;\n    float r = (as > 0.0f) ? 448.0f / as : 0.0f;"),
     "fp8_weight_index": ("acc += dq[kk] * e4m3_decode(wr[kk]);", "acc += dq[kk] * e4m3_decode(wr[(kk + 1) % k]);"),
     "fp8_signed_zero": ("float t = (y[i] * up) * r + 0.0f;", "float t = (y[i] * up) * r;"),
+    "fp8_backward_no_fold": ("rotate_row(dy + i * n, n, 1, sw, yr);\n                quantize_row_fp8",
+                             "rotate_row(dy + i * n, n, 1, NULL, yr);\n                quantize_row_fp8"),
+    "fp8_backward_weight_transposed": ("acc[kk] += dq[j] * e4m3_decode(wr[kk]);",
+                                       "acc[kk] += dq[j] * e4m3_decode(qw[kk * n + j]);"),
+    "fp8_backward_no_inverse_rotation": ("z[kk] = (float)acc[kk] * sdy;\n                }\n                if (g > 1) {",
+                                         "z[kk] = (float)acc[kk] * sdy;\n                }\n                if (0) {"),
+    "fp8_backward_scale_dropped": ("z[kk] = (float)acc[kk] * sdy;", "z[kk] = (float)acc[kk];"),
+    "fp8_backward_lora_b_transposed": (
+        "s += (double)bf16_decode(dy[i * n + j]) * (double)bf16_decode(lora_b[(int64_t)r * n + j]);",
+        "s += (double)bf16_decode(dy[i * n + j]) * (double)bf16_decode(lora_b[(int64_t)j * rank + r]);"),
     "f32_input_no_normalization": ("                    for (int64_t i = 0; i < cols; i++)\n                        y[i] = y[i] * c;",
                                    "                    for (int64_t i = 0; i < cols; i++)\n                        y[i] = y[i];"),
 }

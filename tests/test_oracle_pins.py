@@ -589,6 +589,70 @@ def test_fp8_forward_dequant_and_lora_terms():
     assert np.linalg.norm(base - exact) / np.linalg.norm(exact) < 0.06
 
 
+@pytest.mark.parametrize("g", [1, 64, 256])
+def test_fp8_backward_steps_against_independent_computations(g):
+    """The FP8 input gradient, step by step: the fold and per-token E4M3 codes
+    equal the (separately pinned) FP8 quantizer with the weight scales as the
+    column scale and g = 1; the accumulators equal the exact sum of torch's E4M3
+    values; dxbase equals the fp64 dense normalized block Hadamard product of
+    fl32(fl32(acc) * s_dy) within binary32 rounding; dx is its bf16 rounding."""
+    rng = np.random.default_rng(40 + g)
+    m, n, k = 6, 320, 512
+    dy = bf(rng.standard_normal((m, n)) * 1e-3)
+    w = bf(rng.standard_normal((n, k)) * 0.02)
+    qw, sw = oracle.rotate_quantize_fp8(w, g)
+    out = oracle.qlinear_backward_input_fp8(dy, qw, sw, g)
+    q2, s2 = oracle.rotate_quantize_fp8(dy, 1, col_scale=sw)
+    assert np.array_equal(q2, out["qdy"]) and np.array_equal(s2.view(np.uint32), out["sdy"].view(np.uint32))
+    av, wv = torch_e4m3_value(out["qdy"]), torch_e4m3_value(qw)
+    for i, kk in [(0, 0), (2, 17), (5, k - 1), (3, 300)]:
+        exact = sum(Fraction(float(av[i, j])) * Fraction(float(wv[j, kk])) for j in range(n))
+        assert Fraction(float(out["acc"][i, kk])) == exact
+    assert np.allclose(out["acc"], av @ wv, rtol=0, atol=1e-9 * np.abs(av @ wv).max())
+    z = (out["acc"].astype(np.float32) * out["sdy"][:, None]).astype(np.float32).astype(np.float64)
+    if g > 1:
+        r = np.kron(np.eye(k // g), scipy.linalg.hadamard(g) / np.sqrt(g))
+        ref = z @ r.T
+        assert np.abs(out["dxbase"] - ref).max() <= 1e-5 * np.abs(ref).max()
+    else:
+        assert np.array_equal(out["dxbase"], z.astype(np.float32))
+    assert np.array_equal(out["dx"], oracle.bf16_from_f64(out["dxbase"].astype(np.float64)))
+
+
+def test_fp8_backward_lora_terms_against_torch_autograd():
+    """The LoRA part of the FP8 dX and the LoRA gradients equal torch autograd
+    (fp64) of sum(dY * ((x A) B * scale)) up to the final bf16 rounding."""
+    d = synth.make_linear(20, 256, 128, seed=13, lora_rank=16, backward=True)
+    scale = 0.5
+    qw, sw = oracle.rotate_quantize_fp8(d["w"], 64)
+    out = oracle.qlinear_backward_input_fp8(d["dy"], qw, sw, 64, d["x"], d["lora_a"], d["lora_b"], scale)
+    t = lambda a, grad=False: torch.tensor(synth.bf16_bits_to_f32(a).astype(np.float64), requires_grad=grad)
+    x, A, B, dY = t(d["x"], True), t(d["lora_a"], True), t(d["lora_b"], True), t(d["dy"])
+    ((x @ A @ B * scale) * dY).sum().backward()
+    for name, ref in (("grad_a", A.grad), ("grad_b", B.grad)):
+        assert np.array_equal(out[name], oracle.bf16_from_f64(ref.numpy())), name
+    assert np.array_equal(out["dx"], oracle.bf16_from_f64(out["dxbase"].astype(np.float64) + x.grad.numpy()))
+    # with all-zero weight codes the LoRA term is the whole input gradient
+    zero = oracle.qlinear_backward_input_fp8(d["dy"], np.zeros_like(qw), np.zeros_like(sw), 64, None, d["lora_a"],
+                                            d["lora_b"], scale)
+    assert np.array_equal(zero["dx"], oracle.bf16_from_f64(x.grad.numpy()))
+
+
+def test_fp8_backward_approximates_unquantized_input_gradient():
+    """dX ~ dY W (original bf16 weight) up to the E4M3 quantization error (3 mantissa
+    bits: about 2^-5 relative per code, twice over)."""
+    d = synth.make_linear(32, 768, 512, seed=14, backward=True)
+    qw, sw = oracle.rotate_quantize_fp8(d["w"], 256)
+    out = oracle.qlinear_backward_input_fp8(d["dy"], qw, sw, 256)
+    ref = synth.bf16_bits_to_f32(d["dy"]).astype(np.float64) @ synth.bf16_bits_to_f32(d["w"]).astype(np.float64)
+    dx = synth.bf16_bits_to_f32(out["dx"]).astype(np.float64)
+    err = np.linalg.norm(dx - ref) / np.linalg.norm(ref)
+    assert err < 0.06
+    out8 = oracle.qlinear_backward_input(d["dy"], *oracle.rotate_quantize(d["w"], 256), 256)
+    err8 = np.linalg.norm(synth.bf16_bits_to_f32(out8["dx"]).astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert err8 < err  # int8 keeps more bits than E4M3 on these rows
+
+
 # ----------------------------------------------------------- weight gradient --
 # Full fine-tuning through the quantized matmul ("SDNQ: SD.Next Quantization
 # Engine": quantized matmul in the backward pass, full-parameter quantized
