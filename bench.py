@@ -226,6 +226,12 @@ def measure_rows(torch, h, synth, reps: int = 100, warmup: int = 10) -> dict:
     row("peft_backward_16384x3072x3072_g256_r64",
         lambda: h.sdnq_qlinear_backward_input(dy, qw, sw, 256, x, la, lb, c.lora_scale, workspace=ws), ops,
         {"note": "dX through the int8 weight + LoRA dX, dA, dB"})
+    qw8, sw8 = h.sdnq_rotate_quantize_weight_fp8(w, 256)
+    row("fp8_peft_backward_16384x3072x3072_g256_r64",
+        lambda: h.sdnq_qlinear_backward_input_fp8(dy, qw8, sw8, 256, x, la, lb, c.lora_scale, workspace=ws), ops,
+        {"note": "dX through the E4M3 weight + LoRA dX, dA, dB; fp8 dense peak 5.0 PFLOP/s"},
+        peak=5000.0, unit="TFLOP/s")
+    del qw8, sw8
     wws = torch.empty(h.sdnq_weight_grad_workspace_bytes(c.m, c.n, c.k), dtype=torch.uint8, device=dev)
     dw = torch.empty((c.n, c.k), dtype=torch.bfloat16, device=dev)
     row("weight_grad_16384x3072x3072_g256", lambda: h.sdnq_qlinear_weight_grad(dy, x, 256, out=dw, workspace=wws),

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     sdnq_gemm_fp8_f32,
     sdnq_gemm_i8_i32,
     sdnq_qlinear_backward_input,
+    sdnq_qlinear_backward_input_fp8,
     sdnq_qlinear_forward,
     sdnq_qlinear_forward_noalloc,
     SDNQ_NOALLOC_SCRATCH_BYTES,

@@ -45,6 +45,7 @@ def lib() -> ctypes.CDLL:
         "sdnq_qlinear_forward_noalloc": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p],
         "sdnq_qlinear_forward_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
         "sdnq_qlinear_backward_input": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
+        "sdnq_qlinear_backward_input_fp8": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
         "sdnq_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p, sz, p],
         "sdnq_rotate_quantize_weight_fp8": [p, i64, i64, i32, p, p, p],
         "sdnq_rotate_quantize_act_fp8": [p, i64, i64, i32, p, p, p, p],
@@ -253,8 +254,20 @@ def _forward_quantized(name, code_dtype, qx, x_scale, qw, w_scale, t, lora_b, lo
 def sdnq_qlinear_backward_input(dy, qw, w_scale, g, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
                                 want_lora_grads=True, workspace=None):
     """Returns (dx [m, k] bf16, grad_a [k, r] or None, grad_b [r, n] or None)."""
+    return _backward("sdnq_qlinear_backward_input", torch.int8, dy, qw, w_scale, g, x, lora_a, lora_b, lora_scale,
+                     want_lora_grads, workspace)
+
+
+def sdnq_qlinear_backward_input_fp8(dy, qw, w_scale, g, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
+                                    want_lora_grads=True, workspace=None):
+    """The FP8 input gradient: qw are E4M3 codes (uint8) from sdnq_rotate_quantize_weight_fp8."""
+    return _backward("sdnq_qlinear_backward_input_fp8", torch.uint8, dy, qw, w_scale, g, x, lora_a, lora_b,
+                     lora_scale, want_lora_grads, workspace)
+
+
+def _backward(name, code_dtype, dy, qw, w_scale, g, x, lora_a, lora_b, lora_scale, want_lora_grads, workspace):
     _need(dy, torch.bfloat16, 2, "dy")
-    _need(qw, torch.int8, 2, "qw")
+    _need(qw, code_dtype, 2, "qw")
     _need(w_scale, torch.float32, 1, "w_scale")
     m, n = dy.shape
     k = qw.shape[1]
@@ -271,10 +284,9 @@ def sdnq_qlinear_backward_input(dy, qw, w_scale, g, x=None, lora_a=None, lora_b=
     dx = torch.empty((m, k), dtype=torch.bfloat16, device=dy.device)
     nb = sdnq_workspace_bytes(m, n, k, rank, True)
     ws = _workspace(nb, dy.device, workspace)
-    _check(lib().sdnq_qlinear_backward_input(_ptr(dy), m, n, _ptr(qw), _ptr(w_scale), k, g, _ptr(x), _ptr(lora_a),
-                                             _ptr(lora_b), rank, float(lora_scale), _ptr(dx), _ptr(ga), _ptr(gb),
-                                             _ptr(ws), ws.numel(), _stream(dy.device)),
-           "sdnq_qlinear_backward_input")
+    _check(getattr(lib(), name)(_ptr(dy), m, n, _ptr(qw), _ptr(w_scale), k, g, _ptr(x), _ptr(lora_a), _ptr(lora_b),
+                                rank, float(lora_scale), _ptr(dx), _ptr(ga), _ptr(gb), _ptr(ws), ws.numel(),
+                                _stream(dy.device)), name)
     return dx, ga, gb
 
 

@@ -356,11 +356,15 @@ sdnq_status_t sdnq_qlinear_forward_noalloc(const uint16_t *x, int64_t m, int64_t
   return forward(false, x, m, k, qw, w_scale, n, g, lora_a, lora_b, rank, lora_scale, y, ws, kScratchBytes, stream);
 }
 
-sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw,
-                                          const float *w_scale, int64_t k, int32_t g, const uint16_t *x,
-                                          const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
-                                          float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
-                                          void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The input gradient through the int8 (fp8 = false) or E4M3 (fp8 = true) weight codes.
+sdnq_status_t backward(bool fp8, const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw, const float *w_scale,
+                       int64_t k, int32_t g, const uint16_t *x, const uint16_t *lora_a, const uint16_t *lora_b,
+                       int32_t rank, float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                       void *workspace, size_t workspace_bytes, void *stream) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!dy || !dx)) return SDNQ_ERR_INVALID_ARG;
   SDNQ_TRY(check_feature(k));
@@ -389,11 +393,14 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
   float *sdy = reinterpret_cast<float *>(ws_at(workspace, L.sdy));
   int8_t *wt = reinterpret_cast<int8_t *>(ws_at(workspace, L.wt));
   // dY' = dY * w_scale (column fold), per-token quantization, no rotation along n.
-  SDNQ_LAUNCH(launch_rotate_quantize(dy, m, n, 1, w_scale, qdy, sdy, s));
-  SDNQ_LAUNCH(launch_transpose_i8(qw, n, k, wt, s));  // qw [n, k] -> [k, n]
+  if (fp8)
+    SDNQ_LAUNCH(launch_rotate_quantize_fp8(dy, m, n, 1, w_scale, reinterpret_cast<uint8_t *>(qdy), sdy, s));
+  else
+    SDNQ_LAUNCH(launch_rotate_quantize(dy, m, n, 1, w_scale, qdy, sdy, s));
+  SDNQ_LAUNCH(launch_transpose_i8(qw, n, k, wt, s));  // qw [n, k] -> [k, n] (bytes, either code)
 
   GemmArgs ga{};
-  ga.a = qdy; ga.b = wt; ga.m = m; ga.n = k; ga.k = n;
+  ga.a = qdy; ga.b = wt; ga.m = m; ga.n = k; ga.k = n; ga.fp8 = fp8;
   ga.row_scale = sdy; ga.out_bf16 = dx; ga.g = g;
   uint16_t *gr = nullptr, *tx = nullptr, *at = nullptr;
   const int32_t rp = r > 0 ? padded_rank(r) : 0;
@@ -432,6 +439,28 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
     }
   }
   return SDNQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw,
+                                          const float *w_scale, int64_t k, int32_t g, const uint16_t *x,
+                                          const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                          float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+  return backward(false, dy, m, n, qw, w_scale, k, g, x, lora_a, lora_b, rank, lora_scale, dx, grad_a, grad_b,
+                  workspace, workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_qlinear_backward_input_fp8(const uint16_t *dy, int64_t m, int64_t n, const uint8_t *qw,
+                                              const float *w_scale, int64_t k, int32_t g, const uint16_t *x,
+                                              const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                              float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                              void *workspace, size_t workspace_bytes, void *stream) {
+  return backward(true, dy, m, n, reinterpret_cast<const int8_t *>(qw), w_scale, k, g, x, lora_a, lora_b, rank,
+                  lora_scale, dx, grad_a, grad_b, workspace, workspace_bytes, stream);
 }
 
 sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int64_t n, int64_t k, int32_t b_layout,

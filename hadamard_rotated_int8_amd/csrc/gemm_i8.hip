@@ -14,7 +14,8 @@
 //
 // FP8 (E4M3 x E4M3, the float8_e4m3fn quantized matmul of the same pages): the
 // same tiles and loads, one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 tile and
-// 64-byte k-tile with fp32 accumulation, and the forward epilogue's scales.
+// 64 k positions with fp32 accumulation, and the same epilogues (forward scales,
+// or the backward's inverse rotation).
 // Its A and B fragments pair up 64 k positions of a tile the same way (the
 // two 16-byte halves the int8 path reads for its two 32-deep steps), so the
 // contraction is the full 64-k dot product.
@@ -155,7 +156,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int tiles_m, int tiles_n) {
-  static_assert(!FP8 || EPI != Epilogue::kBackward, "FP8 runs the forward only");
   using Cfg = TileCfg<BN>;
   constexpr int kStageBytes = Cfg::kStageBytes;
   constexpr int LPW = Cfg::kLoadsPerWave;
@@ -291,8 +291,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   Frags f0, f1;
   read_frags(0, 0, f0);
 
-  if constexpr (FP8 && BN == 320) {
-    // Ten accumulator tiles leave room for two fragment sets: each FP8 MFMA
+  if constexpr (FP8 && (BN == 320 || SM + SN > 6)) {
+    // Ten accumulator tiles (or nine fragments per set) leave room for two
+    // fragment sets: each FP8 MFMA
     // step (two k-steps, both 16-byte halves of 64 k positions) waits for its
     // own reads, and the other wavefront of the SIMD fills the gap.
     // Iteration kt: MFMA (kt,0..1) | read (kt,2..3), wait, barrier, load tile
@@ -654,11 +655,22 @@ hipError_t launch_typed(const GemmArgs &args, hipStream_t stream) {
 // Backward tiles: 4 x 2 wavefronts where the rotation block fits in a
 // wavefront's 128 columns, else 8 x 1 (all 256 columns per wavefront).  The
 // 4 x 2 layout at g = 256 with the h = 128 stage through LDS measured slower.
-template <int G>
+template <int G, bool FP8>
 hipError_t launch_backward(const GemmArgs &args, hipStream_t stream) {
   constexpr int kWavesM = G <= 128 ? 4 : 8;
-  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 256, kWavesM, G, true>(args, stream)
-                       : launch_typed<Epilogue::kBackward, 256, kWavesM, G, false>(args, stream);
+  return args.rank > 0 ? launch_typed<Epilogue::kBackward, 256, kWavesM, G, true, FP8>(args, stream)
+                       : launch_typed<Epilogue::kBackward, 256, kWavesM, G, false, FP8>(args, stream);
+}
+
+template <bool FP8>
+hipError_t launch_backward_any(const GemmArgs &args, hipStream_t stream) {
+  switch (args.g) {
+    case 1: return launch_backward<1, FP8>(args, stream);
+    case 64: return launch_backward<64, FP8>(args, stream);
+    case 128: return launch_backward<128, FP8>(args, stream);
+    case 256: return launch_backward<256, FP8>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Output tile width along N for the forward and int32 epilogues.  One workgroup
@@ -703,14 +715,7 @@ hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream
       return args.rank > 0 ? launch_forward_like<Epilogue::kForward, true>(args, stream)
                            : launch_forward_like<Epilogue::kForward, false>(args, stream);
     case Epilogue::kBackward:
-      if (args.fp8) return hipErrorInvalidValue;
-      switch (args.g) {
-        case 1: return launch_backward<1>(args, stream);
-        case 64: return launch_backward<64>(args, stream);
-        case 128: return launch_backward<128>(args, stream);
-        case 256: return launch_backward<256>(args, stream);
-        default: return hipErrorInvalidValue;
-      }
+      return args.fp8 ? launch_backward_any<true>(args, stream) : launch_backward_any<false>(args, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -61,8 +61,8 @@ struct GemmArgs {
   int rank;
   int g;                  // backward: inverse rotation block along n (1, 64, 128, 256)
   uint16_t *out_bf16;     // [m, n]
-  bool fp8;               // a and b hold E4M3 codes (forward and the accumulator export only);
-                          // the kInt32 epilogue then stores the fp32 accumulators' bits
+  bool fp8;               // a and b hold E4M3 codes (fp32 accumulators); the kInt32 epilogue
+                          // then stores the accumulators' bits
 };
 
 hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream);

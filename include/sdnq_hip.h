@@ -231,6 +231,21 @@ sdnq_status_t sdnq_qlinear_forward_fp8_quantized(const uint8_t *qx, const float 
                                                  void *workspace, size_t workspace_bytes,
                                                  void *stream);
 
+/* Input gradient through E4M3 weight codes (the SDNQ README's quantized training
+ * runs the quantized matmul in the backward pass too):
+ *   dY'      = dy[m,n] * w_scale[n]             (column-wise fold of the row scales)
+ *   q, s     = per-token E4M3 quantization of dY' (no rotation along n)
+ *   dx[m,k]  = bf16( R_g( fp32(dec(q) . dec(qw)) * s[m] ) + lora_scale * (dy lora_b^T) lora_a^T )
+ * and grad_a / grad_b as for sdnq_qlinear_backward_input, whose arguments,
+ * limits, errors and workspace size (sdnq_workspace_bytes(m, n, k, rank, 1))
+ * this takes, with qw[n,k] the E4M3 codes of sdnq_rotate_quantize_weight_fp8. */
+sdnq_status_t sdnq_qlinear_backward_input_fp8(const uint16_t *dy, int64_t m, int64_t n,
+                                              const uint8_t *qw, const float *w_scale, int64_t k,
+                                              int32_t g, const uint16_t *x, const uint16_t *lora_a,
+                                              const uint16_t *lora_b, int32_t rank, float lora_scale,
+                                              uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* Diagnostics: the FP8 GEMM with an fp32 store instead of the epilogue:
  * c[m,n] = sum_k dec(a[m,k]) * dec(b[n,k]), fp32 accumulation. */
 sdnq_status_t sdnq_gemm_fp8_f32(const uint8_t *a, const uint8_t *b, int64_t m, int64_t n, int64_t k,

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "sdnq_weight_grad_workspace_offset",
               "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset",
               "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset",
-              "sdnq_qlinear_forward_noalloc"):
+              "sdnq_qlinear_forward_noalloc", "sdnq_qlinear_backward_input_fp8"):
         assert n in names
 
 

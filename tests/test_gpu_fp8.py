@@ -209,3 +209,78 @@ def test_fp8_mlp_pair_full_size():
         err = rel_l2(h_bits(y)[rows], ref["y"])
         say(f"    rel-L2 {err:.3e}")
         assert err < REL_L2
+
+
+# ------------------------------------------------------------ FP8 backward --
+# The input gradient through the E4M3 weight codes.  The dY fold and its E4M3
+# codes are bit-exact (the entry point's workspace); dX is within 1e-2 relative
+# L2 of the oracle over the tensor and for every token row (the GPU sums the
+# decoded products with the fp32-accumulating MFMA, the oracle exactly); the LoRA
+# term is checked alone with all-zero weight codes; the LoRA gradients as in the
+# int8 path.
+
+def max_token_rel(got_bits, ref_bits):
+    g = synth.bf16_bits_to_f32(got_bits).astype(np.float64)
+    r = synth.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    return float((np.linalg.norm(g - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)).max())
+
+
+def backward8_case(m, n, k, g, rank=0, seed=0, scale=0.5, zero_weight=False, rows=None):
+    inp = synth.make_linear(m, k, n, seed=seed, lora_rank=rank, backward=True)
+    if zero_weight:
+        inp["w"] = np.zeros_like(inp["w"])
+    say(f"  qlinear_backward_input_fp8 m={m} n={n} k={k} g={g} rank={rank} zero_weight={zero_weight}")
+    qw, sw = h.sdnq_rotate_quantize_weight_fp8(d_bf16(inp["w"]), g)
+    la = d_bf16(inp["lora_a"]) if rank else None
+    lb = d_bf16(inp["lora_b"]) if rank else None
+    ws = torch.empty(h.sdnq_workspace_bytes(m, n, k, rank, True), dtype=torch.uint8, device=DEV)
+    dx, ga, gb = h.sdnq_qlinear_backward_input_fp8(d_bf16(inp["dy"]), qw, sw, g, d_bf16(inp["x"]) if rank else None,
+                                                   la, lb, scale, workspace=ws)
+    torch.cuda.synchronize()
+    qwo, swo = oracle.rotate_quantize_fp8(inp["w"], g)
+    assert np.array_equal(qw.cpu().numpy(), qwo)
+    qdy = ws[: m * n].view(m, n).cpu().numpy()
+    off = (m * n + 255) // 256 * 256
+    sdy = ws[off: off + 4 * m].cpu().numpy().view(np.float32)
+    qo, so = oracle.rotate_quantize_fp8(inp["dy"], 1, swo)
+    assert np.array_equal(qdy, qo), "dY' E4M3 codes"
+    assert np.array_equal(sdy.view(np.uint32), so.view(np.uint32)), "dY' scales"
+    rows = np.arange(m) if rows is None else rows
+    ref = oracle.qlinear_backward_input_fp8(inp["dy"][rows], qwo, swo, g, None, inp.get("lora_a"),
+                                            inp.get("lora_b"), scale, intermediates=False)
+    got = h_bits(dx)[rows]
+    err, tok = rel_l2(got, ref["dx"]), max_token_rel(got, ref["dx"])
+    say(f"    dx rel-L2 {err:.3e}  max-token {tok:.3e}")
+    assert err < REL_L2 and tok < REL_L2
+    if rank and not zero_weight:
+        grads = oracle.qlinear_backward_input(inp["dy"], np.zeros((n, k), np.int8), swo, g, inp["x"], inp["lora_a"],
+                                              inp["lora_b"], scale, want_dx=False)
+        for name, got_g in (("grad_a", ga), ("grad_b", gb)):
+            e = rel_l2(h_bits(got_g), grads[name])
+            say(f"    {name} rel-L2 {e:.3e}")
+            assert e < REL_L2
+
+
+@pytest.mark.parametrize("g", [1, 64, 128, 256])
+def test_fp8_backward(g):
+    backward8_case(300, 640, 768 if g != 256 else 512, g, seed=g)
+
+
+@pytest.mark.parametrize("g,rank", [(256, 64), (64, 32), (128, 24)])
+def test_fp8_backward_with_lora(g, rank):
+    backward8_case(260, 384, 512, g, rank=rank, seed=rank + g)
+    backward8_case(260, 384, 512, g, rank=rank, seed=rank + g + 1, zero_weight=True)
+
+
+def test_fp8_backward_ragged_tiles():
+    """Token rows and dX columns past the last full tile (384 = 1.5 column tiles)."""
+    backward8_case(33, 272, 384, 128, rank=16, seed=5)
+
+
+def test_fp8_backward_peft_size_sampled_rows():
+    """16384 tokens x 3072 x 3072, g = 256, rank 64: every dY' code and scale, and
+    sampled rows of dX."""
+    c = synth.CONFIGS["peft"]
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(c.m - 8, c.m), rng.choice(c.m, 32, replace=False)]))
+    backward8_case(c.m, c.n, c.k, 256, rank=c.lora_rank, seed=0, scale=c.lora_scale, rows=rows)
