@@ -14,35 +14,43 @@ namespace sdnq {
 namespace {
 
 // ----------------------------------------------------------- lora_down --
-// A workgroup of 4 wavefronts handles 16*TT tokens; each wavefront takes a
-// quarter of the contraction and keeps 16*TT x rank fp32 partial sums, which are
-// added in wavefront order through LDS.  MFMA 16x16x32: row operand = R rows
-// (rank index), column operand = x rows (token), so lane l owns token l % 16 and
-// the four consecutive rank indices 4 * (l / 16) + 0..3 of each 16 x 16 tile.
-// The contraction is walked in batches of 4 steps of 32 whose loads are all
-// issued before the batch's MFMAs, so several steps of loads stay in flight.
+// A workgroup handles 16*TT tokens with 4*HV wavefronts: HV groups of 4 take
+// 16*TT/HV tokens each, and the 4 wavefronts of a group split the contraction,
+// each keeping (16*TT/HV) x rank fp32 partial sums, which are added in
+// wavefront order through LDS.  (Two groups double the wavefronts in flight per
+// CU at the same tokens per workgroup, so the rank x cols factor is still read
+// once per 16*TT tokens; the second group's factor reads hit L1.)
+// MFMA 16x16x32: row operand = R rows (rank index), column operand = x rows
+// (token), so lane l owns token l % 16 and the four consecutive rank indices
+// 4 * (l / 16) + 0..3 of each 16 x 16 tile.  The contraction is walked in batches
+// of 4 steps of 32 whose loads are all issued before the batch's MFMAs, so
+// several steps of loads stay in flight.
 constexpr int kMaxRank = 128;
 constexpr int kDownBatch = 4;
 
-template <int RT, int TT>  // RT = rank / 16, TT = tokens / 16
-__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restrict__ x, int64_t m, int64_t cols,
-                                                        const uint16_t *__restrict__ rmat, float scale,
-                                                        uint16_t *__restrict__ out, int64_t out_stride) {
-  __shared__ v4f red[4][TT][RT][64];
+template <int RT, int TT, int HV>  // RT = rank / 16, TT = tokens / 16, HV token groups
+__global__ __launch_bounds__(256 * HV) void lora_down_kernel(const uint16_t *__restrict__ x, int64_t m,
+                                                             int64_t cols, const uint16_t *__restrict__ rmat,
+                                                             float scale, uint16_t *__restrict__ out,
+                                                             int64_t out_stride) {
+  constexpr int TG = TT / HV;  // 16-token subtiles per group
+  static_assert(TT % HV == 0, "whole subtiles per group");
+  __shared__ v4f red[HV][4][TG][RT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * (16 * TT);
+  const int grp = wave >> 2, wq = wave & 3;  // token group, contraction quarter
+  const int64_t t0 = (int64_t)blockIdx.x * (16 * TT) + grp * (16 * TG);
 
   // contraction range of this wavefront, in steps of 32
   const int64_t steps = (cols + 31) / 32;
   const int64_t per = (steps + 3) / 4;
-  const int64_t c_begin = wave * per * 32;
-  int64_t c_end = (wave + 1) * per * 32;
+  const int64_t c_begin = wq * per * 32;
+  int64_t c_end = (wq + 1) * per * 32;
   c_end = c_end < cols ? c_end : cols;
 
   const int koff = 8 * (lane >> 4);
-  const uint16_t *xr[TT];
+  const uint16_t *xr[TG];
 #pragma unroll
-  for (int s = 0; s < TT; ++s) {
+  for (int s = 0; s < TG; ++s) {
     int64_t t = t0 + s * 16 + (lane & 15);
     t = t < m ? t : m - 1;
     xr[s] = x + t * cols + koff;
@@ -51,45 +59,46 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restri
 #pragma unroll
   for (int u = 0; u < RT; ++u) rr[u] = rmat + (int64_t)(u * 16 + (lane & 15)) * cols + koff;
 
-  v4f acc[TT][RT];
+  v4f acc[TG][RT];
 #pragma unroll
-  for (int s = 0; s < TT; ++s)
+  for (int s = 0; s < TG; ++s)
 #pragma unroll
     for (int u = 0; u < RT; ++u) acc[s][u] = v4f{};
 
   for (int64_t cb = c_begin; cb < c_end; cb += 32 * kDownBatch) {
-    v8bf bx[kDownBatch][TT], br[kDownBatch][RT];
+    v8bf bx[kDownBatch][TG], br[kDownBatch][RT];
 #pragma unroll
     for (int b = 0; b < kDownBatch; ++b) {
       const int64_t c0 = cb + 32 * b;
       const bool ok = c0 < c_end && c0 + koff < cols;
 #pragma unroll
-      for (int s = 0; s < TT; ++s) bx[b][s] = ok ? *reinterpret_cast<const v8bf *>(xr[s] + c0) : v8bf{};
+      for (int s = 0; s < TG; ++s) bx[b][s] = ok ? *reinterpret_cast<const v8bf *>(xr[s] + c0) : v8bf{};
 #pragma unroll
       for (int u = 0; u < RT; ++u) br[b][u] = ok ? *reinterpret_cast<const v8bf *>(rr[u] + c0) : v8bf{};
     }
 #pragma unroll
     for (int b = 0; b < kDownBatch; ++b)
 #pragma unroll
-      for (int s = 0; s < TT; ++s)
+      for (int s = 0; s < TG; ++s)
 #pragma unroll
         for (int u = 0; u < RT; ++u)
           acc[s][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br[b][u], bx[b][s], acc[s][u], 0, 0, 0);
   }
 
 #pragma unroll
-  for (int s = 0; s < TT; ++s)
+  for (int s = 0; s < TG; ++s)
 #pragma unroll
-    for (int u = 0; u < RT; ++u) red[wave][s][u][lane] = acc[s][u];
+    for (int u = 0; u < RT; ++u) red[grp][wq][s][u][lane] = acc[s][u];
   __syncthreads();
-  // wavefront w writes token subtiles s = w, w + 4, ... (sums in wavefront order)
-  for (int s = wave; s < TT; s += 4) {
+  // wavefront wq of each group writes the group's token subtiles s = wq, wq + 4,
+  // ... (sums in wavefront order)
+  for (int s = wq; s < TG; s += 4) {
     const int64_t t = t0 + s * 16 + (lane & 15);
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
-      v4f sum = red[0][s][u][lane];
+      v4f sum = red[grp][0][s][u][lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) sum = sum + red[w][s][u][lane];
+      for (int w = 1; w < 4; ++w) sum = sum + red[grp][w][s][u][lane];
       if (t < m) {
         const int r0 = u * 16 + 4 * (lane >> 4);
         uint2 packed;
@@ -410,15 +419,15 @@ hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t
   return hipGetLastError();
 }
 
-template <int TT>
+template <int TT, int HV>
 hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
                               float scale, uint16_t *out, int64_t out_stride, hipStream_t stream) {
   const dim3 grid((unsigned)((m + 16 * TT - 1) / (16 * TT)));
   switch (rank / 16) {
-#define SDNQ_DOWN(RT)                                                                                           \
-  case RT:                                                                                                      \
-    hipLaunchKernelGGL((lora_down_kernel<RT, TT>), grid, dim3(256), 0, stream, x, m, cols, rmat, scale, out,   \
-                       out_stride);                                                                             \
+#define SDNQ_DOWN(RT)                                                                                             \
+  case RT:                                                                                                        \
+    hipLaunchKernelGGL((lora_down_kernel<RT, TT, HV>), grid, dim3(256 * HV), 0, stream, x, m, cols, rmat, scale, \
+                       out, out_stride);                                                                          \
     break;
     SDNQ_DOWN(1) SDNQ_DOWN(2) SDNQ_DOWN(3) SDNQ_DOWN(4) SDNQ_DOWN(5) SDNQ_DOWN(6) SDNQ_DOWN(7) SDNQ_DOWN(8)
 #undef SDNQ_DOWN
@@ -427,18 +436,19 @@ hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const 
   return hipGetLastError();
 }
 
-// 64 tokens per workgroup when there are enough tokens to fill the chip that way
-// (the rank x cols factor is then re-read from L2 half as often), else 32.  Ranks
-// above kMaxRank run as launches over consecutive slices of at most kMaxRank rows
-// of rmat, each writing its columns of out.
+// 64 tokens per workgroup in two groups of 8 wavefronts when there are enough
+// tokens to fill the chip that way (the rank x cols factor is then re-read from
+// L2 half as often), else 32 tokens and 4 wavefronts.  Ranks above kMaxRank run as
+// launches over consecutive slices of at most kMaxRank rows of rmat, each writing
+// its columns of out.
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
                             float scale, uint16_t *out, hipStream_t stream) {
   if (rank <= 0 || rank % 16) return hipErrorInvalidValue;
   for (int r0 = 0; r0 < rank; r0 += kMaxRank) {
     const int rr = rank - r0 < kMaxRank ? rank - r0 : kMaxRank;
     const hipError_t e = m >= 16384
-        ? launch_lora_down_t<4>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream)
-        : launch_lora_down_t<2>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream);
+        ? launch_lora_down_t<4, 2>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream)
+        : launch_lora_down_t<2, 1>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -96,6 +96,10 @@ __device__ __forceinline__ void dpp_stage_xor2(float (&r)[8], float m) {
                : "v"(m));
 }
 
+// Column scales up to this many columns are staged once per workgroup in LDS
+// (dynamic shared memory), instead of re-read from L2 for every row.
+constexpr int64_t kColScaleLds = 16384;
+
 template <int G, bool COLSCALE, int MAXT, bool FP8>
 __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
@@ -117,6 +121,12 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
   if (tid < rows_per_wg) {
     row_max[0][tid] = 0u;
     row_max[1][tid] = 0u;
+  }
+  extern __shared__ __attribute__((aligned(16))) float cs_lds[];  // [cols] when staged
+  const bool cs_staged = COLSCALE && cols <= kColScaleLds;
+  if (cs_staged) {
+    for (int64_t c = 4 * tid; c < cols; c += 4 * blockDim.x)
+      *reinterpret_cast<float4 *>(cs_lds + c) = *reinterpret_cast<const float4 *>(col_scale + c);
   }
   __syncthreads();
 
@@ -167,8 +177,9 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
       for (int i = 0; i < 8; ++i) {
         const int64_t e0 = base + 32 * i;
         if (e0 < cols) {
-          const float4 c0 = *reinterpret_cast<const float4 *>(col_scale + e0);
-          const float4 c1 = *reinterpret_cast<const float4 *>(col_scale + e0 + 4);
+          const float *cs = cs_staged ? cs_lds : col_scale;
+          const float4 c0 = *reinterpret_cast<const float4 *>(cs + e0);
+          const float4 c1 = *reinterpret_cast<const float4 *>(cs + e0 + 4);
           v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
           v[i][2] = v[i][2] * c0.z; v[i][3] = v[i][3] * c0.w;
           v[i][4] = v[i][4] * c1.x; v[i][5] = v[i][5] * c1.y;
@@ -345,18 +356,20 @@ int pick_rows_per_wg(int t_row, int max_threads) {
 
 // Resident workgroups per CU for a kernel at a block size, cached per block size
 // (one atomic word holding both, so concurrent callers read a consistent pair).
+// (One atomic word holds block size, dynamic LDS in 16-byte units and the count.)
 template <int G, bool CS, int MAXT, bool FP8>
-int blocks_per_cu(int threads) {
+int blocks_per_cu(int threads, size_t smem) {
   static std::atomic<uint64_t> cache[kMaxThreads / 4 + 1];
   std::atomic<uint64_t> &slot = cache[threads / 4];
+  const uint64_t key = ((uint64_t)(uint32_t)threads << 12) | (uint64_t)(smem / 16);
   const uint64_t c = slot.load(std::memory_order_relaxed);
-  if ((int)(c >> 32) == threads) return (int)(c & 0xffffffffu);
+  if ((c >> 32) == key) return (int)(c & 0xffffffffu);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8>, threads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8>, threads, smem) !=
           hipSuccess ||
       n < 1)
     n = 1;
-  slot.store(((uint64_t)(uint32_t)threads << 32) | (uint32_t)n, std::memory_order_relaxed);
+  slot.store((key << 32) | (uint32_t)n, std::memory_order_relaxed);
   return n;
 }
 
@@ -365,9 +378,10 @@ hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const flo
                         float *scale, int t_row, int rpw, hipStream_t stream) {
   const int threads = rpw * t_row;
   const int64_t groups = (rows + rpw - 1) / rpw;
-  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8>(threads);
+  const size_t smem = (CS && cols <= kColScaleLds) ? (size_t)cols * 4 : 0;
+  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8>(threads, smem);
   if (blocks > groups) blocks = groups;
-  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8>), dim3((unsigned)blocks), dim3(threads), 0, stream, x, rows,
+  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8>), dim3((unsigned)blocks), dim3(threads), smem, stream, x, rows,
                      cols, col_scale, q, scale, t_row, rpw, groups);
   return hipGetLastError();
 }
