@@ -81,36 +81,31 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
 }
 
 // LoRA term of all of a wavefront's 32 x 32 output tiles at once:
-// o[i][j] += sum_r R[nrow[j], r] * T[mrow[i], r], one 16-wide rank step at a
-// time (bf16 MFMA 32x32x16, fp32 accumulate), with the next step's fragments
-// loaded while this step's MFMAs run, so the loads of all tiles overlap instead
-// of paying one memory round trip per tile.  Lane l holds row l % 32 of its
-// tile and rank entries 8 * (l / 32) .. + 7 of each step.
-template <int SM, int SN>
-__device__ __forceinline__ void lora_all(const uint16_t *__restrict__ T, const uint16_t *__restrict__ R,
-                                         const int64_t (&mrow)[SM], const int64_t (&nrow)[SN], int rank, int lane,
-                                         v16f (&o)[SM][SN]) {
-  const int koff = 8 * (lane >> 5);
-  v8bf ta[SM], rb[SN];
+// o[i][j] += sum_r R[n(j), r] * T[m(i), r] (bf16 MFMA 32x32x16, fp32 accumulate;
+// lane l holds row l % 32 of its tile and rank entries 8 * (l / 32) .. + 7 of
+// each 16-wide step), from operands staged in LDS like a k-tile: the T rows
+// (tokens) where the A tile goes and the R rows (output columns) where the B
+// tile goes, up to 64 rank values (128 bytes) per row in the ring's row
+// layout.  Rank step s (16 values, 32 bytes) sits where the int8 k-step s
+// does: lane l reads 16 bytes of its row at logical chunk 2 s + l / 32, stored
+// at chunk ^ (l & 7).  arow[i] / brow[j]: the tile rows of the wavefront's
+// 32-row blocks.
+template <int SMX, int SN>
+__device__ __forceinline__ void lora_staged(const int8_t *stage, int a_bytes, int row_bytes, const int (&arow)[SMX],
+                                            const int (&brow)[SN], int rank, int lane, v16f (&o)[SMX][SN]) {
+  const int8_t *base = stage + (lane & 31) * row_bytes;
+  for (int st = 0; st < rank / 16; ++st) {
+    const int col = 16 * ((2 * st + (lane >> 5)) ^ (lane & 7));
+    v8bf ta[SMX], rb[SN];
 #pragma unroll
-  for (int i = 0; i < SM; ++i) ta[i] = *reinterpret_cast<const v8bf *>(T + mrow[i] * rank + koff);
+    for (int i = 0; i < SMX; ++i) ta[i] = *reinterpret_cast<const v8bf *>(base + arow[i] * row_bytes + col);
 #pragma unroll
-  for (int j = 0; j < SN; ++j) rb[j] = *reinterpret_cast<const v8bf *>(R + nrow[j] * rank + koff);
-  for (int k0 = 0; k0 < rank; k0 += 16) {
-    const int kn = k0 + 16 < rank ? k0 + 16 : k0;  // the last step reloads its own fragments
-    v8bf tn[SM], rn[SN];
+    for (int j = 0; j < SN; ++j)
+      rb[j] = *reinterpret_cast<const v8bf *>(base + a_bytes + brow[j] * row_bytes + col);
 #pragma unroll
-    for (int i = 0; i < SM; ++i) tn[i] = *reinterpret_cast<const v8bf *>(T + mrow[i] * rank + kn + koff);
-#pragma unroll
-    for (int j = 0; j < SN; ++j) rn[j] = *reinterpret_cast<const v8bf *>(R + nrow[j] * rank + kn + koff);
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
+    for (int i = 0; i < SMX; ++i)
 #pragma unroll
       for (int j = 0; j < SN; ++j) o[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[j], ta[i], o[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < SM; ++i) ta[i] = tn[i];
-#pragma unroll
-    for (int j = 0; j < SN; ++j) rb[j] = rn[j];
   }
 }
 
@@ -220,6 +215,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     }
   };
 
+  // ---- LoRA operands of the epilogue (forward and backward with LoRA): the T
+  // rows (tokens) and R rows (output columns) of the tile, in chunks of 64 rank
+  // values (128 bytes, one stage row), with the same slot layout and swizzle as
+  // a k-tile (T rows where the A rows go, R rows where the B rows go).  Chunk 0
+  // takes the place of the zero-filled tile nk: it is loaded into the ring's
+  // free stage while the last k-tile is multiplied.  Later chunks (rank > 64)
+  // are loaded into the same stage once the previous one has been used.
+  constexpr bool kLoraStaged = LORA && EPI != Epilogue::kInt32;
+  constexpr int kLoraChunk = BK / 2;
+  int8_t *const lora_stage = smem + (nk & (STAGES - 1)) * kStageBytes;
+  auto issue_lora_loads = [&](int chunk) {
+    const int rb = args.rank * 2;
+    const __amdgpu_buffer_rsrc_t rsrc_t = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(args.lora_t + m0 * args.rank), 0, (int)(rows_a * rb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(args.lora_r + n0 * args.rank), 0, (int)(rows_b * rb), 0x00020000);
+    const unsigned cb = (unsigned)(chunk * BK + 16 * lc);
+    const unsigned oob = cb < (unsigned)rb ? 0u : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const bool spare = Cfg::kDummy && j >= ASL && grp[j] < 0;
+      int8_t *dst = spare ? dummy : lora_stage + (j < ASL ? 0 : BM * BK) + grp[j] * 1024;
+      const unsigned row = (unsigned)(8 * (grp[j] < 0 ? 0 : grp[j]) + (lane >> 3));
+      const unsigned off = spare ? kOutOfRange : ((row * (unsigned)rb + cb) | oob);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < ASL ? rsrc_t : rsrc_r, (lds_void *)dst, 16, off, 0, 0, 0);
+    }
+  };
+  // tile t of the loop, or LoRA chunk 0 in place of the first tile past K
+  auto issue_next = [&](int t) {
+    if constexpr (kLoraStaged) {
+      if (t == nk) {
+        issue_lora_loads(0);
+        return;
+      }
+    }
+    issue_loads(t);
+  };
+  // o += the LoRA term of the wavefront's blocks arow (tile rows of T) x brow
+  // (tile rows of R).  `reload`: chunk 0 is no longer in the stage either (a
+  // previous call used more than one chunk).  Every wavefront makes the same
+  // calls: chunk loads end in a barrier.
+  auto lora_term = [&](const auto &arow, const auto &brow, auto &o, bool reload) {
+    const int nch = (args.rank + kLoraChunk - 1) / kLoraChunk;
+    for (int c = 0; c < nch; ++c) {
+      if (c > 0 || reload) {
+        __syncthreads();  // every wavefront is done with the previous chunk
+        issue_lora_loads(c);
+        wait_loads_and_barrier<0>();
+      }
+      const int r = args.rank - c * kLoraChunk < kLoraChunk ? args.rank - c * kLoraChunk : kLoraChunk;
+      lora_staged(lora_stage, BM * BK, BK, arow, brow, r, lane, o);
+    }
+  };
+
   // ---- fragment reads of k-step kk (0..3) of tile kt: lane l reads row (tile
   // row base + l % 32), logical chunk 2*kk + l / 32, stored at chunk ^ (l & 7)
   // (the row base is a multiple of 32).
@@ -286,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     __builtin_amdgcn_sched_barrier(0);
   };
   issue_loads(0);
-  issue_loads(1);
+  issue_next(1);
   wait_loads_and_barrier<LPW>();
   Frags f0, f1;
   read_frags(0, 0, f0);
@@ -306,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       read_frags(kt, 2, f0);
       read_frags(kt, 3, f1);
       wait_tile_and_barrier();
-      issue_loads(kt + 2);
+      issue_next(kt + 2);
       mfma8_all(f0, f1);
       sched(LPW, 0, T);
       read_frags(kt + 1, 0, f0);
@@ -329,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // 1 MFMA
       }
       wait_tile_and_barrier();
-      issue_loads(kt + 2);
+      issue_next(kt + 2);
       read_frags(kt + 1, 0, f0);
       read_frags(kt + 1, 1, f1);
       mfma8_all(g0, g1);
@@ -357,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       mfma_all(f0);
       sched(0, SM + SN, T);
       wait_tile_and_barrier();
-      issue_loads(kt + 2);
+      issue_next(kt + 2);
       read_frags(kt + 1, 0, f0);
       mfma_all(f1);
       sched(LPW, SM + SN, T);
@@ -442,12 +491,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   } else if constexpr (EPI == Epilogue::kForward && LORA) {
     // dequantize every tile, add the LoRA term of all tiles together, then store
     v16f o[SM][SN];
-    int64_t mrow[SM], nrow[SN];
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
-      mrow[i] = m < M ? m : M - 1;
-      const float sx = args.row_scale[mrow[i]];
+      const float sx = args.row_scale[m < M ? m : M - 1];
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
         const int64_t nb = n0 + wn * TN + j * 32 + 4 * half;
@@ -463,12 +510,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         }
       }
     }
+    {
+      int arow[SM], brow[SN];
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
-      nrow[j] = nr < N ? nr : N - 1;
+      for (int i = 0; i < SM; ++i) arow[i] = wm * TM + i * 32;
+#pragma unroll
+      for (int j = 0; j < SN; ++j) brow[j] = wn * TN + j * 32;
+      lora_term(arow, brow, o, false);
     }
-    lora_all<SM, SN>(args.lora_t, args.lora_r, mrow, nrow, args.rank, lane, o);
     v2u pk[SM][SN][4];
 #pragma unroll
     for (int i = 0; i < SM; ++i)
@@ -621,14 +670,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 #pragma unroll
         for (int r = 0; r < 16; ++r) ot[0][j][r] = z[j][r];
       if constexpr (LORA) {
-        const int64_t mrow[1] = {mc};
-        int64_t nrow[SN];
+        const int arow[1] = {wm * TM + i * 32};
+        int brow[SN];
 #pragma unroll
-        for (int j = 0; j < SN; ++j) {
-          const int64_t nr = n0 + wn * TN + j * 32 + (lane & 31);
-          nrow[j] = nr < N ? nr : N - 1;
-        }
-        lora_all<1, SN>(args.lora_t, args.lora_r, mrow, nrow, args.rank, lane, ot);
+        for (int j = 0; j < SN; ++j) brow[j] = wn * TN + j * 32;
+        lora_term(arow, brow, ot, i > 0 && args.rank > kLoraChunk);
       }
 #pragma unroll
       for (int j = 0; j < SN; ++j) {

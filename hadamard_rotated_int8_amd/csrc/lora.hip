@@ -17,9 +17,9 @@ namespace {
 // A workgroup handles 16*TT tokens with 4*HV wavefronts: HV groups of 4 take
 // 16*TT/HV tokens each, and the 4 wavefronts of a group split the contraction,
 // each keeping (16*TT/HV) x rank fp32 partial sums, which are added in
-// wavefront order through LDS.  (Two groups double the wavefronts in flight per
-// CU at the same tokens per workgroup, so the rank x cols factor is still read
-// once per 16*TT tokens; the second group's factor reads hit L1.)
+// wavefront order through LDS.  (HV > 1 doubles the wavefronts in flight per CU
+// at the same tokens per workgroup, but each wavefront then reads the whole
+// factor for half as many tokens; the launches below use HV = 1.)
 // MFMA 16x16x32: row operand = R rows (rank index), column operand = x rows
 // (token), so lane l owns token l % 16 and the four consecutive rank indices
 // 4 * (l / 16) + 0..3 of each 16 x 16 tile.  The contraction is walked in batches
@@ -436,18 +436,19 @@ hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const 
   return hipGetLastError();
 }
 
-// 64 tokens per workgroup in two groups of 8 wavefronts when there are enough
-// tokens to fill the chip that way (the rank x cols factor is then re-read from
-// L2 half as often), else 32 tokens and 4 wavefronts.  Ranks above kMaxRank run as
-// launches over consecutive slices of at most kMaxRank rows of rmat, each writing
-// its columns of out.
+// 64 tokens per workgroup of 4 wavefronts when there are enough tokens to fill
+// the chip that way (the rank x cols factor is then re-read from L2 half as
+// often), else 32.  (Splitting the 64 tokens over two groups of 4 wavefronts
+// doubles the factor's fragment reads per MFMA: 29.6 -> 40 us on 16384 x 3072,
+// rank 64.)  Ranks above kMaxRank run as launches over consecutive slices of at
+// most kMaxRank rows of rmat, each writing its columns of out.
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
                             float scale, uint16_t *out, hipStream_t stream) {
   if (rank <= 0 || rank % 16) return hipErrorInvalidValue;
   for (int r0 = 0; r0 < rank; r0 += kMaxRank) {
     const int rr = rank - r0 < kMaxRank ? rank - r0 : kMaxRank;
     const hipError_t e = m >= 16384
-        ? launch_lora_down_t<4, 2>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream)
+        ? launch_lora_down_t<4, 1>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream)
         : launch_lora_down_t<2, 1>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream);
     if (e != hipSuccess) return e;
   }
