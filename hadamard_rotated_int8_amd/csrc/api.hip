@@ -78,7 +78,7 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
 }
 
 struct BwdLayout {
-  size_t qdy, sdy, wt, gr, tx, at, part, bp, ap, gap, gbp, total;
+  size_t qdy, sdy, wt, gr, tx, at, part, part2, bp, ap, gap, gbp, total;
 };
 BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   BwdLayout L{};
@@ -91,8 +91,9 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
     L.gr = off; off += align_up((size_t)m * rp * 2);
     L.tx = off; off += align_up((size_t)m * rp * 2);
     L.at = off; off += align_up(rp * (size_t)k * 2);
-    const size_t cells = rp * (size_t)(k > n ? k : n);
-    L.part = off; off += align_up((size_t)lora_grad_splits(m) * cells * 4);
+    const size_t splits = (size_t)lora_grad_splits(m);
+    L.part = off; off += align_up(splits * rp * (size_t)k * 4);   // dA partials
+    L.part2 = off; off += align_up(splits * rp * (size_t)n * 4);  // dB partials
     if (rp != (size_t)rank) {
       L.bp = off; off += align_up(rp * (size_t)n * 2);    // padded only: B [rp, n]
       L.ap = off; off += align_up((size_t)k * rp * 2);    // padded only: A [k, rp]
@@ -416,27 +417,35 @@ sdnq_status_t backward(bool fp8, const uint16_t *dy, int64_t m, int64_t n, const
       bsrc = bp;
     }
     gr = reinterpret_cast<uint16_t *>(ws_at(workspace, L.gr));
-    SDNQ_LAUNCH(launch_lora_down(dy, m, n, bsrc, rp, lora_scale, gr, s));  // g_r = scale * dY B^T
+    if (want_gb) {
+      // g_r = scale * dY B^T and t = x A (for dB) in one launch
+      tx = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tx));
+      at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
+      SDNQ_LAUNCH(launch_transpose_u16(asrc, k, rp, at, s));
+      SDNQ_LAUNCH(launch_lora_down2(dy, n, bsrc, lora_scale, gr, x, k, at, 1.0f, tx, m, rp, s));
+    } else {
+      SDNQ_LAUNCH(launch_lora_down(dy, m, n, bsrc, rp, lora_scale, gr, s));  // g_r = scale * dY B^T
+    }
     ga.lora_t = gr; ga.lora_r = asrc; ga.rank = rp;  // + g_r A^T
   }
   SDNQ_LAUNCH(launch_gemm_i8(Epilogue::kBackward, ga, s));
 
-  if (r > 0) {
-    float *part = reinterpret_cast<float *>(ws_at(workspace, L.part));
-    if (want_ga) {  // x^T g_r
-      uint16_t *dst = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gap)) : grad_a;
-      SDNQ_LAUNCH(launch_lora_grad(x, k, gr, rp, m, 1.0f, false, part, dst, s));
-      if (padded) SDNQ_LAUNCH(launch_copy2d_u16(dst, k, rp, grad_a, k, r, s));
-    }
-    if (want_gb) {
-      tx = reinterpret_cast<uint16_t *>(ws_at(workspace, L.tx));
-      at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
-      uint16_t *dst = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gbp)) : grad_b;
-      SDNQ_LAUNCH(launch_transpose_u16(asrc, k, rp, at, s));
-      SDNQ_LAUNCH(launch_lora_down(x, m, k, at, rp, 1.0f, tx, s));                     // t = x A
-      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, rp, m, lora_scale, true, part, dst, s));  // scale * (dY^T t)^T
-      if (padded) SDNQ_LAUNCH(launch_copy2d_u16(dst, rp, n, grad_b, r, n, s));
-    }
+  if (r > 0 && (want_ga || want_gb)) {
+    // dA = x^T g_r and dB = scale * (dY^T t)^T, reduced over the tokens in one
+    // launch (and their sums in another)
+    float *part_a = reinterpret_cast<float *>(ws_at(workspace, L.part));
+    float *part_b = reinterpret_cast<float *>(ws_at(workspace, L.part2));
+    uint16_t *dst_a = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gap)) : grad_a;
+    uint16_t *dst_b = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gbp)) : grad_b;
+    if (want_ga && want_gb)
+      SDNQ_LAUNCH(launch_lora_grad2(x, k, gr, 1.0f, false, part_a, dst_a, dy, n, tx, lora_scale, true, part_b, dst_b,
+                                    rp, m, s));
+    else if (want_ga)
+      SDNQ_LAUNCH(launch_lora_grad(x, k, gr, rp, m, 1.0f, false, part_a, dst_a, s));
+    else
+      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, rp, m, lora_scale, true, part_b, dst_b, s));
+    if (padded && want_ga) SDNQ_LAUNCH(launch_copy2d_u16(dst_a, k, rp, grad_a, k, r, s));
+    if (padded && want_gb) SDNQ_LAUNCH(launch_copy2d_u16(dst_b, rp, n, grad_b, r, n, s));
   }
   return SDNQ_OK;
 }

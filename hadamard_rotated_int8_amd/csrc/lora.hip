@@ -27,18 +27,34 @@ namespace {
 // several steps of loads stay in flight.
 constexpr int kMaxRank = 128;
 constexpr int kDownBatch = 4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One down-projection of a launch: out[m, r] = bf16(scale * x[m, :] . rmat[r, :]).
+struct DownJob {
+  const uint16_t *x;     // [m, cols]
+  int64_t cols;
+  const uint16_t *rmat;  // [rank, cols]
+  float scale;
+  uint16_t *out;         // row stride out_stride
+  int64_t blocks;        // workgroups of this job
+};
 
 template <int RT, int TT, int HV>  // RT = rank / 16, TT = tokens / 16, HV token groups
-__global__ __launch_bounds__(256 * HV) void lora_down_kernel(const uint16_t *__restrict__ x, int64_t m,
-                                                             int64_t cols, const uint16_t *__restrict__ rmat,
-                                                             float scale, uint16_t *__restrict__ out,
-                                                             int64_t out_stride) {
+__global__ __launch_bounds__(256 * HV) void lora_down_kernel(DownJob j0, DownJob j1, int64_t m, int64_t out_stride) {
   constexpr int TG = TT / HV;  // 16-token subtiles per group
   static_assert(TT % HV == 0, "whole subtiles per group");
   __shared__ v4f red[HV][4][TG][RT][64];
+  // the first j0.blocks workgroups compute job 0, the others job 1
+  const bool second = (int64_t)blockIdx.x >= j0.blocks;
+  const uint16_t *__restrict__ x = second ? j1.x : j0.x;
+  const int64_t cols = second ? j1.cols : j0.cols;
+  const uint16_t *__restrict__ rmat = second ? j1.rmat : j0.rmat;
+  const float scale = second ? j1.scale : j0.scale;
+  uint16_t *__restrict__ out = second ? j1.out : j0.out;
+  const int64_t blk = second ? blockIdx.x - j0.blocks : blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave >> 2, wq = wave & 3;  // token group, contraction quarter
-  const int64_t t0 = (int64_t)blockIdx.x * (16 * TT) + grp * (16 * TG);
+  const int64_t t0 = blk * (16 * TT) + grp * (16 * TG);
 
   // contraction range of this wavefront, in steps of 32
   const int64_t steps = (cols + 31) / 32;
@@ -110,6 +126,120 @@ __global__ __launch_bounds__(256 * HV) void lora_down_kernel(const uint16_t *__r
   }
 }
 
+// ------------------------------------------------------ lora_down (staged) --
+// The same projection for many tokens, with the contraction staged through LDS
+// like the int8 GEMM's: a workgroup of 4 wavefronts computes 128 tokens x the
+// whole rank slice (each wavefront 32 tokens x rank), 64 columns (128 bytes of
+// every row) per k-tile.  A stage holds the 128 x rows, then the rank rows of
+// rmat, 128 bytes each, filled by direct-to-LDS buffer loads of 1 KB (8 rows)
+// in a 3-stage ring; 16-byte chunk c of row r is stored at c ^ (r & 7).  The
+// factor is read once per 128 tokens (the register-loading kernel above reads
+// it once per 64), and every load moves whole 128-byte lines.
+// MFMA 32x32x16 bf16: row operand = rmat rows (rank), column operand = x rows
+// (tokens); lane l ends up with token l % 32 and ranks 8 (r / 4) + 4 (l / 32) +
+// r % 4 of each 32-rank block.
+constexpr int kStagedTokens = 128;
+constexpr int kStagedStages = 3;
+
+// one 16-byte direct-to-LDS load per lane (a plain function: issued from the
+// kernel template's lambda, the builtin kept the host pass from emitting the
+// kernel's launch stub)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t *dst, unsigned off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off, 0, 0, 0);
+}
+
+template <int RB>  // ceil(rank / 32) of the slice (1 .. 4); ranks past `rank` read zeros and are not stored
+__global__ __launch_bounds__(256) void lora_down_staged_kernel(DownJob j0, DownJob j1, int64_t m, int rank,
+                                                               int64_t out_stride) {
+  constexpr int kRows = kStagedTokens + 32 * RB;  // staged rows per k-tile
+  constexpr int kStage = kRows * 128;
+  constexpr int kLpw = kRows / 8 / 4;             // 1 KB loads per wavefront per k-tile
+  constexpr int kXGroups = kStagedTokens / 8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStagedStages * kStage];
+  const bool second = (int64_t)blockIdx.x >= j0.blocks;
+  const uint16_t *x = second ? j1.x : j0.x;
+  const int64_t cols = second ? j1.cols : j0.cols;
+  const uint16_t *rmat = second ? j1.rmat : j0.rmat;
+  const float scale = second ? j1.scale : j0.scale;
+  uint16_t *__restrict__ out = second ? j1.out : j0.out;
+  const int64_t blk = second ? blockIdx.x - j0.blocks : blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = blk * kStagedTokens;
+  const int64_t rows_x = (m - t0) < kStagedTokens ? (m - t0) : kStagedTokens;
+  const int64_t row_bytes = cols * 2;
+
+  // slot j of wavefront w loads group g = 4 j + w: x rows 8 g .. (g < kXGroups),
+  // else rmat rows 8 (g - kXGroups) ..; lane i lands at byte 16 i of the group:
+  // row 8 g + i / 8, stored chunk i % 8, holding logical chunk (i & 7) ^ (i >> 3)
+  const __amdgpu_buffer_rsrc_t rs_x =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(x + t0 * cols), 0, (int)(rows_x * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)rmat, 0, (int)(rank * row_bytes), 0x00020000);
+  const int lc = (lane & 7) ^ ((lane >> 3) & 7);
+  unsigned voff[kLpw];
+#pragma unroll
+  for (int j = 0; j < kLpw; ++j) {
+    const int g = 4 * j + wave;
+    const int row = 8 * (g < kXGroups ? g : g - kXGroups) + (lane >> 3);
+    voff[j] = (unsigned)(row * row_bytes + 16 * lc);
+  }
+  const int nk = (int)((row_bytes + 127) / 128);
+  auto issue = [&](int kt) {
+    const unsigned k0 = (unsigned)kt * 128;
+    const unsigned oob = (int64_t)k0 + 16 * lc < row_bytes ? 0u : 0x80000000u;
+    uint8_t *base = smem + (kt % kStagedStages) * kStage;
+#pragma unroll
+    for (int j = 0; j < kLpw; ++j) {
+      const int g = 4 * j + wave;
+      load_lds16(g < kXGroups ? rs_x : rs_r, base + g * 1024, (voff[j] + k0) | oob);
+    }
+  };
+
+  // fragments of k-step kk (0..3): row (block base + l % 32), logical chunk
+  // 2 kk + l / 32, stored at that ^ (l & 7)
+  const int frow = (lane & 31) * 128;
+  v16f acc[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) acc[j] = v16f{};
+  issue(0);
+  issue(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kLpw) : "memory");  // tile kt has landed
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + 2);  // into the stage of tile kt - 1, which every wavefront has finished
+    const uint8_t *base = smem + (kt % kStagedStages) * kStage + frow;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int col = 16 * ((2 * kk + (lane >> 5)) ^ (lane & 7));
+      const v8bf xa = *reinterpret_cast<const v8bf *>(base + (32 * wave) * 128 + col);
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const v8bf rv = *reinterpret_cast<const v8bf *>(base + (kStagedTokens + 32 * j) * 128 + col);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, xa, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the zero-fill loads past the last tile
+
+  const int64_t t = t0 + 32 * wave + (lane & 31);
+  if (t < m) {
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = 32 * j + 8 * q + 4 * (lane >> 5);
+        if (r0 < rank) {  // rank is a multiple of 16, so 4 ranks are all in or all out
+          uint2 packed;
+          packed.x = pack_bf16x2(scale * acc[j][4 * q], scale * acc[j][4 * q + 1]);
+          packed.y = pack_bf16x2(scale * acc[j][4 * q + 2], scale * acc[j][4 * q + 3]);
+          *reinterpret_cast<uint2 *>(out + t * out_stride + r0) = packed;
+        }
+      }
+  }
+}
+
 // ----------------------------------------------------------- lora_grad --
 // partial[split][a][b] = sum over the split's tokens t of P[t, a] * Q[t, b], with
 // P the wide operand (x or dY: a over 3072-ish features) and Q the narrow one
@@ -138,20 +268,41 @@ constexpr int kMaxSplits = 16;
 constexpr int64_t kTokensPerSplit = 1024;
 static_assert(kGradBlocks % 4 == 0, "every wavefront issues the same number of loads");
 
+// One token reduction of a launch (P [m, pa], Q [m, qb], partials [splits, pa, qb]).
+struct GradJob {
+  const uint16_t *p;
+  int64_t pa;
+  const uint16_t *q;
+  float *partials;
+  int64_t tiles;  // column tiles of kGradA of this job
+};
+// and its final sum: out = bf16(scale * sum of the partials), [pa, qb] or transposed
+struct ReduceJob {
+  const float *partials;
+  int64_t pa;
+  float scale;
+  int transposed;
+  uint16_t *out;
+  int64_t count;  // pa * qb
+};
+
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
 
-__global__ __launch_bounds__(256) void lora_grad_partial_kernel(const uint16_t *__restrict__ p, int64_t pa,
-                                                                const uint16_t *__restrict__ q, int64_t qb,
-                                                                int64_t m, int64_t tokens_per_split,
-                                                                float *__restrict__ partials) {
+__global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJob j0, GradJob j1, int64_t qb, int64_t m,
+                                                                int64_t tokens_per_split) {
   constexpr int LPW = kGradBlocks / 4;  // loads per wavefront per step
   constexpr int PSUB = kGradA / 64;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGradStages * kGradStageBytes];
+  // the first j0.tiles column tiles of the grid compute job 0, the others job 1
+  const bool second = (int64_t)blockIdx.x >= j0.tiles;
+  const uint16_t *__restrict__ p = second ? j1.p : j0.p;
+  const int64_t pa = second ? j1.pa : j0.pa;
+  const uint16_t *__restrict__ q = second ? j1.q : j0.q;
+  float *__restrict__ partials = second ? j1.partials : j0.partials;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t a0 = (int64_t)blockIdx.x * kGradA;
+  const int64_t a0 = (second ? blockIdx.x - j0.tiles : (int64_t)blockIdx.x) * kGradA;
   const int64_t b0 = (int64_t)blockIdx.y * kGradB;
   const int split = blockIdx.z;
   const int64_t tb = split * tokens_per_split;
@@ -253,11 +404,18 @@ __global__ __launch_bounds__(256) void lora_grad_partial_kernel(const uint16_t *
 }
 
 // out = bf16(scale * sum over splits of partial), in split order; the partials
-// are [pa][qb]; out is [pa][qb], or [qb][pa] when transposed.
-__global__ void lora_grad_reduce_kernel(const float *__restrict__ partials, int splits, int64_t pa, int64_t qb,
-                                        float scale, int transposed, uint16_t *__restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // index into the partials
-  const int64_t count = pa * qb;
+// are [pa][qb]; out is [pa][qb], or [qb][pa] when transposed.  Threads past job
+// 0's count sum job 1.
+__global__ void lora_grad_reduce_kernel(ReduceJob j0, ReduceJob j1, int splits, int64_t qb) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // index into the partials
+  const bool second = i >= j0.count;
+  if (second) i -= j0.count;
+  const ReduceJob &j = second ? j1 : j0;
+  const float *__restrict__ partials = j.partials;
+  const int64_t pa = j.pa, count = j.count;
+  const float scale = j.scale;
+  const int transposed = j.transposed;
+  uint16_t *__restrict__ out = j.out;
   if (i >= count) return;
   // all splits' loads in flight first (splits <= kMaxSplits, the same for every
   // lane), then the sum in split order
@@ -419,15 +577,38 @@ hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t
   return hipGetLastError();
 }
 
+template <int RB>
+hipError_t launch_lora_down_staged_t(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride,
+                                     hipStream_t stream) {
+  const int64_t per_job = (m + kStagedTokens - 1) / kStagedTokens;
+  j0.blocks = per_job;
+  j1.blocks = j1.x ? per_job : 0;
+  hipLaunchKernelGGL((lora_down_staged_kernel<RB>), dim3((unsigned)(j0.blocks + j1.blocks)), dim3(256), 0, stream, j0,
+                     j1, m, rank, out_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_down_staged(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride,
+                                  hipStream_t stream) {
+  switch ((rank + 31) / 32) {
+    case 1: return launch_lora_down_staged_t<1>(j0, j1, m, rank, out_stride, stream);
+    case 2: return launch_lora_down_staged_t<2>(j0, j1, m, rank, out_stride, stream);
+    case 3: return launch_lora_down_staged_t<3>(j0, j1, m, rank, out_stride, stream);
+    case 4: return launch_lora_down_staged_t<4>(j0, j1, m, rank, out_stride, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int TT, int HV>
-hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
-                              float scale, uint16_t *out, int64_t out_stride, hipStream_t stream) {
-  const dim3 grid((unsigned)((m + 16 * TT - 1) / (16 * TT)));
+hipError_t launch_lora_down_t(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride, hipStream_t stream) {
+  const int64_t per_job = (m + 16 * TT - 1) / (16 * TT);
+  j0.blocks = per_job;
+  j1.blocks = j1.x ? per_job : 0;
+  const dim3 grid((unsigned)(j0.blocks + j1.blocks));
   switch (rank / 16) {
-#define SDNQ_DOWN(RT)                                                                                             \
-  case RT:                                                                                                        \
-    hipLaunchKernelGGL((lora_down_kernel<RT, TT, HV>), grid, dim3(256 * HV), 0, stream, x, m, cols, rmat, scale, \
-                       out, out_stride);                                                                          \
+#define SDNQ_DOWN(RT)                                                                                        \
+  case RT:                                                                                                   \
+    hipLaunchKernelGGL((lora_down_kernel<RT, TT, HV>), grid, dim3(256 * HV), 0, stream, j0, j1, m, out_stride); \
     break;
     SDNQ_DOWN(1) SDNQ_DOWN(2) SDNQ_DOWN(3) SDNQ_DOWN(4) SDNQ_DOWN(5) SDNQ_DOWN(6) SDNQ_DOWN(7) SDNQ_DOWN(8)
 #undef SDNQ_DOWN
@@ -442,17 +623,26 @@ hipError_t launch_lora_down_t(const uint16_t *x, int64_t m, int64_t cols, const 
 // doubles the factor's fragment reads per MFMA: 29.6 -> 40 us on 16384 x 3072,
 // rank 64.)  Ranks above kMaxRank run as launches over consecutive slices of at
 // most kMaxRank rows of rmat, each writing its columns of out.
-hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
-                            float scale, uint16_t *out, hipStream_t stream) {
+hipError_t launch_lora_down2(const uint16_t *x0, int64_t cols0, const uint16_t *rmat0, float scale0, uint16_t *out0,
+                             const uint16_t *x1, int64_t cols1, const uint16_t *rmat1, float scale1, uint16_t *out1,
+                             int64_t m, int rank, hipStream_t stream) {
   if (rank <= 0 || rank % 16) return hipErrorInvalidValue;
   for (int r0 = 0; r0 < rank; r0 += kMaxRank) {
     const int rr = rank - r0 < kMaxRank ? rank - r0 : kMaxRank;
-    const hipError_t e = m >= 16384
-        ? launch_lora_down_t<4, 1>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream)
-        : launch_lora_down_t<2, 1>(x, m, cols, rmat + (int64_t)r0 * cols, rr, scale, out + r0, rank, stream);
+    const DownJob j0{x0, cols0, rmat0 + (int64_t)r0 * cols0, scale0, out0 + r0, 0};
+    const DownJob j1{x1, cols1, x1 ? rmat1 + (int64_t)r0 * cols1 : nullptr, scale1, x1 ? out1 + r0 : nullptr, 0};
+    const int64_t staged_blocks = (x1 ? 2 : 1) * ((m + kStagedTokens - 1) / kStagedTokens);
+    const hipError_t e = staged_blocks >= device_cu_count() ? launch_lora_down_staged(j0, j1, m, rr, rank, stream)
+                         : m >= 16384                      ? launch_lora_down_t<4, 1>(j0, j1, m, rr, rank, stream)
+                                                           : launch_lora_down_t<2, 1>(j0, j1, m, rr, rank, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat, int rank,
+                            float scale, uint16_t *out, hipStream_t stream) {
+  return launch_lora_down2(x, cols, rmat, scale, out, nullptr, 0, nullptr, 0.0f, nullptr, m, rank, stream);
 }
 
 int lora_grad_splits(int64_t m) {
@@ -462,19 +652,31 @@ int lora_grad_splits(int64_t m) {
   return (int)s;
 }
 
-hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m, float scale,
-                            bool transposed, float *partials, uint16_t *out, hipStream_t stream) {
+hipError_t launch_lora_grad2(const uint16_t *p0, int64_t pa0, const uint16_t *q0, float scale0, bool transposed0,
+                             float *partials0, uint16_t *out0, const uint16_t *p1, int64_t pa1, const uint16_t *q1,
+                             float scale1, bool transposed1, float *partials1, uint16_t *out1, int64_t qb, int64_t m,
+                             hipStream_t stream) {
   const int splits = lora_grad_splits(m);
   int64_t per = (m + splits - 1) / splits;
   per = (per + kGradTokens - 1) / kGradTokens * kGradTokens;
-  const dim3 grid((unsigned)((pa + kGradA - 1) / kGradA), (unsigned)((qb + kGradB - 1) / kGradB), (unsigned)splits);
-  hipLaunchKernelGGL(lora_grad_partial_kernel, grid, dim3(256), 0, stream, p, pa, q, qb, m, per, partials);
+  const GradJob g0{p0, pa0, q0, partials0, (pa0 + kGradA - 1) / kGradA};
+  const GradJob g1{p1, pa1, q1, partials1, p1 ? (pa1 + kGradA - 1) / kGradA : 0};
+  const dim3 grid((unsigned)(g0.tiles + g1.tiles), (unsigned)((qb + kGradB - 1) / kGradB), (unsigned)splits);
+  hipLaunchKernelGGL(lora_grad_partial_kernel, grid, dim3(256), 0, stream, g0, g1, qb, m, per);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t count = pa * qb;
-  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
-                     partials, splits, pa, qb, scale, transposed ? 1 : 0, out);
+  const ReduceJob r0{partials0, pa0, scale0, transposed0 ? 1 : 0, out0, pa0 * qb};
+  const ReduceJob r1{partials1, pa1, scale1, transposed1 ? 1 : 0, out1, p1 ? pa1 * qb : 0};
+  const int64_t count = r0.count + r1.count;
+  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, r0, r1,
+                     splits, qb);
   return hipGetLastError();
+}
+
+hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m, float scale,
+                            bool transposed, float *partials, uint16_t *out, hipStream_t stream) {
+  return launch_lora_grad2(p, pa, q, scale, transposed, partials, out, nullptr, 0, nullptr, 0.0f, false, nullptr,
+                           nullptr, qb, m, stream);
 }
 
 hipError_t launch_copy2d_u16(const uint16_t *in, int64_t in_rows, int64_t in_cols, uint16_t *out, int64_t out_rows,

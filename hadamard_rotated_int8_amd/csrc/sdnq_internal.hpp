@@ -89,6 +89,10 @@ hipError_t launch_copy2d_u16(const uint16_t *in, int64_t in_rows, int64_t in_col
 // rank a multiple of 16 (any number of 128-row slices).
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const uint16_t *rmat,
                             int rank, float scale, uint16_t *out, hipStream_t stream);
+// Two such projections sharing m and rank in one launch (x1 == nullptr: only the first).
+hipError_t launch_lora_down2(const uint16_t *x0, int64_t cols0, const uint16_t *rmat0, float scale0, uint16_t *out0,
+                             const uint16_t *x1, int64_t cols1, const uint16_t *rmat1, float scale1, uint16_t *out1,
+                             int64_t m, int rank, hipStream_t stream);
 
 // Token reduction: part[s, a, b] = sum over the tokens of split s of p[t, a] * q[t, b]
 // (p [m, pa] the wide operand, q [m, qb] the narrow one, qb a multiple of 16; bf16), then
@@ -96,6 +100,12 @@ hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const ui
 int lora_grad_splits(int64_t m);
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
                             float scale, bool transposed, float *partials, uint16_t *out, hipStream_t stream);
+// Two such reductions sharing m and qb in one launch each for the partials and
+// the sums (p1 == nullptr: only the first); each job has its own partials.
+hipError_t launch_lora_grad2(const uint16_t *p0, int64_t pa0, const uint16_t *q0, float scale0, bool transposed0,
+                             float *partials0, uint16_t *out0, const uint16_t *p1, int64_t pa1, const uint16_t *q1,
+                             float scale1, bool transposed1, float *partials1, uint16_t *out1, int64_t qb, int64_t m,
+                             hipStream_t stream);
 
 // Rotate (block g along the tokens) + per-feature int8 quantization of two
 // operands sharing the token count m, each x [m, f] bf16 read as it is: q [f, m]

@@ -347,8 +347,13 @@ def test_backward_ragged_tokens_and_tiles():
     assert_lora_grads(dx, ga, gb, ref)
 
 
-def test_backward_many_tokens_with_lora():
-    inp, (dx, ga, gb), ref, _ = backward_case(16400, 272, 256, 128, rank=48, seed=11, scale=0.5)
+@pytest.mark.parametrize("rank,g", [(48, 128), (200, 64)])
+def test_backward_many_tokens_with_lora(rank, g):
+    """16400 tokens: the down-projections of g_r and t run as one launch of the
+    LDS-staged kernel (128 tokens per workgroup, a ragged last workgroup of 16),
+    rank 48 with a half-empty 32-rank block, rank 200 as slices of 128 and 80;
+    272 columns leave the last 128-byte k-tile partly past the row."""
+    inp, (dx, ga, gb), ref, _ = backward_case(16400, 272, 256, g, rank=rank, seed=11 + rank, scale=0.5)
     assert_lora_grads(dx, ga, gb, ref)
 
 
