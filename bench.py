@@ -225,15 +225,21 @@ def measure_rows(torch, h, synth, reps: int = 100, warmup: int = 10) -> dict:
     qw, sw = h.sdnq_rotate_quantize_weight(w, 256)
     ws = torch.empty(h.sdnq_workspace_bytes(c.m, c.n, c.k, c.lora_rank, True), dtype=torch.uint8, device=dev)
     ops = 2.0 * c.m * c.n * c.k
+    # the frozen weight's codes are transposed once, at weight preparation
+    qwt = h.sdnq_transpose_codes(qw)
+    per_call = timed(lambda: h.sdnq_qlinear_backward_input(dy, qw, sw, 256, x, la, lb, c.lora_scale, workspace=ws))
     row("peft_backward_16384x3072x3072_g256_r64",
-        lambda: h.sdnq_qlinear_backward_input(dy, qw, sw, 256, x, la, lb, c.lora_scale, workspace=ws), ops,
-        {"note": "dX through the int8 weight + LoRA dX, dA, dB"})
+        lambda: h.sdnq_qlinear_backward_input_wt(dy, qwt, sw, 256, x, la, lb, c.lora_scale, workspace=ws), ops,
+        {"note": "dX through the int8 weight + LoRA dX, dA, dB; weight codes transposed once at preparation",
+         "us_codes_transposed_per_call": round(per_call[0], 2)})
     qw8, sw8 = h.sdnq_rotate_quantize_weight_fp8(w, 256)
+    qwt8 = h.sdnq_transpose_codes(qw8)
     row("fp8_peft_backward_16384x3072x3072_g256_r64",
-        lambda: h.sdnq_qlinear_backward_input_fp8(dy, qw8, sw8, 256, x, la, lb, c.lora_scale, workspace=ws), ops,
-        {"note": "dX through the E4M3 weight + LoRA dX, dA, dB; fp8 dense peak 5.0 PFLOP/s"},
+        lambda: h.sdnq_qlinear_backward_input_fp8_wt(dy, qwt8, sw8, 256, x, la, lb, c.lora_scale, workspace=ws),
+        ops, {"note": "dX through the E4M3 weight + LoRA dX, dA, dB; weight codes transposed once at preparation; "
+                      "fp8 dense peak 5.0 PFLOP/s"},
         peak=5000.0, unit="TFLOP/s")
-    del qw8, sw8
+    del qw8, sw8, qwt, qwt8
     wws = torch.empty(h.sdnq_weight_grad_workspace_bytes(c.m, c.n, c.k), dtype=torch.uint8, device=dev)
     dw = torch.empty((c.n, c.k), dtype=torch.bfloat16, device=dev)
     row("weight_grad_16384x3072x3072_g256", lambda: h.sdnq_qlinear_weight_grad(dy, x, 256, out=dw, workspace=wws),

@@ -46,6 +46,9 @@ def lib() -> ctypes.CDLL:
         "sdnq_qlinear_forward_quantized": [p, p, i64, i64, p, p, i64, p, p, i32, f32, p, p, sz, p],
         "sdnq_qlinear_backward_input": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
         "sdnq_qlinear_backward_input_fp8": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
+        "sdnq_qlinear_backward_input_wt": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
+        "sdnq_qlinear_backward_input_fp8_wt": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
+        "sdnq_transpose_codes": [p, i64, i64, p, p],
         "sdnq_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p, sz, p],
         "sdnq_rotate_quantize_weight_fp8": [p, i64, i64, i32, p, p, p],
         "sdnq_rotate_quantize_act_fp8": [p, i64, i64, i32, p, p, p, p],
@@ -265,12 +268,40 @@ def sdnq_qlinear_backward_input_fp8(dy, qw, w_scale, g, x=None, lora_a=None, lor
                      lora_scale, want_lora_grads, workspace)
 
 
-def _backward(name, code_dtype, dy, qw, w_scale, g, x, lora_a, lora_b, lora_scale, want_lora_grads, workspace):
+def sdnq_transpose_codes(codes):
+    """[rows, cols] int8 or uint8 codes -> [cols, rows] (the backward's qw_t)."""
+    if not isinstance(codes, torch.Tensor) or codes.dtype not in (torch.int8, torch.uint8) or codes.dim() != 2:
+        raise ValueError("codes: expected a 2-d int8 or uint8 tensor")
+    if not codes.is_contiguous():
+        raise ValueError("codes: must be contiguous")
+    rows, cols = codes.shape
+    out = torch.empty((cols, rows), dtype=codes.dtype, device=codes.device)
+    _check(lib().sdnq_transpose_codes(_ptr(codes), rows, cols, _ptr(out), _stream(codes.device)),
+           "sdnq_transpose_codes")
+    return out
+
+
+def sdnq_qlinear_backward_input_wt(dy, qw_t, w_scale, g, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
+                                   want_lora_grads=True, workspace=None):
+    """sdnq_qlinear_backward_input with qw_t = qw^T [k, n] (sdnq_transpose_codes(qw))."""
+    return _backward("sdnq_qlinear_backward_input_wt", torch.int8, dy, qw_t, w_scale, g, x, lora_a, lora_b,
+                     lora_scale, want_lora_grads, workspace, transposed=True)
+
+
+def sdnq_qlinear_backward_input_fp8_wt(dy, qw_t, w_scale, g, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
+                                       want_lora_grads=True, workspace=None):
+    """The FP8 input gradient with the E4M3 codes given transposed, qw_t [k, n]."""
+    return _backward("sdnq_qlinear_backward_input_fp8_wt", torch.uint8, dy, qw_t, w_scale, g, x, lora_a, lora_b,
+                     lora_scale, want_lora_grads, workspace, transposed=True)
+
+
+def _backward(name, code_dtype, dy, qw, w_scale, g, x, lora_a, lora_b, lora_scale, want_lora_grads, workspace,
+              transposed=False):
     _need(dy, torch.bfloat16, 2, "dy")
     _need(qw, code_dtype, 2, "qw")
     _need(w_scale, torch.float32, 1, "w_scale")
     m, n = dy.shape
-    k = qw.shape[1]
+    k = qw.shape[0] if transposed else qw.shape[1]
     rank = 0
     ga = gb = None
     if lora_a is not None or lora_b is not None:

@@ -362,7 +362,10 @@ sdnq_status_t sdnq_qlinear_forward_noalloc(const uint16_t *x, int64_t m, int64_t
 namespace {
 
 // The input gradient through the int8 (fp8 = false) or E4M3 (fp8 = true) weight codes.
-sdnq_status_t backward(bool fp8, const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw, const float *w_scale,
+// qw_transposed: qw holds the codes as [k, n] (made once by sdnq_transpose_codes)
+// instead of [n, k], and the per-call transpose is skipped.
+sdnq_status_t backward(bool fp8, bool qw_transposed, const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw,
+                       const float *w_scale,
                        int64_t k, int32_t g, const uint16_t *x, const uint16_t *lora_a, const uint16_t *lora_b,
                        int32_t rank, float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                        void *workspace, size_t workspace_bytes, void *stream) {
@@ -392,13 +395,14 @@ sdnq_status_t backward(bool fp8, const uint16_t *dy, int64_t m, int64_t n, const
   (void)hipGetLastError();
   int8_t *qdy = reinterpret_cast<int8_t *>(ws_at(workspace, L.qdy));
   float *sdy = reinterpret_cast<float *>(ws_at(workspace, L.sdy));
-  int8_t *wt = reinterpret_cast<int8_t *>(ws_at(workspace, L.wt));
+  const int8_t *wt = qw_transposed ? qw : reinterpret_cast<int8_t *>(ws_at(workspace, L.wt));
   // dY' = dY * w_scale (column fold), per-token quantization, no rotation along n.
   if (fp8)
     SDNQ_LAUNCH(launch_rotate_quantize_fp8(dy, m, n, 1, w_scale, reinterpret_cast<uint8_t *>(qdy), sdy, s));
   else
     SDNQ_LAUNCH(launch_rotate_quantize(dy, m, n, 1, w_scale, qdy, sdy, s));
-  SDNQ_LAUNCH(launch_transpose_i8(qw, n, k, wt, s));  // qw [n, k] -> [k, n] (bytes, either code)
+  if (!qw_transposed)  // qw [n, k] -> [k, n] (bytes, either code)
+    SDNQ_LAUNCH(launch_transpose_i8(qw, n, k, const_cast<int8_t *>(wt), s));
 
   GemmArgs ga{};
   ga.a = qdy; ga.b = wt; ga.m = m; ga.n = k; ga.k = n; ga.fp8 = fp8;
@@ -459,8 +463,17 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
                                           const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
                                           float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                                           void *workspace, size_t workspace_bytes, void *stream) {
-  return backward(false, dy, m, n, qw, w_scale, k, g, x, lora_a, lora_b, rank, lora_scale, dx, grad_a, grad_b,
-                  workspace, workspace_bytes, stream);
+  return backward(false, false, dy, m, n, qw, w_scale, k, g, x, lora_a, lora_b, rank, lora_scale, dx, grad_a,
+                  grad_b, workspace, workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_qlinear_backward_input_wt(const uint16_t *dy, int64_t m, int64_t n, const int8_t *qw_t,
+                                             const float *w_scale, int64_t k, int32_t g, const uint16_t *x,
+                                             const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                             float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  return backward(false, true, dy, m, n, qw_t, w_scale, k, g, x, lora_a, lora_b, rank, lora_scale, dx, grad_a,
+                  grad_b, workspace, workspace_bytes, stream);
 }
 
 sdnq_status_t sdnq_qlinear_backward_input_fp8(const uint16_t *dy, int64_t m, int64_t n, const uint8_t *qw,
@@ -468,8 +481,27 @@ sdnq_status_t sdnq_qlinear_backward_input_fp8(const uint16_t *dy, int64_t m, int
                                               const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
                                               float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                                               void *workspace, size_t workspace_bytes, void *stream) {
-  return backward(true, dy, m, n, reinterpret_cast<const int8_t *>(qw), w_scale, k, g, x, lora_a, lora_b, rank,
-                  lora_scale, dx, grad_a, grad_b, workspace, workspace_bytes, stream);
+  return backward(true, false, dy, m, n, reinterpret_cast<const int8_t *>(qw), w_scale, k, g, x, lora_a, lora_b,
+                  rank, lora_scale, dx, grad_a, grad_b, workspace, workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_qlinear_backward_input_fp8_wt(const uint16_t *dy, int64_t m, int64_t n, const uint8_t *qw_t,
+                                                 const float *w_scale, int64_t k, int32_t g, const uint16_t *x,
+                                                 const uint16_t *lora_a, const uint16_t *lora_b, int32_t rank,
+                                                 float lora_scale, uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                                 void *workspace, size_t workspace_bytes, void *stream) {
+  return backward(true, true, dy, m, n, reinterpret_cast<const int8_t *>(qw_t), w_scale, k, g, x, lora_a, lora_b,
+                  rank, lora_scale, dx, grad_a, grad_b, workspace, workspace_bytes, stream);
+}
+
+sdnq_status_t sdnq_transpose_codes(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out, void *stream) {
+  if (!in || !out || rows < 0 || cols < 0) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_feature(rows));
+  SDNQ_TRY(check_feature(cols));
+  if (!aligned16(in) || !aligned16(out)) return SDNQ_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return launched(launch_transpose_i8(reinterpret_cast<const int8_t *>(in), rows, cols,
+                                      reinterpret_cast<int8_t *>(out), (hipStream_t)stream));
 }
 
 sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int64_t n, int64_t k, int32_t b_layout,

@@ -132,6 +132,26 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
                                           uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Byte transpose of weight codes (int8 or E4M3): out[cols, rows] = in[rows, cols]^T,
+ * rows and cols multiples of 16, at most 65536; in and out 16-byte aligned, not
+ * overlapping.  The input gradient reads the codes across their rows; during
+ * adapter training the quantized weight is frozen ("ConvRot / Hadamard SDNQ",
+ * "PEFT Behavior": the adapter trains on top of the frozen quantized base), so
+ * the transpose can be made once, next to sdnq_rotate_quantize_weight, and
+ * passed to sdnq_qlinear_backward_input_wt. */
+sdnq_status_t sdnq_transpose_codes(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out, void *stream);
+
+/* sdnq_qlinear_backward_input with the weight codes given transposed: qw_t[k,n] =
+ * qw^T (sdnq_transpose_codes(qw, n, k, qw_t)).  Same arguments otherwise, same
+ * results bit for bit, same limits, errors and workspace size; the call skips
+ * its per-call transpose of qw. */
+sdnq_status_t sdnq_qlinear_backward_input_wt(const uint16_t *dy, int64_t m, int64_t n,
+                                             const int8_t *qw_t, const float *w_scale, int64_t k,
+                                             int32_t g, const uint16_t *x, const uint16_t *lora_a,
+                                             const uint16_t *lora_b, int32_t rank, float lora_scale,
+                                             uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): sdnq_qlinear_forward
  * with the same arguments and results, minus the workspace, which comes from a
@@ -245,6 +265,16 @@ sdnq_status_t sdnq_qlinear_backward_input_fp8(const uint16_t *dy, int64_t m, int
                                               const uint16_t *lora_b, int32_t rank, float lora_scale,
                                               uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
                                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* sdnq_qlinear_backward_input_fp8 with the E4M3 codes given transposed, qw_t[k,n]
+ * (sdnq_transpose_codes), as sdnq_qlinear_backward_input_wt is to
+ * sdnq_qlinear_backward_input. */
+sdnq_status_t sdnq_qlinear_backward_input_fp8_wt(const uint16_t *dy, int64_t m, int64_t n,
+                                                 const uint8_t *qw_t, const float *w_scale, int64_t k,
+                                                 int32_t g, const uint16_t *x, const uint16_t *lora_a,
+                                                 const uint16_t *lora_b, int32_t rank, float lora_scale,
+                                                 uint16_t *dx, uint16_t *grad_a, uint16_t *grad_b,
+                                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* Diagnostics: the FP8 GEMM with an fp32 store instead of the epilogue:
  * c[m,n] = sum_k dec(a[m,k]) * dec(b[n,k]), fp32 accumulation. */

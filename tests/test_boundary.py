@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "sdnq_weight_grad_workspace_offset",
               "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset",
               "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset",
-              "sdnq_qlinear_forward_noalloc", "sdnq_qlinear_backward_input_fp8"):
+              "sdnq_qlinear_forward_noalloc", "sdnq_qlinear_backward_input_fp8", "sdnq_transpose_codes",
+              "sdnq_qlinear_backward_input_wt", "sdnq_qlinear_backward_input_fp8_wt"):
         assert n in names
 
 
@@ -169,6 +170,23 @@ def test_forward_workspace_limit_is_exact():
 ])
 def test_backward_validation(kw, expect):
     assert bwd(**kw) == expect
+
+
+@no_gpu
+def test_transposed_weight_entry_points_validate():
+    L = h.lib()
+    assert L.sdnq_transpose_codes(None, 32, 32, B, None) == INVALID
+    assert L.sdnq_transpose_codes(A, 32, 32, None, None) == INVALID
+    assert L.sdnq_transpose_codes(A, 0, 32, B, None) == INVALID
+    assert L.sdnq_transpose_codes(A, 24, 32, B, None) == UNSUPPORTED
+    assert L.sdnq_transpose_codes(A, 32, 65552, B, None) == UNSUPPORTED
+    assert L.sdnq_transpose_codes(A + 8, 32, 32, B, None) == INVALID
+    for fn in (L.sdnq_qlinear_backward_input_wt, L.sdnq_qlinear_backward_input_fp8_wt):
+        # dy, m, n, qw_t, w_scale, k, g, x, lora_a, lora_b, rank, scale, dx, ga, gb, ws, wsb, stream
+        assert fn(A, 4, 256, B, C, 256, 7, None, None, None, 0, 0.0, D, None, None, W, WS, None) == UNSUPPORTED
+        assert fn(A, 4, 256, None, C, 256, 256, None, None, None, 0, 0.0, D, None, None, W, WS, None) == INVALID
+        assert fn(A, 4, 256, B, C, 256, 256, None, None, None, 0, 0.0, D, None, None, None, 0, None) == WORKSPACE
+        assert fn(A, 4, 256, B, C, 256, 256, None, A, B, 300, 0.5, D, None, None, W, WS, None) == UNSUPPORTED
 
 
 @no_gpu

@@ -394,3 +394,25 @@ def test_forward_quantized_any_lora_rank(rank):
     qwo, swo = oracle.rotate_quantize(inp["w"], 128)
     ref = oracle.qlinear_forward(inp["x"], qwo, swo, 128, inp["lora_a"], inp["lora_b"], 1.0)
     assert_close(h_bits(y), ref["y"], f"rank {rank} y")
+
+
+# ------------------------------------------------- transposed weight codes --
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_backward_with_transposed_codes_is_the_same_call(fp8):
+    """qw_t made once by sdnq_transpose_codes gives the backward's results bit for bit."""
+    inp = synth.make_linear(300, 768, 640, seed=21, lora_rank=32, backward=True)
+    quant = h.sdnq_rotate_quantize_weight_fp8 if fp8 else h.sdnq_rotate_quantize_weight
+    say(f"  transposed codes fp8={fp8}")
+    qw, sw = quant(d_bf16(inp["w"]), 128)
+    qwt = h.sdnq_transpose_codes(qw)
+    torch.cuda.synchronize()
+    assert torch.equal(qwt.cpu(), qw.cpu().t().contiguous())
+    f, ft = ((h.sdnq_qlinear_backward_input_fp8, h.sdnq_qlinear_backward_input_fp8_wt) if fp8 else
+             (h.sdnq_qlinear_backward_input, h.sdnq_qlinear_backward_input_wt))
+    dy, x, la, lb = (d_bf16(inp[k]) for k in ("dy", "x", "lora_a", "lora_b"))
+    a = f(dy, qw, sw, 128, x, la, lb, 0.5)
+    b = ft(dy, qwt, sw, 128, x, la, lb, 0.5)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
