@@ -724,9 +724,9 @@ hipError_t launch_backward_any(const GemmArgs &args, hipStream_t stream) {
 // long as one tile (proportional to its width).  The width with the fewest
 // column-rounds wins (ties go to 256): e.g. 4096 x 10240 takes 2 rounds of
 // 256 x 320 tiles instead of 2.5 (so 3) of 256 x 256, and 4096 x 3072 one round
-// of 256 x 192 instead of 0.75 of 256 x 256.
-// (FP8 keeps two fragment sets of both halves live, which 320 columns do not fit.)
-int gemm_tile_n(int64_t m, int64_t n, bool fp8) {
+// of 256 x 192 instead of 0.75 of 256 x 256.  The same widths serve the FP8
+// path (its 320-column tiles keep two fragment sets in flight instead of four).
+int gemm_tile_n(int64_t m, int64_t n) {
   const int64_t cus = device_cu_count();
   const int64_t tiles_m = (m + BM - 1) / BM;
   auto cost = [&](int bn) { return (tiles_m * ((n + bn - 1) / bn) + cus - 1) / cus * bn; };
@@ -739,13 +739,13 @@ int gemm_tile_n(int64_t m, int64_t n, bool fp8) {
 template <Epilogue EPI, bool LORA>
 hipError_t launch_forward_like(const GemmArgs &args, hipStream_t stream) {
   if (args.fp8) {
-    switch (gemm_tile_n(args.m, args.n, true)) {
+    switch (gemm_tile_n(args.m, args.n)) {
       case 320: return launch_typed<EPI, 320, 4, 1, LORA, true>(args, stream);
       case 192: return launch_typed<EPI, 192, 4, 1, LORA, true>(args, stream);
       default: return launch_typed<EPI, 256, 2, 1, LORA, true>(args, stream);
     }
   }
-  switch (gemm_tile_n(args.m, args.n, false)) {
+  switch (gemm_tile_n(args.m, args.n)) {
     case 320: return launch_typed<EPI, 320, 4, 1, LORA>(args, stream);
     case 192: return launch_typed<EPI, 192, 4, 1, LORA>(args, stream);
     default: return launch_typed<EPI, 256, 2, 1, LORA>(args, stream);
