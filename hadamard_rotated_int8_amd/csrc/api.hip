@@ -26,7 +26,12 @@ int device_cu_count() {
 
 namespace {
 
-constexpr int64_t kMaxFeature = 65536;  // a whole row stays on chip in the rotate+quantize kernel
+// Feature dimensions of the weight gradient, the low-rank split and their kernels.
+constexpr int64_t kMaxFeature = 65536;
+// Feature dimensions of the linear layer's forward and input gradient: 127 * 127 *
+// K stays below 2^31 (exact int32 accumulators) up to K = 133144; the largest
+// multiple of 16 below it.  Rows above 65536 values are quantized in segments.
+constexpr int64_t kMaxLinearFeature = 133136;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -48,6 +53,12 @@ int32_t padded_rank(int32_t rank) { return (rank + 15) / 16 * 16; }
 sdnq_status_t check_feature(int64_t d) {
   if (d <= 0) return SDNQ_ERR_INVALID_ARG;
   if (d % 16 != 0 || d > kMaxFeature) return SDNQ_ERR_UNSUPPORTED;
+  return SDNQ_OK;
+}
+
+sdnq_status_t check_linear(int64_t d) {
+  if (d <= 0) return SDNQ_ERR_INVALID_ARG;
+  if (d % 16 != 0 || d > kMaxLinearFeature) return SDNQ_ERR_UNSUPPORTED;
   return SDNQ_OK;
 }
 
@@ -156,7 +167,7 @@ sdnq_status_t check_rotq(const void *x, int64_t m, int64_t k, int32_t g, const v
                          const void *s) {
   if (m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!x || !q || !s)) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(k));
+  SDNQ_TRY(check_linear(k));
   if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return SDNQ_ERR_INVALID_ARG;
   if (col_scale && !aligned16(col_scale)) return SDNQ_ERR_INVALID_ARG;
@@ -179,7 +190,7 @@ const char *sdnq_status_string(sdnq_status_t status) {
 }
 
 size_t sdnq_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t rank, int32_t is_backward) {
-  if (m < 0 || n <= 0 || k <= 0 || rank < 0) return 0;
+  if (m < 0 || check_linear(n) != SDNQ_OK || check_linear(k) != SDNQ_OK || rank < 0) return 0;
   if (rank > 0 && !valid_rank(rank)) return 0;
   return is_backward ? bwd_layout(m, n, k, rank).total : fwd_layout(m, n, k, rank).total;
 }
@@ -210,8 +221,8 @@ sdnq_status_t forward_quantized(bool fp8, const int8_t *qx, const float *x_scale
                                 void *workspace, size_t workspace_bytes, void *stream) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!qx || !x_scale || !y)) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(k));
-  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_linear(k));
+  SDNQ_TRY(check_linear(n));
   if (!aligned16(qx) || !aligned16(x_scale) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y))
     return SDNQ_ERR_INVALID_ARG;
   int32_t r = 0;
@@ -249,8 +260,8 @@ sdnq_status_t check_forward(const uint16_t *x, int64_t m, int64_t k, const int8_
                             const uint16_t *y, int32_t *r) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!x || !y)) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(k));
-  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_linear(k));
+  SDNQ_TRY(check_linear(n));
   if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y)) return SDNQ_ERR_INVALID_ARG;
   return check_lora(lora_a, lora_b, rank, r);
@@ -371,8 +382,8 @@ sdnq_status_t backward(bool fp8, bool qw_transposed, const uint16_t *dy, int64_t
                        void *workspace, size_t workspace_bytes, void *stream) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!dy || !dx)) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(k));
-  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_linear(k));
+  SDNQ_TRY(check_linear(n));
   if (!valid_group(g) || k % g != 0) return SDNQ_ERR_UNSUPPORTED;
   if (!aligned16(dy) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(dx)) return SDNQ_ERR_INVALID_ARG;
   int32_t r = 0;
@@ -496,8 +507,8 @@ sdnq_status_t sdnq_qlinear_backward_input_fp8_wt(const uint16_t *dy, int64_t m, 
 
 sdnq_status_t sdnq_transpose_codes(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out, void *stream) {
   if (!in || !out || rows < 0 || cols < 0) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(rows));
-  SDNQ_TRY(check_feature(cols));
+  SDNQ_TRY(check_linear(rows));
+  SDNQ_TRY(check_linear(cols));
   if (!aligned16(in) || !aligned16(out)) return SDNQ_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return launched(launch_transpose_i8(reinterpret_cast<const int8_t *>(in), rows, cols,
@@ -508,8 +519,8 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
                                int32_t *c, void *workspace, size_t workspace_bytes, void *stream) {
   if (!b || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!a || !c)) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(k));
-  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_linear(k));
+  SDNQ_TRY(check_linear(n));
   if (b_layout != 0 && b_layout != 1) return SDNQ_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return SDNQ_ERR_INVALID_ARG;
   if (b_layout == 1 && (!workspace || workspace_bytes < (size_t)k * (size_t)n || !aligned16(workspace)))
@@ -613,8 +624,8 @@ sdnq_status_t sdnq_gemm_fp8_f32(const uint8_t *a, const uint8_t *b, int64_t m, i
                                 void *stream) {
   if (!b || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!a || !c)) return SDNQ_ERR_INVALID_ARG;
-  SDNQ_TRY(check_feature(k));
-  SDNQ_TRY(check_feature(n));
+  SDNQ_TRY(check_linear(k));
+  SDNQ_TRY(check_linear(n));
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return SDNQ_ERR_INVALID_ARG;
   if (m == 0) return SDNQ_OK;
   (void)hipGetLastError();

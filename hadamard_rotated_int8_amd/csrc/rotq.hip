@@ -42,6 +42,7 @@ namespace {
 
 constexpr int kMaxRowsPerWg = 32;
 constexpr int kMaxThreads = 1024;
+constexpr int64_t kMaxCols = 256 * (kMaxThreads / 4);  // values a workgroup can hold: 65536
 // 1.5 * 2^23: adding it to |t| < 2^22 rounds t to an integer (ties to even) and
 // leaves that integer, two's complement, in the low mantissa bits.
 constexpr float kRoundMagic = 12582912.0f;
@@ -100,10 +101,19 @@ __device__ __forceinline__ void dpp_stage_xor2(float (&r)[8], float m) {
 // (dynamic shared memory), instead of re-read from L2 for every row.
 constexpr int64_t kColScaleLds = 16384;
 
-template <int G, bool COLSCALE, int MAXT, bool FP8>
+// Rows longer than one workgroup can hold (more than 65536 values) are cut into
+// `chunks` equal segments of `cols` values (whole rotation blocks each) and run
+// as the rows of a [rows * chunks, cols] view of the same memory, in phases:
+//   phase 1: each segment's max |y| is merged into scale[row] (binary32 bits,
+//            atomic max; scale zeroed first), nothing else is written;
+//   phase 2: the codes, from the row's max read back from scale[row];
+// then finish_scale_kernel turns the maxima into scales.  SEG = false is the
+// whole-row path (chunks = 1, phase 0).
+template <int G, bool COLSCALE, int MAXT, bool FP8, bool SEG = false>
 __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
-    int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg, int64_t groups) {
+    int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg, int64_t groups, int chunks,
+    int phase) {
   // Persistent: workgroup b handles row groups b, b + gridDim.x, ... and loads the
   // next group's values while it transforms the current one.  Row maxima go
   // through three rotating LDS slots: slot (it+1)%3 is cleared at the start of
@@ -123,7 +133,7 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
     row_max[1][tid] = 0u;
   }
   extern __shared__ __attribute__((aligned(16))) float cs_lds[];  // [cols] when staged
-  const bool cs_staged = COLSCALE && cols <= kColScaleLds;
+  const bool cs_staged = COLSCALE && !SEG && cols <= kColScaleLds;
   if (cs_staged) {
     for (int64_t c = 4 * tid; c < cols; c += 4 * blockDim.x)
       *reinterpret_cast<float4 *>(cs_lds + c) = *reinterpret_cast<const float4 *>(col_scale + c);
@@ -155,6 +165,11 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
   for (int it = 0; grp < groups; ++it, grp += gridDim.x) {
     const int64_t row = grp * rows_per_wg + r_local;
     const bool row_ok = row < rows;
+    int64_t full_row = row, col_off = 0;  // row of the matrix, first column of this segment
+    if constexpr (SEG) {
+      full_row = row / chunks;
+      col_off = (row - full_row * chunks) * cols;
+    }
     if (tid < rows_per_wg) row_max[(it + 1) % 3][tid] = 0u;
 
     float v[8][8];
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
       for (int i = 0; i < 8; ++i) {
         const int64_t e0 = base + 32 * i;
         if (e0 < cols) {
-          const float *cs = cs_staged ? cs_lds : col_scale;
+          const float *cs = cs_staged ? cs_lds : col_scale + col_off;
           const float4 c0 = *reinterpret_cast<const float4 *>(cs + e0);
           const float4 c1 = *reinterpret_cast<const float4 *>(cs + e0 + 4);
           v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
@@ -254,6 +269,13 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
     // LDS-only barrier: the prefetch of the next group stays in flight.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float a = __uint_as_float(slot[r_local]);
+    if constexpr (SEG) {
+      if (phase == 1) {  // segment maximum into the row's maximum
+        if (row_ok && qt == 0) atomicMax(reinterpret_cast<unsigned *>(scale) + full_row, __float_as_uint(a));
+        continue;
+      }
+      a = row_ok ? __uint_as_float(reinterpret_cast<const unsigned *>(scale)[full_row]) : 0.0f;
+    }
 
     // g = 64, 256: norm_const is a power of two, so a = fl32(max|u| * c) = max|fl32(u * c)|.
     if constexpr (G == 64 || G == 256) a = a * norm_const<G>();
@@ -265,7 +287,7 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const float up = tiny ? 0x1p100f : 1.0f;
     const float as = a * up;
     const float r = (as > 0.0f) ? kQMax / as : 0.0f;
-    if (row_ok && qt == 0) scale[row] = s;
+    if (!SEG && row_ok && qt == 0) scale[row] = s;
 
     // Multiplier turning the stored value into fl32(y * r).
     //  - g = 64/256, a >= 2^-100: y = u*c exactly for every value that can get a
@@ -322,6 +344,23 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
   }
 }
 
+// scale[row] = fl32(a / qmax) from the row maxima the segment phases left in
+// scale (binary32 bits), with the same normalization step as the whole-row path.
+template <int G, bool FP8>
+__global__ void finish_scale_kernel(float *__restrict__ scale, int64_t rows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows) return;
+  float a = scale[i];
+  if constexpr (G == 64 || G == 256) a = a * norm_const<G>();
+  constexpr float kQMax = FP8 ? 448.0f : 127.0f;
+  scale[i] = a / kQMax;
+}
+
+__global__ void zero_f32_kernel(float *__restrict__ out, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) out[i] = 0.0f;
+}
+
 // Rows per workgroup.  Smaller workgroups wait on fewer wavefronts at the per-group
 // barrier, which measured faster even with some idle lanes: a [4096, 10240] matrix
 // (160 lanes per row) took 24.7 us at one row per workgroup (three wavefronts, a
@@ -357,7 +396,7 @@ int pick_rows_per_wg(int t_row, int max_threads) {
 // Resident workgroups per CU for a kernel at a block size, cached per block size
 // (one atomic word holding both, so concurrent callers read a consistent pair).
 // (One atomic word holds block size, dynamic LDS in 16-byte units and the count.)
-template <int G, bool CS, int MAXT, bool FP8>
+template <int G, bool CS, int MAXT, bool FP8, bool SEG>
 int blocks_per_cu(int threads, size_t smem) {
   static std::atomic<uint64_t> cache[kMaxThreads / 4 + 1];
   std::atomic<uint64_t> &slot = cache[threads / 4];
@@ -365,7 +404,7 @@ int blocks_per_cu(int threads, size_t smem) {
   const uint64_t c = slot.load(std::memory_order_relaxed);
   if ((c >> 32) == key) return (int)(c & 0xffffffffu);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8>, threads, smem) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8, SEG>, threads, smem) !=
           hipSuccess ||
       n < 1)
     n = 1;
@@ -373,16 +412,46 @@ int blocks_per_cu(int threads, size_t smem) {
   return n;
 }
 
-template <int G, bool CS, int MAXT, bool FP8>
+template <int G, bool CS, int MAXT, bool FP8, bool SEG = false>
 hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
-                        float *scale, int t_row, int rpw, hipStream_t stream) {
+                        float *scale, int t_row, int rpw, hipStream_t stream, int chunks = 1, int phase = 0) {
   const int threads = rpw * t_row;
   const int64_t groups = (rows + rpw - 1) / rpw;
-  const size_t smem = (CS && cols <= kColScaleLds) ? (size_t)cols * 4 : 0;
-  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8>(threads, smem);
+  const size_t smem = (CS && !SEG && cols <= kColScaleLds) ? (size_t)cols * 4 : 0;
+  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8, SEG>(threads, smem);
   if (blocks > groups) blocks = groups;
-  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8>), dim3((unsigned)blocks), dim3(threads), smem, stream, x, rows,
-                     cols, col_scale, q, scale, t_row, rpw, groups);
+  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8, SEG>), dim3((unsigned)blocks), dim3(threads), smem, stream, x,
+                     rows, cols, col_scale, q, scale, t_row, rpw, groups, chunks, phase);
+  return hipGetLastError();
+}
+
+// Segments per row for rows above 65536 values: the fewest equal segments of at
+// most 65536 values that hold whole rotation blocks and keep 16-value alignment.
+int64_t row_segments(int64_t cols, int g) {
+  const int64_t unit = g > 16 ? g : 16;
+  for (int64_t c = (cols + kMaxCols - 1) / kMaxCols; c <= cols / unit; ++c)
+    if (cols % c == 0 && (cols / c) % unit == 0) return c;
+  return 0;
+}
+
+template <int G, bool CS, bool FP8>
+hipError_t launch_segmented(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
+                            float *scale, hipStream_t stream) {
+  const int64_t chunks = row_segments(cols, G);
+  if (chunks < 2) return hipErrorInvalidValue;
+  const int64_t seg = cols / chunks, vrows = rows * chunks;
+  const int t_row = 4 * (int)((seg + 255) / 256);
+  const int rpw = pick_rows_per_wg(t_row, kMaxThreads);
+  const unsigned fb = (unsigned)((rows + 255) / 256);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(fb), dim3(256), 0, stream, scale, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int phase = 1; phase <= 2; ++phase) {
+    e = launch_sized<G, CS, kMaxThreads, FP8, true>(x, vrows, seg, col_scale, q, scale, t_row, rpw, stream,
+                                                    (int)chunks, phase);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((finish_scale_kernel<G, FP8>), dim3(fb), dim3(256), 0, stream, scale, rows);
   return hipGetLastError();
 }
 
@@ -391,6 +460,7 @@ hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const flo
 template <int G, bool CS, bool FP8>
 hipError_t launch_typed(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale,
                         int8_t *q, float *scale, hipStream_t stream) {
+  if (cols > kMaxCols) return launch_segmented<G, CS, FP8>(x, rows, cols, col_scale, q, scale, stream);
   const int t_row = 4 * (int)((cols + 255) / 256);
   if (t_row <= 512) {
     const int rpw = pick_rows_per_wg(t_row, 512);

@@ -39,10 +39,13 @@
  *    error has written nothing.  Errors raised by a kernel that already started
  *    (a memory fault on a bad pointer) surface at the caller's next
  *    synchronization, as with any HIP kernel.
- *  - Shape limits: m >= 0; n, k >= 1; every feature dimension (k, n) must be a
- *    multiple of 16 and at most 65536 (a whole row is held on chip while its
- *    absmax is found; this also keeps 127*127*K far below 2^31, the int32
- *    accumulator bound); k % g == 0.
+ *  - Shape limits: m >= 0; n, k >= 1; every feature dimension (k, n) of the
+ *    linear layer must be a multiple of 16 and at most 133136, so that
+ *    127*127*K stays below 2^31 (exact int32 accumulators); k % g == 0.  Rows
+ *    of up to 65536 values are rotated and quantized with the whole row on
+ *    chip; longer rows in equal segments of whole blocks, in two passes (the
+ *    row's absmax first, then the codes).  The weight gradient, the low-rank
+ *    split and the attention keep their own limits (below).
  *  - m == 0 is an empty batch: pointers to buffers with m rows may be NULL, nothing
  *    is read, and the only work enqueued is zeroing grad_a / grad_b when the
  *    backward pass requests them (empty sums).
@@ -67,7 +70,7 @@ typedef enum {
     SDNQ_OK = 0,
     SDNQ_ERR_INVALID_ARG = 1,  /* null required pointer, negative or zero size, misaligned pointer */
     SDNQ_ERR_UNSUPPORTED = 2,  /* g not in {1,64,128,256}, k % g != 0, a feature dimension not a
-                                  multiple of 16 or above 65536, LoRA rank outside [1, 256] */
+                                  multiple of 16 or above its limit, LoRA rank outside [1, 256] */
     SDNQ_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than sdnq_workspace_bytes() */
     SDNQ_ERR_LAUNCH = 4        /* a kernel launch was rejected by the HIP runtime */
 } sdnq_status_t;
@@ -133,7 +136,7 @@ sdnq_status_t sdnq_qlinear_backward_input(const uint16_t *dy, int64_t m, int64_t
                                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Byte transpose of weight codes (int8 or E4M3): out[cols, rows] = in[rows, cols]^T,
- * rows and cols multiples of 16, at most 65536; in and out 16-byte aligned, not
+ * rows and cols multiples of 16, at most 133136; in and out 16-byte aligned, not
  * overlapping.  The input gradient reads the codes across their rows; during
  * adapter training the quantized weight is frozen ("ConvRot / Hadamard SDNQ",
  * "PEFT Behavior": the adapter trains on top of the frozen quantized base), so

@@ -109,7 +109,7 @@ def bwd(dy=A, m=4, n=256, qw=B, sw=C, k=256, g=256, x=None, la=None, lb=None, r=
     (dict(m=-1), INVALID), (dict(k=0), INVALID), (dict(k=-16), INVALID),
     (dict(g=32), UNSUPPORTED), (dict(g=512), UNSUPPORTED), (dict(g=0), UNSUPPORTED),
     (dict(k=320, g=256), UNSUPPORTED), (dict(k=200, g=1), UNSUPPORTED),
-    (dict(k=65536 + 256, g=256), UNSUPPORTED),
+    (dict(k=133120 + 256, g=256), UNSUPPORTED), (dict(k=133136 + 16, g=1), UNSUPPORTED),  # the int32 bound
     (dict(x=A + 8), INVALID), (dict(q=B + 4), INVALID), (dict(s=C + 2), INVALID),
     (dict(g=1, cs=D + 4), INVALID),
     (dict(m=0), OK),
@@ -179,7 +179,7 @@ def test_transposed_weight_entry_points_validate():
     assert L.sdnq_transpose_codes(A, 32, 32, None, None) == INVALID
     assert L.sdnq_transpose_codes(A, 0, 32, B, None) == INVALID
     assert L.sdnq_transpose_codes(A, 24, 32, B, None) == UNSUPPORTED
-    assert L.sdnq_transpose_codes(A, 32, 65552, B, None) == UNSUPPORTED
+    assert L.sdnq_transpose_codes(A, 32, 133152, B, None) == UNSUPPORTED
     assert L.sdnq_transpose_codes(A + 8, 32, 32, B, None) == INVALID
     for fn in (L.sdnq_qlinear_backward_input_wt, L.sdnq_qlinear_backward_input_fp8_wt):
         # dy, m, n, qw_t, w_scale, k, g, x, lora_a, lora_b, rank, scale, dx, ga, gb, ws, wsb, stream

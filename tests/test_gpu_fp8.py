@@ -73,7 +73,8 @@ def assert_rq8_exact(x_bits, g, col_scale=None):
 
 
 @pytest.mark.parametrize("g,m,k", [(256, 64, 512), (256, 37, 3072), (128, 19, 1152), (64, 33, 320),
-                                   (1, 40, 272), (256, 3, 40960), (64, 2, 65536), (256, 9000, 3840)])
+                                   (1, 40, 272), (256, 3, 40960), (64, 2, 65536), (256, 9000, 3840),
+                                   (256, 2, 98304), (64, 3, 133120)])
 def test_fp8_rotate_quantize_bit_exact(g, m, k):
     assert_rq8_exact(synth.make_linear(m, k, 16, seed=300 + g + m)["x"], g)
 

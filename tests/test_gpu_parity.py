@@ -101,6 +101,8 @@ def assert_rq_exact(x_bits, g, col_scale=None):
     (64, 33, 320), (64, 5, 64), (64, 70, 3072), (64, 9, 192),
     (1, 11, 16), (1, 21, 48), (1, 40, 272), (1, 64, 3072),
     (256, 3, 40960), (64, 2, 65536),        # rows longer than 32768 values: 1024-thread workgroups
+    # rows longer than 65536 values, quantized in 2, 3 and 4 segments of whole blocks
+    (256, 3, 98304), (128, 2, 65664), (64, 2, 133120), (1, 3, 100000),
 ])
 def test_rotate_quantize_bit_exact(g, m, k):
     x = synth.make_linear(m, k, 16, seed=100 + g + m)["x"]
@@ -114,7 +116,7 @@ def test_rotate_quantize_many_rows_bit_exact(g, m, k):
     assert_rq_exact(x, g)
 
 
-@pytest.mark.parametrize("k", [16, 272, 3072])
+@pytest.mark.parametrize("k", [16, 272, 3072, 100000])
 def test_rotate_quantize_column_scale_bit_exact(k):
     rng = np.random.default_rng(5 + k)
     dy = synth.to_bf16_bits(rng.standard_normal((29, k)).astype(np.float32) * 1e-3)
@@ -416,3 +418,20 @@ def test_backward_with_transposed_codes_is_the_same_call(fp8):
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+# ------------------------------------------------- the int32 bound on K --
+
+def test_forward_at_the_largest_contraction_is_bit_exact():
+    """K = 133120 (the largest multiple of 256 with 127 * 127 * K < 2^31): the
+    rows are quantized in segments and the int32 accumulators stay exact."""
+    y, ref = forward_case(64, 133120, 256, 256, seed=31)
+    assert np.array_equal(y, ref["y"]), f"rel-L2 {rel_l2(y, ref['y']):.3e}"
+
+
+def test_backward_with_rows_above_65536_is_bit_exact():
+    """n = 100000: dY rows are folded and quantized in two segments, and n is the
+    GEMM's contraction."""
+    inp, (dx, _, _), ref, swo = backward_case(48, 100000, 256, 64, seed=32)
+    assert np.array_equal(dx, ref["dx"]), f"dx rel-L2 {rel_l2(dx, ref['dx']):.3e}"
+    assert_rq_exact(inp["dy"], 1, swo)
