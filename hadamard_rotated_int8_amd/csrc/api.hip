@@ -293,16 +293,17 @@ sdnq_status_t forward(bool fp8, const uint16_t *x, int64_t m, int64_t k, const i
     uint16_t *t = reinterpret_cast<uint16_t *>(ws_at(workspace, L.t));
     uint16_t *at = reinterpret_cast<uint16_t *>(ws_at(workspace, L.at));
     uint16_t *bt = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bt));
-    const uint16_t *bsrc = lora_b;
-    SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));           // A [k, r] -> A^T [r, k]
-    if (rp != r) {
+    if (rp == r) {
+      // A [k, r] -> A^T [r, k] and B [r, n] -> B^T [n, r] in one launch
+      SDNQ_LAUNCH(launch_transpose_u16_pair(lora_a, k, r, at, lora_b, r, n, bt, s));
+    } else {
       uint16_t *bp = reinterpret_cast<uint16_t *>(ws_at(workspace, L.bp));
+      SDNQ_LAUNCH(launch_transpose_u16(lora_a, k, r, at, s));                           // A^T [r, k]
       SDNQ_LAUNCH(launch_fill_zero_u16(at + (int64_t)r * k, (int64_t)(rp - r) * k, s));  // A^T [rp, k]
       SDNQ_LAUNCH(launch_copy2d_u16(lora_b, r, n, bp, rp, n, s));                       // B [rp, n]
-      bsrc = bp;
+      SDNQ_LAUNCH(launch_transpose_u16(bp, rp, n, bt, s));                              // B^T [n, rp]
     }
     SDNQ_LAUNCH(launch_lora_down(x, m, k, at, rp, lora_scale, t, s));  // t = bf16(scale * x A)
-    SDNQ_LAUNCH(launch_transpose_u16(bsrc, rp, n, bt, s));            // B [rp, n] -> B^T [n, rp]
     ga.lora_t = t; ga.lora_r = bt; ga.rank = rp;
   }
   return launched(launch_gemm_i8(Epilogue::kForward, ga, s));

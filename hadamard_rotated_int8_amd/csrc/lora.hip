@@ -14,12 +14,9 @@ namespace sdnq {
 namespace {
 
 // ----------------------------------------------------------- lora_down --
-// A workgroup handles 16*TT tokens with 4*HV wavefronts: HV groups of 4 take
-// 16*TT/HV tokens each, and the 4 wavefronts of a group split the contraction,
-// each keeping (16*TT/HV) x rank fp32 partial sums, which are added in
-// wavefront order through LDS.  (HV > 1 doubles the wavefronts in flight per CU
-// at the same tokens per workgroup, but each wavefront then reads the whole
-// factor for half as many tokens; the launches below use HV = 1.)
+// A workgroup of 4 wavefronts handles 16*TT tokens; each wavefront takes a
+// quarter of the contraction and keeps 16*TT x rank fp32 partial sums, which are
+// added in wavefront order through LDS.
 // MFMA 16x16x32: row operand = R rows (rank index), column operand = x rows
 // (token), so lane l owns token l % 16 and the four consecutive rank indices
 // 4 * (l / 16) + 0..3 of each 16 x 16 tile.  The contraction is walked in batches
@@ -39,11 +36,10 @@ struct DownJob {
   int64_t blocks;        // workgroups of this job
 };
 
-template <int RT, int TT, int HV>  // RT = rank / 16, TT = tokens / 16, HV token groups
-__global__ __launch_bounds__(256 * HV) void lora_down_kernel(DownJob j0, DownJob j1, int64_t m, int64_t out_stride) {
-  constexpr int TG = TT / HV;  // 16-token subtiles per group
-  static_assert(TT % HV == 0, "whole subtiles per group");
-  __shared__ v4f red[HV][4][TG][RT][64];
+template <int RT, int TT>  // RT = rank / 16, TT = tokens / 16
+__global__ __launch_bounds__(256) void lora_down_kernel(DownJob j0, DownJob j1, int64_t m, int64_t out_stride) {
+  constexpr int TG = TT;  // 16-token subtiles
+  __shared__ v4f red[4][TG][RT][64];
   // the first j0.blocks workgroups compute job 0, the others job 1
   const bool second = (int64_t)blockIdx.x >= j0.blocks;
   const uint16_t *__restrict__ x = second ? j1.x : j0.x;
@@ -53,8 +49,8 @@ __global__ __launch_bounds__(256 * HV) void lora_down_kernel(DownJob j0, DownJob
   uint16_t *__restrict__ out = second ? j1.out : j0.out;
   const int64_t blk = second ? blockIdx.x - j0.blocks : blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = wave >> 2, wq = wave & 3;  // token group, contraction quarter
-  const int64_t t0 = blk * (16 * TT) + grp * (16 * TG);
+  const int wq = wave;  // contraction quarter
+  const int64_t t0 = blk * (16 * TT);
 
   // contraction range of this wavefront, in steps of 32
   const int64_t steps = (cols + 31) / 32;
@@ -104,17 +100,16 @@ __global__ __launch_bounds__(256 * HV) void lora_down_kernel(DownJob j0, DownJob
 #pragma unroll
   for (int s = 0; s < TG; ++s)
 #pragma unroll
-    for (int u = 0; u < RT; ++u) red[grp][wq][s][u][lane] = acc[s][u];
+    for (int u = 0; u < RT; ++u) red[wq][s][u][lane] = acc[s][u];
   __syncthreads();
-  // wavefront wq of each group writes the group's token subtiles s = wq, wq + 4,
-  // ... (sums in wavefront order)
+  // wavefront wq writes token subtiles s = wq, wq + 4, ... (sums in wavefront order)
   for (int s = wq; s < TG; s += 4) {
     const int64_t t = t0 + s * 16 + (lane & 15);
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
-      v4f sum = red[grp][0][s][u][lane];
+      v4f sum = red[0][s][u][lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) sum = sum + red[grp][w][s][u][lane];
+      for (int w = 1; w < 4; ++w) sum = sum + red[w][s][u][lane];
       if (t < m) {
         const int r0 = u * 16 + 4 * (lane >> 4);
         uint2 packed;
@@ -452,10 +447,24 @@ __global__ void copy2d_u16_kernel(const uint16_t *__restrict__ in, int64_t in_ro
 constexpr int kT16 = 64;
 constexpr int kT16Pitch = kT16 + 4;  // in uint16
 
-__global__ __launch_bounds__(256) void transpose_u16_kernel(const uint16_t *__restrict__ in, int64_t rows,
-                                                            int64_t cols, uint16_t *__restrict__ out) {
+// One transpose of a launch (tiles = its 64 x 64 tiles, tiles_c of them per tile row).
+struct TJob {
+  const uint16_t *in;
+  int64_t rows, cols;
+  uint16_t *out;
+  int64_t tiles_c, tiles;
+};
+
+// The first j0.tiles workgroups transpose job 0, the others job 1.
+__global__ __launch_bounds__(256) void transpose_u16_kernel(TJob j0, TJob j1) {
   __shared__ __align__(16) uint16_t tile[kT16 * kT16Pitch];
-  const int64_t r0 = (int64_t)blockIdx.y * kT16, c0 = (int64_t)blockIdx.x * kT16;
+  const bool second = (int64_t)blockIdx.x >= j0.tiles;
+  const uint16_t *__restrict__ in = second ? j1.in : j0.in;
+  uint16_t *__restrict__ out = second ? j1.out : j0.out;
+  const int64_t rows = second ? j1.rows : j0.rows, cols = second ? j1.cols : j0.cols;
+  const int64_t tiles_c = second ? j1.tiles_c : j0.tiles_c;
+  const int64_t t = second ? blockIdx.x - j0.tiles : blockIdx.x;
+  const int64_t r0 = (t / tiles_c) * kT16, c0 = (t % tiles_c) * kT16;
   const int tid = threadIdx.x;
   v4u v[2];
 #pragma unroll
@@ -599,7 +608,7 @@ hipError_t launch_lora_down_staged(DownJob j0, DownJob j1, int64_t m, int rank, 
   }
 }
 
-template <int TT, int HV>
+template <int TT>
 hipError_t launch_lora_down_t(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride, hipStream_t stream) {
   const int64_t per_job = (m + 16 * TT - 1) / (16 * TT);
   j0.blocks = per_job;
@@ -608,7 +617,7 @@ hipError_t launch_lora_down_t(DownJob j0, DownJob j1, int64_t m, int rank, int64
   switch (rank / 16) {
 #define SDNQ_DOWN(RT)                                                                                        \
   case RT:                                                                                                   \
-    hipLaunchKernelGGL((lora_down_kernel<RT, TT, HV>), grid, dim3(256 * HV), 0, stream, j0, j1, m, out_stride); \
+    hipLaunchKernelGGL((lora_down_kernel<RT, TT>), grid, dim3(256), 0, stream, j0, j1, m, out_stride);         \
     break;
     SDNQ_DOWN(1) SDNQ_DOWN(2) SDNQ_DOWN(3) SDNQ_DOWN(4) SDNQ_DOWN(5) SDNQ_DOWN(6) SDNQ_DOWN(7) SDNQ_DOWN(8)
 #undef SDNQ_DOWN
@@ -633,8 +642,8 @@ hipError_t launch_lora_down2(const uint16_t *x0, int64_t cols0, const uint16_t *
     const DownJob j1{x1, cols1, x1 ? rmat1 + (int64_t)r0 * cols1 : nullptr, scale1, x1 ? out1 + r0 : nullptr, 0};
     const int64_t staged_blocks = (x1 ? 2 : 1) * ((m + kStagedTokens - 1) / kStagedTokens);
     const hipError_t e = staged_blocks >= device_cu_count() ? launch_lora_down_staged(j0, j1, m, rr, rank, stream)
-                         : m >= 16384                      ? launch_lora_down_t<4, 1>(j0, j1, m, rr, rank, stream)
-                                                           : launch_lora_down_t<2, 1>(j0, j1, m, rr, rank, stream);
+                         : m >= 16384                      ? launch_lora_down_t<4>(j0, j1, m, rr, rank, stream)
+                                                           : launch_lora_down_t<2>(j0, j1, m, rr, rank, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -701,12 +710,22 @@ hipError_t launch_transpose_i8(const int8_t *in, int64_t rows, int64_t cols, int
   return hipGetLastError();
 }
 
+hipError_t launch_transpose_u16_pair(const uint16_t *in0, int64_t rows0, int64_t cols0, uint16_t *out0,
+                                     const uint16_t *in1, int64_t rows1, int64_t cols1, uint16_t *out1,
+                                     hipStream_t stream) {
+  if (rows0 % 8 || cols0 % 8 || (in1 && (rows1 % 8 || cols1 % 8))) return hipErrorInvalidValue;
+  TJob j0{in0, rows0, cols0, out0, (cols0 + kT16 - 1) / kT16, 0};
+  j0.tiles = j0.tiles_c * ((rows0 + kT16 - 1) / kT16);
+  TJob j1{in1, rows1, cols1, out1, in1 ? (cols1 + kT16 - 1) / kT16 : 1, 0};
+  j1.tiles = in1 ? j1.tiles_c * ((rows1 + kT16 - 1) / kT16) : 0;
+  if (j0.tiles + j1.tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_u16_kernel, dim3((unsigned)(j0.tiles + j1.tiles)), dim3(256), 0, stream, j0, j1);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_u16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream) {
-  if (rows % 8 == 0 && cols % 8 == 0) {
-    const dim3 grid((unsigned)((cols + kT16 - 1) / kT16), (unsigned)((rows + kT16 - 1) / kT16));
-    hipLaunchKernelGGL(transpose_u16_kernel, grid, dim3(256), 0, stream, in, rows, cols, out);
-    return hipGetLastError();
-  }
+  if (rows % 8 == 0 && cols % 8 == 0)
+    return launch_transpose_u16_pair(in, rows, cols, out, nullptr, 0, 0, nullptr, stream);
   const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
   hipLaunchKernelGGL((transpose_kernel<uint16_t, 32>), grid, dim3(256), 0, stream, in, rows, cols, out);
   return hipGetLastError();

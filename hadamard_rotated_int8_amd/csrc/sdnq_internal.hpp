@@ -73,6 +73,10 @@ hipError_t launch_transpose_i8(const int8_t *in, int64_t rows, int64_t cols, int
 // 16-bit [rows, cols] -> [cols, rows]
 hipError_t launch_transpose_u16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out,
                                 hipStream_t stream);
+// two such transposes in one launch (in1 == nullptr: only the first); sides multiples of 8
+hipError_t launch_transpose_u16_pair(const uint16_t *in0, int64_t rows0, int64_t cols0, uint16_t *out0,
+                                     const uint16_t *in1, int64_t rows1, int64_t cols1, uint16_t *out1,
+                                     hipStream_t stream);
 // bf16 [rows, cols] -> bf16(scale * in)^T [cols, rows]
 hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t cols, float scale,
                                        uint16_t *out, hipStream_t stream);
