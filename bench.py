@@ -493,6 +493,8 @@ def main():
                      "timing": "median over 5 passes (alternating kernel order) of the mean launch duration "
                                "over max(K, 50) back-to-back launches between two HIP events on the launch stream",
                      "achieved_in_step_events": round(in_step_tops, 1),
+                     "per_launch_frac": [round(ops_up / (avg_ms[1] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                                         round(ops_down / (avg_ms[3] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)],
                      "per_launch_ops": [ops_up, ops_down]},
         "rotate_quantize_roofline": {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": HBM_PEAK_GBS,
                                      "unit": "GB/s", "frac": round(rot_gbs / HBM_PEAK_GBS, 4),
