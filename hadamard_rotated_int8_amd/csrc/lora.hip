@@ -122,18 +122,20 @@ __global__ __launch_bounds__(256) void lora_down_kernel(DownJob j0, DownJob j1, 
 }
 
 // ------------------------------------------------------ lora_down (staged) --
-// The same projection for many tokens, with the contraction staged through LDS
-// like the int8 GEMM's: a workgroup of 4 wavefronts computes 128 tokens x the
-// whole rank slice (each wavefront 32 tokens x rank), 64 columns (128 bytes of
-// every row) per k-tile.  A stage holds the 128 x rows, then the rank rows of
-// rmat, 128 bytes each, filled by direct-to-LDS buffer loads of 1 KB (8 rows)
-// in a 3-stage ring; 16-byte chunk c of row r is stored at c ^ (r & 7).  The
-// factor is read once per 128 tokens (the register-loading kernel above reads
-// it once per 64), and every load moves whole 128-byte lines.
+// The same projection with the contraction staged through LDS like the int8
+// GEMM's: a workgroup of W wavefronts computes 32 W tokens x the whole rank
+// slice (each wavefront 32 tokens x rank), 64 columns (128 bytes of every row)
+// per k-tile.  A stage holds the x rows, then the rank rows of rmat, 128 bytes
+// each, filled by direct-to-LDS buffer loads of 1 KB (8 rows) in a 3-stage
+// ring; 16-byte chunk c of row r is stored at c ^ (r & 7).  Every load moves
+// whole 128-byte lines.  W = 4 (the factor read once per 128 tokens) when that
+// still gives every CU a workgroup, else W = 2.  With fewer tokens the
+// register-loading kernel is used: one wavefront per workgroup could not hide
+// the load latency (8192 x 3072, rank 32: 15.4 against 14.2 us), while at 16384
+// tokens two wavefronts already win (rank 64: 20.3 against 28.6 us).
 // MFMA 32x32x16 bf16: row operand = rmat rows (rank), column operand = x rows
 // (tokens); lane l ends up with token l % 32 and ranks 8 (r / 4) + 4 (l / 32) +
 // r % 4 of each 32-rank block.
-constexpr int kStagedTokens = 128;
 constexpr int kStagedStages = 3;
 
 // one 16-byte direct-to-LDS load per lane (a plain function: issued from the
@@ -143,12 +145,16 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t *d
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off, 0, 0, 0);
 }
 
-template <int RB>  // ceil(rank / 32) of the slice (1 .. 4); ranks past `rank` read zeros and are not stored
-__global__ __launch_bounds__(256) void lora_down_staged_kernel(DownJob j0, DownJob j1, int64_t m, int rank,
-                                                               int64_t out_stride) {
+// RB = ceil(rank / 32) of the slice (1 .. 4; ranks past `rank` read zeros and are
+// not stored); W = wavefronts, each 32 tokens
+template <int RB, int W>
+__global__ __launch_bounds__(64 * W) void lora_down_staged_kernel(DownJob j0, DownJob j1, int64_t m, int rank,
+                                                                  int64_t out_stride) {
+  constexpr int kStagedTokens = 32 * W;
   constexpr int kRows = kStagedTokens + 32 * RB;  // staged rows per k-tile
   constexpr int kStage = kRows * 128;
-  constexpr int kLpw = kRows / 8 / 4;             // 1 KB loads per wavefront per k-tile
+  constexpr int kLpw = kRows / 8 / W;             // 1 KB loads per wavefront per k-tile
+  static_assert(kRows % (8 * W) == 0, "every wavefront issues the same number of loads");
   constexpr int kXGroups = kStagedTokens / 8;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStagedStages * kStage];
   const bool second = (int64_t)blockIdx.x >= j0.blocks;
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(256) void lora_down_staged_kernel(DownJob j0, DownJ
   const int64_t rows_x = (m - t0) < kStagedTokens ? (m - t0) : kStagedTokens;
   const int64_t row_bytes = cols * 2;
 
-  // slot j of wavefront w loads group g = 4 j + w: x rows 8 g .. (g < kXGroups),
+  // slot j of wavefront w loads group g = W j + w: x rows 8 g .. (g < kXGroups),
   // else rmat rows 8 (g - kXGroups) ..; lane i lands at byte 16 i of the group:
   // row 8 g + i / 8, stored chunk i % 8, holding logical chunk (i & 7) ^ (i >> 3)
   const __amdgpu_buffer_rsrc_t rs_x =
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(256) void lora_down_staged_kernel(DownJob j0, DownJ
   unsigned voff[kLpw];
 #pragma unroll
   for (int j = 0; j < kLpw; ++j) {
-    const int g = 4 * j + wave;
+    const int g = W * j + wave;
     const int row = 8 * (g < kXGroups ? g : g - kXGroups) + (lane >> 3);
     voff[j] = (unsigned)(row * row_bytes + 16 * lc);
   }
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(256) void lora_down_staged_kernel(DownJob j0, DownJ
     uint8_t *base = smem + (kt % kStagedStages) * kStage;
 #pragma unroll
     for (int j = 0; j < kLpw; ++j) {
-      const int g = 4 * j + wave;
+      const int g = W * j + wave;
       load_lds16(g < kXGroups ? rs_x : rs_r, base + g * 1024, (voff[j] + k0) | oob);
     }
   };
@@ -586,26 +592,36 @@ hipError_t launch_transpose_scale_bf16(const uint16_t *in, int64_t rows, int64_t
   return hipGetLastError();
 }
 
-template <int RB>
+template <int RB, int W>
 hipError_t launch_lora_down_staged_t(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride,
                                      hipStream_t stream) {
-  const int64_t per_job = (m + kStagedTokens - 1) / kStagedTokens;
+  const int64_t per_job = (m + 32 * W - 1) / (32 * W);
   j0.blocks = per_job;
   j1.blocks = j1.x ? per_job : 0;
-  hipLaunchKernelGGL((lora_down_staged_kernel<RB>), dim3((unsigned)(j0.blocks + j1.blocks)), dim3(256), 0, stream, j0,
-                     j1, m, rank, out_stride);
+  hipLaunchKernelGGL((lora_down_staged_kernel<RB, W>), dim3((unsigned)(j0.blocks + j1.blocks)), dim3(64 * W), 0,
+                     stream, j0, j1, m, rank, out_stride);
   return hipGetLastError();
 }
 
-hipError_t launch_lora_down_staged(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride,
-                                  hipStream_t stream) {
+template <int W>
+hipError_t launch_lora_down_staged_w(DownJob j0, DownJob j1, int64_t m, int rank, int64_t out_stride,
+                                     hipStream_t stream) {
   switch ((rank + 31) / 32) {
-    case 1: return launch_lora_down_staged_t<1>(j0, j1, m, rank, out_stride, stream);
-    case 2: return launch_lora_down_staged_t<2>(j0, j1, m, rank, out_stride, stream);
-    case 3: return launch_lora_down_staged_t<3>(j0, j1, m, rank, out_stride, stream);
-    case 4: return launch_lora_down_staged_t<4>(j0, j1, m, rank, out_stride, stream);
+    case 1: return launch_lora_down_staged_t<1, W>(j0, j1, m, rank, out_stride, stream);
+    case 2: return launch_lora_down_staged_t<2, W>(j0, j1, m, rank, out_stride, stream);
+    case 3: return launch_lora_down_staged_t<3, W>(j0, j1, m, rank, out_stride, stream);
+    case 4: return launch_lora_down_staged_t<4, W>(j0, j1, m, rank, out_stride, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Wavefronts per workgroup of the staged kernel: the most (4 or 2) that still
+// give every CU a workgroup, or 0 when even 2 would not (the register kernel then).
+int staged_waves(int64_t m, int64_t jobs) {
+  const int64_t cus = device_cu_count();
+  if (jobs * ((m + 127) / 128) >= cus) return 4;
+  if (jobs * ((m + 63) / 64) >= cus) return 2;
+  return 0;
 }
 
 template <int TT>
@@ -626,12 +642,11 @@ hipError_t launch_lora_down_t(DownJob j0, DownJob j1, int64_t m, int rank, int64
   return hipGetLastError();
 }
 
-// 64 tokens per workgroup of 4 wavefronts when there are enough tokens to fill
-// the chip that way (the rank x cols factor is then re-read from L2 half as
-// often), else 32.  (Splitting the 64 tokens over two groups of 4 wavefronts
-// doubles the factor's fragment reads per MFMA: 29.6 -> 40 us on 16384 x 3072,
-// rank 64.)  Ranks above kMaxRank run as launches over consecutive slices of at
-// most kMaxRank rows of rmat, each writing its columns of out.
+// The staged kernel when its workgroups of 2 or 4 wavefronts fill the chip,
+// else the register-loading one with 64 tokens per workgroup when that fills it
+// (the rank x cols factor is then re-read from L2 half as often) or 32.  Ranks
+// above kMaxRank run as launches over consecutive slices of at most kMaxRank
+// rows of rmat, each writing its columns of out.
 hipError_t launch_lora_down2(const uint16_t *x0, int64_t cols0, const uint16_t *rmat0, float scale0, uint16_t *out0,
                              const uint16_t *x1, int64_t cols1, const uint16_t *rmat1, float scale1, uint16_t *out1,
                              int64_t m, int rank, hipStream_t stream) {
@@ -640,10 +655,11 @@ hipError_t launch_lora_down2(const uint16_t *x0, int64_t cols0, const uint16_t *
     const int rr = rank - r0 < kMaxRank ? rank - r0 : kMaxRank;
     const DownJob j0{x0, cols0, rmat0 + (int64_t)r0 * cols0, scale0, out0 + r0, 0};
     const DownJob j1{x1, cols1, x1 ? rmat1 + (int64_t)r0 * cols1 : nullptr, scale1, x1 ? out1 + r0 : nullptr, 0};
-    const int64_t staged_blocks = (x1 ? 2 : 1) * ((m + kStagedTokens - 1) / kStagedTokens);
-    const hipError_t e = staged_blocks >= device_cu_count() ? launch_lora_down_staged(j0, j1, m, rr, rank, stream)
-                         : m >= 16384                      ? launch_lora_down_t<4>(j0, j1, m, rr, rank, stream)
-                                                           : launch_lora_down_t<2>(j0, j1, m, rr, rank, stream);
+    const int w = staged_waves(m, x1 ? 2 : 1);
+    const hipError_t e = w == 4       ? launch_lora_down_staged_w<4>(j0, j1, m, rr, rank, stream)
+                         : w == 2     ? launch_lora_down_staged_w<2>(j0, j1, m, rr, rank, stream)
+                         : m >= 16384 ? launch_lora_down_t<4>(j0, j1, m, rr, rank, stream)
+                                      : launch_lora_down_t<2>(j0, j1, m, rr, rank, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
