@@ -52,8 +52,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;    // the softmax offset moves when the maximum grows past 2^8
 constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128))
 
-__device__ __forceinline__ float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
 // ---- Prep ----------------------------------------------------------------
 // Rows of D values are handled by groups of 4 lanes: lane j of a group holds
 // elements 32a + 8j + b (a < D/32, b < 8), loaded as D/32 runs of 8 bf16.  The
