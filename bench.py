@@ -422,6 +422,35 @@ def main():
             b2b[p, j] = e0.elapsed_time(e1) / n_char
     avg_ms = np.median(b2b, axis=0)
 
+    # GEMM ceiling: the same kernel with the global loads of its k loop removed
+    # (mode 1), then also its LDS fragment reads (mode 2: the MFMA instructions
+    # alone, on operand bytes of the real codes), timed like the launches above in
+    # 3 passes of alternating order.  Mode 0 is the product launch itself.
+    y_ceil = [torch.empty_like(y_up), torch.empty_like(y_down)]
+    ceil_args = [(qx, sx, M, K_UP, qw_up, sw_up, N_UP), (qh, shh, M, K_DOWN, qw_down, sw_down, N_DOWN)]
+
+    def ceiling_call(mode, i):
+        a, sa, m, k, b, sb, n = ceil_args[i]
+        return lambda: check(L.sdnq_gemm_i8_ceiling(P(a), P(sa), m, k, P(b), P(sb), n, mode, P(y_ceil[i]), sp),
+                             f"gemm ceiling mode {mode}")
+
+    ceil_jobs = [(mode, i) for mode in (0, 1, 2) for i in (0, 1)]
+    ceil = np.zeros((3, len(ceil_jobs)))
+    for p in range(3):
+        for j in (range(len(ceil_jobs)) if p % 2 == 0 else reversed(range(len(ceil_jobs)))):
+            c = ceiling_call(*ceil_jobs[j])
+            for _ in range(5):
+                c()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n_char):
+                c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ceil[p, j] = e0.elapsed_time(e1) / n_char
+    ceil_ms = np.median(ceil, axis=0).reshape(3, 2)
+    del y_ceil
+
     # per-kernel times inside steps: n_char steps with HIP events on the launch
     # stream between the kernels (each event pair adds about 5 us to the kernel
     # it brackets)
@@ -505,6 +534,16 @@ def main():
                                      "timing": "median over 5 passes (alternating kernel order) of the mean launch "
                                                "duration over max(K, 50) back-to-back launches between two "
                                                "HIP events on the launch stream"},
+        "gemm_ceiling": {
+            "entry_point": "sdnq_gemm_i8_ceiling (the forward GEMM kernel with parts of its k loop removed)",
+            "modes": ["0: the product kernel", "1: no global loads in the k loop (MFMA + LDS fragment reads)",
+                      "2: no global loads and no LDS reads (MFMA instructions on the first fragments' bytes)"],
+            "us_up_down": [[round(float(v) * 1e3, 2) for v in ceil_ms[mode]] for mode in range(3)],
+            "frac_of_peak_up_down": [[round(ops / (float(v) * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+                                      for ops, v in zip((ops_up, ops_down), ceil_ms[mode])] for mode in range(3)],
+            "product_over_mode2": [round(float(ceil_ms[2, i] / ceil_ms[0, i]), 4) for i in range(2)],
+            "timing": "median over 3 passes (alternating order) of the mean launch duration over max(K, 50) "
+                      "back-to-back launches between two HIP events on the launch stream"},
         "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
         "kernel_back_to_back_passes_us": {k: [round(float(v) * 1e3, 2) for v in b2b[:, j]]
                                           for j, k in enumerate(kernels)},

@@ -50,6 +50,7 @@ def lib() -> ctypes.CDLL:
         "sdnq_qlinear_backward_input_fp8_wt": [p, i64, i64, p, p, i64, i32, p, p, p, i32, f32, p, p, p, p, sz, p],
         "sdnq_transpose_codes": [p, i64, i64, p, p],
         "sdnq_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p, sz, p],
+        "sdnq_gemm_i8_ceiling": [p, p, i64, i64, p, p, i64, i32, p, p],
         "sdnq_rotate_quantize_weight_fp8": [p, i64, i64, i32, p, p, p],
         "sdnq_rotate_quantize_act_fp8": [p, i64, i64, i32, p, p, p, p],
         "sdnq_qlinear_forward_fp8": [p, i64, i64, p, p, i64, i32, p, p, i32, f32, p, p, sz, p],
@@ -332,6 +333,20 @@ def sdnq_gemm_i8_i32(a, b, b_layout: int = 0, workspace=None):
     _check(lib().sdnq_gemm_i8_i32(_ptr(a), _ptr(b), m, n, k, b_layout, _ptr(c), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(a.device)), "sdnq_gemm_i8_i32")
     return c
+
+
+def sdnq_gemm_i8_ceiling(qx, x_scale, qw, w_scale, mode: int, y=None):
+    """The forward GEMM kernel with parts of its k loop removed (0: none, 1: global
+    loads, 2: also LDS reads); y [m,n] bf16 is the forward's only for mode 0."""
+    _need(qx, torch.int8, 2, "qx")
+    _need(qw, torch.int8, 2, "qw")
+    m, k = qx.shape
+    n = qw.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=qx.device)
+    _check(lib().sdnq_gemm_i8_ceiling(_ptr(qx), _ptr(x_scale), m, k, _ptr(qw), _ptr(w_scale), n, mode, _ptr(y),
+                                      _stream(qx.device)), "sdnq_gemm_i8_ceiling")
+    return y
 
 
 def sdnq_gemm_fp8_f32(a, b):

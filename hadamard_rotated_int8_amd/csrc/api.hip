@@ -540,6 +540,24 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
   return launched(launch_gemm_i8(Epilogue::kInt32, ga, s));
 }
 
+sdnq_status_t sdnq_gemm_i8_ceiling(const int8_t *qx, const float *x_scale, int64_t m, int64_t k, const int8_t *qw,
+                                   const float *w_scale, int64_t n, int32_t mode, uint16_t *y, void *stream) {
+  if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
+  if (m > 0 && (!qx || !x_scale || !y)) return SDNQ_ERR_INVALID_ARG;
+  if (mode < 0 || mode > 2) return SDNQ_ERR_INVALID_ARG;
+  SDNQ_TRY(check_linear(k));
+  SDNQ_TRY(check_linear(n));
+  if (!aligned16(qx) || !aligned16(x_scale) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y))
+    return SDNQ_ERR_INVALID_ARG;
+  if (m == 0) return SDNQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  GemmArgs ga{};
+  ga.a = qx; ga.b = qw; ga.m = m; ga.n = n; ga.k = k;
+  ga.row_scale = x_scale; ga.col_scale = w_scale; ga.out_bf16 = y; ga.g = 1;
+  return launched(launch_gemm_i8_ceiling(ga, mode, s));
+}
+
 // ----------------------------------------------------- weight gradient --
 size_t sdnq_weight_grad_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || check_feature(n) != SDNQ_OK || check_feature(k) != SDNQ_OK) return 0;

@@ -149,8 +149,13 @@ __device__ __forceinline__ float acc_f32(int v) { return (float)v; }
 __device__ __forceinline__ float acc_f32(float v) { return v; }
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8>
+// DIAG (the ceiling diagnostic; 0 in every product launch): 1 drops the k loop's
+// global loads after the first two k-tiles, so every k-tile multiplies what those
+// left in LDS; 2 also drops the LDS reads, so every MFMA multiplies the fragments
+// of the first k-step, held in registers.  Prologue and epilogue are unchanged.
+template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8, int DIAG = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  static_assert(DIAG == 0 || (EPI == Epilogue::kForward && !LORA && !FP8), "diagnostic modes: int8 forward only");
   using Cfg = TileCfg<BN>;
   constexpr int kStageBytes = Cfg::kStageBytes;
   constexpr int LPW = Cfg::kLoadsPerWave;
@@ -279,12 +284,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   struct Frags {
     v4i a[SM], b[SN];
   };
+  Frags fkeep;
   auto read_frags = [&](int kt, int kk, Frags &f) {
+    if constexpr (DIAG == 2) {
+      if (kt > 0 || kk > 0) {
+        f = fkeep;
+        return;
+      }
+    }
     const int8_t *base = smem + (kt & (STAGES - 1)) * kStageBytes + frow + fcol[kk];
 #pragma unroll
     for (int i = 0; i < SM; ++i) f.a[i] = *reinterpret_cast<const v4i *>(base + (wm * TM + i * 32) * BK);
 #pragma unroll
     for (int j = 0; j < SN; ++j) f.b[j] = *reinterpret_cast<const v4i *>(base + BM * BK + (wn * TN + j * 32) * BK);
+    if constexpr (DIAG == 2) fkeep = f;
   };
 
   typedef typename AccOf<FP8>::type AccT;
@@ -406,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       mfma_all(f0);
       sched(0, SM + SN, T);
       wait_tile_and_barrier();
-      issue_next(kt + 2);
+      if constexpr (DIAG == 0) issue_next(kt + 2);
       read_frags(kt + 1, 0, f0);
       mfma_all(f1);
       sched(LPW, SM + SN, T);
@@ -689,12 +702,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   }
 }
 
-template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8 = false>
+template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8 = false, int DIAG = 0>
 hipError_t launch_typed(const GemmArgs &args, hipStream_t stream) {
   const int tiles_m = (int)((args.m + BM - 1) / BM);
   const int tiles_n = (int)((args.n + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<EPI, BN, WAVES_M, G, LORA, FP8>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
-                     stream, args, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_i8_kernel<EPI, BN, WAVES_M, G, LORA, FP8, DIAG>), dim3(tiles_m * tiles_n), dim3(kThreads),
+                     0, stream, args, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -752,7 +765,25 @@ hipError_t launch_forward_like(const GemmArgs &args, hipStream_t stream) {
   }
 }
 
+template <int DIAG>
+hipError_t launch_ceiling(const GemmArgs &args, hipStream_t stream) {
+  switch (gemm_tile_n(args.m, args.n)) {
+    case 320: return launch_typed<Epilogue::kForward, 320, 4, 1, false, false, DIAG>(args, stream);
+    case 192: return launch_typed<Epilogue::kForward, 192, 4, 1, false, false, DIAG>(args, stream);
+    default: return launch_typed<Epilogue::kForward, 256, 2, 1, false, false, DIAG>(args, stream);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemm_i8_ceiling(const GemmArgs &args, int mode, hipStream_t stream) {
+  switch (mode) {
+    case 0: return launch_ceiling<0>(args, stream);
+    case 1: return launch_ceiling<1>(args, stream);
+    case 2: return launch_ceiling<2>(args, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream) {
   switch (epi) {

@@ -189,6 +189,23 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
                                int32_t b_layout, int32_t *c, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Diagnostics: the rate ceiling of the forward GEMM kernel on the device it runs
+ * on.  Launches the kernel sdnq_qlinear_forward_quantized launches for these
+ * arguments without LoRA (same tiles, prologue and dequantization epilogue, same
+ * argument checks), with parts of its k loop removed:
+ *   mode 0: nothing removed; y is exactly sdnq_qlinear_forward_quantized's y;
+ *   mode 1: no global loads after the first two k-tiles: every k-tile multiplies
+ *           what those two left in LDS (y is meaningless);
+ *   mode 2: also no LDS reads: every MFMA multiplies the fragments of the first
+ *           k-step, held in registers (y is meaningless).
+ * Mode 2 issues the same MFMA instructions on operand bytes of the real codes
+ * with no data movement in the k loop: the kernel's rate on the device's clock
+ * and power budget when nothing but the matrix cores work.  SDNQ_ERR_INVALID_ARG
+ * for a mode outside 0..2; the other errors as sdnq_qlinear_forward_quantized. */
+sdnq_status_t sdnq_gemm_i8_ceiling(const int8_t *qx, const float *x_scale, int64_t m, int64_t k,
+                                   const int8_t *qw, const float *w_scale, int64_t n, int32_t mode,
+                                   uint16_t *y, void *stream);
+
 /* Weight gradient through the quantized matmul (full fine-tuning: "SDNQ: SD.Next
  * Quantization Engine", the training example runs the quantized matmul in the
  * backward pass and the feature list includes full-parameter quantized training):

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
               "sdnq_svd_quantize_weight", "sdnq_svd_workspace_bytes", "sdnq_svd_workspace_q_offset",
               "sdnq_attention_int8", "sdnq_attention_workspace_bytes", "sdnq_attention_workspace_offset",
               "sdnq_qlinear_forward_noalloc", "sdnq_qlinear_backward_input_fp8", "sdnq_transpose_codes",
-              "sdnq_qlinear_backward_input_wt", "sdnq_qlinear_backward_input_fp8_wt"):
+              "sdnq_qlinear_backward_input_wt", "sdnq_qlinear_backward_input_fp8_wt", "sdnq_gemm_i8_ceiling"):
         assert n in names
 
 
@@ -197,6 +197,13 @@ def test_gemm_validation():
     assert L.sdnq_gemm_i8_i32(A, B, 4, 30, 32, 0, C, None, 0, None) == UNSUPPORTED
     assert L.sdnq_gemm_i8_i32(A, B, 4, 32, 32, 1, C, None, 0, None) == WORKSPACE
     assert L.sdnq_gemm_i8_i32(A, B, 0, 32, 32, 0, C, None, 0, None) == OK
+    # qx, x_scale, m, k, qw, w_scale, n, mode, y, stream
+    assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, B, C, 32, 3, D, None) == INVALID
+    assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, B, C, 32, -1, D, None) == INVALID
+    assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, None, C, 32, 0, D, None) == INVALID
+    assert L.sdnq_gemm_i8_ceiling(A, C, 4, 30, B, C, 32, 0, D, None) == UNSUPPORTED
+    assert L.sdnq_gemm_i8_ceiling(A + 8, C, 4, 32, B, C, 32, 0, D, None) == INVALID
+    assert L.sdnq_gemm_i8_ceiling(A, C, 0, 32, B, C, 32, 2, D, None) == OK
 
 
 def test_binding_rejects_wrong_types_before_calling():
