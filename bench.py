@@ -451,6 +451,28 @@ def main():
     ceil_ms = np.median(ceil, axis=0).reshape(3, 2)
     del y_ceil
 
+    # Same-traffic reference for rotate+quantize: a device-to-device copy that
+    # moves as many bytes as the kernel does for x and for h (3 bytes per element:
+    # 1.5 read and 1.5 written), timed the same way.
+    cp_n = [M * K_UP * 3 // 2, M * K_DOWN * 3 // 2]
+    cp_src = torch.empty(max(cp_n), dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cast_calls = [lambda: cp_dst[:cp_n[0]].copy_(cp_src[:cp_n[0]]), lambda: cp_dst[:cp_n[1]].copy_(cp_src[:cp_n[1]])]
+    cast = np.zeros((3, 2))
+    for p in range(3):
+        for j in ((0, 1) if p % 2 == 0 else (1, 0)):
+            for _ in range(5):
+                cast_calls[j]()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n_char):
+                cast_calls[j]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cast[p, j] = e0.elapsed_time(e1) / n_char
+    cast_ms = np.median(cast, axis=0)
+    del cp_src, cp_dst
+
     # per-kernel times inside steps: n_char steps with HIP events on the launch
     # stream between the kernels (each event pair adds about 5 us to the kernel
     # it brackets)
@@ -531,6 +553,13 @@ def main():
                                      "traffic_per_launch": rot_traffic,
                                      "per_launch_bytes": [M * K_UP * 3 + M * 4, M * K_DOWN * 3 + M * 4],
                                      "kernel": "rotq_kernel (x [4096, 3840], h [4096, 10240])",
+                                     "same_traffic_copy_us": [round(float(v) * 1e3, 2) for v in cast_ms],
+                                     "same_traffic_copy_frac": round(
+                                         (M * K_UP * 3 + M * K_DOWN * 3) / float(cast_ms.sum() * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+                                     "same_traffic_copy_note": "device-to-device copies moving the kernel's bytes "
+                                                               "for x and for h (1.5 bytes read and 1.5 written "
+                                                               "per element), timed like the kernel",
                                      "timing": "median over 5 passes (alternating kernel order) of the mean launch "
                                                "duration over max(K, 50) back-to-back launches between two "
                                                "HIP events on the launch stream"},

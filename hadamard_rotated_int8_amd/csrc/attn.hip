@@ -45,6 +45,20 @@
 namespace sdnq {
 namespace {
 
+// The maximum and the sum of a value over lanes l and l ^ 32 (the two halves of a
+// score row), with one v_permlane32_swap instead of an LDS-routed shuffle: the
+// swap of (v, v) gives s[0] = v of lane l % 32 and s[1] = v of lane l % 32 + 32.
+// The sum adds the lane's own value first, as own + partner.
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float lo = __uint_as_float(s[0]), hi = __uint_as_float(s[1]);
+  return (threadIdx.x & 32) ? hi + lo : lo + hi;
+}
+
 constexpr int kMeanBlock = 64;       // tokens per block of the K-mean sum
 constexpr int kBM = 128;             // query rows per workgroup
 constexpr int kBN = 64;              // keys per step
@@ -566,7 +580,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
         float mx = sv[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * qscale;
+        mx = xhalf_max(mx) * qscale;
         // Lazy reference: the exponent's offset m_run moves only when the row's
         // maximum exceeds it by more than kLazyLog2, so p <= 2^kLazyLog2 and the
         // running output is rescaled rarely.  softmax is unchanged: numerator and
@@ -605,7 +619,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
           pf[c] = __builtin_bit_cast(v8bf, packed);
         }
         float psum = psum2[0] + psum2[1];
-        psum += __shfl_xor(psum, 32);
+        psum = xhalf_sum(psum);
         l_run = l_run * alpha + psum;
         m_run = m_new;
         // rescale the running output only when some row's offset moved (alpha is
