@@ -90,6 +90,7 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
 
 struct BwdLayout {
   size_t qdy, sdy, wt, gr, tx, at, part, part2, bp, ap, gap, gbp, total;
+  int splits;  // token splits of the LoRA gradient reduction
 };
 BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
   BwdLayout L{};
@@ -102,7 +103,8 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int32_t rank) {
     L.gr = off; off += align_up((size_t)m * rp * 2);
     L.tx = off; off += align_up((size_t)m * rp * 2);
     L.at = off; off += align_up(rp * (size_t)k * 2);
-    const size_t splits = (size_t)lora_grad_splits(m);
+    L.splits = lora_grad_splits(m, lora_grad_tiles(k, n, (int64_t)rp));
+    const size_t splits = (size_t)L.splits;
     L.part = off; off += align_up(splits * rp * (size_t)k * 4);   // dA partials
     L.part2 = off; off += align_up(splits * rp * (size_t)n * 4);  // dB partials
     if (rp != (size_t)rank) {
@@ -455,11 +457,11 @@ sdnq_status_t backward(bool fp8, bool qw_transposed, const uint16_t *dy, int64_t
     uint16_t *dst_b = padded ? reinterpret_cast<uint16_t *>(ws_at(workspace, L.gbp)) : grad_b;
     if (want_ga && want_gb)
       SDNQ_LAUNCH(launch_lora_grad2(x, k, gr, 1.0f, false, part_a, dst_a, dy, n, tx, lora_scale, true, part_b, dst_b,
-                                    rp, m, s));
+                                    rp, m, L.splits, s));
     else if (want_ga)
-      SDNQ_LAUNCH(launch_lora_grad(x, k, gr, rp, m, 1.0f, false, part_a, dst_a, s));
+      SDNQ_LAUNCH(launch_lora_grad(x, k, gr, rp, m, 1.0f, false, part_a, dst_a, L.splits, s));
     else
-      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, rp, m, lora_scale, true, part_b, dst_b, s));
+      SDNQ_LAUNCH(launch_lora_grad(dy, n, tx, rp, m, lora_scale, true, part_b, dst_b, L.splits, s));
     if (padded && want_ga) SDNQ_LAUNCH(launch_copy2d_u16(dst_a, k, rp, grad_a, k, r, s));
     if (padded && want_gb) SDNQ_LAUNCH(launch_copy2d_u16(dst_b, rp, n, grad_b, r, n, s));
   }

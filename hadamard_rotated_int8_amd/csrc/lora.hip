@@ -6,7 +6,7 @@
 //                (t = x A with R = A^T, and g_r = scale * dY B^T with R = B);
 //  - lora_grad:  out[a, b] = bf16(scale * sum_t P[t, a] * Q[t, b])
 //                (dA = x^T g_r and dB = scale * t^T dY), reduced over tokens in
-//                fixed-size splits whose fp32 partials are summed in split order.
+//                equal splits whose fp32 partials are summed in split order.
 // All products run on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.
 #include "sdnq_internal.hpp"
 
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(64 * W) void lora_down_staged_kernel(DownJob j0, Do
 // P the wide operand (x or dY: a over 3072-ish features) and Q the narrow one
 // (g_r or t: b over the rank).  Workgroup tile: 128 (a) x 64 (b), 4 wavefronts
 // of 32 (a) x 64 (b) (two v_mfma_f32_32x32x16_bf16 accumulators each), over one
-// split of at most 1024 tokens, 64 tokens per step.
+// token split (lora_grad_splits), 64 tokens per step.
 // The contraction runs over tokens, the slow index of both P and Q, so the
 // tiles are staged row-major in LDS (direct-to-LDS buffer loads, a 3-stage
 // ring) and the MFMA operands are read with ds_read_b64_tr_b16: within each group of
@@ -266,7 +266,12 @@ constexpr int kGradSub = kGradTokens * 64 * 2;               // one 64 x 64 bf16
 constexpr int kGradStageBytes = (kGradA / 64 + 1) * kGradSub;  // P sub-tiles then the Q sub-tile
 constexpr int kGradBlocks = kGradStageBytes / 1024;          // 1 KB direct loads per stage
 constexpr int kMaxSplits = 16;
-constexpr int64_t kTokensPerSplit = 1024;
+// Splits per launch: enough for about this many workgroups (1.5 per CU of a
+// 256-CU chip).  On the 16384-token PEFT backward (48 column tiles) that is 8
+// splits of 2048 tokens: 298 us for the whole backward against 313 us with 16
+// splits of 1024 (a second, half-empty round of workgroups) and 302-314 us with
+// 6, 5 or 4 longer splits.
+constexpr int64_t kGradTargetBlocks = 384;
 static_assert(kGradBlocks % 4 == 0, "every wavefront issues the same number of loads");
 
 // One token reduction of a launch (P [m, pa], Q [m, qb], partials [splits, pa, qb]).
@@ -670,18 +675,24 @@ hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t cols, const ui
   return launch_lora_down2(x, cols, rmat, scale, out, nullptr, 0, nullptr, 0.0f, nullptr, m, rank, stream);
 }
 
-int lora_grad_splits(int64_t m) {
-  int64_t s = (m + kTokensPerSplit - 1) / kTokensPerSplit;
-  if (s < 1) s = 1;
+int64_t lora_grad_tiles(int64_t pa0, int64_t pa1, int64_t qb) {
+  return ((pa0 + kGradA - 1) / kGradA + (pa1 + kGradA - 1) / kGradA) * ((qb + kGradB - 1) / kGradB);
+}
+
+int lora_grad_splits(int64_t m, int64_t tiles) {
+  int64_t s = tiles > 0 ? (kGradTargetBlocks + tiles - 1) / tiles : 1;
+  const int64_t steps = (m + kGradTokens - 1) / kGradTokens;  // at least one 64-token step per split
+  if (s > steps) s = steps;
   if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
   return (int)s;
 }
 
 hipError_t launch_lora_grad2(const uint16_t *p0, int64_t pa0, const uint16_t *q0, float scale0, bool transposed0,
                              float *partials0, uint16_t *out0, const uint16_t *p1, int64_t pa1, const uint16_t *q1,
                              float scale1, bool transposed1, float *partials1, uint16_t *out1, int64_t qb, int64_t m,
-                             hipStream_t stream) {
-  const int splits = lora_grad_splits(m);
+                             int splits, hipStream_t stream) {
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   int64_t per = (m + splits - 1) / splits;
   per = (per + kGradTokens - 1) / kGradTokens * kGradTokens;
   const GradJob g0{p0, pa0, q0, partials0, (pa0 + kGradA - 1) / kGradA};
@@ -699,9 +710,9 @@ hipError_t launch_lora_grad2(const uint16_t *p0, int64_t pa0, const uint16_t *q0
 }
 
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m, float scale,
-                            bool transposed, float *partials, uint16_t *out, hipStream_t stream) {
+                            bool transposed, float *partials, uint16_t *out, int splits, hipStream_t stream) {
   return launch_lora_grad2(p, pa, q, scale, transposed, partials, out, nullptr, 0, nullptr, 0.0f, false, nullptr,
-                           nullptr, qb, m, stream);
+                           nullptr, qb, m, splits, stream);
 }
 
 hipError_t launch_copy2d_u16(const uint16_t *in, int64_t in_rows, int64_t in_cols, uint16_t *out, int64_t out_rows,

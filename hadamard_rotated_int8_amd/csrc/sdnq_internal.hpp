@@ -105,15 +105,20 @@ hipError_t launch_lora_down2(const uint16_t *x0, int64_t cols0, const uint16_t *
 // Token reduction: part[s, a, b] = sum over the tokens of split s of p[t, a] * q[t, b]
 // (p [m, pa] the wide operand, q [m, qb] the narrow one, qb a multiple of 16; bf16), then
 // out[a, b] (or out[b, a] when transposed) = bf16(scale * sum_s part[s, a, b]).
-int lora_grad_splits(int64_t m);
+// The tokens are cut into `splits` (1..16) equal runs; lora_grad_splits picks it
+// from the token count and the launch's workgroups per split (lora_grad_tiles of
+// the two jobs' widths pa0, pa1 and qb), and the partials hold that many slices.
+int64_t lora_grad_tiles(int64_t pa0, int64_t pa1, int64_t qb);
+int lora_grad_splits(int64_t m, int64_t tiles);
 hipError_t launch_lora_grad(const uint16_t *p, int64_t pa, const uint16_t *q, int64_t qb, int64_t m,
-                            float scale, bool transposed, float *partials, uint16_t *out, hipStream_t stream);
+                            float scale, bool transposed, float *partials, uint16_t *out, int splits,
+                            hipStream_t stream);
 // Two such reductions sharing m and qb in one launch each for the partials and
 // the sums (p1 == nullptr: only the first); each job has its own partials.
 hipError_t launch_lora_grad2(const uint16_t *p0, int64_t pa0, const uint16_t *q0, float scale0, bool transposed0,
                              float *partials0, uint16_t *out0, const uint16_t *p1, int64_t pa1, const uint16_t *q1,
                              float scale1, bool transposed1, float *partials1, uint16_t *out1, int64_t qb, int64_t m,
-                             hipStream_t stream);
+                             int splits, hipStream_t stream);
 
 // Rotate (block g along the tokens) + per-feature int8 quantization of two
 // operands sharing the token count m, each x [m, f] bf16 read as it is: q [f, m]
