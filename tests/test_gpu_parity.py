@@ -334,6 +334,46 @@ def test_backward_with_lora_grads(g, rank):
     assert_close(dx, ref["dx"], "LoRA dx term")
 
 
+@pytest.mark.parametrize("m,rank", [(100, 16), (2000, 40), (5000, 64)])
+def test_backward_one_lora_gradient(m, rank):
+    """grad_a alone and grad_b alone (the C ABI's nullable outputs): each equals
+    the two-gradient call bit for bit (same token splits, independent jobs) and
+    the oracle within the tolerance.  m spans one split per 64 tokens up to the
+    split count the workgroup target sets; rank 40 is zero-padded to 48."""
+    import ctypes
+    n, k, g = 640, 768, 128
+    inp = synth.make_linear(m, k, n, seed=m + rank, lora_rank=rank, backward=True)
+    say(f"  one LoRA gradient m={m} n={n} k={k} rank={rank}")
+    qw, sw = h.sdnq_rotate_quantize_weight(d_bf16(inp["w"]), g)
+    dy, x = d_bf16(inp["dy"]), d_bf16(inp["x"])
+    la, lb = d_bf16(inp["lora_a"]), d_bf16(inp["lora_b"])
+    ws = torch.empty(h.sdnq_workspace_bytes(m, n, k, rank, True), dtype=torch.uint8, device=DEV)
+    L = h.lib()
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(want_a, want_b):
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device=DEV)
+        ga = torch.empty((k, rank), dtype=torch.bfloat16, device=DEV) if want_a else None
+        gb = torch.empty((rank, n), dtype=torch.bfloat16, device=DEV) if want_b else None
+        rc = L.sdnq_qlinear_backward_input(P(dy), m, n, P(qw), P(sw), k, g, P(x), P(la), P(lb), rank, 0.5, P(dx),
+                                           P(ga), P(gb), P(ws), ws.numel(), sp)
+        assert rc == 0, h.status_string(rc)
+        torch.cuda.synchronize()
+        return dx, ga, gb
+
+    dx2, ga2, gb2 = call(True, True)
+    dxa, ga1, _ = call(True, False)
+    dxb, _, gb1 = call(False, True)
+    assert torch.equal(dxa.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dxb.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(ga1.view(torch.int16), ga2.view(torch.int16))
+    assert torch.equal(gb1.view(torch.int16), gb2.view(torch.int16))
+    qwo, swo = oracle.rotate_quantize(inp["w"], g)
+    ref = oracle.qlinear_backward_input(inp["dy"], qwo, swo, g, inp["x"], inp["lora_a"], inp["lora_b"], 0.5)
+    assert_lora_grads(h_bits(dx2), h_bits(ga1), h_bits(gb1), ref)
+
+
 @pytest.mark.parametrize("g,k", [(128, 384), (64, 320), (256, 512)])
 def test_backward_partial_column_tile(g, k):
     """The last 256-column tile of dX is partly past K; the rotation blocks stay whole."""
