@@ -53,6 +53,8 @@ def parse():
                     help="do not start rocm-smi for the clock record (under a profiler that preloads into children)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 256 MiB device-to-device copy first (scales the HBM byte counters)")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="also time the GEMM kernel (product and MFMA-only) over K at one and two rounds of tiles")
     return ap.parse_args()
 
 
@@ -321,6 +323,50 @@ def measure_rows(torch, h, synth, reps: int = 100, warmup: int = 10) -> dict:
     return rows
 
 
+def gemm_k_sweep(torch, L, P, sp, stream, check) -> dict:
+    """Launch duration of the forward GEMM kernel (sdnq_gemm_i8_ceiling mode 0, the
+    product kernel, and mode 2, its MFMA instructions alone) against K, with N = 10240
+    (256 x 320 tiles) at M = 2048 (one round of 256 tiles) and 4096 (two rounds);
+    a line t = fixed + slope * K through the medians splits each launch into its
+    k loop and its per-launch fixed part."""
+    dev = torch.device("cuda", 0)
+    n, ks, ms = 10240, (1920, 3840, 5760, 7680), (2048, 4096)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    a_all = torch.randint(-127, 128, (max(ms), max(ks)), dtype=torch.int8, generator=gen).to(dev)
+    b_all = torch.randint(-127, 128, (n, max(ks)), dtype=torch.int8, generator=gen).to(dev)
+    sa = (torch.rand(max(ms), generator=gen) * 1e-3 + 1e-4).to(dev)
+    sb = (torch.rand(n, generator=gen) * 1e-3 + 1e-4).to(dev)
+    y = torch.empty((max(ms), n), dtype=torch.bfloat16, device=dev)
+    ops = {k: (a_all[:, :k].contiguous(), b_all[:, :k].contiguous()) for k in ks}
+    res = {}
+    for p in range(3):
+        for mode in ((0, 2) if p % 2 == 0 else (2, 0)):
+            for m in ms:
+                for k in ks:
+                    a, b = ops[k]
+                    c = lambda: check(L.sdnq_gemm_i8_ceiling(P(a), P(sa), m, k, P(b), P(sb), n, mode, P(y), sp),
+                                      "k sweep")
+                    for _ in range(5):
+                        c()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(30):
+                        c()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    res.setdefault((mode, m, k), []).append(e0.elapsed_time(e1) * 1e3 / 30)
+    fits = {}
+    for mode in (0, 2):
+        for m in ms:
+            ts = np.array([np.median(res[(mode, m, k)]) for k in ks])
+            slope, fixed = np.polyfit(np.array(ks, dtype=float), ts, 1)
+            fits[f"mode{mode}_m{m}"] = {"us": [round(float(t), 2) for t in ts], "fixed_us": round(float(fixed), 2),
+                                        "us_per_1000_k": round(float(slope) * 1000, 3)}
+    del ops, a_all, b_all, y
+    return {"n": n, "k": list(ks), "m": list(ms), "rounds_of_tiles": {"2048": 1, "4096": 2}, "fits": fits,
+            "timing": "median over 3 passes of the mean over 30 back-to-back launches between two HIP events"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -424,8 +470,9 @@ def main():
 
     # GEMM ceiling: the same kernel with the global loads of its k loop removed
     # (mode 1), then also its LDS fragment reads (mode 2: the MFMA instructions
-    # alone, on operand bytes of the real codes), timed like the launches above in
-    # 3 passes of alternating order.  Mode 0 is the product launch itself.
+    # alone, on operand bytes of the real codes; mode 3: on loop-index operands),
+    # timed like the launches above in 3 passes of alternating order.  Mode 0 is
+    # the product launch itself.
     y_ceil = [torch.empty_like(y_up), torch.empty_like(y_down)]
     ceil_args = [(qx, sx, M, K_UP, qw_up, sw_up, N_UP), (qh, shh, M, K_DOWN, qw_down, sw_down, N_DOWN)]
 
@@ -434,7 +481,8 @@ def main():
         return lambda: check(L.sdnq_gemm_i8_ceiling(P(a), P(sa), m, k, P(b), P(sb), n, mode, P(y_ceil[i]), sp),
                              f"gemm ceiling mode {mode}")
 
-    ceil_jobs = [(mode, i) for mode in (0, 1, 2) for i in (0, 1)]
+    n_modes = 4
+    ceil_jobs = [(mode, i) for mode in range(n_modes) for i in (0, 1)]
     ceil = np.zeros((3, len(ceil_jobs)))
     for p in range(3):
         for j in (range(len(ceil_jobs)) if p % 2 == 0 else reversed(range(len(ceil_jobs)))):
@@ -448,7 +496,7 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             ceil[p, j] = e0.elapsed_time(e1) / n_char
-    ceil_ms = np.median(ceil, axis=0).reshape(3, 2)
+    ceil_ms = np.median(ceil, axis=0).reshape(n_modes, 2)
     del y_ceil
 
     # Same-traffic reference for rotate+quantize: a device-to-device copy that
@@ -566,10 +614,11 @@ def main():
         "gemm_ceiling": {
             "entry_point": "sdnq_gemm_i8_ceiling (the forward GEMM kernel with parts of its k loop removed)",
             "modes": ["0: the product kernel", "1: no global loads in the k loop (MFMA + LDS fragment reads)",
-                      "2: no global loads and no LDS reads (MFMA instructions on the first fragments' bytes)"],
-            "us_up_down": [[round(float(v) * 1e3, 2) for v in ceil_ms[mode]] for mode in range(3)],
+                      "2: no global loads and no LDS reads (MFMA instructions on the first fragments' bytes)",
+                      "3: as 2 with operands made of loop indices (few toggling bits)"],
+            "us_up_down": [[round(float(v) * 1e3, 2) for v in ceil_ms[mode]] for mode in range(n_modes)],
             "frac_of_peak_up_down": [[round(ops / (float(v) * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
-                                      for ops, v in zip((ops_up, ops_down), ceil_ms[mode])] for mode in range(3)],
+                                      for ops, v in zip((ops_up, ops_down), ceil_ms[mode])] for mode in range(n_modes)],
             "product_over_mode2": [round(float(ceil_ms[2, i] / ceil_ms[0, i]), 4) for i in range(2)],
             "timing": "median over 3 passes (alternating order) of the mean launch duration over max(K, 50) "
                       "back-to-back launches between two HIP events on the launch stream"},
@@ -593,6 +642,8 @@ def main():
                                       for j, k in enumerate(kernels)},
         "env": environment(torch, not args.no_smi),
     }
+    if args.k_sweep:
+        out["gemm_k_sweep"] = gemm_k_sweep(torch, L, P, sp, stream, check)
     if not args.no_rows:
         out["rows"] = measure_rows(torch, h, synth)
     if not args.no_cpu_baseline:

@@ -337,7 +337,8 @@ def sdnq_gemm_i8_i32(a, b, b_layout: int = 0, workspace=None):
 
 def sdnq_gemm_i8_ceiling(qx, x_scale, qw, w_scale, mode: int, y=None):
     """The forward GEMM kernel with parts of its k loop removed (0: none, 1: global
-    loads, 2: also LDS reads); y [m,n] bf16 is the forward's only for mode 0."""
+    loads, 2: also LDS reads, 3: as 2 on loop-index operands); y [m,n] bf16 is
+    the forward's only for mode 0."""
     _need(qx, torch.int8, 2, "qx")
     _need(qw, torch.int8, 2, "qw")
     m, k = qx.shape

@@ -546,7 +546,7 @@ sdnq_status_t sdnq_gemm_i8_ceiling(const int8_t *qx, const float *x_scale, int64
                                    const float *w_scale, int64_t n, int32_t mode, uint16_t *y, void *stream) {
   if (!qw || !w_scale || m < 0) return SDNQ_ERR_INVALID_ARG;
   if (m > 0 && (!qx || !x_scale || !y)) return SDNQ_ERR_INVALID_ARG;
-  if (mode < 0 || mode > 2) return SDNQ_ERR_INVALID_ARG;
+  if (mode < 0 || mode > 3) return SDNQ_ERR_INVALID_ARG;
   SDNQ_TRY(check_linear(k));
   SDNQ_TRY(check_linear(n));
   if (!aligned16(qx) || !aligned16(x_scale) || !aligned16(qw) || !aligned16(w_scale) || !aligned16(y))

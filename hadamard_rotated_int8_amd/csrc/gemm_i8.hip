@@ -152,7 +152,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // DIAG (the ceiling diagnostic; 0 in every product launch): 1 drops the k loop's
 // global loads after the first two k-tiles, so every k-tile multiplies what those
 // left in LDS; 2 also drops the LDS reads, so every MFMA multiplies the fragments
-// of the first k-step, held in registers.  Prologue and epilogue are unchanged.
+// of the first k-step, held in registers; 3 is 2 with fragments made of the loop
+// indices instead of the codes (few toggling bits).  Prologue and epilogue are
+// unchanged.
 template <Epilogue EPI, int BN, int WAVES_M, int G, bool LORA, bool FP8, int DIAG = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int tiles_m, int tiles_n) {
   static_assert(DIAG == 0 || (EPI == Epilogue::kForward && !LORA && !FP8), "diagnostic modes: int8 forward only");
@@ -291,6 +293,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         f = fkeep;
         return;
       }
+    }
+    if constexpr (DIAG == 3) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i) f.a[i] = v4i{kt, kk, i, 1};
+#pragma unroll
+      for (int j = 0; j < SN; ++j) f.b[j] = v4i{kk, kt, j, 3};
+      return;
     }
     const int8_t *base = smem + (kt & (STAGES - 1)) * kStageBytes + frow + fcol[kk];
 #pragma unroll
@@ -781,6 +790,7 @@ hipError_t launch_gemm_i8_ceiling(const GemmArgs &args, int mode, hipStream_t st
     case 0: return launch_ceiling<0>(args, stream);
     case 1: return launch_ceiling<1>(args, stream);
     case 2: return launch_ceiling<2>(args, stream);
+    case 3: return launch_ceiling<3>(args, stream);
   }
   return hipErrorInvalidValue;
 }

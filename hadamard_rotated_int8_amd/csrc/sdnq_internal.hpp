@@ -68,7 +68,8 @@ struct GemmArgs {
 hipError_t launch_gemm_i8(Epilogue epi, const GemmArgs &args, hipStream_t stream);
 // The int8 forward GEMM (no LoRA) with parts of its k loop removed, to measure
 // its rate ceiling: mode 0 none (the product kernel), 1 the global loads after
-// the first two k-tiles, 2 also the LDS fragment reads.
+// the first two k-tiles, 2 also the LDS fragment reads, 3 as 2 on operands made
+// of loop indices.
 hipError_t launch_gemm_i8_ceiling(const GemmArgs &args, int mode, hipStream_t stream);
 
 // int8 [rows, cols] -> [cols, rows]

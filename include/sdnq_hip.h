@@ -197,11 +197,14 @@ sdnq_status_t sdnq_gemm_i8_i32(const int8_t *a, const int8_t *b, int64_t m, int6
  *   mode 1: no global loads after the first two k-tiles: every k-tile multiplies
  *           what those two left in LDS (y is meaningless);
  *   mode 2: also no LDS reads: every MFMA multiplies the fragments of the first
- *           k-step, held in registers (y is meaningless).
+ *           k-step, held in registers (y is meaningless);
+ *   mode 3: as mode 2, with fragments made of the loop indices instead of the
+ *           codes (y is meaningless).
  * Mode 2 issues the same MFMA instructions on operand bytes of the real codes
  * with no data movement in the k loop: the kernel's rate on the device's clock
- * and power budget when nothing but the matrix cores work.  SDNQ_ERR_INVALID_ARG
- * for a mode outside 0..2; the other errors as sdnq_qlinear_forward_quantized. */
+ * and power budget when nothing but the matrix cores work.  Mode 3 shows how much
+ * of that power the operands' bit patterns draw.  SDNQ_ERR_INVALID_ARG for a mode
+ * outside 0..3; the other errors as sdnq_qlinear_forward_quantized. */
 sdnq_status_t sdnq_gemm_i8_ceiling(const int8_t *qx, const float *x_scale, int64_t m, int64_t k,
                                    const int8_t *qw, const float *w_scale, int64_t n, int32_t mode,
                                    uint16_t *y, void *stream);

@@ -198,7 +198,7 @@ def test_gemm_validation():
     assert L.sdnq_gemm_i8_i32(A, B, 4, 32, 32, 1, C, None, 0, None) == WORKSPACE
     assert L.sdnq_gemm_i8_i32(A, B, 0, 32, 32, 0, C, None, 0, None) == OK
     # qx, x_scale, m, k, qw, w_scale, n, mode, y, stream
-    assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, B, C, 32, 3, D, None) == INVALID
+    assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, B, C, 32, 4, D, None) == INVALID
     assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, B, C, 32, -1, D, None) == INVALID
     assert L.sdnq_gemm_i8_ceiling(A, C, 4, 32, None, C, 32, 0, D, None) == INVALID
     assert L.sdnq_gemm_i8_ceiling(A, C, 4, 30, B, C, 32, 0, D, None) == UNSUPPORTED
