@@ -499,6 +499,32 @@ def main():
     ceil_ms = np.median(ceil, axis=0).reshape(n_modes, 2)
     del y_ceil
 
+    # Vendor reference for the GEMM: torch._int_mm (hipBLASLt) on the same operand
+    # bytes, int32 out (no scales, no bf16 epilogue), timed the same way.
+    vendor_ms = None
+    try:
+        wt = [qw_up.t(), qw_down.t()]  # [K, N] views of the row-major weights
+        vcalls = [lambda: torch._int_mm(qx, wt[0]), lambda: torch._int_mm(qh, wt[1])]
+        vend = np.zeros((3, 2))
+        for p in range(3):
+            for j in ((0, 1) if p % 2 == 0 else (1, 0)):
+                for _ in range(5):
+                    vcalls[j]()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n_char):
+                    vcalls[j]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                vend[p, j] = e0.elapsed_time(e1) / n_char
+        vendor_ms = np.median(vend, axis=0)
+        del wt
+    except (RuntimeError, AttributeError) as e:  # not available on this build
+        vendor_note = f"torch._int_mm unavailable: {e}"
+    else:
+        vendor_note = ("torch._int_mm (hipBLASLt) on the same int8 operands, int32 out (no scales or bf16 "
+                       "epilogue), timed like the kernels")
+
     # Same-traffic reference for rotate+quantize: a device-to-device copy that
     # moves as many bytes as the kernel does for x and for h (3 bytes per element:
     # 1.5 read and 1.5 written), timed the same way.
@@ -620,6 +646,12 @@ def main():
             "frac_of_peak_up_down": [[round(ops / (float(v) * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
                                       for ops, v in zip((ops_up, ops_down), ceil_ms[mode])] for mode in range(n_modes)],
             "product_over_mode2": [round(float(ceil_ms[2, i] / ceil_ms[0, i]), 4) for i in range(2)],
+            "vendor_int8_gemm_us_up_down": None if vendor_ms is None else [round(float(v) * 1e3, 2)
+                                                                           for v in vendor_ms],
+            "vendor_int8_gemm_frac_up_down": None if vendor_ms is None else [
+                round(ops / (float(v) * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+                for ops, v in zip((ops_up, ops_down), vendor_ms)],
+            "vendor_note": vendor_note,
             "timing": "median over 3 passes (alternating order) of the mean launch duration over max(K, 50) "
                       "back-to-back launches between two HIP events on the launch stream"},
         "kernel_avg_us": {k: round(float(v) * 1e3, 2) for k, v in zip(kernels, avg_ms)},
