@@ -207,20 +207,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   int8_t *const dummy = smem + STAGES * kStageBytes;
 
   const int nk = (int)((K + BK - 1) / BK);
-  auto issue_loads = [&](int kt) {
-    const int st = kt & (STAGES - 1);
+  // Load slot j of k-tile kt into its stage.  The tile's first byte k0 is uniform
+  // and rides in the scalar offset; the lane's part (and the out-of-range bit,
+  // which keeps any sum past num_records) stays in the vector offset.  Only a
+  // k-tile that runs past K needs the per-lane range check.
+  auto load_slot = [&](int kt, int j) {
     const unsigned k0 = (unsigned)kt * BK;
-    // Only a k-tile that runs past K needs the per-lane range check.
     const unsigned oob = ((int64_t)k0 + BK <= K) ? 0u : (((int64_t)k0 + 16 * lc < K) ? 0u : kOutOfRange);
-    int8_t *base = smem + st * kStageBytes;
+    int8_t *base = smem + (kt & (STAGES - 1)) * kStageBytes;
+    // wavefront-uniform selects, no branch: a spare slot loads nothing into the dummy area
+    const bool spare = Cfg::kDummy && j >= ASL && grp[j] < 0;
+    int8_t *dst = spare ? dummy : base + (j < ASL ? 0 : BM * BK) + grp[j] * 1024;
+    const unsigned off = spare ? kOutOfRange : (voff[j] | oob);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(j < ASL ? rsrc_a : rsrc_b, (lds_void *)dst, 16, off, (int)k0, 0, 0);
+  };
+  auto issue_loads = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      // wavefront-uniform selects, no branch: a spare slot loads nothing into the dummy area
-      const bool spare = Cfg::kDummy && j >= ASL && grp[j] < 0;
-      int8_t *dst = spare ? dummy : base + (j < ASL ? 0 : BM * BK) + grp[j] * 1024;
-      const unsigned off = spare ? kOutOfRange : ((voff[j] + k0) | oob);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < ASL ? rsrc_a : rsrc_b, (lds_void *)dst, 16, off, 0, 0, 0);
-    }
+    for (int j = 0; j < LPW; ++j) load_slot(kt, j);
   };
 
   // ---- LoRA operands of the epilogue (forward and backward with LoRA): the T
@@ -416,8 +419,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   } else {
     // Iteration kt: read (kt,1) | MFMA (kt,0); read (kt,2) | MFMA (kt,1);
     // read (kt,3) | MFMA (kt,2); wait, barrier, load tile kt+2 | read (kt+1,0) |
-    // MFMA (kt,3).
+    // MFMA (kt,3).  Without LoRA operands to stage, the last step is interleaved
+    // by hand, load u | read u | MFMA u with nothing moved across: left to the
+    // compiler, every load and its address arithmetic came first, ahead of the
+    // step's MFMAs (about 1 % on the MLP GEMMs).
     constexpr int T = SM * SN;
+    constexpr bool kByHand = !kLoraStaged && DIAG == 0;
     for (int kt = 0; kt < nk; ++kt) {
       read_frags(kt, 1, f1);
       mfma_all(f0);
@@ -429,10 +436,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       mfma_all(f0);
       sched(0, SM + SN, T);
       wait_tile_and_barrier();
-      if constexpr (DIAG == 0) issue_next(kt + 2);
-      read_frags(kt + 1, 0, f0);
-      mfma_all(f1);
-      sched(LPW, SM + SN, T);
+      if constexpr (kByHand) {
+        const int8_t *rbase = smem + ((kt + 1) & (STAGES - 1)) * kStageBytes + frow + fcol[0];
+        auto read_one = [&](int u) {  // fragment u of (kt+1, 0) into f0
+          if (u < SM) f0.a[u] = *reinterpret_cast<const v4i *>(rbase + (wm * TM + u * 32) * BK);
+          else f0.b[u - SM] = *reinterpret_cast<const v4i *>(rbase + BM * BK + (wn * TN + (u - SM) * 32) * BK);
+        };
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          if (u < LPW) load_slot(kt + 2, u);
+          if (u < SM + SN) read_one(u);
+          const int i = u / SN, j = u % SN;
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int u = T; u < LPW; ++u) load_slot(kt + 2, u);
+#pragma unroll
+        for (int u = T; u < SM + SN; ++u) read_one(u);
+      } else {
+        if constexpr (DIAG == 0) issue_next(kt + 2);
+        read_frags(kt + 1, 0, f0);
+        mfma_all(f1);
+        sched(LPW, SM + SN, T);
+      }
     }
   }
   // The zero-fill loads of the last iterations may still be landing in LDS.
