@@ -404,16 +404,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // 1 MFMA
       }
       wait_tile_and_barrier();
-      issue_next(kt + 2);
-      read_frags(kt + 1, 0, f0);
-      read_frags(kt + 1, 1, f1);
-      mfma8_all(g0, g1);
+      if constexpr (!kLoraStaged) {
+        // interleaved by hand, as in the int8 loop: load u | its share of the
+        // reads of (kt+1, 0..1) | MFMA u, nothing moved across
+        const int8_t *rbase = smem + ((kt + 1) & (STAGES - 1)) * kStageBytes + frow;
+        auto read_one = [&](int r) {  // fragment r % (SM + SN) of step r / (SM + SN)
+          const int st = r / (SM + SN), q = r % (SM + SN);
+          Frags &f = st == 0 ? f0 : f1;
+          const int8_t *b = rbase + fcol[st];
+          if (q < SM) f.a[q] = *reinterpret_cast<const v4i *>(b + (wm * TM + q * 32) * BK);
+          else f.b[q - SM] = *reinterpret_cast<const v4i *>(b + BM * BK + (wn * TN + (q - SM) * 32) * BK);
+        };
 #pragma unroll
-      for (int u = 0; u < T; ++u) {
-        if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // 1 global->LDS load
-        __builtin_amdgcn_sched_group_barrier(0x100, R / T, 0);                  // LDS reads
-        if (u < R % T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // 1 MFMA
+        for (int u = 0; u < T; ++u) {
+          if (u < LPW) load_slot(kt + 2, u);
+#pragma unroll
+          for (int r = u * R / T; r < (u + 1) * R / T; ++r) read_one(r);
+          const int i = u / SN, j = u % SN;
+          const v8i bv = __builtin_shufflevector(g0.b[j], g1.b[j], 0, 1, 2, 3, 4, 5, 6, 7);
+          const v8i av = __builtin_shufflevector(g0.a[i], g1.a[i], 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int u = T; u < LPW; ++u) load_slot(kt + 2, u);
+      } else {
+        issue_next(kt + 2);
+        read_frags(kt + 1, 0, f0);
+        read_frags(kt + 1, 1, f1);
+        mfma8_all(g0, g1);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          if (u < LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // 1 global->LDS load
+          __builtin_amdgcn_sched_group_barrier(0x100, R / T, 0);                // LDS reads
+          if (u < R % T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // 1 MFMA
+        }
       }
     }
   } else {
