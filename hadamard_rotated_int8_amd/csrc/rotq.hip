@@ -109,7 +109,11 @@ constexpr int64_t kColScaleLds = 16384;
 //   phase 2: the codes, from the row's max read back from scale[row];
 // then finish_scale_kernel turns the maxima into scales.  SEG = false is the
 // whole-row path (chunks = 1, phase 0).
-template <int G, bool COLSCALE, int MAXT, bool FP8, bool SEG = false>
+// WHOLE: cols is a multiple of 256, so all 8 loads and stores of every lane lie
+// inside its row; they share one vector offset and add 64*i (32*i) bytes as the
+// scalar offset, instead of holding 16 per-load offsets in VGPRs.
+// NT: the codes are stored non-temporally (see kStreamCodesMax).
+template <int G, bool COLSCALE, int MAXT, bool FP8, bool SEG = false, bool WHOLE = false, bool NT = false>
 __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
     int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg, int64_t groups, int chunks,
@@ -151,11 +155,12 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const int64_t nrows = group_rows(grp);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(x + (grp < groups ? grp : 0) * rows_per_wg * cols), 0, (int)(nrows * cols * 2), 0x00020000);
+    const unsigned off0 = (unsigned)((r_local * cols + base) * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t e0 = base + 32 * i;
-      const unsigned off = (e0 < cols) ? (unsigned)((r_local * cols + e0) * 2) : 0x80000000u;
-      raw[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      const unsigned off = WHOLE ? off0 : (e0 < cols) ? (unsigned)((r_local * cols + e0) * 2) : 0x80000000u;
+      raw[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, off, WHOLE ? 64 * i : 0, 0));
     }
   };
 
@@ -313,10 +318,11 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
       const int64_t nrows = group_rows(grp);
       const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(q + grp * rows_per_wg * cols), 0, (int)(nrows * cols), 0x00020000);
+      const unsigned soff0 = (unsigned)(r_local * cols + base);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t e0 = base + 32 * i;
-        const unsigned off = (e0 < cols) ? (unsigned)(r_local * cols + e0) : 0x80000000u;
+        const unsigned off = WHOLE ? soff0 : (e0 < cols) ? (unsigned)(r_local * cols + e0) : 0x80000000u;
         v2u packed;
         if constexpr (FP8) {
           float t[8];
@@ -338,7 +344,8 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
           }
           packed = (v2u){pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
         }
-        __builtin_amdgcn_raw_buffer_store_b64(packed, rq, off, 0, 0);
+        // aux 2: the non-temporal bit of gfx950 buffer stores
+        __builtin_amdgcn_raw_buffer_store_b64(packed, rq, off, WHOLE ? 32 * i : 0, NT ? 2 : 0);
       }
     }
   }
@@ -396,7 +403,7 @@ int pick_rows_per_wg(int t_row, int max_threads) {
 // Resident workgroups per CU for a kernel at a block size, cached per block size
 // (one atomic word holding both, so concurrent callers read a consistent pair).
 // (One atomic word holds block size, dynamic LDS in 16-byte units and the count.)
-template <int G, bool CS, int MAXT, bool FP8, bool SEG>
+template <int G, bool CS, int MAXT, bool FP8, bool SEG, bool WHOLE, bool NT>
 int blocks_per_cu(int threads, size_t smem) {
   static std::atomic<uint64_t> cache[kMaxThreads / 4 + 1];
   std::atomic<uint64_t> &slot = cache[threads / 4];
@@ -404,7 +411,7 @@ int blocks_per_cu(int threads, size_t smem) {
   const uint64_t c = slot.load(std::memory_order_relaxed);
   if ((c >> 32) == key) return (int)(c & 0xffffffffu);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8, SEG>, threads, smem) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)rotq_kernel<G, CS, MAXT, FP8, SEG, WHOLE, NT>, threads, smem) !=
           hipSuccess ||
       n < 1)
     n = 1;
@@ -412,17 +419,43 @@ int blocks_per_cu(int threads, size_t smem) {
   return n;
 }
 
-template <int G, bool CS, int MAXT, bool FP8, bool SEG = false>
-hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
-                        float *scale, int t_row, int rpw, hipStream_t stream, int chunks = 1, int phase = 0) {
+// Codes written by plain stores stay dirty in the L2s (4 MB per XCD) when the
+// whole output fits there, and the write-back at the kernel's end then runs after
+// its last wave: x [4096, 3840] (15.7 MB of codes) took 10.5 us against 8.8 us
+// with non-temporal stores.  Larger outputs are evicted while the kernel runs, as
+// whole lines; non-temporal stores of them measured slower (h [4096, 10240], 42 MB:
+// 23.8 against 27.6 us), so only outputs up to this size stream out.
+constexpr int64_t kStreamCodesMax = 24ll << 20;
+
+template <int G, bool CS, int MAXT, bool FP8, bool SEG, bool WHOLE, bool NT>
+hipError_t launch_grid(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
+                       float *scale, int t_row, int rpw, hipStream_t stream, int chunks, int phase) {
   const int threads = rpw * t_row;
   const int64_t groups = (rows + rpw - 1) / rpw;
   const size_t smem = (CS && !SEG && cols <= kColScaleLds) ? (size_t)cols * 4 : 0;
-  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8, SEG>(threads, smem);
+  // As many workgroups as fit at once, then evened out so that every workgroup
+  // walks the same number of row groups: with 1280 resident and 4096 groups, 1024
+  // workgroups of 4 groups, not 3.2 rounds whose last one leaves most CUs idle.
+  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8, SEG, WHOLE, NT>(threads, smem);
   if (blocks > groups) blocks = groups;
-  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8, SEG>), dim3((unsigned)blocks), dim3(threads), smem, stream, x,
-                     rows, cols, col_scale, q, scale, t_row, rpw, groups, chunks, phase);
+  const int64_t rounds = (groups + blocks - 1) / blocks;
+  blocks = (groups + rounds - 1) / rounds;
+  hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8, SEG, WHOLE, NT>), dim3((unsigned)blocks), dim3(threads), smem,
+                     stream, x, rows, cols, col_scale, q, scale, t_row, rpw, groups, chunks, phase);
   return hipGetLastError();
+}
+
+template <int G, bool CS, int MAXT, bool FP8, bool SEG = false>
+hipError_t launch_sized(const uint16_t *x, int64_t rows, int64_t cols, const float *col_scale, int8_t *q,
+                        float *scale, int t_row, int rpw, hipStream_t stream, int chunks = 1, int phase = 0) {
+  if (cols % 256 != 0)
+    return launch_grid<G, CS, MAXT, FP8, SEG, false, false>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream,
+                                                            chunks, phase);
+  if (rows * cols <= kStreamCodesMax)
+    return launch_grid<G, CS, MAXT, FP8, SEG, true, true>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream,
+                                                          chunks, phase);
+  return launch_grid<G, CS, MAXT, FP8, SEG, true, false>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream,
+                                                         chunks, phase);
 }
 
 // Segments per row for rows above 65536 values: the fewest equal segments of at
