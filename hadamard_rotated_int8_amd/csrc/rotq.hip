@@ -21,7 +21,7 @@
 // lane-within-quad: stages h = 1, 2, 4, 32, 64, 128 are register butterflies and
 // h = 8, 16 are quad_perm DPP exchanges.  The whole row stays in registers until
 // its absmax is known (one workgroup holds `rows_per_wg` complete rows at a
-// time and walks over row groups persistently, prefetching the next group).
+// time; a persistent grid walks over row groups, prefetching the next one).
 //
 // FP8 variant (the float8_e4m3fn quantized matmul listed next to INT8 in "SDNQ:
 // SD.Next Quantization Engine"): s = fl32(a / 448), r = fl32(448 / a), and each
@@ -118,8 +118,10 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ col_scale,
     int8_t *__restrict__ q, float *__restrict__ scale, int t_row, int rows_per_wg, int64_t groups, int chunks,
     int phase) {
-  // Persistent: workgroup b handles row groups b, b + gridDim.x, ... and loads the
-  // next group's values while it transforms the current one.  Row maxima go
+  // Workgroup b handles row groups b, b + gridDim.x, ...: one each in the usual
+  // launch of one workgroup per group, several in a persistent grid (column scales
+  // staged in LDS), where it loads the next group's values while it transforms
+  // the current one (a load past the last group reads nothing).  Row maxima go
   // through three rotating LDS slots: slot (it+1)%3 is cleared at the start of
   // iteration it, before that iteration's barrier, so one barrier per group
   // separates every clear from the atomics that follow it and from the reads
@@ -433,13 +435,22 @@ hipError_t launch_grid(const uint16_t *x, int64_t rows, int64_t cols, const floa
   const int threads = rpw * t_row;
   const int64_t groups = (rows + rpw - 1) / rpw;
   const size_t smem = (CS && !SEG && cols <= kColScaleLds) ? (size_t)cols * 4 : 0;
-  // As many workgroups as fit at once, then evened out so that every workgroup
-  // walks the same number of row groups: with 1280 resident and 4096 groups, 1024
-  // workgroups of 4 groups, not 3.2 rounds whose last one leaves most CUs idle.
-  int64_t blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8, SEG, WHOLE, NT>(threads, smem);
-  if (blocks > groups) blocks = groups;
-  const int64_t rounds = (groups + blocks - 1) / blocks;
-  blocks = (groups + rounds - 1) / rounds;
+  // One workgroup per row group: the hardware starts each one as a slot frees,
+  // which measured faster than a persistent grid walking the groups with its
+  // prefetch (h [4096, 10240]: 23.2 against 24.9 us; x [8192, 3072] at g = 64:
+  // 19.1 against 22.1 us).  With column scales staged in LDS every workgroup
+  // first copies them (up to 64 KB), and the persistent grid, which copies them
+  // once per workgroup, stays faster (dY [16384, 3072]: 26.9 against 28.6 us).
+  // It takes as many workgroups as fit at once, evened out so that each walks the
+  // same number of row groups (no last round that leaves most CUs idle).  So does
+  // a group count beyond the grid's 2^31 - 1 workgroups.
+  int64_t blocks = groups;
+  if (smem > 0 || groups > 0x7fffffff) {
+    blocks = (int64_t)device_cu_count() * blocks_per_cu<G, CS, MAXT, FP8, SEG, WHOLE, NT>(threads, smem);
+    if (blocks > groups) blocks = groups;
+    const int64_t rounds = (groups + blocks - 1) / blocks;
+    blocks = (groups + rounds - 1) / rounds;
+  }
   hipLaunchKernelGGL((rotq_kernel<G, CS, MAXT, FP8, SEG, WHOLE, NT>), dim3((unsigned)blocks), dim3(threads), smem,
                      stream, x, rows, cols, col_scale, q, scale, t_row, rpw, groups, chunks, phase);
   return hipGetLastError();
