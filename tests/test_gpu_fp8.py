@@ -74,22 +74,24 @@ def assert_rq8_exact(x_bits, g, col_scale=None):
 
 @pytest.mark.parametrize("g,m,k", [(256, 64, 512), (256, 37, 3072), (128, 19, 1152), (64, 33, 320),
                                    (1, 40, 272), (256, 3, 40960), (64, 2, 65536), (256, 9000, 3840),
+                                   (256, 7, 1536), (128, 5, 10240), (64, 9, 1536), (1, 3, 10240),
                                    (256, 2, 98304), (64, 3, 133120)])
 def test_fp8_rotate_quantize_bit_exact(g, m, k):
     assert_rq8_exact(synth.make_linear(m, k, 16, seed=300 + g + m)["x"], g)
 
 
-def test_fp8_rotate_quantize_column_scale_bit_exact():
+@pytest.mark.parametrize("k", [272, 1536])
+def test_fp8_rotate_quantize_column_scale_bit_exact(k):
     rng = np.random.default_rng(12)
-    dy = synth.to_bf16_bits(rng.standard_normal((29, 272)).astype(np.float32) * 1e-3)
-    cs = (rng.uniform(0.5, 2.0, 272) * 1e-3).astype(np.float32)
+    dy = synth.to_bf16_bits(rng.standard_normal((29, k)).astype(np.float32) * 1e-3)
+    cs = (rng.uniform(0.5, 2.0, k) * 1e-3).astype(np.float32)
     assert_rq8_exact(dy, 1, cs)
 
 
+@pytest.mark.parametrize("k", [512, 1536])   # 4 and 8 lanes per superblock
 @pytest.mark.parametrize("g", [1, 64, 128, 256])
-def test_fp8_rotate_quantize_stress_rows(g):
+def test_fp8_rotate_quantize_stress_rows(g, k):
     rng = np.random.default_rng(9)
-    k = 512
     rows = [np.zeros(k, np.float32)]
     r = rng.standard_normal(k).astype(np.float32); r[17] = 1e30; rows.append(r)
     rows.append((rng.standard_normal(k) * 1e-38).astype(np.float32))      # a below 2^-100

@@ -100,6 +100,10 @@ def assert_rq_exact(x_bits, g, col_scale=None):
     (128, 37, 384), (128, 19, 1152), (128, 64, 3072),
     (64, 33, 320), (64, 5, 64), (64, 70, 3072), (64, 9, 192),
     (1, 11, 16), (1, 21, 48), (1, 40, 272), (1, 64, 3072),
+    # rows of 1536, 10240 and 14336 values: 8 lanes per 256-value superblock, a
+    # row group of 4 rows (1536) or 1 row, with a partial last group
+    (256, 7, 1536), (128, 13, 1536), (64, 5, 1536), (1, 9, 1536),
+    (128, 3, 10240), (64, 6, 10240), (1, 4, 10240), (256, 5, 14336),
     (256, 3, 40960), (64, 2, 65536),        # rows longer than 32768 values: 1024-thread workgroups
     # rows longer than 65536 values, quantized in 2, 3 and 4 segments of whole blocks
     (256, 3, 98304), (128, 2, 65664), (64, 2, 133120), (1, 3, 100000),
@@ -116,7 +120,7 @@ def test_rotate_quantize_many_rows_bit_exact(g, m, k):
     assert_rq_exact(x, g)
 
 
-@pytest.mark.parametrize("k", [16, 272, 3072, 100000])
+@pytest.mark.parametrize("k", [16, 272, 1536, 3072, 10240, 100000])
 def test_rotate_quantize_column_scale_bit_exact(k):
     rng = np.random.default_rng(5 + k)
     dy = synth.to_bf16_bits(rng.standard_normal((29, k)).astype(np.float32) * 1e-3)
@@ -124,10 +128,10 @@ def test_rotate_quantize_column_scale_bit_exact(k):
     assert_rq_exact(dy, 1, cs)
 
 
+@pytest.mark.parametrize("k", [512, 1536])   # 4 and 8 lanes per superblock
 @pytest.mark.parametrize("g", [1, 64, 128, 256])
-def test_rotate_quantize_stress_rows(g):
+def test_rotate_quantize_stress_rows(g, k):
     rng = np.random.default_rng(7)
-    k = 512
     rows = []
     rows.append(np.zeros(k, np.float32))                                   # all-zero row
     r = rng.standard_normal(k).astype(np.float32); r[17] = 1e30; rows.append(r)   # one huge channel
