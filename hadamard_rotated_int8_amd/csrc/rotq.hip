@@ -155,7 +155,8 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
   __shared__ uint32_t row_max[3][kMaxRowsPerWg];
 
   const int tid = threadIdx.x;
-  const int r_local = tid / t_row;
+  // one row per workgroup (the MLP widths) needs no division by t_row
+  const int r_local = rows_per_wg == 1 ? 0 : tid / t_row;
   const int qt = tid - r_local * t_row;
   static_assert(LPS == 4 || LPS == 8, "4 or 8 lanes per superblock");
   constexpr int NI = 32 / LPS;   // 16-byte loads per lane and row group
