@@ -225,17 +225,29 @@ __global__ __launch_bounds__(MAXT) void rotq_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (COLSCALE) {
+      // Two loops, one per memory: a pointer that could be either would make
+      // these flat loads, which wait for every outstanding global access too
+      // (the next group's prefetch and this workgroup's code stores).
+      auto fold = [&](int i, const float4 c0, const float4 c1) {
+        v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
+        v[i][2] = v[i][2] * c0.z; v[i][3] = v[i][3] * c0.w;
+        v[i][4] = v[i][4] * c1.x; v[i][5] = v[i][5] * c1.y;
+        v[i][6] = v[i][6] * c1.z; v[i][7] = v[i][7] * c1.w;
+      };
+      if (cs_staged) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int64_t e0 = base + SPAN * i;
-        if (e0 < cols) {
-          const float *cs = cs_staged ? cs_lds : col_scale + col_off;
-          const float4 c0 = *reinterpret_cast<const float4 *>(cs + e0);
-          const float4 c1 = *reinterpret_cast<const float4 *>(cs + e0 + 4);
-          v[i][0] = v[i][0] * c0.x; v[i][1] = v[i][1] * c0.y;
-          v[i][2] = v[i][2] * c0.z; v[i][3] = v[i][3] * c0.w;
-          v[i][4] = v[i][4] * c1.x; v[i][5] = v[i][5] * c1.y;
-          v[i][6] = v[i][6] * c1.z; v[i][7] = v[i][7] * c1.w;
+        for (int i = 0; i < NI; ++i) {
+          const int64_t e0 = base + SPAN * i;
+          if (e0 < cols)
+            fold(i, *reinterpret_cast<const float4 *>(cs_lds + e0), *reinterpret_cast<const float4 *>(cs_lds + e0 + 4));
+        }
+      } else {
+        const float *cg = col_scale + col_off;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int64_t e0 = base + SPAN * i;
+          if (e0 < cols)
+            fold(i, *reinterpret_cast<const float4 *>(cg + e0), *reinterpret_cast<const float4 *>(cg + e0 + 4));
         }
       }
     }
@@ -560,10 +572,12 @@ hipError_t launch_typed(const uint16_t *x, int64_t rows, int64_t cols, const flo
     const int rpw = pick_rows_per_wg(t_row, 512);
     // 8 lanes per superblock where that leaves fewer lanes idle: a 10240-wide row
     // fills five wavefronts (against three with a sixth of the lanes idle), 21.4
-    // against 22.7 us for h [4096, 10240].
+    // against 22.7 us for h [4096, 10240].  With column scales staged in LDS also
+    // where both leave as many idle (dY [16384, 3072]: 25.9 against 26.9 us).
     if (cols % 512 == 0 && 2 * t_row <= 512) {
       const int rpw8 = pick_rows_per_wg(2 * t_row, 512);
-      if (idle_lanes(2 * t_row, 2 * t_row, rpw8) < idle_lanes(t_row, t_row, rpw))
+      const double i8 = idle_lanes(2 * t_row, 2 * t_row, rpw8), i4 = idle_lanes(t_row, t_row, rpw);
+      if (i8 < i4 || (CS && cols <= kColScaleLds && i8 <= i4))
         return launch_sized<G, CS, 512, FP8, false, 8>(x, rows, cols, col_scale, q, scale, 2 * t_row, rpw8, stream);
     }
     return launch_sized<G, CS, 512, FP8>(x, rows, cols, col_scale, q, scale, t_row, rpw, stream);

@@ -80,7 +80,7 @@ def test_fp8_rotate_quantize_bit_exact(g, m, k):
     assert_rq8_exact(synth.make_linear(m, k, 16, seed=300 + g + m)["x"], g)
 
 
-@pytest.mark.parametrize("k", [272, 1536])
+@pytest.mark.parametrize("k", [272, 1536, 3072, 10240])
 def test_fp8_rotate_quantize_column_scale_bit_exact(k):
     rng = np.random.default_rng(12)
     dy = synth.to_bf16_bits(rng.standard_normal((29, k)).astype(np.float32) * 1e-3)
