@@ -134,7 +134,9 @@ struct TileCfg {
   static constexpr int kASlots = (BM / 8) / 8;
   static constexpr int kLoadsPerWave = (kGroups + 7) / 8;
   static constexpr bool kDummy = kGroups % 8 != 0;
-  static constexpr int kLdsBytes = STAGES * kStageBytes + (kDummy ? 1024 : 0);
+  // the forward epilogue's column scales of the tile (BN floats) follow the ring
+  static constexpr int kScaleOff = STAGES * kStageBytes + (kDummy ? 1024 : 0);
+  static constexpr int kLdsBytes = kScaleOff + BN_ * 4;
   static_assert(BN_ % 32 == 0 && (BM / 8) % 8 == 0, "the A groups fill whole load slots");
 };
 
@@ -488,6 +490,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
       }
     }
   }
+  // Forward epilogue without LoRA: the tile's row and column scales are fetched
+  // now, while the last MFMAs drain, rather than by each 32 x 32 tile as it is
+  // dequantized.  Row scales go to registers; the column scales (BN / 4 lanes,
+  // one float4 each) to an LDS area of their own, published by the epilogue's
+  // first barrier.
+  constexpr bool kScalesAhead = EPI == Epilogue::kForward && !LORA;
+  float sxr[SM];
+  if constexpr (kScalesAhead) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);
+      sxr[i] = args.row_scale[m < M ? m : M - 1];
+    }
+    if (tid < BN / 4) {
+      int64_t n = n0 + 4 * tid;
+      n = n < N ? n : N - 4;  // N is a multiple of 16: a float4 is whole or past the end
+      *reinterpret_cast<float4 *>(smem + Cfg::kScaleOff + 16 * tid) = *reinterpret_cast<const float4 *>(args.col_scale + n);
+    }
+  }
   // The zero-fill loads of the last iterations may still be landing in LDS.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -510,13 +531,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
   int8_t *const stage = smem;
   // stores the staged rows of pass `pass` (N is a multiple of 16, so a 16-byte
   // chunk is whole or past the end); consecutive lanes cover a row contiguously
+  // All of a lane's LDS reads are issued before its first store, so their
+  // latencies overlap instead of adding up chunk by chunk.
+  constexpr int kStoreIters = kPassRows * kRowChunks / kThreads;
+  static_assert(kPassRows * kRowChunks % kThreads == 0, "whole store rounds");
   auto store_pass = [&](int pass) {
-    for (int c = tid; c < kPassRows * kRowChunks; c += kThreads) {
-      const int r = c / kRowChunks, k = c - r * kRowChunks;
+    v4u v[kStoreIters];
+#pragma unroll
+    for (int u = 0; u < kStoreIters; ++u) {
+      const int c = tid + u * kThreads, r = c / kRowChunks, k = c - r * kRowChunks;
+      v[u] = *reinterpret_cast<const v4u *>(stage + r * kPitch + 16 * k);
+    }
+#pragma unroll
+    for (int u = 0; u < kStoreIters; ++u) {
+      const int c = tid + u * kThreads, r = c / kRowChunks, k = c - r * kRowChunks;
       const int64_t m = m0 + pass * kPassRows + r, n = n0 + 8 * k;
-      if (m < M && n < N)
-        __builtin_nontemporal_store(*reinterpret_cast<const v4u *>(stage + r * kPitch + 16 * k),
-                                    reinterpret_cast<v4u *>(args.out_bf16 + m * N + n));
+      if (m < M && n < N) __builtin_nontemporal_store(v[u], reinterpret_cast<v4u *>(args.out_bf16 + m * N + n));
     }
   };
   // a wavefront's packed outputs pk[i][j][q4]: tile row wm*TM + 32 i + lane % 32,
@@ -614,18 +644,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
           const int row = wm * TM + i * 32 + (lane & 31);
-          const int64_t m = m0 + row;
-          const int64_t mc = m < M ? m : M - 1;
-          const float sx = args.row_scale[mc];
+          const float sx = sxr[i];
 #pragma unroll
           for (int j = 0; j < SN; ++j) {
             const int col = wn * TN + j * 32 + 4 * half;
             v16f o;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-              int64_t n = n0 + col + 8 * q4;
-              n = n < N ? n : N - 4;
-              const float4 sw = *reinterpret_cast<const float4 *>(args.col_scale + n);
+              const float4 sw = *reinterpret_cast<const float4 *>(smem + Cfg::kScaleOff + 4 * (col + 8 * q4));
               o[4 * q4 + 0] = acc_f32(acc[i][j][4 * q4 + 0]) * (sx * sw.x);
               o[4 * q4 + 1] = acc_f32(acc[i][j][4 * q4 + 1]) * (sx * sw.y);
               o[4 * q4 + 2] = acc_f32(acc[i][j][4 * q4 + 2]) * (sx * sw.z);
