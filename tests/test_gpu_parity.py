@@ -259,6 +259,16 @@ def test_forward_without_lora_is_bit_exact(m, k, n, g):
     assert np.array_equal(y, ref["y"]), f"rel-L2 {rel_l2(y, ref['y']):.3e}"
 
 
+# More tiles than CUs (two rounds: 512 tiles of 256 x 320 and of 256 x 192, 480
+# of 256 x 256), with short contractions of even and odd k-tile counts and a
+# partial last k-tile, so the oracle can check every output of the large grids.
+@pytest.mark.parametrize("m,k,n,g", [(4096, 256, 10240, 256), (4096, 384, 10240, 128), (4096, 272, 10240, 1),
+                                     (8192, 128, 3072, 64), (8192, 256, 3840, 256)])
+def test_forward_two_rounds_of_tiles_bit_exact(m, k, n, g):
+    y, ref = forward_case(m, k, n, g, seed=m + k + n)
+    assert np.array_equal(y, ref["y"]), f"rel-L2 {rel_l2(y, ref['y']):.3e}"
+
+
 @pytest.mark.parametrize("g,rank,scale", [(64, 32, 1.0), (128, 32, 1.0), (256, 16, 2.0), (128, 64, 0.5),
                                           (64, 128, 0.25)])
 def test_forward_with_lora(g, rank, scale):
