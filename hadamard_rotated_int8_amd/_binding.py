@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.sdnq_attention_workspace_bytes.restype = sz
     L.sdnq_attention_workspace_offset.argtypes = [i64, i64, i64, i64, i64, i64, i32]
     L.sdnq_attention_workspace_offset.restype = sz
+    L.sdnq_attention_set_handover_polls.argtypes = [ctypes.c_uint32]
+    L.sdnq_attention_set_handover_polls.restype = ctypes.c_int
     L.sdnq_status_string.argtypes = [ctypes.c_int]
     L.sdnq_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -443,3 +445,13 @@ def sdnq_attention_int8(q, k, v, is_causal: bool = False, scale: float | None = 
                                      float(scale), int(bool(smooth_k)), int(hadamard_group), _ptr(o), _ptr(ws),
                                      ws.numel(), _stream(q.device)), "sdnq_attention_int8")
     return o
+
+
+# default bound of sdnq_attention_int8's shared-tile wait (the header's SDNQ_ATTENTION_HANDOVER_POLLS)
+SDNQ_ATTENTION_HANDOVER_POLLS = 16777216
+
+
+def sdnq_attention_set_handover_polls(polls: int) -> None:
+    """Bound of sdnq_attention_int8's shared-tile wait for later calls, in polls
+    (0: give up before the first poll; SDNQ_ATTENTION_HANDOVER_POLLS: the default)."""
+    _check(lib().sdnq_attention_set_handover_polls(int(polls)), "sdnq_attention_set_handover_polls")

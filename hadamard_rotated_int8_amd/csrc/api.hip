@@ -736,4 +736,9 @@ sdnq_status_t sdnq_attention_int8(const uint16_t *q, const uint16_t *k, const ui
                                         scale, smooth_k != 0, hadamard_group, out, workspace, (hipStream_t)stream));
 }
 
+sdnq_status_t sdnq_attention_set_handover_polls(uint32_t polls) {
+  set_attention_handover_polls(polls);
+  return SDNQ_OK;
+}
+
 }  // extern "C"

@@ -422,8 +422,13 @@ struct AttnSplit {
   uint32_t *flags;    // [1 + 2 tiles]
   int64_t tiles;      // query tiles x heads x batch
   int64_t per;        // key tiles per workgroup
+  uint32_t polls;     // bound of the hand-over wait (polls of about 64 clocks); 0: give up at once
 };
-constexpr int kSpinLimit = 1 << 24;  // polls of about 64 clocks: about a second
+constexpr uint32_t kSpinLimit = SDNQ_ATTENTION_HANDOVER_POLLS;  // about a second
+// The hand-over wait's bound for the launches that follow; a test lowers it to
+// make the wait give up, so that the status word's path runs with every kernel
+// still exiting normally.
+std::atomic<uint32_t> handover_polls{kSpinLimit};
 constexpr int kSegFull = 0, kSegHead = 1, kSegTail = 2;
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -688,14 +693,14 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(const int8_t *__restri
       // workgroup.  The wait is bounded all the same, so no wavefront can spin
       // forever; running out marks the call's status word.
       if (tid == 0) {
-        int spin = 0;
-        while (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          if (++spin == kSpinLimit) {
-            __hip_atomic_store(split.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
+        bool ok = split.polls > 0;
+        for (uint32_t spin = 0; ok && __hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;) {
+          if (++spin >= split.polls)
+            ok = false;
+          else
+            __builtin_amdgcn_s_sleep(2);
         }
+        if (!ok) __hip_atomic_store(split.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
       const v2u ml = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_ml, ml_off, 0, kSc1));
@@ -920,6 +925,7 @@ hipError_t attention_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
     sp.flags = pa.flags;
     sp.tiles = tiles;
     sp.per = (tiles * nkt + slots - 1) / slots;  // >= nkt since tiles > slots
+    sp.polls = handover_polls.load(std::memory_order_relaxed);
     hipLaunchKernelGGL((attn_fwd_kernel<D, false, true>), dim3((unsigned)slots), dim3(256), 0, s, qc, qs, kc, ks, vt,
                        (int)hq, (int)hkv, sq, sk, sl, out, sp);
     return hipGetLastError();
@@ -930,6 +936,8 @@ hipError_t attention_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
 }
 
 }  // namespace
+
+void set_attention_handover_polls(uint32_t polls) { handover_polls.store(polls, std::memory_order_relaxed); }
 
 size_t attention_workspace_bytes(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d) {
   return attn_layout(bsz, hq, hkv, sq, sk, d).total;

@@ -389,6 +389,16 @@ size_t sdnq_attention_workspace_bytes(int64_t batch, int64_t heads_q, int64_t he
 size_t sdnq_attention_workspace_offset(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t seq_q,
                                        int64_t seq_k, int64_t head_dim, int32_t which);
 
+/* Test hook for the status word above: the bound of the shared-tile wait, in polls
+ * of about 64 clocks, for sdnq_attention_int8 calls enqueued after this one, in
+ * this process, on every device.  The default is SDNQ_ATTENTION_HANDOVER_POLLS
+ * (about a second); pass it to restore.  With 0 the wait gives up before its
+ * first poll: every shared tile is finished with whatever its partner's share
+ * holds by then and the status word is set, while every kernel still exits
+ * normally.  Always SDNQ_OK. */
+#define SDNQ_ATTENTION_HANDOVER_POLLS 16777216u
+sdnq_status_t sdnq_attention_set_handover_polls(uint32_t polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -349,3 +349,9 @@ def test_noalloc_forward_validation():
     assert f(m=8192, k=8192 + 256) == WORKSPACE                       # more than 64 MiB of codes
     assert h.SDNQ_NOALLOC_SCRATCH_BYTES == 64 << 20
     assert f"((size_t)64 << 20)" in open(HEADER).read()
+
+
+def test_handover_bound_constant_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "sdnq_hip.h")).read()
+    m = re.search(r"#define SDNQ_ATTENTION_HANDOVER_POLLS (\d+)u", text)
+    assert m and int(m.group(1)) == h.SDNQ_ATTENTION_HANDOVER_POLLS

@@ -240,6 +240,51 @@ def test_attention_repeat_runs_are_bit_identical(heads, causal):
         assert not diff.any().item(), f"{int(diff.any(-1).sum().item())} rows differ between runs"
 
 
+def test_attention_handover_give_up_is_flagged():
+    """The shared-tile wait bounded from the host.  With a bound of 0 the waiting
+    workgroup gives up before its first poll: every call must set the status word,
+    and every launch still ends.  With a bound of 1 it gives up only if its
+    partner's share is not yet published: each call's output is the normal call's
+    bit for bit, or its status word is set.  The default bound, restored, gives the
+    normal output and a clear status word."""
+    b, heads, s, d = 1, 24, 4608, 128  # 864 query tiles on 768 resident workgroups: shared tiles
+    g = torch.Generator(device=DEV).manual_seed(99)
+    q = torch.randn((b, heads, s, d), device=DEV, generator=g).to(torch.bfloat16)
+    k = torch.randn((b, heads, s, d), device=DEV, generator=g).to(torch.bfloat16)
+    v = torch.randn((b, heads, s, d), device=DEV, generator=g).to(torch.bfloat16)
+    ws = torch.empty(h.sdnq_attention_workspace_bytes(b, heads, heads, s, s, d), dtype=torch.uint8, device=DEV)
+    so = h.sdnq_attention_workspace_offset(b, heads, heads, s, s, d, 5)
+
+    def status():
+        return int(ws[so: so + 4].cpu().numpy().view(np.uint32)[0])
+
+    normal = h.sdnq_attention_int8(q, k, v, False, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert status() == 0
+    flagged = 0
+    try:
+        h.sdnq_attention_set_handover_polls(0)
+        for _ in range(2):
+            h.sdnq_attention_int8(q, k, v, False, workspace=ws)
+            torch.cuda.synchronize()
+            assert status() != 0, "a wait that gave up left the status word clear"
+        h.sdnq_attention_set_handover_polls(1)
+        for _ in range(3):
+            out = h.sdnq_attention_int8(q, k, v, False, workspace=ws)
+            torch.cuda.synchronize()
+            st = status()
+            same = torch.equal(out.view(torch.int16), normal.view(torch.int16))
+            assert st != 0 or same, "output changed without a status"
+            flagged += st != 0
+    finally:
+        h.sdnq_attention_set_handover_polls(h.SDNQ_ATTENTION_HANDOVER_POLLS)
+    say(f"    one-poll bound: {flagged} of 3 calls flagged")
+    out = h.sdnq_attention_int8(q, k, v, False, workspace=ws)
+    torch.cuda.synchronize()
+    assert status() == 0
+    assert torch.equal(out.view(torch.int16), normal.view(torch.int16))
+
+
 def stress_rows(d, n, seed):
     """n rows of d values: the quantizer's edge cases (as the linear layer's stress
     rows, with the large channel kept at 1e15 so that scores stay finite), then
