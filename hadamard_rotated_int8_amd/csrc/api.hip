@@ -22,6 +22,9 @@ int device_cu_count() {
   }
   return n;
 }
+// bound of attn.hip's split-tile hand-over wait for later launches (0: give up
+// at once)
+void set_attention_handover_polls(uint32_t polls);
 }  // namespace sdnq
 
 namespace {

@@ -144,8 +144,6 @@ hipError_t launch_svd_quantize_weight(const uint16_t *w, int64_t n, int64_t k, i
 // status word (uint32) at the six offsets attention_workspace_offsets() returns,
 // then scratch.
 size_t attention_workspace_bytes(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d);
-// bound of the split-tile hand-over wait for later launches (0: give up at once)
-void set_attention_handover_polls(uint32_t polls);
 void attention_workspace_offsets(int64_t bsz, int64_t hq, int64_t hkv, int64_t sq, int64_t sk, int64_t d,
                                  size_t *offsets);
 hipError_t launch_attention_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t bsz, int64_t hq,
