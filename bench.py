@@ -519,7 +519,7 @@ def main():
                 vend[p, j] = e0.elapsed_time(e1) / n_char
         vendor_ms = np.median(vend, axis=0)
         del wt
-    except (RuntimeError, AttributeError) as e:  # not available on this build
+    except (RuntimeError, AttributeError) as e:  # torch without the int8 matmul
         vendor_note = f"torch._int_mm unavailable: {e}"
     else:
         vendor_note = ("torch._int_mm (hipBLASLt) on the same int8 operands, int32 out (no scales or bf16 "
