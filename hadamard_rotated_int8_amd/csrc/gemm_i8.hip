@@ -44,6 +44,8 @@
 // Workgroups are dispatched round-robin over the 8 XCDs; the block index is
 // remapped so that each XCD walks a contiguous run of tiles, ordered in groups
 // of 4 tile-rows, which keeps the tiles sharing A and B rows in one L2.
+#include <type_traits>
+
 #include "sdnq_internal.hpp"
 
 namespace sdnq {
@@ -453,7 +455,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
     // step's MFMAs (about 1 % on the MLP GEMMs).
     constexpr int T = SM * SN;
     constexpr bool kByHand = !kLoraStaged && DIAG == 0;
-    for (int kt = 0; kt < nk; ++kt) {
+    auto ktile = [&](int kt, auto with_loads) {
+      constexpr bool kLoads = decltype(with_loads)::value;
       read_frags(kt, 1, f1);
       mfma_all(f0);
       sched(0, SM + SN, T);
@@ -472,14 +475,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         };
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-          if (u < LPW) load_slot(kt + 2, u);
+          if (kLoads && u < LPW) load_slot(kt + 2, u);
           if (u < SM + SN) read_one(u);
           const int i = u / SN, j = u % SN;
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int u = T; u < LPW; ++u) load_slot(kt + 2, u);
+        for (int u = T; u < LPW; ++u)
+          if (kLoads) load_slot(kt + 2, u);
 #pragma unroll
         for (int u = T; u < SM + SN; ++u) read_one(u);
       } else {
@@ -488,6 +492,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmArgs args, int
         mfma_all(f1);
         sched(LPW, SM + SN, T);
       }
+    };
+    if constexpr (kByHand) {
+      // The last two k-tiles would only load zeros past K into the free stage:
+      // they run as a copy of the loop body without the loads.
+      int kt = 0;
+      for (; kt < nk - 2; ++kt) ktile(kt, std::true_type{});
+      for (; kt < nk; ++kt) ktile(kt, std::false_type{});
+    } else {
+      for (int kt = 0; kt < nk; ++kt) ktile(kt, std::true_type{});
     }
   }
   // Forward epilogue without LoRA: the tile's row and column scales are fetched
